@@ -1,0 +1,606 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU evaluation of join-agg einsum
+ * specs over tensor relations.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * library; it parses specs, lays out blocks and rounds to bfloat16 by itself.
+ *
+ * Source: "Every Kernel Is a Join: Automatic Multi-GPU Parallelism for AI
+ * Computations in Einsummable" (Ding et al.).
+ *   - Def. 3.1  tensor type: per index a half-open interval [lower, upper).
+ *   - Def. 3.2  tiling: index sets cover the tensor and are pairwise disjoint.
+ *   - Sec. 1 / Sec. 3.2  tensor relation: a set of (sub_tensor_key, sub_tensor)
+ *               pairs; the key is the tensor type of the sub-tensor.
+ *   - Def. 3.6  join-agg spec; Def. 3.7 implementation = join, aggregate with
+ *               an associative and commutative op, recompose.
+ *   - Sec. 3.3  one function specification per combination of intervals.
+ * Everything is computed in IEEE double.  SUM accumulates in double, MAX is
+ * exact, and rounding to the stored type happens once, at the end, in
+ * oracle_round().
+ *
+ * Readings of points the page leaves open (each one is listed with the rest
+ * of the design notes):
+ *   - blocking of an index of extent n into k blocks: block extent
+ *     e = ceil(n/k); block kappa covers [kappa*e, min((kappa+1)*e, n)); a
+ *     blocking whose last block would be empty is rejected.
+ *   - storage of a relation: tuples in row-major order of the block
+ *     coordinates, in the relation's own letter order; each block dense and
+ *     row-major over the padded extents e; padding holds +0.
+ *   - join-list order: by output tuple id, then by the block coordinates of
+ *     the reduced letters, row-major in order of first appearance in the spec.
+ *   - causal letters (s, t): the join keeps a combination only when some
+ *     element with t <= s lies in it, and inside f every term with t > s is
+ *     dropped; an output element whose own s, t have t > s is defined as 0.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+#include <stdio.h>
+
+#define OR_MAX_IN 3
+#define OR_OK 0
+#define OR_BAD_SPEC -1
+#define OR_BAD_SHAPE -2
+#define OR_BAD_BLOCKING -3
+#define OR_UNSUPPORTED -4
+
+/* elementwise functions g applied to the joined values before aggregation */
+enum { G_MUL = 0, G_IDENT = 1, G_SQUARE = 2, G_EXP_SUB = 3, G_EXP_SUB_DIV = 4,
+       G_RMS_SCALE = 5, G_SILU_MUL = 6, G_ADD = 7 };
+/* aggregation (the page's associative, commutative combine) */
+enum { AGG_NONE = 0, AGG_SUM = 1, AGG_MAX = 2 };
+
+typedef struct {
+  int n_in;
+  char in[OR_MAX_IN][27];
+  int in_len[OR_MAX_IN];
+  char out[27];
+  int out_len;
+  char order[27];   /* every letter once, in order of first appearance */
+  int n_letters;
+  char reduced[27]; /* letters absent from the output, first-appearance order */
+  int n_reduced;
+} ospec;
+
+static int letter_ok(char c) { return c >= 'a' && c <= 'z'; }
+
+/* "ab,bc->ac": up to three inputs, lower-case letters, no letter twice in
+ * one operand, every output letter present in some input. */
+static int parse_spec(const char *s, ospec *p) {
+  memset(p, 0, sizeof(*p));
+  const char *arrow = strstr(s, "->");
+  if (!arrow) return OR_BAD_SPEC;
+  int cur = 0, len = 0;
+  for (const char *c = s; c < arrow; ++c) {
+    if (*c == ',') {
+      if (len == 0) return OR_BAD_SPEC;
+      p->in[cur][len] = 0; p->in_len[cur] = len;
+      if (++cur >= OR_MAX_IN) return OR_BAD_SPEC;
+      len = 0;
+    } else if (letter_ok(*c)) {
+      if (len >= 26) return OR_BAD_SPEC;
+      p->in[cur][len++] = *c;
+    } else {
+      return OR_BAD_SPEC;
+    }
+  }
+  if (len == 0) return OR_BAD_SPEC;
+  p->in[cur][len] = 0; p->in_len[cur] = len;
+  p->n_in = cur + 1;
+  for (const char *c = arrow + 2; *c; ++c) {
+    if (!letter_ok(*c) || p->out_len >= 26) return OR_BAD_SPEC;
+    p->out[p->out_len++] = *c;
+  }
+  p->out[p->out_len] = 0;
+  /* no repeated letter inside one operand */
+  for (int j = 0; j <= p->n_in; ++j) {
+    const char *o = j < p->n_in ? p->in[j] : p->out;
+    int n = (int)strlen(o);
+    for (int a = 0; a < n; ++a)
+      for (int b = a + 1; b < n; ++b)
+        if (o[a] == o[b]) return OR_BAD_SPEC;
+  }
+  for (int j = 0; j < p->n_in; ++j)
+    for (int a = 0; a < p->in_len[j]; ++a)
+      if (!strchr(p->order, p->in[j][a])) p->order[p->n_letters++] = p->in[j][a];
+  for (int a = 0; a < p->out_len; ++a)
+    if (!strchr(p->order, p->out[a])) return OR_BAD_SPEC; /* output letter from nowhere */
+  for (int a = 0; a < p->n_letters; ++a)
+    if (!strchr(p->out, p->order[a])) p->reduced[p->n_reduced++] = p->order[a];
+  return OR_OK;
+}
+
+static double apply_g(int g, int n_in, const double *x, double beta, double eps) {
+  switch (g) {
+    case G_MUL: { double r = 1.0; for (int j = 0; j < n_in; ++j) r *= x[j]; return r; }
+    case G_IDENT: return x[0];
+    case G_SQUARE: return x[0] * x[0];
+    case G_EXP_SUB: return exp(x[0] - x[1]);
+    case G_EXP_SUB_DIV: return exp(x[0] - x[1]) / x[2];
+    case G_RMS_SCALE: return x[0] / sqrt(x[1] * beta + eps) * x[2];
+    case G_SILU_MUL: return x[0] / (1.0 + exp(-x[0])) * x[1];
+    case G_ADD: { double r = 0.0; for (int j = 0; j < n_in; ++j) r += x[j]; return r; }
+  }
+  return NAN;
+}
+
+static int g_arity_ok(int g, int n_in) {
+  switch (g) {
+    case G_MUL: case G_ADD: return n_in >= 1;
+    case G_IDENT: case G_SQUARE: return n_in == 1;
+    case G_EXP_SUB: case G_SILU_MUL: return n_in == 2;
+    case G_EXP_SUB_DIV: case G_RMS_SCALE: return n_in == 3;
+  }
+  return 0;
+}
+
+static int check_common(const ospec *p, int g, int agg, int causal_s, int causal_t) {
+  if (agg < AGG_NONE || agg > AGG_MAX) return OR_UNSUPPORTED;
+  if (!g_arity_ok(g, p->n_in)) return OR_UNSUPPORTED;
+  if (agg == AGG_NONE && p->n_reduced) return OR_UNSUPPORTED; /* nothing to combine with */
+  if ((causal_s >= 0) != (causal_t >= 0)) return OR_BAD_SPEC;
+  if (causal_s >= 0) {
+    if (!strchr(p->order, 'a' + causal_s) || !strchr(p->order, 'a' + causal_t)) return OR_BAD_SPEC;
+    if (causal_s == causal_t) return OR_BAD_SPEC;
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dense form: out[o] = alpha * AGG_{r} g(in_1[..], ..., in_n[..]).           */
+/* ------------------------------------------------------------------------ */
+
+/* Evaluates the outputs whose row-major flat indices are listed in `idx`
+ * (or all of them when idx == NULL, n_out then being the output size).
+ * Inputs are dense, row-major in each operand's own letter order.  The
+ * result is left unrounded in double. */
+int oracle_dense(const char *spec, int g, int agg, double alpha, double beta, double eps,
+                 int causal_s, int causal_t, const int64_t *ext26,
+                 const double *const *ins, const int64_t *idx, int64_t n_out, double *out) {
+  ospec p;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if ((rc = check_common(&p, g, agg, causal_s, causal_t))) return rc;
+  for (int a = 0; a < p.n_letters; ++a)
+    if (ext26[p.order[a] - 'a'] < 1) return OR_BAD_SHAPE;
+
+  /* strides of each letter in each input (0 when the input lacks it) */
+  int64_t in_stride[OR_MAX_IN][26];
+  memset(in_stride, 0, sizeof(in_stride));
+  for (int j = 0; j < p.n_in; ++j) {
+    int64_t s = 1;
+    for (int a = p.in_len[j] - 1; a >= 0; --a) {
+      in_stride[j][p.in[j][a] - 'a'] = s;
+      s *= ext26[p.in[j][a] - 'a'];
+    }
+  }
+  int64_t out_total = 1;
+  for (int a = 0; a < p.out_len; ++a) out_total *= ext26[p.out[a] - 'a'];
+  int64_t red_total = 1;
+  for (int a = 0; a < p.n_reduced; ++a) red_total *= ext26[p.reduced[a] - 'a'];
+  if (!idx) n_out = out_total;
+
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t q = 0; q < n_out; ++q) {
+    int64_t flat = idx ? idx[q] : q;
+    int64_t coord[26];
+    memset(coord, 0, sizeof(coord));
+    int64_t rem = flat;
+    for (int a = p.out_len - 1; a >= 0; --a) {
+      int64_t e = ext26[p.out[a] - 'a'];
+      coord[p.out[a] - 'a'] = rem % e;
+      rem /= e;
+    }
+    double acc = agg == AGG_MAX ? -INFINITY : 0.0;
+    int any = 0;
+    for (int64_t r = 0; r < red_total; ++r) {
+      int64_t rr = r;
+      for (int a = p.n_reduced - 1; a >= 0; --a) {
+        int64_t e = ext26[p.reduced[a] - 'a'];
+        coord[p.reduced[a] - 'a'] = rr % e;
+        rr /= e;
+      }
+      if (causal_s >= 0 && coord[causal_t] > coord[causal_s]) continue;
+      double x[OR_MAX_IN];
+      for (int j = 0; j < p.n_in; ++j) {
+        int64_t off = 0;
+        for (int a = 0; a < p.in_len[j]; ++a) off += coord[p.in[j][a] - 'a'] * in_stride[j][p.in[j][a] - 'a'];
+        x[j] = ins[j][off];
+      }
+      double v = apply_g(g, p.n_in, x, beta, eps);
+      if (agg == AGG_MAX) { if (!any || v > acc) acc = v; }
+      else acc += v;
+      any = 1;
+    }
+    /* an element with no surviving term: 0 (the empty sum; under the causal
+     * mask also for maps and maxima) */
+    out[q] = any ? alpha * acc : 0.0;
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Relation geometry (Def. 3.1 intervals, padded blocks).                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int r;
+  char letters[27];
+  int64_t n[26];      /* extents, by position in `letters` */
+  int64_t k[26];      /* block counts */
+  int64_t e[26];      /* padded block extents */
+  int64_t n_tuples;
+  int64_t block_elems;
+} orel;
+
+static int make_rel(const char *letters, const int64_t *ext26, const int32_t *nblk26, orel *R) {
+  memset(R, 0, sizeof(*R));
+  R->r = (int)strlen(letters);
+  if (R->r > 26) return OR_BAD_SPEC;
+  strcpy(R->letters, letters);
+  R->n_tuples = 1; R->block_elems = 1;
+  for (int a = 0; a < R->r; ++a) {
+    int L = letters[a] - 'a';
+    if (L < 0 || L >= 26) return OR_BAD_SPEC;
+    R->n[a] = ext26[L];
+    R->k[a] = nblk26[L];
+    if (R->n[a] < 1 || R->k[a] < 1 || R->k[a] > R->n[a]) return OR_BAD_BLOCKING;
+    R->e[a] = (R->n[a] + R->k[a] - 1) / R->k[a];
+    if ((R->k[a] - 1) * R->e[a] >= R->n[a]) return OR_BAD_BLOCKING; /* empty last block */
+    R->n_tuples *= R->k[a];
+    R->block_elems *= R->e[a];
+  }
+  return OR_OK;
+}
+
+/* block coordinates of tuple t (row-major over the relation's letters) */
+static void tuple_coords(const orel *R, int64_t t, int64_t *kappa) {
+  for (int a = R->r - 1; a >= 0; --a) { kappa[a] = t % R->k[a]; t /= R->k[a]; }
+}
+
+static int64_t lo_of(const orel *R, int a, int64_t kappa) { return kappa * R->e[a]; }
+static int64_t hi_of(const orel *R, int a, int64_t kappa) {
+  int64_t h = (kappa + 1) * R->e[a];
+  return h < R->n[a] ? h : R->n[a];
+}
+
+int oracle_relation_elems(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *elems) {
+  orel R;
+  int rc = make_rel(letters, ext26, nblk26, &R);
+  if (rc) return rc;
+  *elems = R.n_tuples * R.block_elems;
+  return OR_OK;
+}
+
+/* dense (row-major) -> relation storage, padding = +0; elements of `esz` bytes */
+int oracle_to_relation(const void *dense, int esz, const char *letters, const int64_t *ext26,
+                       const int32_t *nblk26, void *rel) {
+  orel R;
+  int rc = make_rel(letters, ext26, nblk26, &R);
+  if (rc) return rc;
+  memset(rel, 0, (size_t)(R.n_tuples * R.block_elems) * (size_t)esz);
+  int64_t dstride[26], s = 1;
+  for (int a = R.r - 1; a >= 0; --a) { dstride[a] = s; s *= R.n[a]; }
+  for (int64_t t = 0; t < R.n_tuples; ++t) {
+    int64_t kappa[26];
+    tuple_coords(&R, t, kappa);
+    for (int64_t w = 0; w < R.block_elems; ++w) {
+      int64_t rem = w, doff = 0, valid = 1;
+      for (int a = R.r - 1; a >= 0; --a) {
+        int64_t x = kappa[a] * R.e[a] + rem % R.e[a];
+        rem /= R.e[a];
+        if (x >= R.n[a]) { valid = 0; break; }
+        doff += x * dstride[a];
+      }
+      if (valid)
+        memcpy((char *)rel + (size_t)(t * R.block_elems + w) * esz, (const char *)dense + (size_t)doff * esz, esz);
+    }
+  }
+  return OR_OK;
+}
+
+/* relation storage -> dense (row-major); padding is dropped */
+int oracle_from_relation(const void *rel, int esz, const char *letters, const int64_t *ext26,
+                         const int32_t *nblk26, void *dense) {
+  orel R;
+  int rc = make_rel(letters, ext26, nblk26, &R);
+  if (rc) return rc;
+  int64_t dstride[26], s = 1;
+  for (int a = R.r - 1; a >= 0; --a) { dstride[a] = s; s *= R.n[a]; }
+  for (int64_t t = 0; t < R.n_tuples; ++t) {
+    int64_t kappa[26];
+    tuple_coords(&R, t, kappa);
+    for (int64_t w = 0; w < R.block_elems; ++w) {
+      int64_t rem = w, doff = 0, valid = 1;
+      for (int a = R.r - 1; a >= 0; --a) {
+        int64_t x = kappa[a] * R.e[a] + rem % R.e[a];
+        rem /= R.e[a];
+        if (x >= R.n[a]) { valid = 0; break; }
+        doff += x * dstride[a];
+      }
+      if (valid)
+        memcpy((char *)dense + (size_t)doff * esz, (const char *)rel + (size_t)(t * R.block_elems + w) * esz, esz);
+    }
+  }
+  return OR_OK;
+}
+
+/* Repartition: densify the source, then re-block into the destination's
+ * letter order and blocking.  Works on raw element bytes, so it is exact. */
+int oracle_repartition(const void *src, int esz, const char *src_letters, const int32_t *src_nblk26,
+                       void *dst, const char *dst_letters, const int32_t *dst_nblk26,
+                       const int64_t *ext26) {
+  if (strlen(src_letters) != strlen(dst_letters)) return OR_BAD_SHAPE;
+  for (const char *c = src_letters; *c; ++c)
+    if (!strchr(dst_letters, *c)) return OR_BAD_SHAPE;
+  int64_t n = 1;
+  for (const char *c = src_letters; *c; ++c) n *= ext26[*c - 'a'];
+  char *dense_src = malloc((size_t)n * esz), *dense_dst = malloc((size_t)n * esz);
+  if (!dense_src || !dense_dst) { free(dense_src); free(dense_dst); return OR_BAD_SHAPE; }
+  int rc = oracle_from_relation(src, esz, src_letters, ext26, src_nblk26, dense_src);
+  if (!rc) {
+    /* permute the dense tensor from the source letter order to the destination's */
+    int r = (int)strlen(src_letters);
+    int64_t sstride[26], s = 1;
+    for (int a = r - 1; a >= 0; --a) { sstride[src_letters[a] - 'a'] = s; s *= ext26[src_letters[a] - 'a']; }
+    for (int64_t i = 0; i < n; ++i) {
+      int64_t rem = i, soff = 0;
+      for (int a = r - 1; a >= 0; --a) {
+        int64_t e = ext26[dst_letters[a] - 'a'];
+        soff += (rem % e) * sstride[dst_letters[a] - 'a'];
+        rem /= e;
+      }
+      memcpy(dense_dst + (size_t)i * esz, dense_src + (size_t)soff * esz, esz);
+    }
+    rc = oracle_to_relation(dense_dst, esz, dst_letters, ext26, dst_nblk26, dst);
+  }
+  free(dense_src); free(dense_dst);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Relational form, Def. 3.7 taken literally.                                */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t out_id;
+  int64_t red_key;          /* row-major rank of the reduced letters' block coords */
+  int64_t in_id[OR_MAX_IN];
+} combo;
+
+static int cmp_combo(const void *a, const void *b) {
+  const combo *x = a, *y = b;
+  if (x->out_id != y->out_id) return x->out_id < y->out_id ? -1 : 1;
+  if (x->red_key != y->red_key) return x->red_key < y->red_key ? -1 : 1;
+  return 0;
+}
+
+/* Join step: nested loops over the cross product of the input tuple sets,
+ * keeping each combination whose key intervals agree on every letter the
+ * inputs share (and, with causal letters, that holds some t <= s).
+ * Returns a malloc'd array of combos sorted in canonical order. */
+static int join(const ospec *p, const orel *in, const orel *out, const int64_t *ext26, const int32_t *nblk26,
+                int causal_s, int causal_t, combo **res, int64_t *n_res) {
+  int64_t total = 1;
+  for (int j = 0; j < p->n_in; ++j) total *= in[j].n_tuples;
+  combo *list = malloc(sizeof(combo) * (size_t)(total ? total : 1));
+  if (!list) return OR_BAD_SHAPE;
+  int64_t n = 0;
+  for (int64_t c = 0; c < total; ++c) {
+    int64_t tid[OR_MAX_IN], rem = c;
+    for (int j = p->n_in - 1; j >= 0; --j) { tid[j] = rem % in[j].n_tuples; rem /= in[j].n_tuples; }
+    /* interval of every letter as fixed by the first input that holds it */
+    int64_t lo[26], hi[26];
+    int have[26];
+    memset(have, 0, sizeof(have));
+    int keep = 1;
+    for (int j = 0; j < p->n_in && keep; ++j) {
+      int64_t kappa[26];
+      tuple_coords(&in[j], tid[j], kappa);
+      for (int a = 0; a < in[j].r; ++a) {
+        int L = in[j].letters[a] - 'a';
+        int64_t l = lo_of(&in[j], a, kappa[a]), h = hi_of(&in[j], a, kappa[a]);
+        if (!have[L]) { lo[L] = l; hi[L] = h; have[L] = 1; }
+        else if (lo[L] != l || hi[L] != h) { keep = 0; break; }
+      }
+    }
+    if (!keep) continue;
+    if (causal_s >= 0 && lo[causal_t] > hi[causal_s] - 1) continue;
+    /* output key: the intervals of the output letters, as a tuple id */
+    int64_t out_id = 0;
+    for (int a = 0; a < out->r; ++a) {
+      int L = out->letters[a] - 'a';
+      out_id = out_id * out->k[a] + lo[L] / out->e[a];
+    }
+    int64_t red_key = 0;
+    for (int a = 0; a < p->n_reduced; ++a) {
+      int L = p->reduced[a] - 'a';
+      int64_t e = (ext26[L] + nblk26[L] - 1) / nblk26[L];
+      red_key = red_key * nblk26[L] + lo[L] / e;
+    }
+    list[n].out_id = out_id;
+    list[n].red_key = red_key;
+    for (int j = 0; j < OR_MAX_IN; ++j) list[n].in_id[j] = j < p->n_in ? tid[j] : -1;
+    ++n;
+  }
+  qsort(list, (size_t)n, sizeof(combo), cmp_combo);
+  *res = list;
+  *n_res = n;
+  return OR_OK;
+}
+
+static int build_rels(const ospec *p, const int64_t *ext26, const int32_t *nblk26, orel *in, orel *out) {
+  int rc;
+  for (int j = 0; j < p->n_in; ++j)
+    if ((rc = make_rel(p->in[j], ext26, nblk26, &in[j]))) return rc;
+  return make_rel(p->out, ext26, nblk26, out);
+}
+
+/* Join list only: entries [out_id, in_id_0, ..., in_id_{n-1}] (int64), in
+ * canonical order.  Pass list == NULL to get the count. */
+int oracle_join_list(const char *spec, const int64_t *ext26, const int32_t *nblk26, int causal_s,
+                     int causal_t, int64_t *list, int64_t cap, int64_t *n_entries) {
+  ospec p;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if ((causal_s >= 0) != (causal_t >= 0)) return OR_BAD_SPEC;
+  orel in[OR_MAX_IN], out;
+  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  combo *c;
+  int64_t n;
+  if ((rc = join(&p, in, &out, ext26, nblk26, causal_s, causal_t, &c, &n))) return rc;
+  *n_entries = n;
+  if (list) {
+    if (cap < n) { free(c); return OR_BAD_SHAPE; }
+    for (int64_t i = 0; i < n; ++i) {
+      list[i * (p.n_in + 1)] = c[i].out_id;
+      for (int j = 0; j < p.n_in; ++j) list[i * (p.n_in + 1) + 1 + j] = c[i].in_id[j];
+    }
+  }
+  free(c);
+  return OR_OK;
+}
+
+/* Relational evaluation.  Inputs are relation buffers (double values) in the
+ * operands' letter orders under `nblk26`; the output relation buffer gets the
+ * aggregated blocks, +0 in its padding, unrounded.  `present` (optional, one
+ * byte per output tuple) marks the output keys that the join produced. */
+int oracle_relational(const char *spec, int g, int agg, double alpha, double beta, double eps,
+                      int causal_s, int causal_t, const int64_t *ext26, const int32_t *nblk26,
+                      const double *const *in_rel, double *out_rel, uint8_t *present) {
+  ospec p;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if ((rc = check_common(&p, g, agg, causal_s, causal_t))) return rc;
+  orel in[OR_MAX_IN], out;
+  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  combo *c;
+  int64_t n;
+  if ((rc = join(&p, in, &out, ext26, nblk26, causal_s, causal_t, &c, &n))) return rc;
+
+  memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
+  if (present) memset(present, 0, (size_t)out.n_tuples);
+  double *agg_blk = malloc(sizeof(double) * (size_t)out.block_elems);
+  uint8_t *touched = malloc((size_t)out.block_elems);
+
+  for (int64_t first = 0; first < n;) {
+    int64_t last = first;
+    while (last < n && c[last].out_id == c[first].out_id) ++last;
+    /* (2) Aggregate: combine the outputs of all combinations of this key */
+    for (int64_t ci = first; ci < last; ++ci) {
+      /* the combination's intervals per letter */
+      int64_t lo[26], hi[26];
+      for (int j = 0; j < p.n_in; ++j) {
+        int64_t kappa[26];
+        tuple_coords(&in[j], c[ci].in_id[j], kappa);
+        for (int a = 0; a < in[j].r; ++a) {
+          lo[in[j].letters[a] - 'a'] = lo_of(&in[j], a, kappa[a]);
+          hi[in[j].letters[a] - 'a'] = hi_of(&in[j], a, kappa[a]);
+        }
+      }
+      /* (1) Join: f on the projected blocks, i.e. the dense form restricted to
+       * the valid index ranges of this combination's intervals */
+      int64_t out_box = 1, red_box = 1;
+      for (int a = 0; a < out.r; ++a) out_box *= hi[out.letters[a] - 'a'] - lo[out.letters[a] - 'a'];
+      for (int a = 0; a < p.n_reduced; ++a) red_box *= hi[p.reduced[a] - 'a'] - lo[p.reduced[a] - 'a'];
+      int64_t kout[26];
+      tuple_coords(&out, c[ci].out_id, kout);
+      for (int64_t o = 0; o < out_box; ++o) {
+        int64_t x[26], rem = o;
+        for (int a = out.r - 1; a >= 0; --a) {
+          int L = out.letters[a] - 'a';
+          x[L] = lo[L] + rem % (hi[L] - lo[L]);
+          rem /= hi[L] - lo[L];
+        }
+        /* position inside the padded output block */
+        int64_t w = 0;
+        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - kout[a] * out.e[a]);
+        double acc = agg == AGG_MAX ? -INFINITY : 0.0;
+        int any = 0;
+        for (int64_t r = 0; r < red_box; ++r) {
+          int64_t rr = r;
+          for (int a = p.n_reduced - 1; a >= 0; --a) {
+            int L = p.reduced[a] - 'a';
+            x[L] = lo[L] + rr % (hi[L] - lo[L]);
+            rr /= hi[L] - lo[L];
+          }
+          if (causal_s >= 0 && x[causal_t] > x[causal_s]) continue;
+          double v[OR_MAX_IN];
+          for (int j = 0; j < p.n_in; ++j) {
+            int64_t kappa[26], off = 0;
+            tuple_coords(&in[j], c[ci].in_id[j], kappa);
+            for (int a = 0; a < in[j].r; ++a) {
+              int L = in[j].letters[a] - 'a';
+              off = off * in[j].e[a] + (x[L] - kappa[a] * in[j].e[a]);
+            }
+            v[j] = in_rel[j][c[ci].in_id[j] * in[j].block_elems + off];
+          }
+          double gv = apply_g(g, p.n_in, v, beta, eps);
+          if (agg == AGG_MAX) { if (!any || gv > acc) acc = gv; }
+          else acc += gv;
+          any = 1;
+        }
+        if (ci == first) { agg_blk[w] = any ? acc : (agg == AGG_MAX ? -INFINITY : 0.0); touched[w] = (uint8_t)any; }
+        else if (any) {
+          if (agg == AGG_MAX) { if (!touched[w] || acc > agg_blk[w]) agg_blk[w] = acc; }
+          else agg_blk[w] += acc;
+          touched[w] = 1;
+        }
+      }
+    }
+    /* (3) Recompose: the aggregated block takes its place in the output */
+    int64_t kout[26], out_box = 1;
+    tuple_coords(&out, c[first].out_id, kout);
+    for (int a = 0; a < out.r; ++a) out_box *= hi_of(&out, a, kout[a]) - lo_of(&out, a, kout[a]);
+    for (int64_t o = 0; o < out_box; ++o) {
+      int64_t rem = o, w = 0, sub[26];
+      for (int a = out.r - 1; a >= 0; --a) {
+        int64_t ext = hi_of(&out, a, kout[a]) - lo_of(&out, a, kout[a]);
+        sub[a] = rem % ext;
+        rem /= ext;
+      }
+      for (int a = 0; a < out.r; ++a) w = w * out.e[a] + sub[a];
+      double v = touched[w] ? alpha * agg_blk[w] : 0.0;
+      out_rel[c[first].out_id * out.block_elems + w] = v;
+    }
+    if (present) present[c[first].out_id] = 1;
+    first = last;
+  }
+  free(agg_blk); free(touched); free(c);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rounding to the stored type, once, round-to-nearest-even.                 */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16: 8 significant bits, the exponent range of binary32.  Rounds the
+ * exact double to the nearest representable value, ties to even, written
+ * from the definition (scale so the quantum is 1, round, scale back). */
+static double round_bf16(double x) {
+  if (isnan(x) || isinf(x) || x == 0.0) return x;
+  int ex;
+  frexp(x, &ex);                 /* |x| = m * 2^ex, 0.5 <= m < 1 */
+  int q = ex - 8;                /* quantum of an 8-bit significand */
+  if (q < -133) q = -133;        /* subnormal quantum: 2^-126 * 2^-7 */
+  double r = ldexp(nearbyint(ldexp(x, -q)), q);
+  if (fabs(r) >= ldexp(1.0, 128)) r = copysign(INFINITY, x); /* beyond the largest finite */
+  return r;
+}
+
+/* dtype 0 = float32, 1 = bfloat16; rounds n doubles in place */
+void oracle_round(double *x, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i) x[i] = dtype == 1 ? round_bf16(x[i]) : (double)(float)x[i];
+}
+
+/* padded block extents of a relation, in its letter order */
+int oracle_block_shape(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *e) {
+  orel R;
+  int rc = make_rel(letters, ext26, nblk26, &R);
+  if (rc) return rc;
+  for (int a = 0; a < R.r; ++a) e[a] = R.e[a];
+  return OR_OK;
+}

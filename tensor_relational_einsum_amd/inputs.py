@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs and workload recipes.
+
+This module is shared by the tests, the benchmark and the smoke check: it
+only draws random numbers and describes workloads (shapes, blockings, spec
+strings).  It holds none of the method's arithmetic and imports neither the
+HIP binding nor the oracle.
+
+Random numbers: ``numpy.random.Generator(PCG64)`` seeded from
+``SeedSequence(1000 + config)``, one spawned child stream per tensor, in the
+order the tensors are listed in each recipe.  uniform[-1, 1) and N(0, sigma^2)
+are drawn in float64, cast to float32, and rounded to bfloat16 (torch's CPU
+cast, round-to-nearest-even) where the tensor is bfloat16.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+def streams(seed: int, n: int):
+    ss = np.random.SeedSequence(seed)
+    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(n)]
+
+
+def draw(gen, shape, dist: str, dtype: str, sigma: float = 1.0, mean: float = 0.0) -> torch.Tensor:
+    """One tensor from one stream. dist: 'uniform' (on [-1,1)), 'normal'."""
+    shape = tuple(int(s) for s in shape)
+    if dist == "uniform":
+        x = gen.uniform(-1.0, 1.0, size=shape)
+    elif dist == "normal":
+        x = gen.standard_normal(size=shape) * sigma + mean
+    else:
+        raise ValueError(dist)
+    t = torch.from_numpy(x).to(torch.float32)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return t
+
+
+@dataclass
+class Step:
+    """One join-agg spec of a workload chain (names only, no arithmetic)."""
+    out: str
+    spec: str
+    ins: list
+    g: str = "mul"
+    agg: str = "sum"
+    out_dtype: str = "f32"
+    blockings: dict = field(default_factory=dict)
+    alpha: float = 1.0
+    beta: float = 0.0
+    eps: float = 0.0
+    causal: tuple | None = None
+
+
+@dataclass
+class Relayout:
+    """Re-block a relation (letters and blocking of the destination)."""
+    out: str
+    src: str
+    letters: str
+    blockings: dict
+
+
+@dataclass
+class Workload:
+    name: str
+    extents: dict
+    tensors: list            # (name, letters, dist, dtype, sigma, mean, blockings)
+    chain: list              # Step / Relayout in execution order
+    seed: int
+
+
+def matmul_256(n: int = 256, nb: int = 4) -> Workload:
+    """'ij,jk->ik', I=J=K=256 fp32, each index in 4 blocks, uniform[-1,1)."""
+    ext = {"i": n, "j": n, "k": n}
+    blk = {"i": nb, "j": nb, "k": nb}
+    return Workload(
+        name=f"matmul_ij_jk_{n}_fp32_blk{nb}", extents=ext,
+        tensors=[("A", "ij", "uniform", "f32", 1.0, 0.0, blk), ("B", "jk", "uniform", "f32", 1.0, 0.0, blk)],
+        chain=[Step("C", "ij,jk->ik", ["A", "B"], blockings=blk)], seed=1001)
+
+
+def repartition_2d(n: int = 8192) -> Workload:
+    """n x n bf16 N(0,1), {i8, j1} row blocks -> {i1, j8} column blocks."""
+    ext = {"i": n, "j": n}
+    return Workload(
+        name=f"repartition_ij_{n}_bf16_i8j1_to_i1j8", extents=ext,
+        tensors=[("X", "ij", "normal", "bf16", 1.0, 0.0, {"i": 8, "j": 1})],
+        chain=[Relayout("Y", "X", "ij", {"i": 1, "j": 8})], seed=1002)
+
+
+def repartition_4d(shape=(32, 128, 64, 64)) -> Workload:
+    """'abcd' bf16 N(0,1) {a4,b8,c1,d1} -> 'acbd' {a1,b1,c4,d2}."""
+    ext = dict(zip("abcd", shape))
+    return Workload(
+        name="repartition_abcd_32x128x64x64_bf16_to_acbd", extents=ext,
+        tensors=[("X", "abcd", "normal", "bf16", 1.0, 0.0, {"a": 4, "b": 8, "c": 1, "d": 1})],
+        chain=[Relayout("Y", "X", "acbd", {"a": 1, "b": 1, "c": 4, "d": 2})], seed=1002)
+
+
+def attention_chain(b=4, h=32, s=2048, d=128, nb=16) -> Workload:
+    """Unfused attention as join-aggs: QK^T, row MAX, row SUM of exp, normalize, PV.
+    No 1/sqrt(d) scale; Q, K, V bf16 N(0,1); s and t each in `nb` blocks."""
+    ext = {"b": b, "h": h, "s": s, "t": s, "d": d}
+    blk = {"b": 1, "h": 1, "s": nb, "t": nb, "d": 1}
+    tens = [("Q", "bhsd", "normal", "bf16", 1.0, 0.0, blk), ("K", "bhtd", "normal", "bf16", 1.0, 0.0, blk),
+            ("V", "bhtd", "normal", "bf16", 1.0, 0.0, blk)]
+    chain = [
+        Step("S", "bhsd,bhtd->bhst", ["Q", "K"], "mul", "sum", "f32", blk),
+        Step("M", "bhst->bhs", ["S"], "ident", "max", "f32", blk),
+        Step("L", "bhst,bhs->bhs", ["S", "M"], "exp_sub", "sum", "f32", blk),
+        Step("P", "bhst,bhs,bhs->bhst", ["S", "M", "L"], "exp_sub_div", "none", "bf16", blk),
+        Step("O", "bhst,bhtd->bhsd", ["P", "V"], "mul", "sum", "f32", blk),
+    ]
+    return Workload(name=f"attention_chain_b{b}_h{h}_s{s}_d{d}_bf16_st{nb}", extents=ext, tensors=tens,
+                    chain=chain, seed=1003)
+
+
+def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8) -> Workload:
+    """LLaMA-7B-shaped decoder block, every op a join-agg spec.
+
+    x (fp32) -> RMSNorm*g1 -> Q,K,V -> relayout to head-major -> causal
+    attention (scale 1/sqrt(d)) -> relayout back -> Wo -> +x -> RMSNorm*g2 ->
+    gate, up -> silu(gate)*up -> down -> +residual.  No RoPE, no biases.
+    """
+    ext = {"b": b, "s": s, "t": s, "h": hid, "q": heads, "d": d, "f": ffn}
+    proj = {"b": 1, "s": s_blk, "t": s_blk, "h": h_blk, "q": q_blk, "d": 1}
+    att = {"b": 1, "q": 1, "s": s_blk, "t": s_blk, "d": 1}
+    ffb = {"b": 1, "s": s_blk, "h": h_blk, "f": f_blk}
+    w = 0.02
+    tens = [
+        ("x", "bsh", "normal", "f32", 1.0, 0.0, proj),
+        ("g1", "h", "normal", "bf16", w, 1.0, proj),
+        ("Wq", "hqd", "normal", "bf16", w, 0.0, proj),
+        ("Wk", "hqd", "normal", "bf16", w, 0.0, proj),
+        ("Wv", "hqd", "normal", "bf16", w, 0.0, proj),
+        ("Wo", "qdh", "normal", "bf16", w, 0.0, proj),
+        ("g2", "h", "normal", "bf16", w, 1.0, ffb),
+        ("Wg", "hf", "normal", "bf16", w, 0.0, ffb),
+        ("Wu", "hf", "normal", "bf16", w, 0.0, ffb),
+        ("Wd", "fh", "normal", "bf16", w, 0.0, ffb),
+    ]
+    inv_h = 1.0 / hid
+    c = ("s", "t")
+    chain = [
+        Step("ss1", "bsh->bs", ["x"], "square", "sum", "f32", proj),
+        Step("r1", "bsh,bs,h->bsh", ["x", "ss1", "g1"], "rms_scale", "none", "bf16", proj, beta=inv_h, eps=1e-6),
+        Step("Qp", "bsh,hqd->bsqd", ["r1", "Wq"], "mul", "sum", "bf16", proj),
+        Step("Kp", "bth,hqd->btqd", ["r1", "Wk"], "mul", "sum", "bf16", proj),
+        Step("Vp", "bth,hqd->btqd", ["r1", "Wv"], "mul", "sum", "bf16", proj),
+        Relayout("Q", "Qp", "bqsd", att),
+        Relayout("K", "Kp", "bqtd", att),
+        Relayout("V", "Vp", "bqtd", att),
+        Step("S", "bqsd,bqtd->bqst", ["Q", "K"], "mul", "sum", "f32", att, alpha=1.0 / math.sqrt(d), causal=c),
+        Step("M", "bqst->bqs", ["S"], "ident", "max", "f32", att, causal=c),
+        Step("L", "bqst,bqs->bqs", ["S", "M"], "exp_sub", "sum", "f32", att, causal=c),
+        Step("P", "bqst,bqs,bqs->bqst", ["S", "M", "L"], "exp_sub_div", "none", "bf16", att, causal=c),
+        Step("Oh", "bqst,bqtd->bqsd", ["P", "V"], "mul", "sum", "bf16", att, causal=c),
+        Relayout("O", "Oh", "bsqd", proj),
+        Step("A", "bsqd,qdh->bsh", ["O", "Wo"], "mul", "sum", "f32", proj),
+        Step("x2", "bsh,bsh->bsh", ["x", "A"], "add", "none", "f32", proj),
+        Step("ss2", "bsh->bs", ["x2"], "square", "sum", "f32", ffb),
+        Step("r2", "bsh,bs,h->bsh", ["x2", "ss2", "g2"], "rms_scale", "none", "bf16", ffb, beta=inv_h, eps=1e-6),
+        Step("G", "bsh,hf->bsf", ["r2", "Wg"], "mul", "sum", "f32", ffb),
+        Step("U", "bsh,hf->bsf", ["r2", "Wu"], "mul", "sum", "f32", ffb),
+        Step("H", "bsf,bsf->bsf", ["G", "U"], "silu_mul", "none", "bf16", ffb),
+        Step("D", "bsf,fh->bsh", ["H", "Wd"], "mul", "sum", "f32", ffb),
+        Step("y", "bsh,bsh->bsh", ["x2", "D"], "add", "none", "f32", ffb),
+    ]
+    return Workload(name=f"llama7b_block_b{b}_s{s}_bf16", extents=ext, tensors=tens, chain=chain, seed=1004)
+
+
+def multi_index(a=96, b=300, c=64, d=48, e=1000, blk=(5, 7, 4, 3, 6)) -> Workload:
+    """'abcd,cde->abe' fp32 uniform[-1,1), padded tail blocks, SUM over c, d."""
+    ext = dict(zip("abcde", (a, b, c, d, e)))
+    bl = dict(zip("abcde", blk))
+    return Workload(
+        name=f"contract_abcd_cde_{a}x{b}x{c}x{d}x{e}_fp32_blk" + "".join(map(str, blk)), extents=ext,
+        tensors=[("A", "abcd", "uniform", "f32", 1.0, 0.0, bl), ("B", "cde", "uniform", "f32", 1.0, 0.0, bl)],
+        chain=[Step("C", "abcd,cde->abe", ["A", "B"], "mul", "sum", "f32", bl)], seed=1005)
+
+
+def generate(w: Workload) -> dict:
+    """Dense CPU tensors for every input of a workload, in recipe order."""
+    gens = streams(w.seed, len(w.tensors))
+    out = {}
+    for gen, (name, letters, dist, dtype, sigma, mean, _) in zip(gens, w.tensors):
+        shape = [w.extents[c] for c in letters]
+        out[name] = draw(gen, shape, dist, dtype, sigma, mean)
+    return out
+
+
+def tensor_info(w: Workload, name: str):
+    for t in w.tensors:
+        if t[0] == name:
+            return t
+    raise KeyError(name)
