@@ -1,0 +1,180 @@
+/*
+ * jagg.h -- C ABI of the join-agg einsum executor for AMD MI355X (gfx950).
+ *
+ * A tensor is held as a *tensor relation*: a set of (sub_tensor_key,
+ * sub_tensor) tuples, one per block of a blocking of every index ("Every
+ * Kernel Is a Join", Ding et al., Sec. 1 and Sec. 3.2; keys are tensor types,
+ * Def. 3.1).  An einsum spec is executed as a join-agg spec (Def. 3.6) by the
+ * three steps of Def. 3.7: join the input tuples whose keys agree on every
+ * shared index, apply a block function to each joined tuple, combine the
+ * results of equal output key with an associative and commutative
+ * aggregation, and recompose.  Re-tiling a relation (the exchange step of
+ * Sec. 5.3, on one GPU: decompose into atoms and recompose) is
+ * jagg_repartition.
+ *
+ * Conventions shared by every entry point
+ *  - Letters: an index is named by one lower-case letter 'a'..'z'.
+ *  - Blocking (Sec. 3.3, one interval count per index): an index of extent n
+ *    cut into k blocks has block extent e = ceil(n/k); block kappa covers
+ *    [kappa*e, min((kappa+1)*e, n)).  A blocking whose last block would be
+ *    empty ((k-1)*e >= n) is rejected with JAGG_E_BLOCKING.
+ *  - Storage of a relation (caller-owned device memory): tuples in row-major
+ *    order of their block coordinates, in the relation's letter order; each
+ *    tuple is a dense row-major block over the padded extents e, so a
+ *    relation occupies prod(k) * prod(e) elements.  Positions beyond an
+ *    index's extent (padding) hold +0: every producer in this library writes
+ *    them, and the kernels rely on it.
+ *  - Ownership: the caller allocates and frees all device memory (relation
+ *    storage, workspaces, join lists).  The library never allocates device
+ *    memory; it owns only the host-side metadata behind jagg_ctx and
+ *    jagg_relation handles.
+ *  - Streams: every launch goes, asynchronously, onto the stream given to
+ *    jagg_ctx_create.  A context is used by one host thread at a time.
+ *  - Errors: argument, shape, blocking and workspace errors, and spec forms
+ *    the kernels do not implement, are found before anything is launched
+ *    and reported by a negative status; jagg_last_error() gives the detail.
+ *    There is no fallback path: an unsupported spec is an error.
+ */
+#ifndef JAGG_H
+#define JAGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JAGG_OK = 0,
+  JAGG_E_INVALID = -1,     /* malformed argument: NULL handle, bad spec string, bad enum */
+  JAGG_E_SHAPE = -2,       /* extents or letters disagree, buffer too small */
+  JAGG_E_BLOCKING = -3,    /* bad block count, or the out relation's blocking differs */
+  JAGG_E_UNSUPPORTED = -4, /* a spec form the kernels do not implement */
+  JAGG_E_WORKSPACE = -5,   /* workspace missing or smaller than jagg_einsum_workspace() */
+  JAGG_E_DEVICE = -6       /* a HIP call or kernel launch failed */
+} jagg_status;
+
+typedef enum { JAGG_F32 = 0, JAGG_BF16 = 1 } jagg_dtype;
+
+/* The aggregation of Def. 3.7 step (2); both are associative and commutative. */
+typedef enum { JAGG_AGG_NONE = 0, JAGG_AGG_SUM = 1, JAGG_AGG_MAX = 2 } jagg_agg;
+
+/* Block function g applied, element by element, to the joined input values
+ * x0, x1, x2 before aggregation.  With g = MUL and agg = SUM the spec is a
+ * contraction (the matmul of Example 3.4 is 'ij,jk->ik'). */
+typedef enum {
+  JAGG_G_MUL = 0,         /* x0 * x1 (* x2)                          */
+  JAGG_G_IDENT = 1,       /* x0                                      */
+  JAGG_G_SQUARE = 2,      /* x0 * x0                                 */
+  JAGG_G_EXP_SUB = 3,     /* exp(x0 - x1)                            */
+  JAGG_G_EXP_SUB_DIV = 4, /* exp(x0 - x1) / x2                       */
+  JAGG_G_RMS_SCALE = 5,   /* x0 / sqrt(x1 * beta + eps) * x2         */
+  JAGG_G_SILU_MUL = 6,    /* x0 / (1 + exp(-x0)) * x1                */
+  JAGG_G_ADD = 7          /* x0 + x1 (+ x2)                          */
+} jagg_g;
+
+/* One join-agg spec.  out[o] = alpha * AGG over the reduced letters of
+ * g(x0, ...).  `einsum` is "in0,in1,...->out" (1 to 3 inputs); operand
+ * letters bind to the relations' dimensions by position, so a relation
+ * created with letters "bsh" may appear in a spec as "bth" provided the
+ * extents and block counts agree.  A letter may not repeat inside one
+ * operand, and every output letter must occur in some input.
+ * causal_s / causal_t: 0 for none, else two letters (s, t) of the spec; then
+ * only elements with t <= s take part: the join drops every tuple
+ * combination whose t-block starts after its s-block ends, terms with t > s
+ * are left out of the aggregation, and an output element whose own t > s is
+ * written as 0.  A causal pair needs s and t of equal extent and block
+ * count. */
+typedef struct {
+  const char *einsum;
+  jagg_g g;
+  jagg_agg agg;
+  jagg_dtype out_dtype;
+  float alpha; /* scales the aggregated result; 1 for none */
+  float beta;  /* parameter of JAGG_G_RMS_SCALE */
+  float eps;   /* parameter of JAGG_G_RMS_SCALE */
+  char causal_s;
+  char causal_t;
+} jagg_spec;
+
+typedef struct jagg_ctx jagg_ctx;
+typedef struct jagg_relation jagg_relation;
+
+/* Context bound to one device and one stream (a hipStream_t, borrowed: the
+ * library never creates, synchronises or destroys it; NULL = the default
+ * stream).  Makes `device` current on the calling thread. */
+jagg_status jagg_ctx_create(int device, void *hip_stream, jagg_ctx **out);
+jagg_status jagg_ctx_destroy(jagg_ctx *ctx);
+
+/* Padded storage size in bytes of a relation with `rank` letters (see the
+ * storage convention above); host only. */
+jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, const int32_t *nblocks,
+                                jagg_dtype dtype, size_t *bytes);
+
+/* Describes a relation over caller-owned device memory `dev_buf` of
+ * `buf_bytes` bytes (at least jagg_relation_bytes(), 16-byte aligned).
+ * letters[i] names dimension i, extents[i] >= 1 its extent, nblocks[i] its
+ * block count.  Host metadata only; nothing is launched, the buffer is not
+ * touched.  Limits: at most 8 letters, at most 2^31 elements. */
+jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64_t *extents,
+                                 const int32_t *nblocks, jagg_dtype dtype, void *dev_buf, size_t buf_bytes,
+                                 jagg_relation **out);
+/* Frees the metadata only, never dev_buf. */
+jagg_status jagg_relation_destroy(jagg_relation *rel);
+
+/* Repartition (Sec. 5.3): writes into `dst` the tensor held by `src`,
+ * re-tiled to dst's blocking and letter order.  src and dst must carry the
+ * same set of letters with equal extents and the same dtype; their order
+ * and blocking may differ.  Every element of dst, padding (+0) included, is
+ * written; the copy is bit-exact.  src and dst must not overlap. */
+jagg_status jagg_repartition(jagg_ctx *ctx, const jagg_relation *src, jagg_relation *dst);
+
+/* Bytes of device workspace jagg_einsum needs for this call (join list,
+ * key counts, and room for re-blocking any input whose blocking differs
+ * from `blockings`). `blockings` gives the block count of every letter of
+ * the spec, in order of first appearance in the einsum string. */
+jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in,
+                                  int n_in, const int32_t *blockings, size_t *bytes);
+
+/* Executes one join-agg spec (Def. 3.7) on the ctx stream:
+ *   (0) an input whose blocking differs from `blockings` is repartitioned
+ *       into the workspace first;
+ *   (1) join: the join-enumeration kernel lists, for every output key, the
+ *       input tuples that agree on every shared letter;
+ *   (2) each joined tuple goes through g and is aggregated into its output
+ *       key, accumulation in fp32 (MFMA for contractions);
+ *   (3) recompose: the output relation `out` (letters of the spec's output,
+ *       blocked by `blockings`, dtype spec->out_dtype) is written in place,
+ *       padding +0.
+ * Inputs are bf16 or f32 (a contraction needs both inputs of one dtype).
+ * `workspace` (device, 256-byte aligned) holds at least
+ * jagg_einsum_workspace() bytes and is clobbered.  `out` must not overlap an
+ * input. */
+jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                        const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes);
+
+/* Number of output keys and reduced-letter combinations per key of the join
+ * of this spec under `blockings`; host only. */
+jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter,
+                            const int32_t *blockings, int64_t *n_keys, int64_t *per_key);
+
+/* Runs only the join-enumeration kernel (step 1) into caller device memory:
+ * `dev_list` receives int32 [n_keys][per_key][1 + n_in] and `dev_counts`
+ * int32 [n_keys].  For output key o the first dev_counts[o] slots hold its
+ * joined tuples as [out_tuple, in_tuple_0, ...], ordered by the block
+ * coordinates of the reduced letters (row-major, in order of first
+ * appearance); the remaining slots of the key are filled with -1.  Without a
+ * causal pair every count is per_key.  `extents_by_letter` gives every
+ * letter's extent, in the order of `blockings`. */
+jagg_status jagg_join_list(jagg_ctx *ctx, const jagg_spec *spec, const int64_t *extents_by_letter,
+                           const int32_t *blockings, int32_t *dev_list, int32_t *dev_counts);
+
+const char *jagg_status_str(jagg_status s);
+/* Detail of the last error on this context (empty string if none). */
+const char *jagg_last_error(const jagg_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JAGG_H */

@@ -1,0 +1,1018 @@
+// abi.cpp -- the C ABI of include/jagg.h: argument checking, relation
+// geometry, and the planner that turns one join-agg spec into kernel
+// launches on the context's stream.
+//
+// "Every Kernel Is a Join" (Ding et al.):
+//   Def. 3.1 / Sec. 3.2  a block key is a tensor type, one interval per index;
+//   Sec. 3.3             interval counts per index give the spec's blocking;
+//   Def. 3.6 / 3.7       join, aggregate, recompose;
+//   Sec. 5.3             repartition over the overlay (atoms) of two blockings.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/jagg.h"
+#include "jagg_internal.h"
+
+using namespace jagg;
+
+struct jagg_ctx {
+  int device;
+  hipStream_t stream;
+  std::string err;
+  bool trace;
+  bool debug_sync;
+};
+
+struct jagg_relation {
+  jagg_ctx *ctx;
+  int r;
+  char letters[kMaxLetters + 1];
+  int64_t n[kMaxLetters];
+  int32_t k[kMaxLetters];
+  int64_t e[kMaxLetters];
+  jagg_dtype dt;
+  void *buf;
+  size_t bytes;
+  int64_t n_tuples;
+  int64_t be;  // elements per block
+};
+
+namespace {
+
+jagg_status fail(jagg_ctx *ctx, jagg_status s, const char *fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+  }
+  return s;
+}
+
+int esz_of(jagg_dtype d) { return d == JAGG_BF16 ? 2 : 4; }
+
+// ------------------------------------------------------------ geometry
+// Fills block extents, tuple count and block size; checks the blocking.
+jagg_status geometry(jagg_ctx *ctx, int r, const int64_t *n, const int32_t *k, int64_t *e, int64_t *n_tuples,
+                     int64_t *be) {
+  int64_t nt = 1, b = 1;
+  for (int i = 0; i < r; ++i) {
+    if (n[i] < 1) return fail(ctx, JAGG_E_SHAPE, "extent %d of dimension %d must be >= 1", int(n[i]), i);
+    if (k[i] < 1 || k[i] > n[i])
+      return fail(ctx, JAGG_E_BLOCKING, "block count %d of dimension %d is outside [1, %lld]", k[i], i,
+                  (long long)n[i]);
+    e[i] = (n[i] + k[i] - 1) / k[i];
+    if ((k[i] - 1) * e[i] >= n[i])
+      return fail(ctx, JAGG_E_BLOCKING, "dimension %d: %lld cut into %d blocks of %lld leaves the last empty", i,
+                  (long long)n[i], k[i], (long long)e[i]);
+    nt *= k[i];
+    b *= e[i];
+  }
+  *n_tuples = nt;
+  *be = b;
+  return JAGG_OK;
+}
+
+// tuple-id weight of dimension p (row-major over block coordinates)
+int64_t tuple_w(const jagg_relation &R, int p) {
+  int64_t w = 1;
+  for (int q = p + 1; q < R.r; ++q) w *= R.k[q];
+  return w;
+}
+// in-block stride of dimension p
+int64_t inblock_s(const jagg_relation &R, int p) {
+  int64_t s = 1;
+  for (int q = p + 1; q < R.r; ++q) s *= R.e[q];
+  return s;
+}
+
+// ------------------------------------------------------------ spec parsing
+struct Spec {
+  int n_in = 0;
+  std::string in[kMaxIn];
+  std::string out;
+  std::string order;    // letters in order of first appearance
+  std::string reduced;  // letters absent from the output, same order
+};
+
+jagg_status parse(jagg_ctx *ctx, const char *s, Spec &p) {
+  if (!s) return fail(ctx, JAGG_E_INVALID, "NULL einsum string");
+  const char *arrow = strstr(s, "->");
+  if (!arrow) return fail(ctx, JAGG_E_INVALID, "einsum '%s' has no '->'", s);
+  std::string cur;
+  for (const char *c = s; c <= arrow; ++c) {
+    if (c == arrow || *c == ',') {
+      if (cur.empty()) return fail(ctx, JAGG_E_INVALID, "einsum '%s' has an empty operand", s);
+      if (p.n_in >= kMaxIn) return fail(ctx, JAGG_E_UNSUPPORTED, "einsum '%s': more than %d inputs", s, kMaxIn);
+      p.in[p.n_in++] = cur;
+      cur.clear();
+    } else if (*c >= 'a' && *c <= 'z') {
+      cur.push_back(*c);
+    } else {
+      return fail(ctx, JAGG_E_INVALID, "einsum '%s': unexpected character '%c'", s, *c);
+    }
+  }
+  for (const char *c = arrow + 2; *c; ++c) {
+    if (*c < 'a' || *c > 'z') return fail(ctx, JAGG_E_INVALID, "einsum '%s': unexpected character '%c'", s, *c);
+    p.out.push_back(*c);
+  }
+  for (int j = 0; j <= p.n_in; ++j) {
+    const std::string &o = j < p.n_in ? p.in[j] : p.out;
+    if (int(o.size()) > kMaxLetters)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "einsum '%s': operand with more than %d letters", s, kMaxLetters);
+    for (size_t a = 0; a < o.size(); ++a)
+      for (size_t b = a + 1; b < o.size(); ++b)
+        if (o[a] == o[b]) return fail(ctx, JAGG_E_INVALID, "einsum '%s': letter '%c' repeats in an operand", s, o[a]);
+  }
+  for (int j = 0; j < p.n_in; ++j)
+    for (char c : p.in[j])
+      if (p.order.find(c) == std::string::npos) p.order.push_back(c);
+  for (char c : p.out)
+    if (p.order.find(c) == std::string::npos)
+      return fail(ctx, JAGG_E_INVALID, "einsum '%s': output letter '%c' is in no input", s, c);
+  for (char c : p.order)
+    if (p.out.find(c) == std::string::npos) p.reduced.push_back(c);
+  return JAGG_OK;
+}
+
+bool g_arity_ok(int g, int n) {
+  switch (g) {
+    case JAGG_G_MUL:
+    case JAGG_G_ADD: return n >= 1;
+    case JAGG_G_IDENT:
+    case JAGG_G_SQUARE: return n == 1;
+    case JAGG_G_EXP_SUB:
+    case JAGG_G_SILU_MUL: return n == 2;
+    case JAGG_G_EXP_SUB_DIV:
+    case JAGG_G_RMS_SCALE: return n == 3;
+  }
+  return false;
+}
+
+jagg_status check_spec(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p) {
+  if (sp->g < JAGG_G_MUL || sp->g > JAGG_G_ADD) return fail(ctx, JAGG_E_INVALID, "unknown g %d", int(sp->g));
+  if (sp->agg < JAGG_AGG_NONE || sp->agg > JAGG_AGG_MAX) return fail(ctx, JAGG_E_INVALID, "unknown aggregation");
+  if (sp->out_dtype != JAGG_F32 && sp->out_dtype != JAGG_BF16) return fail(ctx, JAGG_E_INVALID, "unknown out dtype");
+  if (!g_arity_ok(sp->g, p.n_in))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "g %d does not take %d inputs", int(sp->g), p.n_in);
+  if (sp->agg == JAGG_AGG_NONE && !p.reduced.empty())
+    return fail(ctx, JAGG_E_UNSUPPORTED, "letters '%s' are reduced but the aggregation is NONE", p.reduced.c_str());
+  if ((sp->causal_s != 0) != (sp->causal_t != 0))
+    return fail(ctx, JAGG_E_INVALID, "a causal pair needs both letters");
+  if (sp->causal_s) {
+    if (sp->causal_s == sp->causal_t) return fail(ctx, JAGG_E_INVALID, "causal letters must differ");
+    if (p.order.find(sp->causal_s) == std::string::npos || p.order.find(sp->causal_t) == std::string::npos)
+      return fail(ctx, JAGG_E_INVALID, "causal letters are not in the spec");
+    if (p.out.find(sp->causal_s) == std::string::npos)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "causal letter s must be an output letter");
+  }
+  return JAGG_OK;
+}
+
+// per-letter extents and block counts of a spec (index: letter - 'a')
+struct LetterInfo {
+  int64_t n[26];
+  int32_t k[26];
+};
+
+// ------------------------------------------------------------ join
+// Fills the join kernel's arguments from letters, extents and block counts.
+jagg_status plan_join(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p, const LetterInfo &L, JoinArgs &a) {
+  memset(&a, 0, sizeof(a));
+  a.n_in = p.n_in;
+  a.n_out = int(p.out.size());
+  a.n_red = int(p.reduced.size());
+  int64_t n_keys = 1, per_key = 1;
+  for (int i = 0; i < a.n_out; ++i) {
+    const int c = p.out[i] - 'a';
+    a.out_k[i] = L.k[c];
+    a.out_div[i] = make_fastdiv(uint32_t(L.k[c]));
+    n_keys *= L.k[c];
+  }
+  for (int i = 0; i < a.n_red; ++i) {
+    const int c = p.reduced[i] - 'a';
+    a.red_k[i] = L.k[c];
+    a.red_div[i] = make_fastdiv(uint32_t(L.k[c]));
+    per_key *= L.k[c];
+  }
+  if (n_keys * per_key > (int64_t(1) << 30))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "join of %lld tuples is too large", (long long)(n_keys * per_key));
+  for (int j = 0; j < p.n_in; ++j) {
+    const std::string &lt = p.in[j];
+    for (size_t q = 0; q < lt.size(); ++q) {
+      int64_t w = 1;
+      for (size_t q2 = q + 1; q2 < lt.size(); ++q2) w *= L.k[lt[q2] - 'a'];
+      const size_t io = p.out.find(lt[q]);
+      if (io != std::string::npos) a.w_out[j][io] = w;
+      const size_t ir = p.reduced.find(lt[q]);
+      if (ir != std::string::npos) a.w_red[j][ir] = w;
+    }
+  }
+  a.per_key = int32_t(per_key);
+  a.n_keys = n_keys;
+  if (sp->causal_s) {
+    const int cs = sp->causal_s - 'a', ct = sp->causal_t - 'a';
+    if (L.n[cs] != L.n[ct] || L.k[cs] != L.k[ct])
+      return fail(ctx, JAGG_E_UNSUPPORTED, "causal letters need equal extents and block counts");
+    a.causal = 1;
+    a.s_red = 0;
+    a.s_idx = int32_t(p.out.find(sp->causal_s));
+    const size_t to = p.out.find(sp->causal_t);
+    a.t_red = to == std::string::npos;
+    a.t_idx = int32_t(a.t_red ? p.reduced.find(sp->causal_t) : to);
+    a.e_s = (L.n[cs] + L.k[cs] - 1) / L.k[cs];
+    a.e_t = (L.n[ct] + L.k[ct] - 1) / L.k[ct];
+    a.n_s = L.n[cs];
+  }
+  return JAGG_OK;
+}
+
+// ------------------------------------------------------------ relayout planner
+struct Dim {
+  int64_t ext, src, dst;
+  int chk;
+  int64_t xs;
+};
+
+int64_t largest_divisor_le(int64_t n, int64_t cap) {
+  for (int64_t f = std::min(n, cap); f >= 1; --f)
+    if (n % f == 0) return f;
+  return 1;
+}
+
+jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_relation &D, RelayoutArgs &a,
+                          int &vec_bytes) {
+  memset(&a, 0, sizeof(a));
+  const int r = D.r;
+  const int64_t beS = S.be, beD = D.be;
+  std::vector<Dim> kd, rd;
+  int n_chk = 0;
+  for (int p = 0; p < r; ++p) {
+    const char c = D.letters[p];
+    int q = 0;
+    while (q < S.r && S.letters[q] != c) ++q;
+    const int64_t n = D.n[p];
+    const int64_t kD = D.k[p], eD = D.e[p], eS = S.e[q];
+    const int64_t TKd = tuple_w(D, p) * beD, Ed = inblock_s(D, p);
+    const int64_t TKs = tuple_w(S, q) * beS, Es = inblock_s(S, q);
+    int slot = -1;
+    auto need_slot = [&](int64_t rl, int64_t wl, bool irr) -> jagg_status {
+      if (n_chk >= kMaxChk) return fail(ctx, JAGG_E_UNSUPPORTED, "too many padded letters");
+      slot = n_chk++;
+      a.read_lim[slot] = rl;
+      a.write_lim[slot] = wl;
+      a.irr[slot] = irr;
+      if (irr) {
+        a.irr_div[slot] = make_fastdiv(uint32_t(eS));
+        a.irr_K[slot] = TKs;
+        a.irr_E[slot] = Es;
+      }
+      return JAGG_OK;
+    };
+    jagg_status st = JAGG_OK;
+    if (eD == eS) {
+      if (kD * eD > n) st = need_slot(n, kD * eD, false);
+      kd.push_back({kD, TKs, TKd, slot, eD});
+      rd.push_back({eD, Es, Ed, slot, 1});
+    } else if (eD % eS == 0) {
+      const int64_t m = eD / eS;
+      if (kD * eD > n) st = need_slot(n, kD * eD, false);
+      kd.push_back({kD, m * TKs, TKd, slot, eD});
+      rd.push_back({m, TKs, eS * Ed, slot, eS});
+      rd.push_back({eS, Es, Ed, slot, 1});
+    } else if (eS % eD == 0) {
+      const int64_t m = eS / eD;
+      const int64_t kh = (kD + m - 1) / m;
+      if (kh * m * eD > n) st = need_slot(n, kD * eD, false);
+      kd.push_back({kh, TKs, m * TKd, slot, eS});
+      kd.push_back({m, eD * Es, TKd, slot, eD});
+      rd.push_back({eD, Es, Ed, slot, 1});
+    } else {
+      st = need_slot(n, kD * eD, true);
+      kd.push_back({kD, 0, TKd, slot, eD});
+      rd.push_back({eD, 0, Ed, slot, 1});
+    }
+    if (st != JAGG_OK) return st;
+  }
+  a.n_chk = n_chk;
+  std::vector<Dim> dims;
+  for (auto &d : kd)
+    if (d.ext > 1) dims.push_back(d);
+  for (auto &d : rd)
+    if (d.ext > 1) dims.push_back(d);
+  if (dims.empty()) dims.push_back({1, 0, 0, -1, 0});
+  // merge neighbours that walk both sides contiguously
+  for (size_t i = dims.size() - 1; i >= 1 && i < dims.size(); --i) {
+    Dim &o = dims[i - 1], &in = dims[i];
+    const bool x_ok = (o.chk == -1 && in.chk == -1) || (o.chk == in.chk && o.xs == in.ext * in.xs);
+    if (o.src == in.ext * in.src && o.dst == in.ext * in.dst && x_ok) {
+      Dim m = in;
+      m.ext = o.ext * in.ext;
+      dims[i - 1] = m;
+      dims.erase(dims.begin() + i);
+    }
+  }
+  // vector width along the innermost destination dim
+  const int esz = esz_of(D.dt);
+  const Dim &inner = dims.back();
+  int v = 16 / esz;
+  for (; v > 1; v >>= 1) {
+    bool ok = inner.dst == 1 && inner.ext % v == 0;
+    if (inner.chk >= 0 && a.irr[inner.chk]) {
+      ok = ok && a.irr_E[inner.chk] == 1 && a.irr_div[inner.chk].d % v == 0 && a.irr_K[inner.chk] % v == 0;
+    } else {
+      ok = ok && inner.src == 1;
+    }
+    if (inner.chk >= 0) ok = ok && a.read_lim[inner.chk] % v == 0 && a.write_lim[inner.chk] % v == 0;
+    for (size_t i = 0; i + 1 < dims.size(); ++i) ok = ok && dims[i].src % v == 0 && dims[i].dst % v == 0;
+    for (int c = 0; c < n_chk; ++c)
+      if (a.irr[c]) ok = ok && a.irr_K[c] % v == 0 && (a.irr_E[c] % v == 0 || (inner.chk == c));
+    if (ok) break;
+  }
+  vec_bytes = v * esz;
+  // lane dims: the vectorised inner dim, then dims that extend contiguity
+  std::vector<Dim> lane, rest(dims.begin(), dims.end() - 1);
+  int64_t lanes = 1;
+  {
+    Dim in = inner;
+    const int64_t ev = in.ext / v;
+    const int64_t f = largest_divisor_le(ev, 256);
+    Dim l = in;
+    l.ext = f;
+    lane.push_back(l);
+    lanes = f;
+    if (f < ev) {
+      Dim o = in;
+      o.ext = ev / f;
+      o.src *= f * v;
+      o.dst *= f * v;
+      o.xs *= f * v;
+      rest.push_back(o);
+    }
+  }
+  int64_t src_run = lane[0].src == 1 ? lane[0].ext * v : 0;
+  while (lanes < 256 && !rest.empty()) {
+    int pick = -1;
+    for (size_t i = 0; i < rest.size(); ++i)
+      if (src_run > 0 && rest[i].src == src_run) pick = int(i);
+    if (pick < 0) {
+      int64_t best = -1;
+      for (size_t i = 0; i < rest.size(); ++i)
+        if (best < 0 || rest[i].dst < best) {
+          best = rest[i].dst;
+          pick = int(i);
+        }
+    }
+    Dim d = rest[pick];
+    const int64_t f = largest_divisor_le(d.ext, 256 / lanes);
+    if (f <= 1) break;
+    Dim l = d;
+    l.ext = f;
+    lane.push_back(l);
+    lanes *= f;
+    if (src_run > 0 && d.src == src_run) src_run *= f;
+    if (f < d.ext) {
+      rest[pick].ext = d.ext / f;
+      rest[pick].src *= f;
+      rest[pick].dst *= f;
+      rest[pick].xs *= f;
+    } else {
+      rest.erase(rest.begin() + pick);
+    }
+  }
+  std::sort(rest.begin(), rest.end(), [](const Dim &x, const Dim &y) { return x.dst > y.dst; });
+  if (int(rest.size()) > kMaxDims || int(lane.size()) > kMaxDims)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "repartition needs too many dims");
+  int64_t n_tiles = 1;
+  for (auto &d : rest) n_tiles *= d.ext;
+  if (n_tiles >= (int64_t(1) << 32)) return fail(ctx, JAGG_E_UNSUPPORTED, "repartition too large");
+  a.n_tile = int(rest.size());
+  for (size_t i = 0; i < rest.size(); ++i) {
+    a.tile[i] = {rest[i].ext, rest[i].src, rest[i].dst, rest[i].chk, rest[i].xs, make_fastdiv(uint32_t(rest[i].ext))};
+  }
+  a.n_lane = int(lane.size());
+  for (size_t i = 0; i < lane.size(); ++i)
+    a.lane[i] = {lane[i].ext, lane[i].src, lane[i].dst, lane[i].chk, lane[i].xs, make_fastdiv(uint32_t(lane[i].ext))};
+  a.n_tiles = n_tiles;
+  a.lanes = int32_t(lanes);
+  a.src = S.buf;
+  a.dst = D.buf;
+  if (ctx->trace) {
+    fprintf(stderr, "[jagg] relayout %s -> %s: vec %dB lanes %lld tiles %lld chk %d |", S.letters, D.letters, vec_bytes,
+            (long long)lanes, (long long)n_tiles, n_chk);
+    for (auto &d : lane) fprintf(stderr, " L(%lld s%lld d%lld)", (long long)d.ext, (long long)d.src, (long long)d.dst);
+    for (auto &d : rest) fprintf(stderr, " T(%lld s%lld d%lld)", (long long)d.ext, (long long)d.src, (long long)d.dst);
+    fprintf(stderr, "\n");
+  }
+  return JAGG_OK;
+}
+
+jagg_status after_launch(jagg_ctx *ctx, hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  if (ctx->debug_sync) {
+    e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  }
+  return JAGG_OK;
+}
+
+jagg_status do_repartition(jagg_ctx *ctx, const jagg_relation &S, const jagg_relation &D) {
+  RelayoutArgs a;
+  int vb = 0;
+  jagg_status st = plan_relayout(ctx, S, D, a, vb);
+  if (st != JAGG_OK) return st;
+  return after_launch(ctx, launch_relayout(a, vb, esz_of(D.dt), ctx->stream), "relayout");
+}
+
+// ------------------------------------------------------------ einsum binding
+struct Bound {
+  Spec p;
+  LetterInfo L;
+  const jagg_relation *in[kMaxIn];
+  bool needs_reblock[kMaxIn];
+  size_t list_bytes, counts_bytes, reblock_bytes[kMaxIn], total;
+  JoinArgs join;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+jagg_status bind(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const *in, int n_in,
+                 const int32_t *blockings, Bound &b) {
+  if (!sp || !in || !blockings) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  jagg_status st = parse(ctx, sp->einsum, b.p);
+  if (st != JAGG_OK) return st;
+  if (n_in != b.p.n_in)
+    return fail(ctx, JAGG_E_INVALID, "einsum has %d inputs, %d relations given", b.p.n_in, n_in);
+  if ((st = check_spec(ctx, sp, b.p)) != JAGG_OK) return st;
+  for (int i = 0; i < 26; ++i) {
+    b.L.n[i] = 0;
+    b.L.k[i] = 0;
+  }
+  for (size_t i = 0; i < b.p.order.size(); ++i) {
+    if (blockings[i] < 1) return fail(ctx, JAGG_E_BLOCKING, "blocking of '%c' must be >= 1", b.p.order[i]);
+    b.L.k[b.p.order[i] - 'a'] = blockings[i];
+  }
+  for (int j = 0; j < n_in; ++j) {
+    const jagg_relation *R = in[j];
+    if (!R) return fail(ctx, JAGG_E_INVALID, "input %d is NULL", j);
+    b.in[j] = R;
+    if (R->r != int(b.p.in[j].size()))
+      return fail(ctx, JAGG_E_SHAPE, "input %d has %d dimensions, operand '%s' names %d", j, R->r,
+                  b.p.in[j].c_str(), int(b.p.in[j].size()));
+    b.needs_reblock[j] = false;
+    for (int q = 0; q < R->r; ++q) {
+      const int c = b.p.in[j][q] - 'a';
+      if (b.L.n[c] == 0) b.L.n[c] = R->n[q];
+      if (b.L.n[c] != R->n[q])
+        return fail(ctx, JAGG_E_SHAPE, "letter '%c' has extent %lld and %lld", 'a' + c, (long long)b.L.n[c],
+                    (long long)R->n[q]);
+      if (R->k[q] != b.L.k[c]) b.needs_reblock[j] = true;
+    }
+  }
+  // the requested blocking must be valid for every letter
+  for (char c : b.p.order) {
+    const int i = c - 'a';
+    const int64_t e = (b.L.n[i] + b.L.k[i] - 1) / b.L.k[i];
+    if (b.L.k[i] > b.L.n[i] || (b.L.k[i] - 1) * e >= b.L.n[i])
+      return fail(ctx, JAGG_E_BLOCKING, "letter '%c': %lld cut into %d blocks leaves an empty block", c,
+                  (long long)b.L.n[i], b.L.k[i]);
+  }
+  if ((st = plan_join(ctx, sp, b.p, b.L, b.join)) != JAGG_OK) return st;
+  b.list_bytes = align256(size_t(b.join.n_keys) * b.join.per_key * (1 + n_in) * 4);
+  b.counts_bytes = align256(size_t(b.join.n_keys) * 4);
+  b.total = b.list_bytes + b.counts_bytes;
+  for (int j = 0; j < n_in; ++j) {
+    b.reblock_bytes[j] = 0;
+    if (b.needs_reblock[j]) {
+      int64_t nt = 1, be = 1;
+      for (int q = 0; q < in[j]->r; ++q) {
+        const int c = b.p.in[j][q] - 'a';
+        const int64_t e = (b.L.n[c] + b.L.k[c] - 1) / b.L.k[c];
+        nt *= b.L.k[c];
+        be *= e;
+      }
+      b.reblock_bytes[j] = align256(size_t(nt * be) * esz_of(in[j]->dt));
+      b.total += b.reblock_bytes[j];
+    }
+  }
+  return JAGG_OK;
+}
+
+// ------------------------------------------------------------ map / reduce planning
+jagg_status plan_ew(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, const jagg_relation *const *ins,
+                    const jagg_relation *out, const int32_t *list, const int32_t *counts, EwArgs &a) {
+  memset(&a, 0, sizeof(a));
+  const Spec &p = b.p;
+  a.n_in = p.n_in;
+  for (int j = 0; j < p.n_in; ++j) {
+    a.in[j] = ins[j]->buf;
+    a.in_dt[j] = ins[j]->dt == JAGG_BF16;
+    a.be_in[j] = ins[j]->be;
+  }
+  a.out = out->buf;
+  a.out_dt = sp->out_dtype == JAGG_BF16;
+  a.g = sp->g;
+  a.agg = sp->agg;
+  a.alpha = sp->alpha;
+  a.beta = sp->beta;
+  a.eps = sp->eps;
+  a.list = list;
+  a.counts = counts;
+  a.per_key = b.join.per_key;
+  a.n_keys = b.join.n_keys;
+  a.r_out = int(p.out.size());
+  a.be_out = out->be;
+  a.rows_per_block = 1;
+  for (int i = 0; i < a.r_out; ++i) {
+    a.e_out[i] = out->e[i];
+    a.n_out[i] = out->n[i];
+    a.k_out[i] = out->k[i];
+    if (i < a.r_out - 1) a.rows_per_block *= out->e[i];
+  }
+  a.n_red = int(p.reduced.size());
+  for (int i = 0; i < a.n_red; ++i) {
+    const int c = p.reduced[i] - 'a';
+    a.n_red_ext[i] = b.L.n[c];
+    a.k_red[i] = b.L.k[c];
+    a.e_red[i] = (b.L.n[c] + b.L.k[c] - 1) / b.L.k[c];
+  }
+  for (int j = 0; j < p.n_in; ++j) {
+    const jagg_relation &R = *ins[j];
+    for (int q = 0; q < R.r; ++q) {
+      const char c = p.in[j][q];
+      const size_t io = p.out.find(c), ir = p.reduced.find(c);
+      if (io != std::string::npos) a.s_out[j][io] = inblock_s(R, q);
+      if (ir != std::string::npos) {
+        a.s_red[j][ir] = inblock_s(R, q);
+        if (j == 0) a.w_red0[ir] = tuple_w(R, q);
+      }
+    }
+  }
+  if (sp->causal_s) {
+    a.causal = 1;
+    a.s_red_flag = 0;
+    a.s_pos = int32_t(p.out.find(sp->causal_s));
+    const size_t to = p.out.find(sp->causal_t);
+    a.t_red_flag = to == std::string::npos;
+    a.t_pos = int32_t(a.t_red_flag ? p.reduced.find(sp->causal_t) : to);
+  }
+  a.inner_red = -1;
+  a.vec = 1;
+  if (sp->agg == JAGG_AGG_NONE) {
+    if (a.causal && (a.t_red_flag || a.t_pos != a.r_out - 1))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "a causal map needs t as the innermost output letter");
+    a.vec = (a.e_out[a.r_out - 1] % 4 == 0) ? 4 : 1;
+  } else {
+    // reduce: input 0 holds every letter, the others a subset
+    if (p.in[0].size() != p.order.size())
+      return fail(ctx, JAGG_E_UNSUPPORTED, "a reduce needs input 0 to hold every letter of the spec");
+    if (a.n_red == 0) return fail(ctx, JAGG_E_UNSUPPORTED, "SUM/MAX with no reduced letter; use NONE");
+    const char last = p.in[0].back();
+    const size_t ir = p.reduced.find(last);
+    a.inner_red = ir == std::string::npos ? -1 : int32_t(ir);
+    if (a.causal && !a.t_red_flag)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "a causal reduce needs t among the reduced letters");
+    if (a.causal && a.inner_red >= 0 && a.t_pos != a.inner_red)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "a causal row reduce needs t innermost in input 0");
+  }
+  return JAGG_OK;
+}
+
+// ------------------------------------------------------------ contraction planning
+struct Group {
+  std::string letters;  // in canonical order
+  int64_t ext = 1;
+};
+
+// Checks that `g`'s letters sit next to each other in operand `lt` in the
+// same order with nesting strides, and returns the flattened stride.
+bool group_stride(const Group &g, const std::string &lt, const jagg_relation &R, int64_t &stride) {
+  if (g.letters.empty()) {
+    stride = 0;
+    return true;
+  }
+  const size_t p0 = lt.find(g.letters[0]);
+  if (p0 == std::string::npos) return false;
+  for (size_t i = 0; i < g.letters.size(); ++i)
+    if (p0 + i >= lt.size() || lt[p0 + i] != g.letters[i]) return false;
+  stride = inblock_s(R, int(p0 + g.letters.size() - 1));
+  return true;
+}
+
+jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, const jagg_relation *const *ins,
+                          const jagg_relation *out, const int32_t *list, const int32_t *counts, ContractArgs &a,
+                          int &dtype, bool &a_kc, bool &b_kc, int &va, int &vb) {
+  memset(&a, 0, sizeof(a));
+  const Spec &p = b.p;
+  if (ins[0]->dt != ins[1]->dt) return fail(ctx, JAGG_E_UNSUPPORTED, "contraction inputs differ in dtype");
+  dtype = ins[0]->dt == JAGG_BF16;
+  int ia = 0, ib = 1;
+  Group Gb, Gm, Gn, Gk;
+  auto build = [&]() {
+    Gb = Group();
+    Gm = Group();
+    Gn = Group();
+    Gk = Group();
+    for (char c : p.out) {
+      const bool inA = p.in[ia].find(c) != std::string::npos, inB = p.in[ib].find(c) != std::string::npos;
+      Group &g = inA && inB ? Gb : (inA ? Gm : Gn);
+      g.letters.push_back(c);
+    }
+    for (char c : p.in[ia])
+      if (p.out.find(c) == std::string::npos) Gk.letters.push_back(c);
+    for (Group *g : {&Gb, &Gm, &Gn, &Gk}) {
+      g->ext = 1;
+      for (char c : g->letters) g->ext *= (b.L.n[c - 'a'] + b.L.k[c - 'a'] - 1) / b.L.k[c - 'a'];
+    }
+  };
+  build();
+  for (char c : p.reduced)
+    if (p.in[0].find(c) == std::string::npos || p.in[1].find(c) == std::string::npos)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "contraction letter '%c' is reduced but not in both inputs", c);
+  int64_t sCn = 0, sCm = 0, sCb = 0;
+  if (!group_stride(Gn, p.out, *out, sCn) || !group_stride(Gm, p.out, *out, sCm) || !group_stride(Gb, p.out, *out, sCb))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "output letters of one class are not adjacent in '%s'", p.out.c_str());
+  if (!(sCn == 1 || Gn.letters.empty())) {
+    // the output is contiguous along the other input's letters: swap roles
+    std::swap(ia, ib);
+    build();
+    if (!group_stride(Gn, p.out, *out, sCn) || !group_stride(Gm, p.out, *out, sCm) ||
+        !group_stride(Gb, p.out, *out, sCb))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "output letters of one class are not adjacent");
+    if (!(sCn == 1 || Gn.letters.empty()))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "output '%s' is not contiguous along a non-batch letter", p.out.c_str());
+  }
+  const jagg_relation &RA = *ins[ia], &RB = *ins[ib];
+  int64_t sAb, sAm, sAk, sBb, sBn, sBk;
+  if (!group_stride(Gb, p.in[ia], RA, sAb) || !group_stride(Gm, p.in[ia], RA, sAm) ||
+      !group_stride(Gk, p.in[ia], RA, sAk) || !group_stride(Gb, p.in[ib], RB, sBb) ||
+      !group_stride(Gn, p.in[ib], RB, sBn) || !group_stride(Gk, p.in[ib], RB, sBk))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "contraction letters of one class are not adjacent in an input");
+  if (Gm.letters.empty()) sAm = 0;
+  if (Gn.letters.empty()) sBn = 0;
+  a_kc = sAk == 1;
+  b_kc = sBk == 1;
+  if (!a_kc && !(sAm == 1)) return fail(ctx, JAGG_E_UNSUPPORTED, "input A is contiguous along a batch letter");
+  if (!b_kc && !(sBn == 1)) return fail(ctx, JAGG_E_UNSUPPORTED, "input B is contiguous along a batch letter");
+  const int F = dtype ? 8 : 4;
+  auto vec_ok = [&](bool kc, int64_t rows, int64_t sRow, int64_t sK, int64_t sBat, int64_t be) {
+    const int64_t contig = kc ? Gk.ext : rows;
+    const int64_t other = kc ? sRow : sK;
+    return contig % F == 0 && other % F == 0 && sBat % F == 0 && be % F == 0;
+  };
+  va = vec_ok(a_kc, Gm.ext, sAm, sAk, sAb, RA.be) ? F : 1;
+  vb = vec_ok(b_kc, Gn.ext, sBn, sBk, sBb, RB.be) ? F : 1;
+  a.A = RA.buf;
+  a.B = RB.buf;
+  a.C = out->buf;
+  a.list = list;
+  a.counts = counts;
+  a.per_key = b.join.per_key;
+  a.a_slot = 1 + ia;
+  a.b_slot = 1 + ib;
+  a.beA = RA.be;
+  a.beB = RB.be;
+  a.beC = out->be;
+  if (Gb.ext > (1 << 30) || Gm.ext > (1 << 30) || Gn.ext > (1 << 30) || Gk.ext > (1 << 30))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "block too large");
+  a.batch = int32_t(Gb.ext);
+  a.M = int32_t(Gm.ext);
+  a.N = int32_t(Gn.ext);
+  a.K = int32_t(Gk.ext);
+  a.sAb = sAb;
+  a.sAm = sAm;
+  a.sAk = sAk;
+  a.sBb = sBb;
+  a.sBn = sBn;
+  a.sBk = sBk;
+  a.sCb = sCb;
+  a.sCm = sCm;
+  a.alpha = sp->alpha;
+  a.tiles_m = (a.M + 127) / 128;
+  a.tiles_n = (a.N + 127) / 128;
+  a.n_keys = b.join.n_keys;
+  if (sp->causal_s) {
+    const char s = sp->causal_s, t = sp->causal_t;
+    const int cs = s - 'a', ct = t - 'a';
+    auto out_w = [&](char c) {
+      int64_t w = 1;
+      for (size_t q = p.out.find(c) + 1; q < p.out.size(); ++q) w *= b.L.k[p.out[q] - 'a'];
+      return w;
+    };
+    a.e_s = int32_t((b.L.n[cs] + b.L.k[cs] - 1) / b.L.k[cs]);
+    a.e_t = int32_t((b.L.n[ct] + b.L.k[ct] - 1) / b.L.k[ct]);
+    a.cs_w = out_w(s);
+    a.cs_k = b.L.k[cs];
+    a.ct_k = b.L.k[ct];
+    if (Gm.letters.empty() || Gm.letters.back() != s)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "causal contraction needs s innermost among the M letters");
+    if (p.out.find(t) != std::string::npos) {
+      if (Gn.letters.empty() || Gn.letters.back() != t)
+        return fail(ctx, JAGG_E_UNSUPPORTED, "causal contraction needs t innermost among the N letters");
+      a.causal_out = 1;
+      a.ct_w = out_w(t);
+    } else {
+      if (Gk.letters.empty() || Gk.letters.back() != t)
+        return fail(ctx, JAGG_E_UNSUPPORTED, "causal contraction needs t innermost among the K letters");
+      a.causal_red = 1;
+      const size_t q = p.in[ia].find(t);
+      a.ct_w = tuple_w(RA, int(q));
+    }
+  }
+  if (ctx->trace)
+    fprintf(stderr, "[jagg] contract %s: %s batch %d M %d N %d K %d A%s/v%d B%s/v%d keys %lld per_key %d\n",
+            sp->einsum, dtype ? "bf16" : "f32", a.batch, a.M, a.N, a.K, a_kc ? "k" : "m", va, b_kc ? "k" : "n", vb,
+            (long long)a.n_keys, a.per_key);
+  return JAGG_OK;
+}
+
+const char *env_or(const char *k) {
+  const char *v = getenv(k);
+  return v ? v : "";
+}
+
+}  // namespace
+
+// ================================================================= C ABI
+extern "C" {
+
+jagg_status jagg_ctx_create(int device, void *hip_stream, jagg_ctx **out) {
+  if (!out) return JAGG_E_INVALID;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return JAGG_E_DEVICE;
+  if (hipSetDevice(device) != hipSuccess) return JAGG_E_DEVICE;
+  jagg_ctx *c = new jagg_ctx;
+  c->device = device;
+  c->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  c->trace = env_or("JAGG_TRACE")[0] == '1';
+  c->debug_sync = env_or("JAGG_DEBUG_SYNC")[0] == '1';
+  *out = c;
+  return JAGG_OK;
+}
+
+jagg_status jagg_ctx_destroy(jagg_ctx *ctx) {
+  if (!ctx) return JAGG_E_INVALID;
+  delete ctx;
+  return JAGG_OK;
+}
+
+jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, const int32_t *nblocks, jagg_dtype dtype,
+                                size_t *bytes) {
+  if (!letters || !extents || !nblocks || !bytes) return JAGG_E_INVALID;
+  if (dtype != JAGG_F32 && dtype != JAGG_BF16) return JAGG_E_INVALID;
+  const int r = int(strlen(letters));
+  if (r < 1 || r > kMaxLetters) return JAGG_E_UNSUPPORTED;
+  int64_t e[kMaxLetters], nt, be;
+  jagg_status st = geometry(nullptr, r, extents, nblocks, e, &nt, &be);
+  if (st != JAGG_OK) return st;
+  *bytes = size_t(nt * be) * size_t(esz_of(dtype));
+  return JAGG_OK;
+}
+
+jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64_t *extents, const int32_t *nblocks,
+                                 jagg_dtype dtype, void *dev_buf, size_t buf_bytes, jagg_relation **out) {
+  if (!ctx || !letters || !extents || !nblocks || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  *out = nullptr;
+  if (dtype != JAGG_F32 && dtype != JAGG_BF16) return fail(ctx, JAGG_E_INVALID, "unknown dtype %d", int(dtype));
+  const int r = int(strlen(letters));
+  if (r < 1 || r > kMaxLetters) return fail(ctx, JAGG_E_UNSUPPORTED, "relation rank %d outside [1, %d]", r, kMaxLetters);
+  for (int i = 0; i < r; ++i) {
+    if (letters[i] < 'a' || letters[i] > 'z') return fail(ctx, JAGG_E_INVALID, "bad letter '%c'", letters[i]);
+    for (int j = i + 1; j < r; ++j)
+      if (letters[i] == letters[j]) return fail(ctx, JAGG_E_INVALID, "letter '%c' repeats", letters[i]);
+  }
+  jagg_relation R;
+  R.ctx = ctx;
+  R.r = r;
+  memset(R.letters, 0, sizeof(R.letters));
+  memcpy(R.letters, letters, size_t(r));
+  for (int i = 0; i < r; ++i) {
+    R.n[i] = extents[i];
+    R.k[i] = nblocks[i];
+  }
+  jagg_status st = geometry(ctx, r, R.n, R.k, R.e, &R.n_tuples, &R.be);
+  if (st != JAGG_OK) return st;
+  const int64_t elems = R.n_tuples * R.be;
+  if (elems >= (int64_t(1) << 31)) return fail(ctx, JAGG_E_UNSUPPORTED, "relation of %lld elements exceeds 2^31", (long long)elems);
+  const size_t need = size_t(elems) * size_t(esz_of(dtype));
+  if (!dev_buf) return fail(ctx, JAGG_E_INVALID, "NULL device buffer");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 16) return fail(ctx, JAGG_E_INVALID, "device buffer not 16-byte aligned");
+  if (buf_bytes < need)
+    return fail(ctx, JAGG_E_SHAPE, "buffer of %zu bytes, relation needs %zu", buf_bytes, need);
+  R.dt = dtype;
+  R.buf = dev_buf;
+  R.bytes = buf_bytes;
+  *out = new jagg_relation(R);
+  return JAGG_OK;
+}
+
+jagg_status jagg_relation_destroy(jagg_relation *rel) {
+  if (!rel) return JAGG_E_INVALID;
+  delete rel;
+  return JAGG_OK;
+}
+
+jagg_status jagg_repartition(jagg_ctx *ctx, const jagg_relation *src, jagg_relation *dst) {
+  if (!ctx || !src || !dst) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  if (src->dt != dst->dt) return fail(ctx, JAGG_E_SHAPE, "source and destination dtypes differ");
+  if (src->r != dst->r) return fail(ctx, JAGG_E_SHAPE, "source and destination ranks differ");
+  for (int p = 0; p < dst->r; ++p) {
+    const char *q = strchr(src->letters, dst->letters[p]);
+    if (!q) return fail(ctx, JAGG_E_SHAPE, "letter '%c' is not in the source", dst->letters[p]);
+    if (src->n[q - src->letters] != dst->n[p])
+      return fail(ctx, JAGG_E_SHAPE, "letter '%c' has extent %lld in the source, %lld in the destination",
+                  dst->letters[p], (long long)src->n[q - src->letters], (long long)dst->n[p]);
+  }
+  const char *sb = static_cast<const char *>(src->buf), *db = static_cast<const char *>(dst->buf);
+  const size_t sn = size_t(src->n_tuples * src->be) * esz_of(src->dt), dn = size_t(dst->n_tuples * dst->be) * esz_of(dst->dt);
+  if (sb < db + dn && db < sb + sn) return fail(ctx, JAGG_E_INVALID, "source and destination overlap");
+  return do_repartition(ctx, *src, *dst);
+}
+
+jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                                  const int32_t *blockings, size_t *bytes) {
+  if (!ctx || !bytes) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  Bound b;
+  jagg_status st = bind(ctx, spec, in, n_in, blockings, b);
+  if (st != JAGG_OK) return st;
+  *bytes = b.total;
+  return JAGG_OK;
+}
+
+jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                        const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes) {
+  if (!ctx || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  Bound b;
+  jagg_status st = bind(ctx, spec, in, n_in, blockings, b);
+  if (st != JAGG_OK) return st;
+  // output relation must be the spec's output under `blockings`
+  if (out->r != int(b.p.out.size()))
+    return fail(ctx, JAGG_E_SHAPE, "out relation has %d dimensions, output '%s' names %d", out->r, b.p.out.c_str(),
+                int(b.p.out.size()));
+  for (int q = 0; q < out->r; ++q) {
+    const int c = b.p.out[q] - 'a';
+    if (out->n[q] != b.L.n[c])
+      return fail(ctx, JAGG_E_SHAPE, "out letter '%c' has extent %lld, expected %lld", 'a' + c, (long long)out->n[q],
+                  (long long)b.L.n[c]);
+    if (out->k[q] != b.L.k[c])
+      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has %d blocks, the spec asks %d", 'a' + c, out->k[q], b.L.k[c]);
+  }
+  if (out->dt != spec->out_dtype) return fail(ctx, JAGG_E_SHAPE, "out relation dtype differs from spec->out_dtype");
+  {
+    const char *ob = static_cast<const char *>(out->buf);
+    const size_t on = size_t(out->n_tuples * out->be) * esz_of(out->dt);
+    for (int j = 0; j < n_in; ++j) {
+      const char *ib = static_cast<const char *>(in[j]->buf);
+      const size_t inn = size_t(in[j]->n_tuples * in[j]->be) * esz_of(in[j]->dt);
+      if (ib < ob + on && ob < ib + inn) return fail(ctx, JAGG_E_INVALID, "out relation overlaps input %d", j);
+    }
+  }
+  if (!workspace || ws_bytes < b.total)
+    return fail(ctx, JAGG_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, b.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(ctx, JAGG_E_WORKSPACE, "workspace not 256-byte aligned");
+
+  // classify before launching anything: a contraction is a MUL/SUM over two
+  // inputs where every reduced letter is in both inputs and each input
+  // contributes output letters of its own; any other aggregating spec is a
+  // streaming reduce, and a spec without aggregation is a map.
+  enum { MAP, REDUCE, CONTRACT } kind = MAP;
+  if (spec->agg != JAGG_AGG_NONE) {
+    kind = REDUCE;
+    if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
+      bool both = true, m_any = false, n_any = false;
+      for (char c : b.p.reduced)
+        both = both && b.p.in[0].find(c) != std::string::npos && b.p.in[1].find(c) != std::string::npos;
+      for (char c : b.p.out) {
+        const bool i0 = b.p.in[0].find(c) != std::string::npos, i1 = b.p.in[1].find(c) != std::string::npos;
+        m_any = m_any || (i0 && !i1);
+        n_any = n_any || (i1 && !i0);
+      }
+      if (both && m_any && n_any) kind = CONTRACT;
+    }
+  }
+
+  char *ws = static_cast<char *>(workspace);
+  int32_t *list = reinterpret_cast<int32_t *>(ws);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + b.list_bytes);
+  size_t off = b.list_bytes + b.counts_bytes;
+  // (0) inputs blocked differently: re-block into the workspace
+  jagg_relation tmp[kMaxIn];
+  const jagg_relation *use[kMaxIn];
+  for (int j = 0; j < n_in; ++j) {
+    use[j] = in[j];
+    if (!b.needs_reblock[j]) continue;
+    jagg_relation &T = tmp[j];
+    T = *in[j];
+    for (int q = 0; q < T.r; ++q) T.k[q] = b.L.k[b.p.in[j][q] - 'a'];
+    if ((st = geometry(ctx, T.r, T.n, T.k, T.e, &T.n_tuples, &T.be)) != JAGG_OK) return st;
+    T.buf = ws + off;
+    T.bytes = b.reblock_bytes[j];
+    off += b.reblock_bytes[j];
+    use[j] = &T;
+  }
+  // plan the block kernel (host only) before any launch
+  EwArgs ew;
+  ContractArgs ca;
+  int dtype = 0, va = 1, vb = 1;
+  bool akc = true, bkc = true;
+  if (kind == CONTRACT) {
+    if ((st = plan_contract(ctx, spec, b, use, out, list, counts, ca, dtype, akc, bkc, va, vb)) != JAGG_OK) return st;
+  }
+  if (kind != CONTRACT && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK) return st;
+  std::vector<RelayoutArgs> reblocks;
+  std::vector<int> reblock_vec;
+  for (int j = 0; j < n_in; ++j) {
+    if (!b.needs_reblock[j]) continue;
+    RelayoutArgs ra;
+    int vbytes = 0;
+    if ((st = plan_relayout(ctx, *in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
+    reblocks.push_back(ra);
+    reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
+  }
+  // launches
+  for (size_t i = 0; i < reblocks.size(); ++i)
+    if ((st = after_launch(ctx, launch_relayout(reblocks[i], reblock_vec[i] / 16, reblock_vec[i] % 16, ctx->stream),
+                           "reblock input")) != JAGG_OK)
+      return st;
+  b.join.list = list;
+  b.join.counts = counts;
+  if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
+  if (kind == CONTRACT)
+    return after_launch(ctx, launch_contract(ca, dtype, spec->out_dtype == JAGG_BF16, akc, bkc, va, vb, ctx->stream),
+                        "contract");
+  if (kind == MAP) return after_launch(ctx, launch_map(ew, ctx->stream), "map");
+  return after_launch(ctx, launch_reduce(ew, ctx->stream), "reduce");
+}
+
+jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter, const int32_t *blockings,
+                            int64_t *n_keys, int64_t *per_key) {
+  if (!spec || !extents_by_letter || !blockings || !n_keys || !per_key) return JAGG_E_INVALID;
+  Spec p;
+  jagg_status st = parse(nullptr, spec->einsum, p);
+  if (st != JAGG_OK) return st;
+  int64_t nk = 1, pk = 1;
+  for (size_t i = 0; i < p.order.size(); ++i) {
+    if (blockings[i] < 1 || blockings[i] > extents_by_letter[i]) return JAGG_E_BLOCKING;
+    if (p.out.find(p.order[i]) != std::string::npos) nk *= blockings[i];
+    else pk *= blockings[i];
+  }
+  *n_keys = nk;
+  *per_key = pk;
+  return JAGG_OK;
+}
+
+jagg_status jagg_join_list(jagg_ctx *ctx, const jagg_spec *spec, const int64_t *extents_by_letter,
+                           const int32_t *blockings, int32_t *dev_list, int32_t *dev_counts) {
+  if (!ctx || !spec || !extents_by_letter || !blockings || !dev_list || !dev_counts)
+    return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  Spec p;
+  jagg_status st = parse(ctx, spec->einsum, p);
+  if (st != JAGG_OK) return st;
+  if ((st = check_spec(ctx, spec, p)) != JAGG_OK) return st;
+  LetterInfo L;
+  for (int i = 0; i < 26; ++i) {
+    L.n[i] = 0;
+    L.k[i] = 0;
+  }
+  for (size_t i = 0; i < p.order.size(); ++i) {
+    const int c = p.order[i] - 'a';
+    L.n[c] = extents_by_letter[i];
+    L.k[c] = blockings[i];
+    if (L.n[c] < 1) return fail(ctx, JAGG_E_SHAPE, "extent of '%c' must be >= 1", p.order[i]);
+    const int64_t e = (L.n[c] + L.k[c] - 1) / std::max(L.k[c], 1);
+    if (L.k[c] < 1 || L.k[c] > L.n[c] || (L.k[c] - 1) * e >= L.n[c])
+      return fail(ctx, JAGG_E_BLOCKING, "bad blocking %d of '%c'", L.k[c], p.order[i]);
+  }
+  JoinArgs a;
+  if ((st = plan_join(ctx, spec, p, L, a)) != JAGG_OK) return st;
+  a.list = dev_list;
+  a.counts = dev_counts;
+  return after_launch(ctx, launch_join(a, ctx->stream), "join");
+}
+
+const char *jagg_status_str(jagg_status s) {
+  switch (s) {
+    case JAGG_OK: return "ok";
+    case JAGG_E_INVALID: return "invalid argument";
+    case JAGG_E_SHAPE: return "shape mismatch";
+    case JAGG_E_BLOCKING: return "bad blocking";
+    case JAGG_E_UNSUPPORTED: return "unsupported spec";
+    case JAGG_E_WORKSPACE: return "workspace too small";
+    case JAGG_E_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char *jagg_last_error(const jagg_ctx *ctx) { return ctx ? ctx->err.c_str() : "NULL context"; }
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// jagg_internal.h -- argument blocks shared by the host planner (abi.cpp)
+// and the HIP kernels.  Every block is passed to its kernel by value.
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace jagg {
+
+constexpr int kMaxLetters = 8;   // per relation
+constexpr int kMaxIn = 3;        // inputs per spec
+constexpr int kMaxDims = 24;     // relayout dims after splitting (<= 3 per letter)
+constexpr int kMaxChk = 8;       // relayout letters whose range must be checked
+
+// Unsigned 32-bit division by a run-time invariant d >= 1 through a
+// multiply-high, after Granlund and Montgomery, "Division by Invariant
+// Integers using Multiplication" (PLDI 1994), Fig. 4.1:
+//   l = ceil(log2 d); m = floor(2^32 (2^l - d) / d) + 1;
+//   t = mulhi(m, n); q = (t + ((n - t) >> min(l,1))) >> max(l-1, 0).
+// Exact for every 32-bit n.
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+__host__ __device__ inline uint32_t fd_div(uint32_t n, const FastDiv &f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t t = __umulhi(f.m, n);
+#else
+  uint32_t t = uint32_t((uint64_t(f.m) * n) >> 32);
+#endif
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+// ---------------------------------------------------------------- relayout
+// The copy is a strided walk over "dims": every letter's index x is split
+// into digits (block coordinate and in-block offset, each possibly split
+// again where the source and destination block extents nest), so that both
+// the source and the destination offset are affine in the digits.  Dims are
+// grouped into lane dims (decoded once per thread) and tile dims (decoded
+// once per workgroup).  A letter whose blocks do not nest ("irregular") has
+// its source offset computed from x by division.
+struct RelayoutDim {
+  int64_t ext;       // number of digit values
+  int64_t src;       // source stride per digit (elements)
+  int64_t dst;       // destination stride per digit (elements)
+  int32_t chk;       // checked letter slot this digit feeds, or -1
+  int64_t xs;        // contribution of one digit step to that letter's index
+  FastDiv div;       // division by ext (tile dims)
+};
+
+struct RelayoutArgs {
+  const void *src;
+  void *dst;
+  int n_tile;                  // tile dims, outermost first
+  RelayoutDim tile[kMaxDims];
+  int n_lane;                  // lane dims, innermost (vectorised) first
+  RelayoutDim lane[kMaxDims];
+  int64_t n_tiles;
+  int32_t lanes;               // threads that carry a vector
+  int n_chk;
+  int64_t read_lim[kMaxChk];   // x < read_lim: the element exists in the source
+  int64_t write_lim[kMaxChk];  // x < write_lim: the destination slot exists
+  int32_t irr[kMaxChk];        // 1 when the slot's letter is irregular
+  FastDiv irr_div[kMaxChk];    // division by the source block extent
+  int64_t irr_K[kMaxChk];      // source tuple stride of the letter (elements)
+  int64_t irr_E[kMaxChk];      // source in-block stride of the letter
+};
+
+// vec_bytes: 16, 8, 4 or 2; elem_bytes 2 or 4.
+hipError_t launch_relayout(const RelayoutArgs &a, int vec_bytes, int elem_bytes, hipStream_t st);
+
+// ---------------------------------------------------------------- join
+struct JoinArgs {
+  int n_in;
+  int n_out;                       // output letters
+  int n_red;                       // reduced letters
+  int32_t out_k[kMaxLetters];      // block counts, output letter order
+  FastDiv out_div[kMaxLetters];
+  int32_t red_k[26];               // block counts, reduced letters in first-appearance order
+  FastDiv red_div[26];
+  int64_t w_out[kMaxIn][kMaxLetters];  // tuple-id weight of each output letter's block coordinate
+  int64_t w_red[kMaxIn][26];           // tuple-id weight of each reduced letter's block coordinate
+  int32_t per_key;
+  int64_t n_keys;
+  // causal pair: letter s / t located as (is_reduced, index)
+  int32_t causal;
+  int32_t s_red, s_idx, t_red, t_idx;
+  int64_t e_s, e_t, n_s;
+  int32_t *list;
+  int32_t *counts;
+};
+hipError_t launch_join(const JoinArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------- contraction
+struct ContractArgs {
+  const void *A;
+  const void *B;
+  void *C;
+  const int32_t *list;
+  const int32_t *counts;
+  int32_t per_key;
+  int32_t a_slot, b_slot;       // position of A / B tuple ids inside an entry (1 or 2)
+  int64_t beA, beB, beC;        // block elements
+  int32_t batch, M, N, K;       // flattened padded block extents
+  int64_t sAb, sAm, sAk;
+  int64_t sBb, sBn, sBk;
+  int64_t sCb, sCm;             // C is contiguous along N
+  float alpha;
+  int32_t tiles_m, tiles_n;
+  int64_t n_keys;
+  // causal pair with both letters in the output (s innermost of M, t innermost of N)
+  int32_t causal_out;
+  // causal pair with s in the output (innermost of M) and t reduced (innermost of K of A)
+  int32_t causal_red;
+  int64_t cs_w, cs_k;           // kappa_s = (out_tuple / cs_w) % cs_k
+  int64_t ct_w, ct_k;           // kappa_t = (tuple / ct_w) % ct_k  (out tuple, or A tuple when reduced)
+  int32_t e_s, e_t;
+};
+// dtype: 0 f32 inputs, 1 bf16 inputs; out_dtype 0 f32 / 1 bf16;
+// a_kc / b_kc: operand contiguous along K; va / vb: vector width (elements) of global loads.
+hipError_t launch_contract(const ContractArgs &a, int dtype, int out_dtype, bool a_kc, bool b_kc, int va, int vb,
+                           hipStream_t st);
+
+// ---------------------------------------------------------------- map / reduce
+struct EwArgs {
+  int n_in;
+  const void *in[kMaxIn];
+  int32_t in_dt[kMaxIn];        // 0 f32, 1 bf16
+  void *out;
+  int32_t out_dt;
+  int32_t g;                    // jagg_g
+  int32_t agg;                  // jagg_agg
+  float alpha, beta, eps;
+  const int32_t *list;
+  const int32_t *counts;
+  int32_t per_key;
+  int64_t n_keys;
+  // output block: letters in output order
+  int r_out;
+  int64_t e_out[kMaxLetters];
+  int64_t n_out[kMaxLetters];   // extents (valid bound on kappa*e + c)
+  int64_t k_out[kMaxLetters];   // block counts (decode kappa from the output tuple id)
+  int64_t be_out;
+  // reduced letters (reduce only)
+  int n_red;
+  int64_t e_red[kMaxLetters];
+  int64_t n_red_ext[kMaxLetters];
+  int64_t k_red[kMaxLetters];
+  int64_t w_red0[kMaxLetters];  // tuple-id weight of the reduced letter in input 0
+  // inputs: in-block stride of each output / reduced letter (0 = absent)
+  int64_t be_in[kMaxIn];
+  int64_t s_out[kMaxIn][kMaxLetters];
+  int64_t s_red[kMaxIn][kMaxLetters];
+  // causal pair (letters located in the output or among reduced letters)
+  int32_t causal;
+  int32_t s_red_flag, s_pos, t_red_flag, t_pos;
+  // rows: every output letter but the last is a row coordinate
+  int64_t rows_per_block;
+  int32_t vec;                  // elements per vector along the innermost letter (map)
+  int32_t inner_red;            // reduce: index of the reduced letter innermost in input 0, or -1
+};
+hipError_t launch_map(const EwArgs &a, hipStream_t st);
+hipError_t launch_reduce(const EwArgs &a, hipStream_t st);
+
+}  // namespace jagg

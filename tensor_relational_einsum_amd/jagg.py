@@ -1,0 +1,271 @@
+"""ctypes binding of libjagg.so (include/jagg.h): argument marshalling only.
+
+PyTorch provides device memory and the stream; every step of a join-agg
+spec runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, a JaggError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjagg.so")
+
+G = {"mul": 0, "ident": 1, "square": 2, "exp_sub": 3, "exp_sub_div": 4, "rms_scale": 5, "silu_mul": 6, "add": 7}
+AGG = {"none": 0, "sum": 1, "max": 2}
+DT = {"f32": 0, "bf16": 1}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+ESZ = {"f32": 4, "bf16": 2}
+STATUS = {0: "ok", -1: "invalid argument", -2: "shape mismatch", -3: "bad blocking", -4: "unsupported spec",
+          -5: "workspace too small", -6: "device error"}
+
+EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
+           "jagg_relation_destroy", "jagg_repartition", "jagg_einsum_workspace", "jagg_einsum", "jagg_join_shape",
+           "jagg_join_list", "jagg_status_str", "jagg_last_error"]
+
+
+class JaggError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class jagg_spec(ctypes.Structure):
+    _fields_ = [("einsum", ctypes.c_char_p), ("g", ctypes.c_int), ("agg", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("eps", ctypes.c_float),
+                ("causal_s", ctypes.c_char), ("causal_t", ctypes.c_char)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Loads libjagg.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise JaggError(-6, f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64p, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+        L.jagg_ctx_create.argtypes = [ctypes.c_int, vp, ctypes.POINTER(vp)]
+        L.jagg_ctx_destroy.argtypes = [vp]
+        L.jagg_relation_bytes.argtypes = [ctypes.c_char_p, i64p, i32p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.jagg_relation_create.argtypes = [vp, ctypes.c_char_p, i64p, i32p, ctypes.c_int, vp, ctypes.c_size_t,
+                                           ctypes.POINTER(vp)]
+        L.jagg_relation_destroy.argtypes = [vp]
+        L.jagg_repartition.argtypes = [vp, vp, vp]
+        L.jagg_einsum_workspace.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p,
+                                            ctypes.POINTER(ctypes.c_size_t)]
+        L.jagg_einsum.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp, vp,
+                                  ctypes.c_size_t]
+        L.jagg_join_shape.argtypes = [ctypes.POINTER(jagg_spec), i64p, i32p, i64p, i64p]
+        L.jagg_join_list.argtypes = [vp, ctypes.POINTER(jagg_spec), i64p, i32p, vp, vp]
+        L.jagg_status_str.argtypes = [ctypes.c_int]
+        L.jagg_status_str.restype = ctypes.c_char_p
+        L.jagg_last_error.argtypes = [vp]
+        L.jagg_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _i64(vals):
+    return (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+
+
+def _i32(vals):
+    return (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+
+
+def parse(einsum: str):
+    lhs, out = einsum.split("->")
+    ins = lhs.split(",")
+    order = ""
+    for lt in ins:
+        for c in lt:
+            if c not in order:
+                order += c
+    return ins, out, order
+
+
+def make_spec(einsum, g="mul", agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, eps=0.0, causal=None) -> jagg_spec:
+    s = jagg_spec()
+    s._einsum_bytes = einsum.encode()  # keep the string alive with the struct
+    s.einsum = s._einsum_bytes
+    s.g, s.agg, s.out_dtype = G[g], AGG[agg], DT[out_dtype]
+    s.alpha, s.beta, s.eps = alpha, beta, eps
+    s.causal_s = causal[0].encode() if causal else b"\0"
+    s.causal_t = causal[1].encode() if causal else b"\0"
+    return s
+
+
+class Context:
+    """A jagg context bound to one device and one HIP stream (torch's current
+    stream by default)."""
+
+    def __init__(self, device: int = 0, stream: torch.cuda.Stream | None = None):
+        self.device = device
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        h = ctypes.c_void_p()
+        self._check(lib().jagg_ctx_create(device, ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h)), None)
+        self.handle = h
+
+    def _check(self, rc, h=...):
+        if rc != 0:
+            msg = lib().jagg_last_error(self.handle if h is ... else h)
+            raise JaggError(rc, (msg or b"").decode())
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().jagg_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def relation_bytes(letters, extents, nblocks, dtype) -> int:
+    out = ctypes.c_size_t()
+    rc = lib().jagg_relation_bytes(letters.encode(), _i64(extents), _i32(nblocks), DT[dtype], ctypes.byref(out))
+    if rc != 0:
+        raise JaggError(rc, f"relation {letters} {list(extents)} / {list(nblocks)}")
+    return out.value
+
+
+class Relation:
+    """Tensor relation over a flat torch device buffer (padded blocks in
+    canonical tuple order).  ``extents`` / ``nblocks`` follow ``letters``."""
+
+    def __init__(self, ctx: Context, letters: str, extents, nblocks, dtype: str, buffer: torch.Tensor | None = None):
+        self.ctx, self.letters, self.dtype = ctx, letters, dtype
+        self.extents = [int(v) for v in extents]
+        self.nblocks = [int(v) for v in nblocks]
+        nbytes = relation_bytes(letters, self.extents, self.nblocks, dtype)
+        if buffer is None:
+            buffer = torch.empty(nbytes // ESZ[dtype], dtype=TORCH_DT[dtype], device=f"cuda:{ctx.device}")
+        self.data = buffer
+        self.nbytes = nbytes
+        h = ctypes.c_void_p()
+        ctx._check(lib().jagg_relation_create(ctx.handle, letters.encode(), _i64(self.extents), _i32(self.nblocks),
+                                              DT[dtype], ctypes.c_void_p(buffer.data_ptr()),
+                                              buffer.numel() * buffer.element_size(), ctypes.byref(h)))
+        self.handle = h
+
+    @property
+    def block_shape(self):
+        return [-(-n // k) for n, k in zip(self.extents, self.nblocks)]
+
+    def blocking(self) -> dict:
+        return dict(zip(self.letters, self.nblocks))
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib().jagg_relation_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass
+
+
+def repartition(ctx: Context, src: Relation, dst: Relation) -> Relation:
+    ctx._check(lib().jagg_repartition(ctx.handle, src.handle, dst.handle))
+    return dst
+
+
+def relation_like(ctx, letters, extents: dict, blockings: dict, dtype) -> Relation:
+    return Relation(ctx, letters, [extents[c] for c in letters], [blockings.get(c, 1) for c in letters], dtype)
+
+
+def from_dense(ctx: Context, x: torch.Tensor, letters: str, blockings: dict) -> Relation:
+    """Device tensor (row-major over `letters`) -> blocked relation, through the
+    repartition kernel (a dense tensor is a relation with one block per letter)."""
+    dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}[x.dtype]
+    x = x.contiguous()
+    dense = Relation(ctx, letters, list(x.shape), [1] * len(letters), dtype, buffer=x.view(-1))
+    out = Relation(ctx, letters, list(x.shape), [blockings.get(c, 1) for c in letters], dtype)
+    repartition(ctx, dense, out)
+    out._keep = x
+    return out
+
+
+def to_dense(ctx: Context, rel: Relation) -> torch.Tensor:
+    """Blocked relation -> dense device tensor, through the repartition kernel."""
+    buf = torch.empty(int(torch.tensor(rel.extents).prod().item()), dtype=TORCH_DT[rel.dtype],
+                      device=rel.data.device)
+    dense = Relation(ctx, rel.letters, rel.extents, [1] * len(rel.letters), rel.dtype, buffer=buf)
+    repartition(ctx, rel, dense)
+    return buf.view(*rel.extents)
+
+
+class EinsumCall:
+    """One join-agg spec bound to its relations, with arguments marshalled
+    once; ``run()`` is a single call into the library."""
+
+    def __init__(self, ctx: Context, einsum: str, inputs, blockings: dict, out: Relation | None = None, g="mul",
+                 agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, eps=0.0, causal=None,
+                 workspace: torch.Tensor | None = None):
+        ins, out_letters, order = parse(einsum)
+        self.ctx, self.einsum = ctx, einsum
+        self.spec = make_spec(einsum, g, agg, out_dtype, alpha, beta, eps, causal)
+        self.inputs = list(inputs)
+        self.blk = _i32([blockings.get(c, 1) for c in order])
+        self.in_arr = (ctypes.c_void_p * len(self.inputs))(*[r.handle.value for r in self.inputs])
+        if out is None:
+            ext = {}
+            for lt, r in zip(ins, self.inputs):
+                for c, n in zip(lt, r.extents):
+                    ext[c] = n
+            out = Relation(ctx, out_letters, [ext[c] for c in out_letters], [blockings.get(c, 1) for c in out_letters],
+                           out_dtype)
+        self.out = out
+        need = ctypes.c_size_t()
+        ctx._check(lib().jagg_einsum_workspace(ctx.handle, ctypes.byref(self.spec), self.in_arr, len(self.inputs),
+                                               self.blk, ctypes.byref(need)))
+        self.ws_bytes = need.value
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=f"cuda:{ctx.device}")
+        self.workspace = workspace
+
+    def run(self) -> Relation:
+        self.ctx._check(lib().jagg_einsum(self.ctx.handle, ctypes.byref(self.spec), self.in_arr, len(self.inputs),
+                                          self.blk, self.out.handle, ctypes.c_void_p(self.workspace.data_ptr()),
+                                          self.workspace.numel()))
+        return self.out
+
+
+def einsum(ctx: Context, einsum: str, inputs, blockings: dict, out: Relation | None = None, **kw) -> Relation:
+    return EinsumCall(ctx, einsum, inputs, blockings, out, **kw).run()
+
+
+def join_shape(einsum: str, extents: dict, blockings: dict, causal=None):
+    _, _, order = parse(einsum)
+    spec = make_spec(einsum, causal=causal)
+    nk, pk = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().jagg_join_shape(ctypes.byref(spec), _i64([extents[c] for c in order]),
+                               _i32([blockings.get(c, 1) for c in order]), ctypes.byref(nk), ctypes.byref(pk))
+    if rc != 0:
+        raise JaggError(rc, f"join shape of {einsum}")
+    return nk.value, pk.value
+
+
+def join_list(ctx: Context, einsum: str, extents: dict, blockings: dict, causal=None):
+    """Runs the join-enumeration kernel; returns (list [n_keys, per_key, 1+n_in],
+    counts [n_keys]) as int32 device tensors."""
+    ins, _, order = parse(einsum)
+    nk, pk = join_shape(einsum, extents, blockings, causal)
+    spec = make_spec(einsum, causal=causal)
+    dev = f"cuda:{ctx.device}"
+    lst = torch.empty((nk, pk, 1 + len(ins)), dtype=torch.int32, device=dev)
+    cnt = torch.empty(nk, dtype=torch.int32, device=dev)
+    ctx._check(lib().jagg_join_list(ctx.handle, ctypes.byref(spec), _i64([extents[c] for c in order]),
+                                    _i32([blockings.get(c, 1) for c in order]), ctypes.c_void_p(lst.data_ptr()),
+                                    ctypes.c_void_p(cnt.data_ptr())))
+    return lst, cnt

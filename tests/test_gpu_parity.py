@@ -1,0 +1,360 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: join lists, repartition (every byte of the destination, padding
+included), MAX aggregation on identical inputs.  Floating point: the normwise
+error e = max|y - yhat| / max|yhat| (tests/parity_util.py) under 1e-5 for
+fp32 results and 2e-2 for bf16 chains (fp32 accumulation); a single spec
+with a bf16 output is held to 8e-3 (one bf16 rounding, 2^-8 relative, plus
+fp32 summation error).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tensor_relational_einsum_amd import inputs as I
+from tensor_relational_einsum_amd import jagg
+from tensor_relational_einsum_amd.runner import ChainRunner
+from parity_util import bits, normwise_err, oracle_bits, padding_mask, rel_dense, to_np
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_OUT_TOL = 8e-3
+CHAIN_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    c = jagg.Context(0)
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+def upload(ctx, x: torch.Tensor, letters, blk):
+    return jagg.from_dense(ctx, x.to("cuda"), letters, blk)
+
+
+# ----------------------------------------------------------------- repartition
+
+def check_relayout(ctx, shape, src_l, src_b, dst_l, dst_b, dtype, seed=0):
+    ext = dict(zip(src_l, shape))
+    g = I.streams(seed, 1)[0]
+    x = I.draw(g, shape, "normal", dtype)
+    src = upload(ctx, x, src_l, src_b)
+    dst = jagg.relation_like(ctx, dst_l, ext, dst_b, dtype)
+    dst.data.fill_(7)  # every byte must be rewritten, padding included
+    jagg.repartition(ctx, src, dst)
+    torch.cuda.synchronize()
+    xb = bits(x)
+    want_src = O.to_relation(xb, src_l, ext, src_b)
+    assert np.array_equal(bits(src.data), want_src), "dense -> blocked relation differs"
+    want = O.repartition(want_src, src_l, src_b, dst_l, dst_b, ext)
+    got = bits(dst.data)
+    assert got.shape == want.shape
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} elements differ, first at {bad[:5]}"
+    # round trip back to the source blocking is the identity
+    back = jagg.relation_like(ctx, src_l, ext, src_b, dtype)
+    jagg.repartition(ctx, dst, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(back.data), want_src)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape,src_l,src_b,dst_l,dst_b", [
+    ((64, 96), "ij", dict(i=8, j=1), "ij", dict(i=1, j=8)),
+    ((32, 64, 16, 16), "abcd", dict(a=4, b=8, c=1, d=1), "acbd", dict(a=1, b=1, c=4, d=2)),
+    ((30, 100, 50, 70), "abcd", dict(a=1, b=1, c=1, d=1), "abcd", dict(a=4, b=7, c=3, d=6)),
+    ((30, 100, 50, 70), "abcd", dict(a=4, b=7, c=3, d=6), "abcd", dict(a=3, b=5, c=2, d=4)),
+    ((7, 10, 5, 10), "abcd", dict(a=2, b=3, c=2, d=4), "dcba", dict(a=3, b=2, c=1, d=2)),
+    ((6, 8, 4, 5), "abcd", dict(a=2, b=4, c=1, d=1), "acbd", dict(a=1, b=1, c=2, d=5)),
+    ((1000, 167), "ij", dict(i=3, j=6), "ji", dict(i=7, j=2)),
+    ((96, 300, 64, 48), "abcd", dict(a=1, b=1, c=1, d=1), "abcd", dict(a=5, b=7, c=4, d=3)),
+    ((4, 256, 8, 128), "bsqd", dict(b=1, s=4, q=4, d=1), "bqsd", dict(b=1, q=1, s=4, d=1)),
+    ((3,), "a", dict(a=1), "a", dict(a=3)),
+])
+def test_repartition_cases(ctx, shape, src_l, src_b, dst_l, dst_b, dtype):
+    check_relayout(ctx, shape, src_l, src_b, dst_l, dst_b, dtype)
+
+
+def test_repartition_config_8192_square(ctx):
+    w = I.repartition_2d()
+    x = I.generate(w)["X"]
+    st = w.chain[0]
+    check_relayout(ctx, tuple(x.shape), "ij", dict(i=8, j=1), st.letters, st.blockings, "bf16", seed=w.seed)
+
+
+def test_repartition_config_4d(ctx):
+    w = I.repartition_4d()
+    st = w.chain[0]
+    check_relayout(ctx, (32, 128, 64, 64), "abcd", dict(a=4, b=8, c=1, d=1), st.letters, st.blockings, "bf16",
+                   seed=w.seed)
+
+
+# ----------------------------------------------------------------- join lists
+
+JOIN_CASES = [
+    ("ij,jk->ik", dict(i=256, j=512, k=256), dict(i=1, j=2, k=1), None),
+    ("ij,jk->ik", dict(i=256, j=512, k=256), dict(i=2, j=2, k=1), None),
+    ("ij,jk->ik", dict(i=256, j=256, k=256), dict(i=4, j=4, k=4), None),
+    ("abcd,cde->abe", dict(a=96, b=300, c=64, d=48, e=1000), dict(a=5, b=7, c=4, d=3, e=6), None),
+    ("bhsd,bhtd->bhst", dict(b=4, h=32, s=2048, t=2048, d=128), dict(b=1, h=1, s=16, t=16, d=1), None),
+    ("bhst->bhs", dict(b=4, h=32, s=2048, t=2048), dict(b=1, h=1, s=16, t=16), None),
+    ("bhst,bhs,bhs->bhst", dict(b=4, h=32, s=2048, t=2048), dict(b=1, h=1, s=16, t=16), None),
+    ("bhst,bhtd->bhsd", dict(b=4, h=32, s=2048, t=2048, d=128), dict(b=1, h=1, s=16, t=16, d=1), None),
+    ("bsh,hqd->bsqd", dict(b=4, s=2048, h=4096, q=32, d=128), dict(b=1, s=16, h=4, q=4, d=1), None),
+    ("bqsd,bqtd->bqst", dict(b=4, q=32, s=2048, t=2048, d=128), dict(b=1, q=1, s=16, t=16, d=1), ("s", "t")),
+    ("bqst->bqs", dict(b=4, q=32, s=2048, t=2048), dict(b=1, q=1, s=16, t=16), ("s", "t")),
+    ("bqst,bqtd->bqsd", dict(b=4, q=32, s=2048, t=2048, d=128), dict(b=1, q=1, s=16, t=16, d=1), ("s", "t")),
+    ("sd,td->st", dict(s=100, t=100, d=8), dict(s=7, t=7, d=2), ("s", "t")),
+]
+
+
+@pytest.mark.parametrize("spec,ext,blk,causal", JOIN_CASES)
+def test_join_list_bit_exact(ctx, spec, ext, blk, causal):
+    lst, cnt = jagg.join_list(ctx, spec, ext, blk, causal)
+    torch.cuda.synchronize()
+    lst, cnt = lst.cpu().numpy(), cnt.cpu().numpy()
+    got = np.concatenate([lst[k, :cnt[k]] for k in range(lst.shape[0])]) if lst.size else lst.reshape(0, 1)
+    want = O.join_list(spec, ext, blk, causal)
+    assert got.shape == want.shape
+    assert np.array_equal(got.astype(np.int64), want)
+    for k in range(lst.shape[0]):  # unused slots are -1
+        assert np.all(lst[k, cnt[k]:] == -1)
+
+
+# ----------------------------------------------------------------- single specs
+
+def run_spec_case(ctx, spec, ext, blk, g="mul", agg="sum", in_dtypes=None, out_dtype="f32", alpha=1.0, beta=0.0,
+                  eps=0.0, causal=None, seed=1, positive=()):
+    """Runs one spec on seeded inputs and returns (gpu dense, oracle dense,
+    gpu out relation, output letters)."""
+    ins, out = spec.split("->")
+    ins = ins.split(",")
+    in_dtypes = in_dtypes or ["f32"] * len(ins)
+    gens = I.streams(seed, len(ins))
+    xs = []
+    for j, (lt, gen, dt) in enumerate(zip(ins, gens, in_dtypes)):
+        if j in positive:
+            x = I.draw(gen, [ext[c] for c in lt], "uniform", dt, 1.0)
+            x = (x.float().abs() + 0.5).to(x.dtype)
+        else:
+            x = I.draw(gen, [ext[c] for c in lt], "normal", dt)
+        xs.append(x)
+    rels = [upload(ctx, x, lt, blk) for x, lt in zip(xs, ins)]
+    call = jagg.EinsumCall(ctx, spec, rels, blk, g=g, agg=agg, out_dtype=out_dtype, alpha=alpha, beta=beta, eps=eps,
+                           causal=causal)
+    call.out.data.fill_(3)
+    call.run()
+    torch.cuda.synchronize()
+    got_rel = to_np(call.out.data)
+    want = O.dense(spec, [to_np(x) for x in xs], ext, g=g, agg=agg, alpha=alpha, beta=beta, eps=eps, causal=causal)
+    want = O.round_to(want, out_dtype)
+    got = O.from_relation(got_rel, out, ext, blk)
+    pad = padding_mask(out, ext, blk)
+    return got, want, got_rel, pad, call
+
+
+CONTRACT_CASES = [
+    # spec, extents, blockings, input dtypes, out dtype
+    ("ij,jk->ik", dict(i=256, j=256, k=256), dict(i=4, j=4, k=4), "f32", "f32"),
+    ("ij,jk->ik", dict(i=200, j=130, k=70), dict(i=3, j=2, k=2), "f32", "f32"),
+    ("abcd,cde->abe", dict(a=13, b=31, c=16, d=12, e=100), dict(a=5, b=7, c=4, d=3, e=6), "f32", "f32"),
+    ("ij,jk->ik", dict(i=256, j=256, k=256), dict(i=2, j=4, k=2), "bf16", "f32"),
+    ("ij,kj->ik", dict(i=192, j=256, k=160), dict(i=2, j=2, k=1), "bf16", "f32"),
+    ("ji,jk->ik", dict(i=192, j=128, k=160), dict(i=1, j=2, k=1), "bf16", "f32"),
+    ("ji,kj->ik", dict(i=96, j=64, k=80), dict(i=1, j=2, k=1), "f32", "f32"),
+    ("ij,jk->ki", dict(i=96, j=64, k=80), dict(i=2, j=2, k=1), "f32", "f32"),
+    ("bhsd,bhtd->bhst", dict(b=2, h=3, s=256, t=256, d=128), dict(b=1, h=1, s=2, t=2, d=1), "bf16", "f32"),
+    ("bhst,bhtd->bhsd", dict(b=2, h=3, s=256, t=256, d=128), dict(b=1, h=1, s=2, t=2, d=1), "bf16", "f32"),
+    ("bsh,hqd->bsqd", dict(b=2, s=256, h=512, q=4, d=128), dict(b=1, s=2, h=4, q=2, d=1), "bf16", "bf16"),
+    ("bsf,fh->bsh", dict(b=2, s=128, f=688, h=256), dict(b=1, s=1, f=8, h=2), "bf16", "f32"),
+]
+
+
+@pytest.mark.parametrize("spec,ext,blk,idt,odt", CONTRACT_CASES)
+def test_contraction_parity(ctx, spec, ext, blk, idt, odt):
+    n_in = len(spec.split("->")[0].split(","))
+    got, want, got_rel, pad, _ = run_spec_case(ctx, spec, ext, blk, in_dtypes=[idt] * n_in, out_dtype=odt)
+    tol = F32_TOL if odt == "f32" else BF16_OUT_TOL
+    err = normwise_err(got, want)
+    assert err < tol, f"normwise error {err:.3e}"
+    assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
+
+
+EW_CASES = [
+    # spec, g, agg, extents, blockings, in dtypes, out dtype, positive inputs, causal
+    ("bhst->bhs", "ident", "max", dict(b=2, h=3, s=40, t=300), dict(b=1, h=1, s=3, t=4), ["f32"], "f32", (), None),
+    ("bhst,bhs->bhs", "exp_sub", "sum", dict(b=2, h=3, s=40, t=300), dict(b=1, h=1, s=3, t=4), ["f32", "f32"], "f32",
+     (), None),
+    ("bhst,bhs,bhs->bhst", "exp_sub_div", "none", dict(b=2, h=3, s=40, t=300), dict(b=1, h=1, s=3, t=4),
+     ["f32", "f32", "f32"], "bf16", (2,), None),
+    ("bsh->bs", "square", "sum", dict(b=2, s=50, h=1000), dict(b=1, s=3, h=4), ["f32"], "f32", (), None),
+    ("bsh,bs,h->bsh", "rms_scale", "none", dict(b=2, s=50, h=1000), dict(b=1, s=3, h=4), ["f32", "f32", "bf16"],
+     "bf16", (1,), None),
+    ("bsf,bsf->bsf", "silu_mul", "none", dict(b=2, s=50, f=688), dict(b=1, s=3, f=8), ["f32", "f32"], "bf16", (),
+     None),
+    ("bsh,bsh->bsh", "add", "none", dict(b=2, s=50, h=1000), dict(b=1, s=3, h=4), ["f32", "f32"], "f32", (), None),
+    ("ijk->ik", "ident", "sum", dict(i=30, j=70, k=50), dict(i=2, j=3, k=2), ["f32"], "f32", (), None),
+    ("ij,j->i", "mul", "sum", dict(i=300, j=1000), dict(i=3, j=4), ["f32", "f32"], "f32", (), None),
+    ("qst->qs", "ident", "max", dict(q=3, s=200, t=200), dict(q=1, s=4, t=4), ["f32"], "f32", (), ("s", "t")),
+    ("qst,qs->qs", "exp_sub", "sum", dict(q=3, s=200, t=200), dict(q=1, s=4, t=4), ["f32", "f32"], "f32", (),
+     ("s", "t")),
+    ("qst,qs,qs->qst", "exp_sub_div", "none", dict(q=3, s=200, t=200), dict(q=1, s=4, t=4), ["f32", "f32", "f32"],
+     "bf16", (2,), ("s", "t")),
+]
+
+
+@pytest.mark.parametrize("spec,g,agg,ext,blk,idts,odt,pos,causal", EW_CASES)
+def test_map_reduce_parity(ctx, spec, g, agg, ext, blk, idts, odt, pos, causal):
+    kw = dict(beta=1.0 / ext.get("h", 1), eps=1e-6) if g == "rms_scale" else {}
+    got, want, got_rel, pad, call = run_spec_case(ctx, spec, ext, blk, g=g, agg=agg, in_dtypes=idts, out_dtype=odt,
+                                                  positive=pos, causal=causal, **kw)
+    present = call.out.data  # noqa: F841
+    if causal is not None and agg == "none":
+        # tuples above the block diagonal are absent from the output relation
+        s, t = causal
+        out = spec.split("->")[1]
+        e = -(-ext[s] // blk[s])
+        mask = np.zeros(got.shape, dtype=bool)
+        idx = np.indices(got.shape)
+        mask = (idx[out.index(t)] // e) <= (idx[out.index(s)] // e)
+        got = np.where(mask, got, 0.0)
+        want = np.where(mask, want, 0.0)
+    if agg == "max":
+        assert np.array_equal(got, want), "MAX must be bit-exact"
+    else:
+        tol = F32_TOL if odt == "f32" else BF16_OUT_TOL
+        err = normwise_err(got, want)
+        assert err < tol, f"normwise error {err:.3e}"
+    if causal is None:
+        assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
+
+
+# ----------------------------------------------------------------- chains
+
+def oracle_chain(w, dense, stop=None):
+    """Evaluates a workload chain on the oracle, rounding each result to its
+    stored dtype exactly where the HIP path stores it."""
+    vals = {k: to_np(v) for k, v in dense.items()}
+    for st in w.chain:
+        if isinstance(st, I.Step):
+            ins = st.spec.split("->")[0].split(",")
+            xs = []
+            for name, lt in zip(st.ins, ins):
+                xs.append(vals[name])
+            y = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
+                        causal=st.causal)
+            vals[st.out] = O.round_to(y, st.out_dtype)
+        else:
+            src_letters = None
+            for t in w.tensors:
+                if t[0] == st.src:
+                    src_letters = t[1]
+            if src_letters is None:
+                src_letters = next(s for s in w.chain if getattr(s, "out", None) == st.src).spec.split("->")[1]
+            perm = [src_letters.index(c) for c in st.letters]
+            vals[st.out] = np.ascontiguousarray(vals[st.src].transpose(perm))
+        if stop is not None and st.out == stop:
+            break
+    return vals
+
+
+def test_attention_chain_small(ctx):
+    w = I.attention_chain(b=1, h=2, s=256, d=64, nb=4)
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    want = oracle_chain(w, dense)
+    for name in ["S", "M", "L", "P", "O"]:
+        got = rel_dense(run.rel[name], w.extents)
+        err = normwise_err(got, want[name])
+        tol = CHAIN_TOL if name in ("P", "O") else 1e-4
+        assert err < tol, f"{name}: normwise error {err:.3e}"
+    # MAX is exact on the GPU's own scores
+    S = rel_dense(run.rel["S"], w.extents)
+    M = rel_dense(run.rel["M"], w.extents)
+    assert np.array_equal(M, S.max(axis=-1))
+    P = rel_dense(run.rel["P"], w.extents)
+    assert np.allclose(P.sum(-1), 1.0, atol=2e-2)
+
+
+def test_matmul_config_256(ctx):
+    w = I.matmul_256()
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    want = oracle_chain(w, dense)
+    got = rel_dense(run.rel["C"], w.extents)
+    err = normwise_err(got, want["C"])
+    assert err < F32_TOL, f"normwise error {err:.3e}"
+
+
+def test_multi_index_config_sampled(ctx):
+    """'abcd,cde->abe' at full size, checked on sampled outputs."""
+    w = I.multi_index()
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    st = w.chain[0]
+    got = rel_dense(run.rel["C"], w.extents)
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, got.size, size=3000)
+    # include the ragged tail corner
+    idx = np.concatenate([idx, [got.size - 1]])
+    want = O.round_to(O.dense(st.spec, [to_np(dense["A"]), to_np(dense["B"])], w.extents, sample=idx), "f32")
+    err = normwise_err(got.reshape(-1)[idx], want)
+    assert err < F32_TOL, f"normwise error {err:.3e}"
+    blk = st.blockings
+    pad = padding_mask("abe", w.extents, blk)
+    assert np.all(to_np(run.rel["C"].data)[pad] == 0.0)
+
+
+def test_attention_config_sampled_rows(ctx):
+    """The full-size unfused attention chain; every stage checked on sampled
+    (b, h, s) rows against the oracle fed the GPU's stored inputs, and the
+    final output against the oracle chain on those rows."""
+    w = I.attention_chain()
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    B, H, S, T, D = (w.extents[c] for c in "bhstd")
+    rows = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(S))) for _ in range(24)]
+    rows.append((B - 1, H - 1, S - 1))
+    Q, K, V = (to_np(dense[n]) for n in "QKV")
+    Sg = to_np(jagg.to_dense(ctx, run.rel["S"]))
+    Mg = to_np(jagg.to_dense(ctx, run.rel["M"]))
+    Lg = to_np(jagg.to_dense(ctx, run.rel["L"]))
+    Pg = to_np(jagg.to_dense(ctx, run.rel["P"]))
+    Og = to_np(jagg.to_dense(ctx, run.rel["O"]))
+    for b, h, s in rows:
+        ext1 = dict(s=1, t=T, d=D)
+        s_row = O.round_to(O.dense("sd,td->st", [Q[b, h, s:s + 1], K[b, h]], ext1), "f32")
+        assert normwise_err(Sg[b, h, s], s_row[0]) < F32_TOL
+        srow = Sg[b, h, s:s + 1]
+        m = O.dense("st->s", [srow], dict(s=1, t=T), g="ident", agg="max")
+        assert m[0] == Mg[b, h, s]
+        l = O.round_to(O.dense("st,s->s", [srow, Mg[b, h, s:s + 1]], dict(s=1, t=T), g="exp_sub"), "f32")
+        assert normwise_err(Lg[b, h, s:s + 1], l) < F32_TOL
+        p = O.round_to(O.dense("st,s,s->st", [srow, Mg[b, h, s:s + 1], Lg[b, h, s:s + 1]], dict(s=1, t=T),
+                               g="exp_sub_div", agg="none"), "bf16")
+        assert normwise_err(Pg[b, h, s], p[0]) < BF16_OUT_TOL
+        o = O.round_to(O.dense("st,td->sd", [Pg[b, h, s:s + 1], V[b, h]], dict(s=1, t=T, d=D)), "f32")
+        assert normwise_err(Og[b, h, s], o[0]) < F32_TOL
+        # the chain from the original inputs, with the same cast points
+        sc = O.round_to(O.dense("sd,td->st", [Q[b, h, s:s + 1], K[b, h]], ext1), "f32")
+        mc = O.dense("st->s", [sc], dict(s=1, t=T), g="ident", agg="max")
+        lc = O.round_to(O.dense("st,s->s", [sc, mc], dict(s=1, t=T), g="exp_sub"), "f32")
+        pc = O.round_to(O.dense("st,s,s->st", [sc, mc, lc], dict(s=1, t=T), g="exp_sub_div", agg="none"), "bf16")
+        oc = O.dense("st,td->sd", [pc, V[b, h]], dict(s=1, t=T, d=D))
+        assert normwise_err(Og[b, h, s], oc[0]) < CHAIN_TOL
