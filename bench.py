@@ -1,0 +1,251 @@
+"""Benchmark of the join-agg einsum executor on one MI355X.
+
+One step = one pass of the whole hot path over the LLaMA-7B-shaped block
+(4 x 2048 tokens, hidden 4096, 32 heads x 128, SwiGLU 11008, bf16 weights):
+every operator is a join-agg spec (join enumeration, MFMA block contraction,
+streaming map / SUM-MAX reduce) and the head-major relayouts around the
+causal attention are repartitions.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
+
+Prints one JSON line: value = algorithmic TFLOP/s of the step (contraction
+FLOPs, causal attention counted element-wise), a roofline entry for the
+dominant kernel (the bf16 MFMA contraction of the projection / FFN specs),
+the repartition GB/s of the 8192^2 and 4-D reblocking workloads, and the
+CPU oracle timed on a bounded sample of the same specs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from tensor_relational_einsum_amd import inputs as I  # noqa: E402
+from tensor_relational_einsum_amd import jagg  # noqa: E402
+from tensor_relational_einsum_amd.runner import ChainRunner  # noqa: E402
+
+METRIC = "join-agg einsum TFLOP/s (% bf16 MFMA peak) + repartition GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def spec_flops(st: I.Step, ext: dict) -> float:
+    """Algorithmic FLOPs of a contraction spec: 2 per multiply-add over the
+    unpadded index space; under a causal pair only t <= s is counted."""
+    if not (st.g == "mul" and st.agg == "sum" and len(st.ins) == 2):
+        return 0.0
+    letters = set("".join(st.spec.split("->")[0].split(",")))
+    n = 1.0
+    for c in letters:
+        n *= ext[c]
+    if st.causal:
+        s, t = st.causal
+        S = ext[s]
+        n = n / (ext[s] * ext[t]) * (S * (S + 1) / 2)
+    return 2.0 * n
+
+
+def spec_bytes(run: ChainRunner, st, ext: dict) -> float:
+    """Algorithmic bytes of a spec or relayout: every valid element of each
+    input read once and of the output written once."""
+    def rel_bytes(name):
+        r = run.rel[name]
+        return math.prod(r.extents) * jagg.ESZ[r.dtype]
+    if isinstance(st, I.Relayout):
+        return 2.0 * rel_bytes(st.src)
+    b = rel_bytes(st.out) + sum(rel_bytes(n) for n in st.ins)
+    if st.causal:
+        # score-shaped operands only hold t <= s
+        s, t = st.causal
+        frac = (ext[s] + 1) / (2 * ext[s])
+        b = 0.0
+        for n in list(st.ins) + [st.out]:
+            r = run.rel[n]
+            full = math.prod(r.extents) * jagg.ESZ[r.dtype]
+            b += full * frac if (s in r.letters and t in r.letters) else full
+    return b
+
+
+def timed_chain(run: ChainRunner, steps: int, warmup: int):
+    stream = run.ctx.stream
+    n = len(run.calls)
+    for _ in range(warmup):
+        run.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        for i in range(n):
+            run.run_step(i)
+            ev[k][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = np.zeros((steps, n))
+    step_ms = np.zeros(steps)
+    for k in range(steps):
+        for i in range(n):
+            per_call[k, i] = ev[k][i].elapsed_time(ev[k][i + 1])
+        step_ms[k] = ev[k][0].elapsed_time(ev[k][n])
+    return step_ms, per_call, wall
+
+
+def flush_caches(buf):
+    buf.add_(1)  # 512 MiB read-modify-write evicts L2 and the 256 MB Infinity Cache
+
+
+def repartition_rate(ctx, w: I.Workload, reps: int, scratch) -> dict:
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    st = w.chain[0]
+    src, dst = run.rel[st.src], run.rel[st.out]
+    nbytes = 2.0 * math.prod(src.extents) * jagg.ESZ[src.dtype]
+    for _ in range(3):
+        jagg.repartition(ctx, src, dst)
+    times = []
+    for _ in range(reps):
+        flush_caches(scratch)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(ctx.stream)
+        jagg.repartition(ctx, src, dst)
+        b.record(ctx.stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    med = float(np.median(times))
+    gbps = nbytes / (med * 1e-3) / 1e9
+    return {"workload": w.name, "bytes": nbytes, "ms_median": med, "ms_min": float(np.min(times)),
+            "GB/s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS}
+
+
+def cpu_baseline(w: I.Workload, dense: dict, target_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the block's
+    contraction specs: sampled outputs of each projection / FFN spec, scaled
+    to TFLOP/s from the sampled multiply-adds."""
+    from oracle import oracle as O
+
+    vals = {k: v.to(torch.float64).numpy() for k, v in dense.items() if v.dim() > 0}
+    # the projection specs read r1 / r2 (bf16); a stand-in with the same
+    # shape and distribution is enough to time the oracle's loops
+    gen = I.streams(4242, 2)
+    vals["r1"] = I.draw(gen[0], [w.extents[c] for c in "bsh"], "normal", "bf16").to(torch.float64).numpy()
+    vals["r2"] = vals["r1"]
+    vals["O"] = I.draw(gen[1], [w.extents[c] for c in "bsqd"], "normal", "bf16").to(torch.float64).numpy()
+    specs = [st for st in w.chain if isinstance(st, I.Step) and spec_flops(st, w.extents) > 0 and not st.causal
+             and all(n in vals for n in st.ins)]
+    rng = np.random.default_rng(0)
+    # calibrate on a small sample, then size the run to about target_s
+    st = specs[0]
+    out_shape = [w.extents[c] for c in st.spec.split("->")[1]]
+    t0 = time.perf_counter()
+    O.dense(st.spec, [vals[n] for n in st.ins], w.extents, sample=rng.integers(0, math.prod(out_shape), 2000))
+    per_flop = (time.perf_counter() - t0) / (2000 * spec_flops(st, w.extents) / math.prod(out_shape))
+    budget = target_s / len(specs)
+    flops = 0.0
+    t_total = 0.0
+    samples = 0
+    for st in specs:
+        out_shape = [w.extents[c] for c in st.spec.split("->")[1]]
+        per_out = spec_flops(st, w.extents) / math.prod(out_shape)
+        k = max(1000, int(budget / (per_flop * per_out)))
+        idx = rng.integers(0, math.prod(out_shape), k)
+        t0 = time.perf_counter()
+        O.dense(st.spec, [vals[n] for n in st.ins], w.extents, sample=idx)
+        t_total += time.perf_counter() - t0
+        flops += k * per_out
+        samples += k
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{samples} sampled outputs of the {len(specs)} projection/FFN contraction specs "
+                      f"(fp64 nested loops, {t_total:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama", choices=["llama", "attention", "multi_index", "matmul"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-repartition", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this executor has no multi-GPU path "
+              "(the sharding design is described, not built); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    ctx = jagg.Context(0)
+    w = {"llama": I.llama_block, "attention": I.attention_chain, "multi_index": I.multi_index,
+         "matmul": I.matmul_256}[args.workload]()
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    step_ms, per_call, wall = timed_chain(run, args.steps, args.warmup)
+    ms = float(np.mean(step_ms))
+    steps = [st for st in w.chain]
+    flops = sum(spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0 for st in steps)
+    value = flops / (ms * 1e-3) / 1e12
+    call_ms = per_call.mean(axis=0)
+    breakdown = []
+    dom_flops = dom_ms = 0.0
+    dom_launches = 0
+    for i, st in enumerate(steps):
+        f = spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0
+        by = spec_bytes(run, st, w.extents)
+        ent = {"name": st.out, "op": st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}",
+               "ms": round(float(call_ms[i]), 4)}
+        if f:
+            ent["TFLOP/s"] = round(f / (call_ms[i] * 1e-3) / 1e12, 2)
+        ent["GB/s"] = round(by / (call_ms[i] * 1e-3) / 1e9, 1)
+        breakdown.append(ent)
+        if isinstance(st, I.Step) and f and not st.causal and run.rel[st.ins[0]].dtype == "bf16":
+            dom_flops += f
+            dom_ms += float(call_ms[i])
+            dom_launches += 1
+    # the arithmetic type of the dominant kernel: the inputs of the largest contraction
+    big = max((st for st in steps if isinstance(st, I.Step)), key=lambda st: spec_flops(st, w.extents))
+    in_dtype = run.rel[big.ins[0]].dtype
+    if dom_launches:
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "contract_kernel<bf16> (projection / FFN specs)", "launches_per_step": dom_launches,
+                "avg_launch_ms": round(dom_ms / dom_launches, 4)}
+    else:
+        peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS
+        achieved = value
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": f"contract_kernel<{in_dtype}>"}
+    rep = {}
+    if not args.no_repartition:
+        del run
+        torch.cuda.empty_cache()
+        scratch = torch.zeros(512 << 20 >> 2, dtype=torch.float32, device="cuda")
+        rep = {"8192x8192": repartition_rate(ctx, I.repartition_2d(), 15, scratch),
+               "32x128x64x64": repartition_rate(ctx, I.repartition_4d(), 15, scratch)}
+        del scratch
+    cpu = None
+    if not args.no_cpu_baseline and args.workload == "llama":
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, dense)
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": in_dtype, "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": w.name, "extents": w.extents, "step_flops": flops, "wall_s": round(wall, 3)},
+        "roofline": roof, "cpu_baseline": cpu, "repartition": rep, "breakdown": breakdown,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -358,3 +358,86 @@ def test_attention_config_sampled_rows(ctx):
         pc = O.round_to(O.dense("st,s,s->st", [sc, mc, lc], dict(s=1, t=T), g="exp_sub_div", agg="none"), "bf16")
         oc = O.dense("st,td->sd", [pc, V[b, h]], dict(s=1, t=T, d=D))
         assert normwise_err(Og[b, h, s], oc[0]) < CHAIN_TOL
+
+
+def sampled_spec_check(ctx, run, w, n_samples=400, seed=2):
+    """Every spec of a chain checked on sampled outputs against the oracle
+    fed the GPU's own stored inputs; every relayout checked bit-exactly."""
+    rng = np.random.default_rng(seed)
+    dense_cache = {}
+
+    def dense_of(name):
+        if name not in dense_cache:
+            dense_cache[name] = jagg.to_dense(ctx, run.rel[name]).to("cpu")
+        return dense_cache[name]
+
+    for st in w.chain:
+        if isinstance(st, I.Relayout):
+            src, dst = run.rel[st.src], run.rel[st.out]
+            ext = dict(zip(src.letters, src.extents))
+            want = O.repartition(bits(src.data), src.letters, src.blocking(), dst.letters, dst.blocking(), ext)
+            assert np.array_equal(bits(dst.data), want), f"relayout {st.out}"
+            continue
+        out_l = st.spec.split("->")[1]
+        got = dense_of(st.out)
+        idx = rng.integers(0, got.numel(), size=n_samples)
+        idx = np.concatenate([idx, [got.numel() - 1]])
+        xs = [to_np(dense_of(n)) for n in st.ins]
+        want = O.round_to(O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta,
+                                  eps=st.eps, causal=st.causal, sample=idx), st.out_dtype)
+        g = to_np(got).reshape(-1)[idx]
+        if st.causal is not None and st.agg == "none" or (st.causal is not None and st.g == "mul" and
+                                                          st.causal[1] in out_l):
+            # elements in absent tuples (t-block after s-block) are not stored
+            s, t = st.causal
+            shp = [w.extents[c] for c in out_l]
+            coords = np.unravel_index(idx, shp)
+            e = -(-w.extents[s] // st.blockings[s])
+            keep = coords[out_l.index(t)] // e <= coords[out_l.index(s)] // e
+            g, want = g[keep], want[keep]
+        if st.agg == "max":
+            assert np.array_equal(g, want), f"{st.out}: MAX differs"
+        else:
+            tol = F32_TOL if st.out_dtype == "f32" else BF16_OUT_TOL
+            err = normwise_err(g, want)
+            assert err < tol, f"{st.out} ({st.spec}): normwise error {err:.3e}"
+
+
+def test_llama_block_small(ctx):
+    w = I.llama_block(b=1, s=256, hid=512, heads=4, d=128, ffn=1376, s_blk=4, h_blk=4, q_blk=2, f_blk=8)
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    want = oracle_chain(w, dense)
+    for name in ["ss1", "r1", "Qp", "Kp", "Vp", "S", "M", "L", "P", "Oh", "A", "x2", "r2", "G", "U", "H", "D", "y"]:
+        got = rel_dense(run.rel[name], w.extents)
+        ref = want[name]
+        if name in ("S", "P"):
+            mask = np.tril(np.ones((w.extents["s"], w.extents["t"]), dtype=bool))
+            got, ref = got[..., mask], ref[..., mask]
+        err = normwise_err(got, ref)
+        assert err < CHAIN_TOL, f"{name}: normwise error {err:.3e}"
+    sampled_spec_check(ctx, run, w, n_samples=200)
+
+
+def test_llama_block_config_sampled(ctx):
+    """The full LLaMA-7B-shaped block (4 x 2048 tokens), each spec checked on
+    sampled outputs, each relayout bit-exactly."""
+    w = I.llama_block()
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    sampled_spec_check(ctx, run, w, n_samples=300)
+
+
+def test_multi_index_and_attention_configs_per_spec(ctx):
+    for w in (I.multi_index(), I.attention_chain()):
+        dense = I.generate(w)
+        run = ChainRunner(ctx, w, dense)
+        run.run()
+        torch.cuda.synchronize()
+        sampled_spec_check(ctx, run, w, n_samples=300)
+        del run
+        torch.cuda.empty_cache()
