@@ -700,6 +700,10 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
   a.tiles_m = (a.M + 127) / 128;
   a.tiles_n = (a.N + 127) / 128;
   a.n_keys = b.join.n_keys;
+  a.div_s = a.div_t = make_fastdiv(1);
+  // blocks addressed through 32-bit buffer offsets
+  if (RA.be * esz_of(RA.dt) >= (int64_t(1) << 31) || RB.be * esz_of(RB.dt) >= (int64_t(1) << 31))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "contraction block of 2 GiB or more");
   if (sp->causal_s) {
     const char s = sp->causal_s, t = sp->causal_t;
     const int cs = s - 'a', ct = t - 'a';
@@ -710,6 +714,8 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
     };
     a.e_s = int32_t((b.L.n[cs] + b.L.k[cs] - 1) / b.L.k[cs]);
     a.e_t = int32_t((b.L.n[ct] + b.L.k[ct] - 1) / b.L.k[ct]);
+    a.div_s = make_fastdiv(uint32_t(a.e_s));
+    a.div_t = make_fastdiv(uint32_t(a.e_t));
     a.cs_w = out_w(s);
     a.cs_k = b.L.k[cs];
     a.ct_k = b.L.k[ct];
@@ -726,6 +732,9 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
       a.causal_red = 1;
       const size_t q = p.in[ia].find(t);
       a.ct_w = tuple_w(RA, int(q));
+      const int F = dtype ? 8 : 4;
+      if (va != F || vb != F)
+        return fail(ctx, JAGG_E_UNSUPPORTED, "causal contraction over a reduced letter needs 16-byte aligned operands");
     }
   }
   if (ctx->trace)
@@ -947,9 +956,19 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   b.join.list = list;
   b.join.counts = counts;
   if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
-  if (kind == CONTRACT)
-    return after_launch(ctx, launch_contract(ca, dtype, spec->out_dtype == JAGG_BF16, akc, bkc, va, vb, ctx->stream),
-                        "contract");
+  if (kind == CONTRACT) {
+    // 256x256 tiles where the block is large enough and the grid still fills the chip
+    const int F = dtype ? 8 : 4;
+    const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + 255) / 256);
+    const bool big = va == F && vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
+    // per-XCD renumbering pays where several tiles of one output block share panels
+    const int bm = big ? 256 : 128;
+    ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
+    const int ob = spec->out_dtype == JAGG_BF16;
+    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream)
+                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream);
+    return after_launch(ctx, e, "contract");
+  }
   if (kind == MAP) return after_launch(ctx, launch_map(ew, ctx->stream), "map");
   return after_launch(ctx, launch_reduce(ew, ctx->stream), "reduce");
 }

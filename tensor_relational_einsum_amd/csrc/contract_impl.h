@@ -1,0 +1,437 @@
+// contract_impl.h -- MFMA block contraction with the SUM aggregation fused.
+//
+// "Every Kernel Is a Join" (Ding et al.), Sec. 1 and Examples 3.8/3.9: a
+// matrix multiply is a join on the shared inner index followed by a SUM;
+// every joined tuple multiplies one block of each input and the products of
+// equal output key are added (Def. 3.7 step 2).  One workgroup owns one
+// BM x BN tile of one output block (and one batch index) and walks every
+// joined tuple of that output key and the K-tiles of each, accumulating in
+// fp32 registers; the tile is written once, so the aggregation never goes
+// through memory (the page's aggregation pushdown, on one GPU).
+//
+// CDNA4 mapping
+//  - MFMA 32x32: bf16 v_mfma_f32_32x32x16_bf16, fp32 v_mfma_f32_32x32x2_f32.
+//    Lane l of a fragment owns row/column l%32 and the K values
+//    8*(l/32)..+7 (bf16) or 4*(l/32)..+3 (fp32, one per MFMA).
+//  - Each operand tile is staged in LDS in its own global orientation, one
+//    BK-deep slab of 128 bytes per row: K-contiguous tiles as [rows][BK],
+//    M/N-contiguous tiles as [BK][rows].  Global loads (buffer loads whose
+//    out-of-range lanes read zeros) and LDS stores are 16-byte vectors.
+//    Rows are padded (16 bytes for K-contiguous tiles, 64 bytes for the
+//    others) so the fragment reads below spread over the 64 LDS banks while
+//    every fragment address stays a register base plus an immediate.
+//  - Fragment reads: ds_read_b128 for K-contiguous tiles; for bf16
+//    M/N-contiguous tiles two ds_read_b64_tr_b16, whose 16-lane transpose
+//    turns four 4-element row pieces into four 4-element K columns; for
+//    fp32 M/N-contiguous tiles one ds_read_b32 per MFMA.
+//  - Two LDS stages: the global loads of step s+1 are in flight while the
+//    MFMAs of step s run; one barrier per step.
+//  - Workgroups are renumbered so that consecutive tiles of one output row
+//    panel land on the same XCD (dispatch round-robins workgroups over the
+//    8 XCDs, each with its own L2).
+#pragma once
+#include "device_common.h"
+#include "jagg_internal.h"
+
+namespace jagg {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+template <int NB>
+struct VecT;
+template <>
+struct VecT<16> {
+  using type = uint4;
+};
+template <>
+struct VecT<4> {
+  using type = uint32_t;
+};
+template <>
+struct VecT<2> {
+  using type = uint16_t;
+};
+
+constexpr int kSlab = 128;  // bytes of K per tile row (BK = 128 / sizeof(T))
+constexpr int kPitchKC = kSlab + 16;
+
+// LDS row pitch of an operand tile of R rows
+template <bool KC, int R, int ESZ>
+constexpr int tile_pitch() {
+  return KC ? kPitchKC : R * ESZ + 64;
+}
+template <bool KC, int R, int ESZ>
+constexpr int tile_bytes() {
+  return KC ? R * kPitchKC : (kSlab / ESZ) * (R * ESZ + 64);
+}
+
+// Buffer-resource loads: the scalar resource holds the tile origin and the
+// bytes left in the block; a lane whose element lies outside the tile passes
+// an offset past the end, and the hardware returns zeros for it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *origin, int64_t bytes_left) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(origin), (short)0, int(bytes_left), 0x00020000);
+}
+constexpr uint32_t kOob = 0x80000000u;  // past any block (blocks stay under 2 GiB)
+
+template <int NB>
+__device__ __forceinline__ typename VecT<NB>::type buf_load(__amdgpu_buffer_rsrc_t rs, uint32_t off);
+template <>
+__device__ __forceinline__ uint4 buf_load<16>(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+template <>
+__device__ __forceinline__ uint32_t buf_load<4>(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, int(off), 0, 0);
+}
+template <>
+__device__ __forceinline__ uint16_t buf_load<2>(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(rs, int(off), 0, 0);
+}
+
+// One operand tile: R rows (M or N) by BK, KC = contiguous along K.  Thread
+// t's load i covers LDS row lr0 + i*DR (DR rows per sweep of the threads),
+// at element lc0 of that row.
+template <typename T, bool KC, int R, int VEC, int NT>
+struct Tile {
+  static constexpr int ESZ = int(sizeof(T));
+  static constexpr int BK = kSlab / ESZ;
+  static constexpr int PITCH = tile_pitch<KC, R, ESZ>();     // LDS row pitch (bytes)
+  static constexpr int RUN = KC ? BK : R;                   // elements per LDS row
+  static constexpr int RUNV = RUN / VEC;                    // vectors per LDS row
+  static constexpr int DR = NT / RUNV;                      // LDS rows per sweep
+  static constexpr int NV = R * BK / VEC / NT;              // loads per thread
+  static_assert(NV >= 1 && NT % RUNV == 0 && R * BK % (VEC * NT) == 0, "tile does not split over the threads");
+  using V = typename VecT<VEC * ESZ>::type;
+  union U {
+    V v;
+    T e[VEC];
+  };
+  U r[NV];
+  int lr0, lc0;
+  uint32_t voff0;  // byte offset of load 0 from the tile origin
+  uint32_t vstep;  // bytes between consecutive loads (uniform)
+
+  __device__ __forceinline__ void init(int64_t s_row, int64_t s_k) {
+    lr0 = int(threadIdx.x) / RUNV;
+    lc0 = (int(threadIdx.x) % RUNV) * VEC;
+    const int64_t row = KC ? lr0 : lc0, k = KC ? lc0 : lr0;
+    voff0 = uint32_t((row * s_row + k * s_k) * ESZ);
+    vstep = uint32_t(int64_t(DR) * (KC ? s_row : s_k) * ESZ);
+  }
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int rows_left, int k_left) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int lr = lr0 + i * DR;
+      const int row = KC ? lr : lc0, k = KC ? lc0 : lr;
+      const uint32_t off = (row < rows_left && k < k_left) ? voff0 + uint32_t(i) * vstep : kOob;
+      r[i].v = buf_load<VEC * ESZ>(rs, off);
+    }
+  }
+
+  // zero every element with t > s (s along the tile rows, t along K)
+  __device__ __forceinline__ void mask_causal(int64_t s0, int64_t t0, const FastDiv &ds, const FastDiv &dt, int m0,
+                                              int k0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int lr = lr0 + i * DR;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const uint32_t row = KC ? lr : lc0 + u, k = KC ? lc0 + u : lr;
+        const uint32_t mr = m0 + row, kr = k0 + k;
+        const int64_t sg = s0 + (mr - fd_div(mr, ds) * ds.d);
+        const int64_t tg = t0 + (kr - fd_div(kr, dt) * dt.d);
+        if (tg > sg) r[i].e[u] = T(0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char *lds) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<V *>(lds + (lr0 + i * DR) * PITCH + lc0 * ESZ) = r[i].v;
+  }
+};
+
+// Fragment readers --------------------------------------------------------
+// bf16, K-contiguous tile: 8 K values of row `row`, K chunk `kc` (16 wide).
+__device__ __forceinline__ uint4 frag_bf16_kc(const char *lds, int row, int kc, int lhalf) {
+  return *reinterpret_cast<const uint4 *>(lds + row * kPitchKC + kc * 32 + lhalf * 16);
+}
+
+// bf16, M/N-contiguous tile [BK][R]: the same fragment through two
+// transposing reads.  Lane s of each 16-lane group names the 4-element row
+// piece at K row k0 + (s>>2), columns n0 + 4*(s&3); the read hands lane j of
+// the group K rows k0..k0+3 of column n0 + j.
+template <int PITCH>
+__device__ __forceinline__ uint4 frag_bf16_rc(const char *lds, int col0, int kc, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int n = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const int kb = kc * 16 + 8 * (g >> 1) + (s >> 2);
+  typedef __attribute__((address_space(3))) i16x4 *lds_v4;
+  char *p0 = const_cast<char *>(lds) + kb * PITCH + n * 2;
+  // C-style casts lower to an address-space cast from the generic pointer
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0 + 4 * PITCH));
+  uint4 r;
+  __builtin_memcpy(&r.x, &lo, 8);
+  __builtin_memcpy(&r.z, &hi, 8);
+  return r;
+}
+
+// fp32, K-contiguous tile: K values 8*kc + 4*lhalf + 0..3 of row `row`.
+__device__ __forceinline__ uint4 frag_f32_kc(const char *lds, int row, int kc, int lhalf) {
+  return *reinterpret_cast<const uint4 *>(lds + row * kPitchKC + kc * 32 + lhalf * 16);
+}
+
+// fp32, M/N-contiguous tile [BK][R]: the same four K values of column `col`.
+template <int PITCH>
+__device__ __forceinline__ uint4 frag_f32_rc(const char *lds, int col, int kc, int lhalf) {
+  const char *p = lds + (8 * kc + 4 * lhalf) * PITCH + col * 4;
+  uint4 r;
+  r.x = *reinterpret_cast<const uint32_t *>(p);
+  r.y = *reinterpret_cast<const uint32_t *>(p + PITCH);
+  r.z = *reinterpret_cast<const uint32_t *>(p + 2 * PITCH);
+  r.w = *reinterpret_cast<const uint32_t *>(p + 3 * PITCH);
+  return r;
+}
+
+template <typename T>
+struct Mma;
+template <>
+struct Mma<uint16_t> {
+  // one 16-wide K chunk
+  __device__ __forceinline__ static void run(f32x16 &acc, const uint4 &a, const uint4 &b) {
+    bf16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<float> {
+  // one 8-wide K chunk: lane half h holds K = 4h + i for MFMA i, in both
+  // operands alike, so the four MFMAs together cover the chunk
+  __device__ __forceinline__ static void run(f32x16 &acc, const uint4 &a, const uint4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
+          bool MASK>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int ESZ = int(sizeof(T));
+  constexpr int BK = kSlab / ESZ;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int KCH = ESZ == 2 ? BK / 16 : BK / 8;  // fragment chunks per K-tile
+  using TA = Tile<T, A_KC, BM, VA, NT>;
+  using TB = Tile<T, B_KC, BN, VB, NT>;
+  constexpr int A_BYTES = tile_bytes<A_KC, BM, ESZ>(), B_BYTES = tile_bytes<B_KC, BN, ESZ>();
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  // workgroup -> tile; where neighbouring tiles share operand panels, the
+  // numbering gives each XCD a contiguous run of tiles
+  int64_t w = blockIdx.x;
+  {
+    const int64_t G = gridDim.x;
+    if (p.remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+  }
+  const int tn = int(w % p.tiles_n);
+  w /= p.tiles_n;
+  const int tm = int(w % p.tiles_m);
+  w /= p.tiles_m;
+  const int bt = int(w % p.batch);
+  const int64_t key = w / p.batch;
+
+  const int32_t cnt = p.counts[key];
+  if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier
+  const int32_t *ents = p.list + key * int64_t(p.per_key) * 3;
+
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KT = (p.K + BK - 1) / BK;
+  const int steps = cnt * KT;
+  const int64_t a_org = int64_t(bt) * p.sAb + int64_t(m0) * p.sAm;
+  const int64_t b_org = int64_t(bt) * p.sBb + int64_t(n0) * p.sBn;
+  int64_t ks = 0;
+  if (p.causal_out || p.causal_red) ks = (key / p.cs_w) % p.cs_k;
+
+  TA ta;
+  TB tb;
+  ta.init(p.sAm, p.sAk);
+  tb.init(p.sBn, p.sBk);
+  auto load_step = [&](int s) {
+    const int e = s / KT;
+    const int kt = s - e * KT;
+    const int32_t *ent = ents + e * 3;
+    const int64_t aid = ent[p.a_slot], bid = ent[p.b_slot];
+    const int k0 = kt * BK;
+    const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
+    const T *pa = reinterpret_cast<const T *>(p.A) + aid * p.beA + ao;
+    const T *pb = reinterpret_cast<const T *>(p.B) + bid * p.beB + bo;
+    ta.load(tile_rsrc(pa, (p.beA - ao) * ESZ), p.M - m0, p.K - k0);
+    tb.load(tile_rsrc(pb, (p.beB - bo) * ESZ), p.N - n0, p.K - k0);
+  };
+  // causal pair with t reduced: zero A where t > s, on the diagonal block only;
+  // applied just before the LDS store so the loads stay in flight meanwhile
+  auto mask_step = [&](int s) {
+    if (MASK && p.causal_red) {
+      const int e = s / KT;
+      const int k0 = (s - e * KT) * BK;
+      const int64_t aid = ents[e * 3 + p.a_slot];
+      const int64_t kt_blk = (aid / p.ct_w) % p.ct_k;
+      if (kt_blk == ks) ta.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, k0);
+    }
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = (wave / WAVES_N) * WTM, wn = (wave % WAVES_N) * WTN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  load_step(0);
+  mask_step(0);
+  ta.store(smem);
+  tb.store(smem + A_BYTES);
+  __syncthreads();
+
+  for (int s = 0; s < steps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < steps) load_step(s + 1);
+    const char *As = smem + cur * STAGE;
+    const char *Bs = As + A_BYTES;
+    // fragments of K chunk kc+1 are read while the MFMAs of chunk kc run
+    uint4 af[2][TM], bfr[2][TN];
+    auto read_frags = [&](int kc, uint4 *a, uint4 *b) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (ESZ == 2) {
+          if constexpr (A_KC) a[i] = frag_bf16_kc(As, wm + i * 32 + lrow, kc, lhalf);
+          else a[i] = frag_bf16_rc<TA::PITCH>(As, wm + i * 32, kc, lane);
+        } else {
+          if constexpr (A_KC) a[i] = frag_f32_kc(As, wm + i * 32 + lrow, kc, lhalf);
+          else a[i] = frag_f32_rc<TA::PITCH>(As, wm + i * 32 + lrow, kc, lhalf);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (ESZ == 2) {
+          if constexpr (B_KC) b[j] = frag_bf16_kc(Bs, wn + j * 32 + lrow, kc, lhalf);
+          else b[j] = frag_bf16_rc<TB::PITCH>(Bs, wn + j * 32, kc, lane);
+        } else {
+          if constexpr (B_KC) b[j] = frag_f32_kc(Bs, wn + j * 32 + lrow, kc, lhalf);
+          else b[j] = frag_f32_rc<TB::PITCH>(Bs, wn + j * 32 + lrow, kc, lhalf);
+        }
+      }
+    };
+    read_frags(0, af[0], bfr[0]);
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) {
+      if (kc + 1 < KCH) read_frags(kc + 1, af[(kc + 1) & 1], bfr[(kc + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[kc & 1][i], bfr[kc & 1][j]);
+    }
+    if (s + 1 < steps) {
+      char *nx = smem + (cur ^ 1) * STAGE;
+      mask_step(s + 1);
+      ta.store(nx);
+      tb.store(nx + A_BYTES);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: scale, mask, convert, store (row = 8*(v/4) + 4*half + v%4, col = lane%32)
+  const int32_t out_id = ents[0];
+  char *Cb = reinterpret_cast<char *>(p.C);
+  const int64_t cbase = int64_t(out_id) * p.beC + int64_t(bt) * p.sCb;
+  int64_t kt_out = 0;
+  if (p.causal_out) kt_out = (key / p.ct_w) % p.ct_k;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + i * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
+        const int n = n0 + wn + j * 32 + lrow;
+        if (m < p.M && n < p.N) {
+          float x = p.alpha * acc[i][j][v];
+          if (p.causal_out) {
+            const int64_t sg = ks * p.e_s + (uint32_t(m) - fd_div(uint32_t(m), p.div_s) * p.div_s.d);
+            const int64_t tg = kt_out * p.e_t + (uint32_t(n) - fd_div(uint32_t(n), p.div_t) * p.div_t.d);
+            if (tg > sg) x = 0.0f;
+          }
+          const int64_t off = cbase + int64_t(m) * p.sCm + n;
+          if (OUT_BF16)
+            reinterpret_cast<uint16_t *>(Cb)[off] = f32_to_bf16(x);
+          else
+            reinterpret_cast<float *>(Cb)[off] = x;
+        }
+      }
+}
+
+template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false>
+static hipError_t launch_tile(const ContractArgs &a, hipStream_t st) {
+  ContractArgs b = a;
+  b.tiles_m = (a.M + BM - 1) / BM;
+  b.tiles_n = (a.N + BN - 1) / BN;
+  const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
+  hipLaunchKernelGGL((contract_kernel<T, OB, AK, BKC, VA, VB, BM, BN, WM, WN, MASK>), dim3(unsigned(grid)),
+                     dim3(WM * WN * 64), 0, st, b);
+  return hipGetLastError();
+}
+
+// big: 256x256 tiles, 8 wavefronts of 128x64; small: 128x128, 4 of 64x64.
+template <typename T, int OB, bool AK, bool BKC>
+static hipError_t launch_layout(const ContractArgs &a, int va, int vb, bool big, hipStream_t st) {
+  constexpr int F = 16 / int(sizeof(T));
+  if (a.causal_red) {
+    // the masked variant: 128x128 tiles, 16-byte loads only
+    if (va == F && vb == F && !big) return launch_tile<T, OB, AK, BKC, F, F, 128, 128, 2, 2, true>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (va == F && vb == F) {
+    if (big) return launch_tile<T, OB, AK, BKC, F, F, 256, 256, 2, 4>(a, st);
+    return launch_tile<T, OB, AK, BKC, F, F, 128, 128, 2, 2>(a, st);
+  }
+  if (va == F && vb == 1) return launch_tile<T, OB, AK, BKC, F, 1, 128, 128, 2, 2>(a, st);
+  if (va == 1 && vb == F) return launch_tile<T, OB, AK, BKC, 1, F, 128, 128, 2, 2>(a, st);
+  if (va == 1 && vb == 1) return launch_tile<T, OB, AK, BKC, 1, 1, 128, 128, 2, 2>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_typed(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
+                               hipStream_t st) {
+#define JAGG_LAYOUTS(OB)                                                              \
+  if (a_kc && b_kc) return launch_layout<T, OB, true, true>(a, va, vb, big, st);      \
+  if (a_kc && !b_kc) return launch_layout<T, OB, true, false>(a, va, vb, big, st);    \
+  if (!a_kc && b_kc) return launch_layout<T, OB, false, true>(a, va, vb, big, st);    \
+  return launch_layout<T, OB, false, false>(a, va, vb, big, st);
+  if (out_bf16) {
+    JAGG_LAYOUTS(1)
+  } else {
+    JAGG_LAYOUTS(0)
+  }
+#undef JAGG_LAYOUTS
+}
+
+}  // namespace jagg

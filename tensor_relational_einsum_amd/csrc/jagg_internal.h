@@ -126,11 +126,16 @@ struct ContractArgs {
   int64_t cs_w, cs_k;           // kappa_s = (out_tuple / cs_w) % cs_k
   int64_t ct_w, ct_k;           // kappa_t = (tuple / ct_w) % ct_k  (out tuple, or A tuple when reduced)
   int32_t e_s, e_t;
+  FastDiv div_s, div_t;         // division by e_s / e_t
+  int32_t remap;                // renumber workgroups per XCD (tiles share operand panels)
 };
-// dtype: 0 f32 inputs, 1 bf16 inputs; out_dtype 0 f32 / 1 bf16;
-// a_kc / b_kc: operand contiguous along K; va / vb: vector width (elements) of global loads.
-hipError_t launch_contract(const ContractArgs &a, int dtype, int out_dtype, bool a_kc, bool b_kc, int va, int vb,
-                           hipStream_t st);
+// out_bf16: 0 f32 / 1 bf16 output; a_kc / b_kc: operand contiguous along K;
+// va / vb: vector width (elements) of global loads (16 bytes or one element);
+// big: 256x256 tiles (8 wavefronts) instead of 128x128 (4 wavefronts).
+hipError_t launch_contract_bf16(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
+                                hipStream_t st);
+hipError_t launch_contract_f32(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
+                               hipStream_t st);
 
 // ---------------------------------------------------------------- map / reduce
 struct EwArgs {
