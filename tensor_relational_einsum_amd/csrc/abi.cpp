@@ -416,6 +416,61 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
   return JAGG_OK;
 }
 
+// Launch of a map or reduce: the vectorised stream kernels where the spec's
+// layout allows them, the general ones otherwise.
+hipError_t launch_ew(jagg_ctx *ctx, const EwArgs &a, int agg, const char **which) {
+  StreamArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  const int r = a.r_out;
+  for (int i = 0; i < r; ++i) sa.div_out[i] = make_fastdiv(uint32_t(a.e_out[i]));
+  if (agg == JAGG_AGG_NONE) {
+    const int64_t e_last = a.e_out[r - 1];
+    int vec = 1;
+    for (int v : {8, 4}) {
+      bool ok = e_last % v == 0 && a.be_out % v == 0;
+      for (int j = 0; j < a.n_in; ++j) {
+        const int64_t sl = a.s_out[j][r - 1];
+        if (sl == 1) {
+          ok = ok && a.be_in[j] % v == 0;
+          for (int i = 0; i < r - 1; ++i) ok = ok && a.s_out[j][i] % v == 0;
+        }
+      }
+      if (ok) {
+        vec = v;
+        break;
+      }
+    }
+    sa.slots = a.rows_per_block * (e_last / vec);
+    sa.div_vpr = make_fastdiv(uint32_t(e_last / vec));
+    int64_t chunks = (sa.slots + 1023) / 1024;
+    sa.chunks = chunks < 1 ? 1 : chunks;
+    *which = vec == 8 ? "map x8" : (vec == 4 ? "map x4" : "map x1");
+    return launch_map_vec(a, sa, vec, ctx->stream);
+  }
+  // row reduce: one reduced letter, innermost in input 0; other inputs hold
+  // it innermost or not at all; at most 256 joined tuples per key
+  bool row = a.n_red == 1 && a.inner_red == 0 && a.per_key <= 256 && (!a.causal || a.t_red_flag);
+  int vec = a.e_red[0] % 4 == 0 ? 4 : 1;
+  for (int j = 0; j < a.n_in && row; ++j) {
+    const int64_t sr = a.s_red[j][0];
+    row = row && (sr == 0 || sr == 1);
+    if (sr == 1 && (a.be_in[j] % 4 != 0)) vec = 1;
+  }
+  if (row) {
+    int lpr = 4;
+    while (lpr < 64 && lpr * 2 <= a.e_red[0] / vec) lpr *= 2;
+    const int groups = 256 / lpr;
+    int64_t per_key_groups = (a.be_out + groups - 1) / groups;
+    int64_t cap = 4096 / (a.n_keys > 0 ? a.n_keys : 1);
+    if (cap < 1) cap = 1;
+    sa.chunks = per_key_groups < cap ? per_key_groups : cap;
+    *which = "reduce rows";
+    return launch_reduce_row(a, sa, vec, lpr, ctx->stream);
+  }
+  *which = "reduce general";
+  return launch_reduce(a, ctx->stream);
+}
+
 jagg_status after_launch(jagg_ctx *ctx, hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
   if (ctx->debug_sync) {
@@ -969,8 +1024,10 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
                                : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream);
     return after_launch(ctx, e, "contract");
   }
-  if (kind == MAP) return after_launch(ctx, launch_map(ew, ctx->stream), "map");
-  return after_launch(ctx, launch_reduce(ew, ctx->stream), "reduce");
+  const char *which = "";
+  const hipError_t e = launch_ew(ctx, ew, spec->agg, &which);
+  if (ctx->trace) fprintf(stderr, "[jagg] %s: %s, %lld keys\n", spec->einsum, which, (long long)ew.n_keys);
+  return after_launch(ctx, e, which);
 }
 
 jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter, const int32_t *blockings,

@@ -178,4 +178,14 @@ struct EwArgs {
 hipError_t launch_map(const EwArgs &a, hipStream_t st);
 hipError_t launch_reduce(const EwArgs &a, hipStream_t st);
 
+// launch shape of the vectorised map / row-reduce kernels
+struct StreamArgs {
+  int64_t chunks;                  // workgroups per output key
+  int64_t slots;                   // map: vectors per output block
+  FastDiv div_vpr;                 // map: division by vectors per row
+  FastDiv div_out[kMaxLetters];    // division by each output block extent
+};
+hipError_t launch_map_vec(const EwArgs &a, StreamArgs sa, int vec, hipStream_t st);
+hipError_t launch_reduce_row(const EwArgs &a, StreamArgs sa, int vec, int lpr, hipStream_t st);
+
 }  // namespace jagg
