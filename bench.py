@@ -176,6 +176,8 @@ def main():
     ap.add_argument("--workload", default="llama", choices=["llama", "attention", "multi_index", "matmul"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repartition", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this executor has no multi-GPU path "
@@ -233,6 +235,13 @@ def main():
         rep = {"8192x8192": repartition_rate(ctx, I.repartition_2d(), 15, scratch),
                "32x128x64x64": repartition_rate(ctx, I.repartition_4d(), 15, scratch)}
         del scratch
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     cpu = None
     if not args.no_cpu_baseline and args.workload == "llama":
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
