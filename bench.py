@@ -75,6 +75,29 @@ def spec_bytes(run: ChainRunner, st, ext: dict) -> float:
     return b
 
 
+def counter_traffic() -> float | None:
+    """HBM bytes per launch of the bf16 contraction kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernel source is still
+    the one the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "llama_block_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if "traffic_bytes_per_launch" not in vals or "kernel_source_sha256_16" not in vals:
+        return None
+    h = hashlib.sha256()
+    for rel in ("tensor_relational_einsum_amd/csrc/contract_impl.h", "tensor_relational_einsum_amd/csrc/contract_bf16.hip"):
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    if h.hexdigest()[:16] != vals["kernel_source_sha256_16"]:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def timed_chain(run: ChainRunner, steps: int, warmup: int):
     stream = run.ctx.stream
     n = len(run.calls)
@@ -198,7 +221,7 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     call_ms = per_call.mean(axis=0)
     breakdown = []
-    dom_flops = dom_ms = 0.0
+    dom_flops = dom_ms = dom_bytes = 0.0
     dom_launches = 0
     for i, st in enumerate(steps):
         f = spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0
@@ -212,14 +235,18 @@ def main():
         if isinstance(st, I.Step) and f and not st.causal and run.rel[st.ins[0]].dtype == "bf16":
             dom_flops += f
             dom_ms += float(call_ms[i])
+            dom_bytes += by
             dom_launches += 1
     # the arithmetic type of the dominant kernel: the inputs of the largest contraction
     big = max((st for st in steps if isinstance(st, I.Step)), key=lambda st: spec_flops(st, w.extents))
     in_dtype = run.rel[big.ins[0]].dtype
     if dom_launches:
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+        tr = counter_traffic() if args.workload == "llama" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": tr,
+                "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": round(dom_bytes / dom_launches),
                 "kernel": "contract_kernel<bf16> (projection / FFN specs)", "launches_per_step": dom_launches,
                 "avg_launch_ms": round(dom_ms / dom_launches, 4)}
     else:
