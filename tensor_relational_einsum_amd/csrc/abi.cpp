@@ -442,7 +442,7 @@ hipError_t launch_ew(jagg_ctx *ctx, const EwArgs &a, int agg, const char **which
     }
     sa.slots = a.rows_per_block * (e_last / vec);
     sa.div_vpr = make_fastdiv(uint32_t(e_last / vec));
-    int64_t chunks = (sa.slots + 1023) / 1024;
+    int64_t chunks = (sa.slots + 1023) / 1024;  // about one pass of four slots per thread
     sa.chunks = chunks < 1 ? 1 : chunks;
     *which = vec == 8 ? "map x8" : (vec == 4 ? "map x4" : "map x1");
     return launch_map_vec(a, sa, vec, ctx->stream);

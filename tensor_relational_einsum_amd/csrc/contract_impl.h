@@ -25,7 +25,9 @@
 //    turns four 4-element row pieces into four 4-element K columns; for
 //    fp32 M/N-contiguous tiles one ds_read_b32 per MFMA.
 //  - Two LDS stages: the global loads of step s+1 are in flight while the
-//    MFMAs of step s run; one barrier per step.
+//    MFMAs of step s run; one barrier per step.  (Measured on MI355X, the
+//    kernel is bound by its LDS-read / MFMA interleave rather than by global
+//    latency: keeping every K-step's tile L2-resident gains only ~6%.)
 //  - Workgroups are renumbered so that consecutive tiles of one output row
 //    panel land on the same XCD (dispatch round-robins workgroups over the
 //    8 XCDs, each with its own L2).
@@ -264,11 +266,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
   int64_t ks = 0;
   if (p.causal_out || p.causal_red) ks = (key / p.cs_w) % p.cs_k;
 
-  TA ta;
-  TB tb;
-  ta.init(p.sAm, p.sAk);
-  tb.init(p.sBn, p.sBk);
-  auto load_step = [&](int s) {
+  // one register set per operand: the global loads of step s+1 are issued
+  // while step s computes
+  TA ta[1];
+  TB tb[1];
+  ta[0].init(p.sAm, p.sAk);
+  tb[0].init(p.sBn, p.sBk);
+  auto load_step = [&](int s, TA &xa, TB &xb) {
     const int e = s / KT;
     const int kt = s - e * KT;
     const int32_t *ent = ents + e * 3;
@@ -277,18 +281,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
     const T *pa = reinterpret_cast<const T *>(p.A) + aid * p.beA + ao;
     const T *pb = reinterpret_cast<const T *>(p.B) + bid * p.beB + bo;
-    ta.load(tile_rsrc(pa, (p.beA - ao) * ESZ), p.M - m0, p.K - k0);
-    tb.load(tile_rsrc(pb, (p.beB - bo) * ESZ), p.N - n0, p.K - k0);
+    xa.load(tile_rsrc(pa, (p.beA - ao) * ESZ), p.M - m0, p.K - k0);
+    xb.load(tile_rsrc(pb, (p.beB - bo) * ESZ), p.N - n0, p.K - k0);
   };
   // causal pair with t reduced: zero A where t > s, on the diagonal block only;
   // applied just before the LDS store so the loads stay in flight meanwhile
-  auto mask_step = [&](int s) {
+  auto mask_step = [&](int s, TA &xa) {
     if (MASK && p.causal_red) {
       const int e = s / KT;
       const int k0 = (s - e * KT) * BK;
       const int64_t aid = ents[e * 3 + p.a_slot];
       const int64_t kt_blk = (aid / p.ct_w) % p.ct_k;
-      if (kt_blk == ks) ta.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, k0);
+      if (kt_blk == ks) xa.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, k0);
     }
   };
 
@@ -305,17 +309,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  load_step(0);
-  mask_step(0);
-  ta.store(smem);
-  tb.store(smem + A_BYTES);
-  __syncthreads();
-
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < steps) load_step(s + 1);
-    const char *As = smem + cur * STAGE;
+  auto compute = [&](const char *As) {
     const char *Bs = As + A_BYTES;
+    __builtin_amdgcn_iglp_opt(0);  // let the scheduler interleave LDS reads with MFMAs
     // fragments of K chunk kc+1 are read while the MFMAs of chunk kc run
     uint4 af[2][TM], bfr[2][TN];
     auto read_frags = [&](int kc, uint4 *a, uint4 *b) {
@@ -340,21 +336,43 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
         }
       }
     };
-    read_frags(0, af[0], bfr[0]);
+    if constexpr (TM * TN <= 8) {
+      read_frags(0, af[0], bfr[0]);
 #pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) {
-      if (kc + 1 < KCH) read_frags(kc + 1, af[(kc + 1) & 1], bfr[(kc + 1) & 1]);
+      for (int kc = 0; kc < KCH; ++kc) {
+        if (kc + 1 < KCH) read_frags(kc + 1, af[(kc + 1) & 1], bfr[(kc + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[kc & 1][i], bfr[kc & 1][j]);
+          for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[kc & 1][i], bfr[kc & 1][j]);
+      }
+    } else {
+      // 16 MFMAs per chunk give the reads of the next chunk room without a
+      // second fragment set
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) {
+        read_frags(kc, af[0], bfr[0]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[0][i], bfr[0][j]);
+      }
     }
-    if (s + 1 < steps) {
-      char *nx = smem + (cur ^ 1) * STAGE;
-      mask_step(s + 1);
-      ta.store(nx);
-      tb.store(nx + A_BYTES);
-    }
+  };
+  auto store_step = [&](int s, TA &xa, TB &xb, char *lds) {
+    mask_step(s, xa);
+    xa.store(lds);
+    xb.store(lds + A_BYTES);
+  };
+
+  load_step(0, ta[0], tb[0]);
+  store_step(0, ta[0], tb[0], smem);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < steps) load_step(s + 1, ta[0], tb[0]);
+    compute(smem + cur * STAGE);
+    if (s + 1 < steps) store_step(s + 1, ta[0], tb[0], smem + (cur ^ 1) * STAGE);
     __syncthreads();
   }
 

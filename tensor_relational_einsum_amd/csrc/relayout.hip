@@ -41,54 +41,68 @@ __global__ __launch_bounds__(256) void relayout_kernel(const RelayoutArgs a) {
       if (chk == c) lx[c] += dig * a.lane[d].xs;
   }
 
-  for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
-    // tile part: uniform across the workgroup
-    int64_t tsrc = 0, tdst = 0;
-    int64_t tx[kMaxChk];
+  // four tiles per workgroup pass: all four reads are issued before the
+  // first write
+  constexpr int U = 4;
+  for (int64_t t0 = int64_t(blockIdx.x) * U; t0 < a.n_tiles; t0 += int64_t(gridDim.x) * U) {
+    V v[U];
+    int64_t dof[U];
+    bool wr[U];
 #pragma unroll
-    for (int c = 0; c < kMaxChk; ++c) tx[c] = 0;
-    uint32_t r = uint32_t(t);
-    for (int d = a.n_tile - 1; d >= 0; --d) {
-      const uint32_t q = fd_div(r, a.tile[d].div);
-      const int64_t dig = int64_t(r - q * a.tile[d].div.d);
-      r = q;
-      tsrc += dig * a.tile[d].src;
-      tdst += dig * a.tile[d].dst;
-      const int chk = a.tile[d].chk;
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u;
+      wr[u] = false;
+      if (t >= a.n_tiles) continue;
+      // tile part: uniform across the workgroup
+      int64_t tsrc = 0, tdst = 0;
+      int64_t tx[kMaxChk];
 #pragma unroll
-      for (int c = 0; c < kMaxChk; ++c)
-        if (chk == c) tx[c] += dig * a.tile[d].xs;
-    }
-    bool rd = true, wr = true;
-    int64_t so = tsrc + lsrc;
+      for (int c = 0; c < kMaxChk; ++c) tx[c] = 0;
+      uint32_t r = uint32_t(t);
+      for (int d = a.n_tile - 1; d >= 0; --d) {
+        const uint32_t q = fd_div(r, a.tile[d].div);
+        const int64_t dig = int64_t(r - q * a.tile[d].div.d);
+        r = q;
+        tsrc += dig * a.tile[d].src;
+        tdst += dig * a.tile[d].dst;
+        const int chk = a.tile[d].chk;
 #pragma unroll
-    for (int c = 0; c < kMaxChk; ++c) {
-      if (c < a.n_chk) {
-        const int64_t x = tx[c] + lx[c];
-        rd = rd && (x < a.read_lim[c]);
-        wr = wr && (x < a.write_lim[c]);
-        if (a.irr[c]) {
-          const uint32_t xv = uint32_t(x);
-          const uint32_t kb = fd_div(xv, a.irr_div[c]);
-          so += int64_t(kb) * a.irr_K[c] + int64_t(xv - kb * a.irr_div[c].d) * a.irr_E[c];
+        for (int c = 0; c < kMaxChk; ++c)
+          if (chk == c) tx[c] += dig * a.tile[d].xs;
+      }
+      bool rd = true, w = true;
+      int64_t so = tsrc + lsrc;
+#pragma unroll
+      for (int c = 0; c < kMaxChk; ++c) {
+        if (c < a.n_chk) {
+          const int64_t x = tx[c] + lx[c];
+          rd = rd && (x < a.read_lim[c]);
+          w = w && (x < a.write_lim[c]);
+          if (a.irr[c]) {
+            const uint32_t xv = uint32_t(x);
+            const uint32_t kb = fd_div(xv, a.irr_div[c]);
+            so += int64_t(kb) * a.irr_K[c] + int64_t(xv - kb * a.irr_div[c].d) * a.irr_E[c];
+          }
         }
       }
+      wr[u] = w;
+      dof[u] = tdst + ldst;
+      if (w && rd) {
+        v[u] = *reinterpret_cast<const V *>(reinterpret_cast<const char *>(a.src) + so * ESZ);
+      } else {
+        v[u] = V{};
+      }
     }
-    if (!wr) continue;
-    V v;
-    if (rd) {
-      v = *reinterpret_cast<const V *>(reinterpret_cast<const char *>(a.src) + so * ESZ);
-    } else {
-      v = V{};
-    }
-    *reinterpret_cast<V *>(reinterpret_cast<char *>(a.dst) + (tdst + ldst) * ESZ) = v;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (wr[u]) *reinterpret_cast<V *>(reinterpret_cast<char *>(a.dst) + dof[u] * ESZ) = v[u];
   }
 }
 
 template <typename V, int VE>
 static hipError_t go(const RelayoutArgs &a, hipStream_t st) {
   const int block = ((a.lanes + 63) / 64) * 64;
-  int64_t grid = a.n_tiles;
+  int64_t grid = (a.n_tiles + 3) / 4;
   if (grid > (int64_t(1) << 20)) grid = int64_t(1) << 20;
   hipLaunchKernelGGL((relayout_kernel<V, VE>), dim3(unsigned(grid)), dim3(block), 0, st, a);
   return hipGetLastError();
