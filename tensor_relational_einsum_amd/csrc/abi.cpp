@@ -418,7 +418,126 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
 
 // Launch of a map or reduce: the vectorised stream kernels where the spec's
 // layout allows them, the general ones otherwise.
+// Flat-stream plan: every row letter unpadded, every operand's row offset a
+// multiple of the row index, blocks under 2 GiB and 16-byte aligned.
+// Returns false when the general kernels must run instead.
+bool plan_flat(const EwArgs &a, FlatArgs &f, int &vec, int &lpr) {
+  memset(&f, 0, sizeof(f));
+  const bool map = a.agg == JAGG_AGG_NONE;
+  const int r = a.r_out;
+  const int nrow = map ? r - 1 : r;  // row letters
+  const int64_t lim31 = (int64_t(1) << 31) - 1;
+  auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  // row strides of the output walk
+  int64_t R[kMaxLetters];
+  int64_t rows = 1;
+  for (int i = nrow - 1; i >= 0; --i) {
+    R[i] = rows;
+    rows *= a.e_out[i];
+    if (a.n_out[i] % a.e_out[i] != 0) return false;  // padded rows
+  }
+  const int64_t e_in = map ? a.e_out[r - 1] : a.e_red[0];  // walk's innermost extent
+  if (map) {
+    if (e_in % 8 != 0) return false;
+    vec = 8;
+  } else {
+    if (a.n_red != 1 || a.inner_red != 0 || a.s_red[0][0] != 1) return false;
+    vec = e_in % 4 == 0 ? 4 : 1;
+  }
+  f.n_in = a.n_in;
+  for (int j = 0; j < a.n_in; ++j) {
+    const int esz = a.in_dt[j] ? 2 : 4;
+    const int64_t inner = map ? a.s_out[j][r - 1] : a.s_red[j][0];
+    if (inner != 0 && inner != 1) return false;
+    if (!map && j == 0 && inner != 1) return false;
+    int64_t m = 0;
+    for (int i = 0; i < nrow; ++i)
+      if (a.s_out[j][i] != 0) m = a.s_out[j][i] / R[i];
+    for (int i = 0; i < nrow; ++i)
+      if (a.s_out[j][i] != m * R[i]) return false;
+    const int64_t bytes = a.be_in[j] * esz;
+    if (bytes > lim31 || (bytes % 16) != 0 || !aligned(a.in[j])) return false;
+    if (inner && map && (m * esz) % 16 != 0) return false;
+    if (inner && !map && vec == 4 && m % 4 != 0) vec = 1;
+    f.in[j].p = a.in[j];
+    f.in[j].block_bytes = uint32_t(bytes);
+    f.in[j].dt = a.in_dt[j];
+    f.in[j].inner = int32_t(inner);
+    f.in[j].row_mul = int32_t(m);
+  }
+  for (int j = a.n_in; j < kMaxIn; ++j) f.in[j].p = a.in[0];  // block_bytes 0: every load reads zeros
+  const int oesz = a.out_dt ? 2 : 4;
+  if (a.be_out > lim31 || (a.be_out * oesz) % 16 != 0 || !aligned(a.out)) return false;
+  if (a.n_keys > lim31) return false;
+  f.out = a.out;
+  f.out_dt = a.out_dt;
+  f.alpha = a.alpha;
+  f.beta = a.beta;
+  f.eps = a.eps;
+  f.list = a.list;
+  f.counts = a.counts;
+  f.per_key = a.per_key;
+  f.n_keys = int32_t(a.n_keys);
+  f.be_out = int32_t(a.be_out);
+  // causal pair: s a row letter, t the walk's innermost letter
+  if (a.causal) {
+    if (map ? (a.t_red_flag || a.t_pos != r - 1 || a.s_pos >= r - 1) : (!a.t_red_flag || a.t_pos != 0)) return false;
+    const int sp = a.s_pos;
+    int64_t W = 1;
+    for (int i = sp + 1; i < r; ++i) W *= a.k_out[i];
+    f.causal = 1;
+    f.e_s = int32_t(a.e_out[sp]);
+    f.k_s = int32_t(a.k_out[sp]);
+    f.div_Rs = make_fastdiv(uint32_t(R[sp]));
+    f.div_es = make_fastdiv(uint32_t(a.e_out[sp]));
+    f.div_Ws = make_fastdiv(uint32_t(W));
+    f.div_ks = make_fastdiv(uint32_t(a.k_out[sp]));
+  }
+  int64_t chunks;
+  if (map) {
+    const int64_t slots = rows * (e_in / 8);
+    if (slots > lim31) return false;
+    f.slots = int32_t(slots);
+    f.vpr = int32_t(e_in / 8);
+    f.div_vpr = make_fastdiv(uint32_t(f.vpr));
+    f.e_last = int32_t(e_in);
+    f.n_last = int32_t(a.n_out[r - 1]);
+    f.k_last = int32_t(a.k_out[r - 1]);
+    f.div_klast = make_fastdiv(uint32_t(f.k_last));
+    chunks = (slots + 1023) / 1024;  // two passes of two vectors per thread
+  } else {
+    lpr = 4;
+    while (lpr < 64 && lpr * 2 <= e_in / vec) lpr *= 2;
+    const int64_t groups = 256 / lpr;
+    const int64_t per_key = (a.be_out + groups - 1) / groups;
+    int64_t cap = 8192 / (a.n_keys > 0 ? a.n_keys : 1);
+    chunks = per_key < cap ? per_key : (cap < 1 ? 1 : cap);
+    f.e_red = int32_t(a.e_red[0]);
+    f.n_red = int32_t(a.n_red_ext[0]);
+    f.k_red = int32_t(a.k_red[0]);
+    f.div_wred = make_fastdiv(uint32_t(a.w_red0[0]));
+    f.div_kred = make_fastdiv(uint32_t(a.k_red[0]));
+  }
+  if (chunks < 1) chunks = 1;
+  if (chunks * a.n_keys > lim31) return false;
+  f.chunks = int32_t(chunks);
+  f.div_chunks = make_fastdiv(uint32_t(chunks));
+  return true;
+}
+
 hipError_t launch_ew(jagg_ctx *ctx, const EwArgs &a, int agg, const char **which) {
+  {
+    FlatArgs f;
+    int vec = 1, lpr = 4;
+    if (plan_flat(a, f, vec, lpr)) {
+      if (agg == JAGG_AGG_NONE) {
+        *which = "flat map";
+        return launch_flat_map(f, a.g, ctx->stream);
+      }
+      *which = "flat reduce";
+      return launch_flat_reduce(f, vec, lpr, a.g, agg, ctx->stream);
+    }
+  }
   StreamArgs sa;
   memset(&sa, 0, sizeof(sa));
   const int r = a.r_out;

@@ -188,4 +188,47 @@ struct StreamArgs {
 hipError_t launch_map_vec(const EwArgs &a, StreamArgs sa, int vec, hipStream_t st);
 hipError_t launch_reduce_row(const EwArgs &a, StreamArgs sa, int vec, int lpr, hipStream_t st);
 
+// ---------------------------------------------------------------- flat streams
+// Map and row reduce for "row-compatible" operands: the output block is a
+// row-major walk of rows (map: every output letter but the innermost;
+// reduce: every output letter) and each input's in-block offset of row r is
+// r * row_mul, plus, along the innermost letter of the walk, the element
+// index (inner = 1) or nothing (inner = 0, a broadcast).  No row letter has a
+// padded tail, every block is under 2 GiB, and ids fit 31 bits, so all index
+// arithmetic is 32-bit.
+struct FlatIn {
+  const void *p;
+  uint32_t block_bytes;
+  int32_t dt;          // 0 f32, 1 bf16
+  int32_t inner;       // 1 contiguous along the walk's innermost letter, 0 constant along it
+  int32_t row_mul;
+};
+struct FlatArgs {
+  FlatIn in[kMaxIn];
+  int32_t n_in;
+  void *out;
+  int32_t out_dt;
+  float alpha, beta, eps;
+  const int32_t *list;
+  const int32_t *counts;
+  int32_t per_key;
+  int32_t n_keys;
+  int32_t chunks;            // workgroups per output key
+  FastDiv div_chunks;
+  int32_t be_out;            // output block elements
+  // map: rows of vpr vectors; innermost letter valid extent n_last - kappa_last * e_last
+  int32_t slots, vpr, e_last, n_last, k_last;
+  FastDiv div_vpr, div_klast;
+  // causal pair: s is a row letter with c_s = (row / R_s) % e_s and
+  // kappa_s = (key / W_s) % k_s; t is the innermost letter of the walk
+  int32_t causal, e_s, k_s;
+  FastDiv div_Rs, div_es, div_Ws, div_ks;
+  // reduce: the reduced letter (innermost in input 0); block coordinate of a
+  // joined tuple = (input-0 tuple id / w_red) % k_red
+  int32_t e_red, n_red, k_red;
+  FastDiv div_wred, div_kred;
+};
+hipError_t launch_flat_map(const FlatArgs &a, int g, hipStream_t st);  // 8 elements per vector
+hipError_t launch_flat_reduce(const FlatArgs &a, int vec, int lpr, int g, int agg, hipStream_t st);
+
 }  // namespace jagg

@@ -18,20 +18,6 @@
 
 namespace jagg {
 
-__device__ __forceinline__ float g_apply(int g, int n_in, float x0, float x1, float x2, float beta, float eps) {
-  switch (g) {
-    case 0: return n_in == 1 ? x0 : (n_in == 2 ? x0 * x1 : x0 * x1 * x2);
-    case 1: return x0;
-    case 2: return x0 * x0;
-    case 3: return __expf(x0 - x1);
-    case 4: return __expf(x0 - x1) / x2;
-    case 5: return x0 * rsqrtf(x1 * beta + eps) * x2;
-    case 6: return x0 / (1.0f + __expf(-x0)) * x1;
-    case 7: return n_in == 1 ? x0 : (n_in == 2 ? x0 + x1 : x0 + x1 + x2);
-  }
-  return 0.0f;
-}
-
 // V consecutive elements starting at element `off` (aligned to V): a vector
 // load when contiguous, one broadcast load when the stride is 0.
 template <int V>
@@ -89,15 +75,15 @@ __device__ __forceinline__ void store_run(void *base, int64_t off, int dt, const
     uint16_t *p = reinterpret_cast<uint16_t *>(base) + off;
     if constexpr (V == 8) {
       uint4 q;
-      q.x = uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16);
-      q.y = uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16);
-      q.z = uint32_t(f32_to_bf16(x[4])) | (uint32_t(f32_to_bf16(x[5])) << 16);
-      q.w = uint32_t(f32_to_bf16(x[6])) | (uint32_t(f32_to_bf16(x[7])) << 16);
+      q.x = pack_bf16x2(x[0], x[1]);
+      q.y = pack_bf16x2(x[2], x[3]);
+      q.z = pack_bf16x2(x[4], x[5]);
+      q.w = pack_bf16x2(x[6], x[7]);
       *reinterpret_cast<uint4 *>(p) = q;
     } else if constexpr (V == 4) {
       uint2 q;
-      q.x = uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16);
-      q.y = uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16);
+      q.x = pack_bf16x2(x[0], x[1]);
+      q.y = pack_bf16x2(x[2], x[3]);
       *reinterpret_cast<uint2 *>(p) = q;
     } else {
 #pragma unroll
@@ -130,7 +116,7 @@ __device__ __forceinline__ void key_coords(const EwArgs &a, int64_t key, int64_t
 }
 
 // ------------------------------------------------------------------ map
-template <int V>
+template <int V, int G>
 __global__ __launch_bounds__(256) void map_vec_kernel(const EwArgs a, StreamArgs sa) {
   const int64_t key = blockIdx.x / sa.chunks;
   const int64_t chunk = blockIdx.x - key * sa.chunks;
@@ -183,16 +169,20 @@ __global__ __launch_bounds__(256) void map_vec_kernel(const EwArgs a, StreamArgs
       if (j < a.n_in) load_run<V>(a.in[j], ioff[j], a.in_dt[j], s_last[j], x[j]);
       else {
 #pragma unroll
-        for (int u = 0; u < V; ++u) x[j][u] = 0.0f;
+        for (int u = 0; u < V; ++u) x[j][u] = g_fill<G>();
       }
     }
+    // elements [0, keep) of the vector are inside the output (and on the
+    // allowed side of a causal pair); the rest are padding and get +0
     const int64_t xl = kap_last * e_last + inner;
+    int64_t lim = n_last - xl;
+    if (a.causal && s_glob + 1 - xl < lim) lim = s_glob + 1 - xl;
+    const int keep = ok ? int(lim < 0 ? 0 : (lim > V ? V : lim)) : 0;
     float y[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) {
-      const float v = a.alpha * g_apply(a.g, a.n_in, x[0][u], x[1][u], x[2][u], a.beta, a.eps);
-      const bool keep = ok && (xl + u < n_last) && !(a.causal && xl + u > s_glob);
-      y[u] = keep ? v : 0.0f;
+      const float v = a.alpha * g_fn<G>(x[0][u], x[1][u], x[2][u], a.beta, a.eps);
+      y[u] = u < keep ? v : 0.0f;
     }
     store_run<V>(a.out, ooff, a.out_dt, y);
   }
@@ -201,8 +191,8 @@ __global__ __launch_bounds__(256) void map_vec_kernel(const EwArgs a, StreamArgs
 // ------------------------------------------------------------------ row reduce
 constexpr int kMaxRowEntries = 256;
 
-template <int V, int LPR>
-__global__ __launch_bounds__(256) void reduce_row_kernel(const EwArgs a, StreamArgs sa) {
+template <int V, int G, int AGG>
+__global__ __launch_bounds__(256) void reduce_row_kernel(const EwArgs a, StreamArgs sa, int lpr_log2) {
   __shared__ int64_t s_base[kMaxIn][kMaxRowEntries];
   __shared__ int32_t s_lim[kMaxRowEntries];
   __shared__ int64_t s_t0[kMaxRowEntries];
@@ -224,12 +214,15 @@ __global__ __launch_bounds__(256) void reduce_row_kernel(const EwArgs a, StreamA
   int64_t kap[kMaxLetters];
   key_coords(a, key, kap);
   const int r = a.r_out;
-  const int lane = threadIdx.x & 63;
-  const int sub = lane % LPR;                   // lane inside the row group
-  const int group = threadIdx.x / LPR;          // row group inside the workgroup
-  constexpr int GROUPS = 256 / LPR;
-  const bool is_max = a.agg == 2;
-  for (int64_t q0 = chunk * GROUPS; q0 < a.be_out; q0 += sa.chunks * GROUPS) {
+  const int lpr = 1 << lpr_log2;
+  const int sub = threadIdx.x & (lpr - 1);      // lane inside the row group
+  const int group = threadIdx.x >> lpr_log2;    // row group inside the workgroup
+  const int groups = 256 >> lpr_log2;
+  const int step = lpr * V;
+  bool has_red[kMaxIn];
+#pragma unroll
+  for (int j = 0; j < kMaxIn; ++j) has_red[j] = j == 0 || (j < a.n_in && a.s_red[j][0] != 0);
+  for (int64_t q0 = chunk * groups; q0 < a.be_out; q0 += sa.chunks * groups) {
     const int64_t q = q0 + group;
     const bool live = q < a.be_out;
     // output element -> coordinates, input offsets, validity
@@ -250,72 +243,108 @@ __global__ __launch_bounds__(256) void reduce_row_kernel(const EwArgs a, StreamA
       }
     }
     // inputs without the reduced letter: one value per output element
-    float bc[kMaxIn] = {0.f, 0.f, 0.f};
+    float bc[kMaxIn];
 #pragma unroll
-    for (int j = 1; j < kMaxIn; ++j)
-      if (j < a.n_in && a.s_red[j][0] == 0 && ok && cnt > 0) bc[j] = load_dt(a.in[j], s_base[j][0] + off[j], a.in_dt[j]);
-    float acc = is_max ? -INFINITY : 0.0f;
-    int terms = 0;
-    if (ok) {
-      for (int32_t e = 0; e < cnt; ++e) {
-        int32_t lim = s_lim[e];
-        if (a.causal) {
-          const int64_t m = s_glob - s_t0[e] + 1;  // t <= s
-          if (m < lim) lim = int32_t(m < 0 ? 0 : m);
+    for (int j = 0; j < kMaxIn; ++j) {
+      bc[j] = g_fill<G>();
+      if (j < a.n_in && !has_red[j] && ok && cnt > 0) bc[j] = load_dt(a.in[j], s_base[j][0] + off[j], a.in_dt[j]);
+    }
+    float acc = AGG == 2 ? -INFINITY : 0.0f;
+    bool nonempty = false;
+    const int32_t n_e = ok ? cnt : 0;
+    for (int32_t e = 0; e < n_e; ++e) {
+      int32_t lim = s_lim[e];
+      if (a.causal) {
+        const int64_t m = s_glob - s_t0[e] + 1;  // t <= s
+        if (m < lim) lim = int32_t(m < 0 ? 0 : m);
+      }
+      nonempty = nonempty || lim > 0;
+      int64_t base[kMaxIn];
+#pragma unroll
+      for (int j = 0; j < kMaxIn; ++j) base[j] = s_base[j][e] + off[j];
+      for (int v = sub * V; v < lim; v += step) {
+        float x[kMaxIn][V];
+#pragma unroll
+        for (int j = 0; j < kMaxIn; ++j) {
+          if (j < a.n_in && has_red[j]) {
+            load_run<V>(a.in[j], base[j] + v, a.in_dt[j], 1, x[j]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < V; ++u) x[j][u] = bc[j];
+          }
         }
-        for (int v = sub * V; v < lim; v += LPR * V) {
-          float x[kMaxIn][V];
-          load_run<V>(a.in[0], s_base[0][e] + off[0] + v, a.in_dt[0], 1, x[0]);
+        const int keep = lim - v;  // >= 1
 #pragma unroll
-          for (int j = 1; j < kMaxIn; ++j) {
-            if (j < a.n_in && a.s_red[j][0] != 0) {
-              load_run<V>(a.in[j], s_base[j][e] + off[j] + v, a.in_dt[j], 1, x[j]);
-            } else {
-#pragma unroll
-              for (int u = 0; u < V; ++u) x[j][u] = bc[j];
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < V; ++u) {
-            if (v + u < lim) {
-              const float gv = g_apply(a.g, a.n_in, x[0][u], x[1][u], x[2][u], a.beta, a.eps);
-              acc = is_max ? fmaxf(acc, gv) : acc + gv;
-              ++terms;
-            }
-          }
+        for (int u = 0; u < V; ++u) {
+          const float gv = g_fn<G>(x[0][u], x[1][u], x[2][u], a.beta, a.eps);
+          if (u == 0 || u < keep) acc = AGG == 2 ? fmaxf(acc, gv) : acc + gv;
         }
       }
     }
     // butterfly inside the row group (fixed order)
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) {
+    for (int m = lpr >> 1; m >= 1; m >>= 1) {
       const float o = __shfl_xor(acc, m, 64);
-      acc = is_max ? fmaxf(acc, o) : acc + o;
-      terms += __shfl_xor(terms, m, 64);
+      acc = AGG == 2 ? fmaxf(acc, o) : acc + o;
     }
-    if (sub == 0 && live) store_dt(a.out, key * a.be_out + q, a.out_dt, (ok && terms > 0) ? a.alpha * acc : 0.0f);
+    if (sub == 0 && live) store_dt(a.out, key * a.be_out + q, a.out_dt, (ok && nonempty) ? a.alpha * acc : 0.0f);
   }
 }
 
-hipError_t launch_map_vec(const EwArgs &a, StreamArgs sa, int vec, hipStream_t st) {
-  const int64_t grid = a.n_keys * sa.chunks;
-  if (vec == 8) hipLaunchKernelGGL(map_vec_kernel<8>, dim3(unsigned(grid)), dim3(256), 0, st, a, sa);
-  else if (vec == 4) hipLaunchKernelGGL(map_vec_kernel<4>, dim3(unsigned(grid)), dim3(256), 0, st, a, sa);
-  else hipLaunchKernelGGL(map_vec_kernel<1>, dim3(unsigned(grid)), dim3(256), 0, st, a, sa);
+template <int V, int G>
+static void map_go(const EwArgs &a, const StreamArgs &sa, hipStream_t st) {
+  hipLaunchKernelGGL((map_vec_kernel<V, G>), dim3(unsigned(a.n_keys * sa.chunks)), dim3(256), 0, st, a, sa);
+}
+
+template <int V>
+static hipError_t map_vec_g(const EwArgs &a, const StreamArgs &sa, hipStream_t st) {
+  switch (a.g) {
+    case 0: map_go<V, 0>(a, sa, st); break;
+    case 1: map_go<V, 1>(a, sa, st); break;
+    case 2: map_go<V, 2>(a, sa, st); break;
+    case 3: map_go<V, 3>(a, sa, st); break;
+    case 4: map_go<V, 4>(a, sa, st); break;
+    case 5: map_go<V, 5>(a, sa, st); break;
+    case 6: map_go<V, 6>(a, sa, st); break;
+    case 7: map_go<V, 7>(a, sa, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_row(const EwArgs &a, StreamArgs sa, int vec, int lpr, hipStream_t st) {
-  const int64_t grid = a.n_keys * sa.chunks;
-#define JAGG_RR(VV, LL)                                                                                  \
-  if (vec == VV && lpr == LL) {                                                                          \
-    hipLaunchKernelGGL((reduce_row_kernel<VV, LL>), dim3(unsigned(grid)), dim3(256), 0, st, a, sa);      \
-    return hipGetLastError();                                                                            \
+hipError_t launch_map_vec(const EwArgs &a, StreamArgs sa, int vec, hipStream_t st) {
+  if (vec == 8) return map_vec_g<8>(a, sa, st);
+  if (vec == 4) return map_vec_g<4>(a, sa, st);
+  return map_vec_g<1>(a, sa, st);
+}
+
+template <int V, int G>
+static hipError_t reduce_go(const EwArgs &a, const StreamArgs &sa, int lpr_log2, hipStream_t st) {
+  const dim3 grid(unsigned(a.n_keys * sa.chunks));
+  if (a.agg == 2) hipLaunchKernelGGL((reduce_row_kernel<V, G, 2>), grid, dim3(256), 0, st, a, sa, lpr_log2);
+  else hipLaunchKernelGGL((reduce_row_kernel<V, G, 1>), grid, dim3(256), 0, st, a, sa, lpr_log2);
+  return hipGetLastError();
+}
+
+template <int V>
+static hipError_t reduce_row_g(const EwArgs &a, const StreamArgs &sa, int lpr_log2, hipStream_t st) {
+  switch (a.g) {
+    case 0: return reduce_go<V, 0>(a, sa, lpr_log2, st);
+    case 1: return reduce_go<V, 1>(a, sa, lpr_log2, st);
+    case 2: return reduce_go<V, 2>(a, sa, lpr_log2, st);
+    case 3: return reduce_go<V, 3>(a, sa, lpr_log2, st);
+    case 4: return reduce_go<V, 4>(a, sa, lpr_log2, st);
+    case 5: return reduce_go<V, 5>(a, sa, lpr_log2, st);
+    case 6: return reduce_go<V, 6>(a, sa, lpr_log2, st);
+    case 7: return reduce_go<V, 7>(a, sa, lpr_log2, st);
   }
-  JAGG_RR(4, 64) JAGG_RR(4, 32) JAGG_RR(4, 16) JAGG_RR(4, 8) JAGG_RR(4, 4)
-  JAGG_RR(1, 64) JAGG_RR(1, 32) JAGG_RR(1, 16) JAGG_RR(1, 8) JAGG_RR(1, 4)
-#undef JAGG_RR
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce_row(const EwArgs &a, StreamArgs sa, int vec, int lpr, hipStream_t st) {
+  int lg = 0;
+  while ((1 << lg) < lpr) ++lg;
+  if ((1 << lg) != lpr || lpr > 64) return hipErrorInvalidValue;
+  return vec == 4 ? reduce_row_g<4>(a, sa, lg, st) : reduce_row_g<1>(a, sa, lg, st);
 }
 
 }  // namespace jagg

@@ -236,6 +236,118 @@ def test_map_reduce_parity(ctx, spec, g, agg, ext, blk, idts, odt, pos, causal):
         assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
 
 
+# Row-compatible, unpadded-row operands take the flat-stream kernels; each
+# case names the path it must take (read back through JAGG_TRACE).
+FLAT_CASES = [
+    # spec, g, agg, extents, blockings, in dtypes, out dtype, positive inputs, causal, path
+    ("bhst->bhs", "ident", "max", dict(b=2, h=3, s=48, t=256), dict(b=1, h=1, s=3, t=2), ["f32"], "f32", (), None,
+     "flat reduce"),
+    ("bhst->bhs", "ident", "max", dict(b=2, h=3, s=48, t=290), dict(b=1, h=1, s=3, t=4), ["f32"], "f32", (), None,
+     "flat reduce"),
+    ("bhst,bhs->bhs", "exp_sub", "sum", dict(b=2, h=3, s=48, t=256), dict(b=1, h=1, s=3, t=2), ["f32", "f32"], "f32",
+     (), None, "flat reduce"),
+    ("bhst->bhs", "ident", "sum", dict(b=2, h=3, s=48, t=256), dict(b=1, h=1, s=3, t=2), ["bf16"], "f32", (), None,
+     "flat reduce"),
+    ("bsh->bs", "square", "sum", dict(b=2, s=48, h=1000), dict(b=1, s=3, h=4), ["f32"], "bf16", (), None,
+     "flat reduce"),
+    ("ij,j->i", "mul", "sum", dict(i=256, j=1024), dict(i=2, j=4), ["f32", "bf16"], "f32", (), None, "flat reduce"),
+    # a 1000-byte 'j' block is not 16-byte aligned: the general row reduce
+    ("ij,j->i", "mul", "sum", dict(i=256, j=1000), dict(i=2, j=4), ["bf16", "f32"], "f32", (), None, "reduce rows"),
+    ("ij,j->i", "mul", "sum", dict(i=256, j=1000), dict(i=2, j=5), ["bf16", "f32"], "f32", (), None, "flat reduce"),
+    ("bhst,bhs,bhs->bhst", "exp_sub_div", "none", dict(b=2, h=3, s=48, t=300), dict(b=1, h=1, s=3, t=19),
+     ["f32", "f32", "f32"], "bf16", (2,), None, "flat map"),
+    ("bsh,bs,h->bsh", "rms_scale", "none", dict(b=2, s=48, h=1024), dict(b=1, s=3, h=4), ["f32", "f32", "bf16"],
+     "bf16", (1,), None, "flat map"),
+    ("bsf,bsf->bsf", "silu_mul", "none", dict(b=2, s=48, f=704), dict(b=1, s=3, f=8), ["bf16", "bf16"], "f32", (),
+     None, "flat map"),
+    ("bsh,bsh,bsh->bsh", "add", "none", dict(b=2, s=48, h=1000), dict(b=1, s=3, h=5), ["f32", "f32", "f32"], "f32",
+     (), None, "flat map"),
+    ("bsh,bs->bsh", "mul", "none", dict(b=3, s=40, h=64), dict(b=1, s=1, h=1), ["f32", "bf16"], "f32", (), None,
+     "flat map"),
+    ("qst->qs", "ident", "max", dict(q=3, s=256, t=256), dict(q=1, s=4, t=4), ["f32"], "f32", (), ("s", "t"),
+     "flat reduce"),
+    ("qst,qs->qs", "exp_sub", "sum", dict(q=3, s=256, t=256), dict(q=1, s=4, t=4), ["f32", "f32"], "f32", (),
+     ("s", "t"), "flat reduce"),
+    ("qst,qs,qs->qst", "exp_sub_div", "none", dict(q=3, s=256, t=256), dict(q=1, s=4, t=4), ["f32", "f32", "f32"],
+     "bf16", (2,), ("s", "t"), "flat map"),
+]
+
+
+@pytest.fixture(scope="module")
+def trace_ctx():
+    import os
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    old = os.environ.get("JAGG_TRACE")
+    os.environ["JAGG_TRACE"] = "1"
+    try:
+        c = jagg.Context(0)
+    finally:
+        if old is None:
+            del os.environ["JAGG_TRACE"]
+        else:
+            os.environ["JAGG_TRACE"] = old
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+def check_ew_case(got, want, got_rel, pad, spec, ext, blk, agg, odt, causal):
+    if causal is not None and agg == "none":
+        # tuples above the block diagonal are absent from the output relation
+        s, t = causal
+        out = spec.split("->")[1]
+        e = -(-ext[s] // blk[s])
+        idx = np.indices(got.shape)
+        mask = (idx[out.index(t)] // e) <= (idx[out.index(s)] // e)
+        got = np.where(mask, got, 0.0)
+        want = np.where(mask, want, 0.0)
+    if agg == "max":
+        assert np.array_equal(got, want), "MAX must be bit-exact"
+    else:
+        tol = F32_TOL if odt == "f32" else BF16_OUT_TOL
+        err = normwise_err(got, want)
+        assert err < tol, f"normwise error {err:.3e}"
+    if causal is None:
+        assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
+
+
+@pytest.mark.parametrize("spec,g,agg,ext,blk,idts,odt,pos,causal,path", FLAT_CASES)
+def test_flat_stream_parity(trace_ctx, capfd, spec, g, agg, ext, blk, idts, odt, pos, causal, path):
+    kw = dict(beta=1.0 / ext.get("h", 1), eps=1e-6) if g == "rms_scale" else {}
+    capfd.readouterr()
+    got, want, got_rel, pad, _ = run_spec_case(trace_ctx, spec, ext, blk, g=g, agg=agg, in_dtypes=idts,
+                                               out_dtype=odt, positive=pos, causal=causal, **kw)
+    err_text = capfd.readouterr().err
+    assert f"{spec}: {path}," in err_text, f"expected the {path} kernel, trace says: {err_text.strip()}"
+    check_ew_case(got, want, got_rel, pad, spec, ext, blk, agg, odt, causal)
+
+
+def test_bf16_rounding_bit_exact(trace_ctx):
+    """f32 -> bf16 through a map: round to nearest, ties to even, on values
+    chosen to hit every case (ties both ways, subnormals, the overflow edge,
+    signed zeros), compared bit for bit with the oracle's rounding."""
+    specials = np.array([
+        1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -(1.0 + 2.0 ** -8), 0.0, -0.0,
+        2.0 ** -126, 2.0 ** -130, 2.0 ** -133, 3 * 2.0 ** -134, 2.0 ** -149, -(2.0 ** -140),
+        3.3895313892515355e38, 3.3961775292304e38, 3.4028234663852886e38, -3.3961775292304e38,
+        65504.0, 1.00390625, 1.01171875, 123456.789, -0.0078125,
+    ], dtype=np.float64).astype(np.float32)
+    g = I.streams(5, 1)[0]
+    rest = I.draw(g, [4096 - specials.size], "normal", "f32").numpy()
+    x = np.concatenate([specials, rest]).reshape(32, 128)
+    xt = torch.from_numpy(x.copy())
+    ext = dict(i=32, j=128)
+    blk = dict(i=2, j=1)
+    src = upload(trace_ctx, xt, "ij", blk)
+    call = jagg.EinsumCall(trace_ctx, "ij->ij", [src], blk, g="ident", agg="none", out_dtype="bf16")
+    call.run()
+    torch.cuda.synchronize()
+    got = bits(call.out.data)
+    want = oracle_bits(O.to_relation(O.round_to(x.astype(np.float64), "bf16"), "ij", ext, blk), "bf16")
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} values round differently, first at {bad[:5]}"
+
+
 # ----------------------------------------------------------------- chains
 
 def oracle_chain(w, dense, stop=None):
