@@ -123,7 +123,10 @@ def timed_chain(run: ChainRunner, steps: int, warmup: int):
 
 
 def flush_caches(buf):
-    buf.add_(1)  # 512 MiB read-modify-write evicts L2 and the 256 MB Infinity Cache
+    # A 512 MiB read evicts L2 and the 256 MB Infinity Cache.  It must not
+    # write: dirty lines left by the flush would be written back while the
+    # timed kernel runs (a plain 128 MiB copy drops from 5.1-5.4 to 4.0 TB/s).
+    return buf.sum()
 
 
 def repartition_rate(ctx, w: I.Workload, reps: int, scratch) -> dict:

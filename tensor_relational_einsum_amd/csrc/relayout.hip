@@ -15,6 +15,20 @@
 
 namespace jagg {
 
+// tiles per workgroup pass, workgroup cap, streaming stores (affine kernel)
+#ifndef JAGG_RELAYOUT_TILES
+#define JAGG_RELAYOUT_TILES 4
+#endif
+#ifndef JAGG_RELAYOUT_MAX_GRID
+#define JAGG_RELAYOUT_MAX_GRID (1 << 20)
+#endif
+#ifndef JAGG_RELAYOUT_NT
+#define JAGG_RELAYOUT_NT 0
+#endif
+constexpr int kRelayoutTiles = JAGG_RELAYOUT_TILES;
+constexpr int64_t kRelayoutMaxGrid = JAGG_RELAYOUT_MAX_GRID;
+constexpr bool kRelayoutNontemporal = JAGG_RELAYOUT_NT != 0;
+
 template <typename V, int VE>
 __global__ __launch_bounds__(256) void relayout_kernel(const RelayoutArgs a) {
   constexpr int ESZ = int(sizeof(V)) / VE;
@@ -99,8 +113,113 @@ __global__ __launch_bounds__(256) void relayout_kernel(const RelayoutArgs a) {
   }
 }
 
+// The common case: every letter's blocks nest (no checked letter), so each
+// destination vector has a source and both offsets are affine in the
+// digits, and at most six tile dims.  The tile digits are decoded with the
+// tile dims held in scalar registers; tail tiles re-read the last tile
+// instead of branching around the loads, so all U loads are in flight
+// together and only the stores are skipped.
+template <typename V, int VE, int NT, bool STEP>
+__global__ __launch_bounds__(256) void relayout_affine_kernel(const RelayoutArgs a) {
+  constexpr int ESZ = int(sizeof(V)) / VE;
+  const int tid = threadIdx.x;
+  if (tid >= a.lanes) return;  // no barrier below
+  int64_t lsrc = 0, ldst = 0;
+  uint32_t rem = uint32_t(tid);
+  for (int d = 0; d < a.n_lane; ++d) {
+    const uint32_t ext = uint32_t(a.lane[d].ext);
+    const uint32_t q = rem / ext;
+    int64_t dig = int64_t(rem - q * ext);
+    rem = q;
+    if (d == 0) dig *= VE;
+    lsrc += dig * a.lane[d].src;
+    ldst += dig * a.lane[d].dst;
+  }
+  int64_t ts[NT], td[NT];
+  FastDiv dv[NT];
+#pragma unroll
+  for (int d = 0; d < NT; ++d) {
+    ts[d] = a.tile[d].src;
+    td[d] = a.tile[d].dst;
+    dv[d] = a.tile[d].div;
+  }
+  const char *src = reinterpret_cast<const char *>(a.src) + lsrc * ESZ;
+  char *dst = reinterpret_cast<char *>(a.dst) + ldst * ESZ;
+  const uint32_t nt = uint32_t(a.n_tiles);
+  constexpr int U = kRelayoutTiles;
+  for (uint32_t t0 = blockIdx.x * U; t0 < nt; t0 += gridDim.x * U) {
+    int64_t so[U], dof[U];
+    if constexpr (STEP) {
+      // U divides the innermost tile extent and t0: the pass's tiles differ
+      // only in that digit, so one decode serves all of them
+      uint32_t r = t0;
+      int64_t s0 = 0, d0 = 0;
+#pragma unroll
+      for (int d = NT - 1; d >= 0; --d) {
+        const uint32_t q = fd_div(r, dv[d]);
+        const int64_t dig = int64_t(r - q * dv[d].d);
+        r = q;
+        s0 += dig * ts[d];
+        d0 += dig * td[d];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        so[u] = s0 + u * ts[NT - 1];
+        dof[u] = d0 + u * td[NT - 1];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t r = t0 + u < nt ? t0 + u : nt - 1;
+        so[u] = 0;
+        dof[u] = 0;
+#pragma unroll
+        for (int d = NT - 1; d >= 0; --d) {
+          const uint32_t q = fd_div(r, dv[d]);
+          const int64_t dig = int64_t(r - q * dv[d].d);
+          r = q;
+          so[u] += dig * ts[d];
+          dof[u] += dig * td[d];
+        }
+      }
+    }
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const V *>(src + so[u] * ESZ);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u < nt) {
+        V *p = reinterpret_cast<V *>(dst + dof[u] * ESZ);
+        if constexpr (kRelayoutNontemporal) __builtin_nontemporal_store(v[u], p);
+        else *p = v[u];
+      }
+  }
+}
+
+template <typename V, int VE, int NT>
+static hipError_t go_affine(const RelayoutArgs &a, hipStream_t st) {
+  const int block = ((a.lanes + 63) / 64) * 64;
+  int64_t grid = (a.n_tiles + kRelayoutTiles - 1) / kRelayoutTiles;
+  if (grid > kRelayoutMaxGrid) grid = kRelayoutMaxGrid;
+  if (a.tile[NT - 1].ext % kRelayoutTiles == 0)
+    hipLaunchKernelGGL((relayout_affine_kernel<V, VE, NT, true>), dim3(unsigned(grid)), dim3(block), 0, st, a);
+  else
+    hipLaunchKernelGGL((relayout_affine_kernel<V, VE, NT, false>), dim3(unsigned(grid)), dim3(block), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename V, int VE>
 static hipError_t go(const RelayoutArgs &a, hipStream_t st) {
+  if (a.n_chk == 0 && a.n_tiles < (int64_t(1) << 31)) {
+    switch (a.n_tile) {
+      case 1: return go_affine<V, VE, 1>(a, st);
+      case 2: return go_affine<V, VE, 2>(a, st);
+      case 3: return go_affine<V, VE, 3>(a, st);
+      case 4: return go_affine<V, VE, 4>(a, st);
+      case 5: return go_affine<V, VE, 5>(a, st);
+      case 6: return go_affine<V, VE, 6>(a, st);
+    }
+  }
   const int block = ((a.lanes + 63) / 64) * 64;
   int64_t grid = (a.n_tiles + 3) / 4;
   if (grid > (int64_t(1) << 20)) grid = int64_t(1) << 20;
