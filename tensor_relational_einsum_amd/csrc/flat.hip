@@ -327,8 +327,14 @@ __global__ __launch_bounds__(256) void flat_reduce_kernel(const FlatArgs a, int 
 // ------------------------------------------------------------------ launchers
 namespace {
 
-constexpr int kMapU = 2;     // vectors per thread per pass (map)
-constexpr int kReduceEU = 4; // joined tuples loaded together (row reduce)
+#ifndef JAGG_FLAT_MAP_U
+#define JAGG_FLAT_MAP_U 2
+#endif
+#ifndef JAGG_FLAT_REDUCE_EU
+#define JAGG_FLAT_REDUCE_EU 2
+#endif
+constexpr int kMapU = JAGG_FLAT_MAP_U;          // vectors per thread per pass (map)
+constexpr int kReduceEU = JAGG_FLAT_REDUCE_EU;  // joined tuples loaded together (row reduce)
 
 template <int G>
 hipError_t map_go(const FlatArgs &a, hipStream_t st) {

@@ -15,19 +15,15 @@
 
 namespace jagg {
 
-// tiles per workgroup pass, workgroup cap, streaming stores (affine kernel)
+// tiles per workgroup pass and workgroup cap of the affine kernel
 #ifndef JAGG_RELAYOUT_TILES
 #define JAGG_RELAYOUT_TILES 4
 #endif
 #ifndef JAGG_RELAYOUT_MAX_GRID
 #define JAGG_RELAYOUT_MAX_GRID (1 << 20)
 #endif
-#ifndef JAGG_RELAYOUT_NT
-#define JAGG_RELAYOUT_NT 0
-#endif
 constexpr int kRelayoutTiles = JAGG_RELAYOUT_TILES;
 constexpr int64_t kRelayoutMaxGrid = JAGG_RELAYOUT_MAX_GRID;
-constexpr bool kRelayoutNontemporal = JAGG_RELAYOUT_NT != 0;
 
 template <typename V, int VE>
 __global__ __launch_bounds__(256) void relayout_kernel(const RelayoutArgs a) {
@@ -188,11 +184,7 @@ __global__ __launch_bounds__(256) void relayout_affine_kernel(const RelayoutArgs
     for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const V *>(src + so[u] * ESZ);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t0 + u < nt) {
-        V *p = reinterpret_cast<V *>(dst + dof[u] * ESZ);
-        if constexpr (kRelayoutNontemporal) __builtin_nontemporal_store(v[u], p);
-        else *p = v[u];
-      }
+      if (t0 + u < nt) *reinterpret_cast<V *>(dst + dof[u] * ESZ) = v[u];
   }
 }
 
