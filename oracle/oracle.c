@@ -267,6 +267,13 @@ static int64_t hi_of(const orel *R, int a, int64_t kappa) {
   return h < R->n[a] ? h : R->n[a];
 }
 
+/* value at global coordinates x (by letter) inside tuple `tid` (block coords kap) */
+static double rel_at(const orel *R, const double *buf, int64_t tid, const int64_t *kap, const int64_t *x) {
+  int64_t off = 0;
+  for (int a = 0; a < R->r; ++a) off = off * R->e[a] + (x[R->letters[a] - 'a'] - kap[a] * R->e[a]);
+  return buf[tid * R->block_elems + off];
+}
+
 int oracle_relation_elems(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *elems) {
   orel R;
   int rc = make_rel(letters, ext26, nblk26, &R);
@@ -570,6 +577,245 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
     first = last;
   }
   free(agg_blk); free(touched); free(c);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention as one join-agg: the online-softmax triple.                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * "TensorPlay Stax 05" (tensorplay.cn), Section 9.10 and its exercise on the
+ * triple (m, l, a): online softmax lets attention be tiled like a reduction,
+ * the merge of triples being associative and commutative; Section 9.5 /
+ * Proposition 9.1 give the same semigroup on (m, d) pairs for a single-pass
+ * softmax.  With "Every Kernel Is a Join" Def. 3.7, attention over blocked
+ * Q, K, V is then one join-agg: f of a joined (Q, K, V) tuple is the triple
+ * of its key range, the aggregation merges triples, and the recompose step
+ * divides a by l.  The pages print no formula for the merge; the reading
+ * taken here is the standard one:
+ *   (m1, l1, a1) + (m2, l2, a2) = (M, l1 e^(m1-M) + l2 e^(m2-M),
+ *                                    a1 e^(m1-M) + a2 e^(m2-M)),  M = max(m1, m2),
+ * identity (-inf, 0, 0).
+ *
+ * Spec roles, "X s D, X t D, X t E -> X s E": X letters in every operand, s
+ * in Q and the output only, t in K and V only (the reduced key letter), D
+ * letters in Q and K only (contracted into the scores), E letters in V and
+ * the output only.  score(s, t) = alpha * sum_D Q K; t > s is dropped under
+ * a causal pair (s, t).
+ */
+typedef struct {
+  char x[27], d[27], e[27];
+  int nx, nd, ne;
+  int s, t; /* letter indices 0..25 */
+} oroles;
+
+static int attention_roles(const ospec *p, oroles *r) {
+  memset(r, 0, sizeof(*r));
+  r->s = r->t = -1;
+  if (p->n_in != 3) return OR_UNSUPPORTED;
+  for (int a = 0; a < p->n_letters; ++a) {
+    char c = p->order[a];
+    int q = strchr(p->in[0], c) != NULL, k = strchr(p->in[1], c) != NULL;
+    int v = strchr(p->in[2], c) != NULL, o = strchr(p->out, c) != NULL;
+    if (q && k && v && o) r->x[r->nx++] = c;
+    else if (q && !k && !v && o) { if (r->s >= 0) return OR_UNSUPPORTED; r->s = c - 'a'; }
+    else if (!q && k && v && !o) { if (r->t >= 0) return OR_UNSUPPORTED; r->t = c - 'a'; }
+    else if (q && k && !v && !o) r->d[r->nd++] = c;
+    else if (!q && !k && v && o) r->e[r->ne++] = c;
+    else return OR_UNSUPPORTED;
+  }
+  if (r->s < 0 || r->t < 0 || r->nd == 0 || r->ne == 0) return OR_UNSUPPORTED;
+  return OR_OK;
+}
+
+/* offset of coordinate vector x (indexed by letter) in a dense operand */
+static int64_t dense_off(const char *lt, const int64_t *ext26, const int64_t *x) {
+  int64_t off = 0;
+  for (const char *c = lt; *c; ++c) off = off * ext26[*c - 'a'] + x[*c - 'a'];
+  return off;
+}
+
+/* score of (s, t) for the batch coordinates already in x: alpha * sum_D Q K */
+static double att_score(const ospec *p, const oroles *r, const int64_t *ext26, const double *Q, const double *K,
+                        int64_t *x, double alpha) {
+  int64_t nd = 1;
+  for (int a = 0; a < r->nd; ++a) nd *= ext26[r->d[a] - 'a'];
+  double acc = 0.0;
+  for (int64_t i = 0; i < nd; ++i) {
+    int64_t rem = i;
+    for (int a = r->nd - 1; a >= 0; --a) {
+      int L = r->d[a] - 'a';
+      x[L] = rem % ext26[L];
+      rem /= ext26[L];
+    }
+    acc += Q[dense_off(p->in[0], ext26, x)] * K[dense_off(p->in[1], ext26, x)];
+  }
+  return alpha * acc;
+}
+
+/* Dense definition: out[X, s, E] = sum_t softmax_t(score(s, t)) V[X, t, E]
+ * over the t that are kept (all, or t <= s under a causal pair, which must
+ * name the s and t roles); 0 when none is.  Outputs at the row-major flat
+ * indices in `idx` (all when idx == NULL). */
+int oracle_attention_dense(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
+                           const double *Q, const double *K, const double *V, const int64_t *idx, int64_t n_out,
+                           double *out) {
+  ospec p;
+  oroles r;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if ((rc = attention_roles(&p, &r))) return rc;
+  const int causal = causal_s >= 0;
+  if (causal && (causal_s != r.s || causal_t != r.t)) return OR_BAD_SPEC;
+  int64_t out_total = 1;
+  for (int a = 0; a < p.out_len; ++a) out_total *= ext26[p.out[a] - 'a'];
+  if (!idx) n_out = out_total;
+  const int64_t T = ext26[r.t];
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t q = 0; q < n_out; ++q) {
+    int64_t x[26];
+    memset(x, 0, sizeof(x));
+    int64_t rem = idx ? idx[q] : q;
+    for (int a = p.out_len - 1; a >= 0; --a) {
+      int L = p.out[a] - 'a';
+      x[L] = rem % ext26[L];
+      rem /= ext26[L];
+    }
+    const int64_t s = x[r.s];
+    double m = -INFINITY;
+    for (int64_t t = 0; t < T; ++t) {
+      if (causal && t > s) continue;
+      x[r.t] = t;
+      double sc = att_score(&p, &r, ext26, Q, K, x, alpha);
+      if (sc > m) m = sc;
+    }
+    double l = 0.0, acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      if (causal && t > s) continue;
+      x[r.t] = t;
+      double w = exp(att_score(&p, &r, ext26, Q, K, x, alpha) - m);
+      l += w;
+      acc += w * V[dense_off(p.in[2], ext26, x)];
+    }
+    out[q] = l > 0.0 ? acc / l : 0.0;
+  }
+  return OR_OK;
+}
+
+/* the merge of two triples (the aggregation of the attention join-agg) */
+void oracle_softmax_merge(double m1, double l1, double a1, double m2, double l2, double a2, double *res) {
+  double M = m1 > m2 ? m1 : m2;
+  if (M == -INFINITY) { res[0] = -INFINITY; res[1] = 0.0; res[2] = 0.0; return; }
+  double w1 = m1 == -INFINITY ? 0.0 : exp(m1 - M), w2 = m2 == -INFINITY ? 0.0 : exp(m2 - M);
+  res[0] = M;
+  res[1] = l1 * w1 + l2 * w2;
+  res[2] = a1 * w1 + a2 * w2;
+}
+
+/* Relational form: join the Q, K, V tuples (Def. 3.7 step 1, the same join
+ * as every other spec), compute for each joined tuple and each output
+ * element of its key the triple over the tuple's key range, merge the triples
+ * of equal output key in canonical order (step 2), then write a / l into the
+ * output relation (step 3).  Inputs are relation buffers of doubles; the D
+ * letters must be one block each (a triple needs whole scores). */
+int oracle_attention_relational(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
+                                const int32_t *nblk26, const double *const *in_rel, double *out_rel,
+                                uint8_t *present) {
+  ospec p;
+  oroles r;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if ((rc = attention_roles(&p, &r))) return rc;
+  const int causal = causal_s >= 0;
+  if (causal && (causal_s != r.s || causal_t != r.t)) return OR_BAD_SPEC;
+  for (int a = 0; a < r.nd; ++a)
+    if (nblk26[r.d[a] - 'a'] != 1) return OR_UNSUPPORTED;
+  orel in[OR_MAX_IN], out;
+  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  combo *c;
+  int64_t n;
+  if ((rc = join(&p, in, &out, ext26, nblk26, causal ? r.s : -1, causal ? r.t : -1, &c, &n))) return rc;
+  memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
+  if (present) memset(present, 0, (size_t)out.n_tuples);
+  double *tm = malloc(sizeof(double) * (size_t)out.block_elems * 3);
+  double *tl = tm + out.block_elems, *ta = tl + out.block_elems;
+  for (int64_t first = 0; first < n;) {
+    int64_t last = first;
+    while (last < n && c[last].out_id == c[first].out_id) ++last;
+    for (int64_t w = 0; w < out.block_elems; ++w) { tm[w] = -INFINITY; tl[w] = 0.0; ta[w] = 0.0; }
+    int64_t kout[26];
+    tuple_coords(&out, c[first].out_id, kout);
+    for (int64_t ci = first; ci < last; ++ci) {
+      int64_t lo[26], hi[26], kap[OR_MAX_IN][26];
+      for (int j = 0; j < 3; ++j) {
+        tuple_coords(&in[j], c[ci].in_id[j], kap[j]);
+        for (int a = 0; a < in[j].r; ++a) {
+          lo[in[j].letters[a] - 'a'] = lo_of(&in[j], a, kap[j][a]);
+          hi[in[j].letters[a] - 'a'] = hi_of(&in[j], a, kap[j][a]);
+        }
+      }
+      int64_t out_box = 1;
+      for (int a = 0; a < out.r; ++a) out_box *= hi[out.letters[a] - 'a'] - lo[out.letters[a] - 'a'];
+      int64_t nd = 1;
+      for (int a = 0; a < r.nd; ++a) nd *= hi[r.d[a] - 'a'] - lo[r.d[a] - 'a'];
+      for (int64_t o = 0; o < out_box; ++o) {
+        int64_t x[26], rem = o;
+        for (int a = out.r - 1; a >= 0; --a) {
+          int L = out.letters[a] - 'a';
+          x[L] = lo[L] + rem % (hi[L] - lo[L]);
+          rem /= hi[L] - lo[L];
+        }
+        int64_t w = 0;
+        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - kout[a] * out.e[a]);
+        /* f: the triple of this tuple's key range (two passes: max, then sums) */
+        double m = -INFINITY, l = 0.0, acc = 0.0;
+        for (int pass = 0; pass < 2; ++pass) {
+          for (int64_t t = lo[r.t]; t < hi[r.t]; ++t) {
+            if (causal && t > x[r.s]) continue;
+            x[r.t] = t;
+            double sc = 0.0;
+            for (int64_t i = 0; i < nd; ++i) {
+              int64_t rr = i;
+              for (int a = r.nd - 1; a >= 0; --a) {
+                int L = r.d[a] - 'a';
+                x[L] = lo[L] + rr % (hi[L] - lo[L]);
+                rr /= hi[L] - lo[L];
+              }
+              sc += rel_at(&in[0], in_rel[0], c[ci].in_id[0], kap[0], x) * rel_at(&in[1], in_rel[1], c[ci].in_id[1], kap[1], x);
+            }
+            sc *= alpha;
+            if (pass == 0) {
+              if (sc > m) m = sc;
+            } else {
+              double e = exp(sc - m);
+              l += e;
+              acc += e * rel_at(&in[2], in_rel[2], c[ci].in_id[2], kap[2], x);
+            }
+          }
+        }
+        double res[3];
+        oracle_softmax_merge(tm[w], tl[w], ta[w], m, l, acc, res);
+        tm[w] = res[0]; tl[w] = res[1]; ta[w] = res[2];
+      }
+    }
+    /* recompose: a / l into the key's valid box; padding stays +0 */
+    int64_t out_box = 1;
+    for (int a = 0; a < out.r; ++a) out_box *= hi_of(&out, a, kout[a]) - lo_of(&out, a, kout[a]);
+    for (int64_t o = 0; o < out_box; ++o) {
+      int64_t rem = o, w = 0, sub[26];
+      for (int a = out.r - 1; a >= 0; --a) {
+        int64_t ext = hi_of(&out, a, kout[a]) - lo_of(&out, a, kout[a]);
+        sub[a] = rem % ext;
+        rem /= ext;
+      }
+      for (int a = 0; a < out.r; ++a) w = w * out.e[a] + sub[a];
+      out_rel[c[first].out_id * out.block_elems + w] = tl[w] > 0.0 ? ta[w] / tl[w] : 0.0;
+    }
+    if (present) present[c[first].out_id] = 1;
+    first = last;
+  }
+  free(tm);
+  free(c);
   return OR_OK;
 }
 

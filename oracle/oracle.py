@@ -68,6 +68,13 @@ def _load():
         lib.oracle_repartition.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i32p,
                                            ctypes.c_void_p, ctypes.c_char_p, i32p, i64p]
         lib.oracle_block_shape.argtypes = [ctypes.c_char_p, i64p, i32p, i64p]
+        lib.oracle_attention_dense.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int, i64p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i64p,
+                                               ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_attention_relational.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                                    i64p, i32p, dpp, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_softmax_merge.argtypes = [ctypes.c_double] * 6 + [ctypes.c_void_p]
+        lib.oracle_softmax_merge.restype = None
         lib.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         lib.oracle_round.restype = None
         _lib = lib
@@ -242,6 +249,67 @@ def relational(spec, rel_inputs, extents, blockings, g="mul", agg="sum", alpha=1
                                _i64p(ext), _i32p(nb), ptrs, out.ctypes.data, present.ctypes.data)
     _check(rc, "oracle_relational")
     return out, present
+
+
+def attention_dense(spec, inputs, extents, alpha=1.0, causal=None, sample=None):
+    """Attention by its definition: out[X,s,E] = sum_t softmax_t(alpha sum_D Q K) V
+    (unrounded float64); roles as in oracle.c.  ``sample``: flat output indices."""
+    lib = _load()
+    ins, out_letters = _parse(spec)
+    if len(ins) != 3:
+        raise OracleError("attention takes Q, K, V")
+    arrs = []
+    for lt, x in zip(ins, inputs):
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        want = tuple(int(extents.get(c, -1)) for c in lt)
+        if x.shape != want:
+            raise OracleError(f"input {lt} has shape {x.shape}, expected {want}")
+        arrs.append(x)
+    ext = _ext26(extents)
+    cs, ct = _causal(causal)
+    if sample is None:
+        out = np.zeros(tuple(int(extents[c]) for c in out_letters), dtype=np.float64)
+        idx_p, n = None, 0
+    else:
+        idx = np.ascontiguousarray(np.asarray(sample, dtype=np.int64))
+        out = np.zeros(idx.shape[0], dtype=np.float64)
+        idx_p, n = _i64p(idx), idx.shape[0]
+    rc = lib.oracle_attention_dense(spec.encode(), alpha, cs, ct, _i64p(ext), arrs[0].ctypes.data,
+                                    arrs[1].ctypes.data, arrs[2].ctypes.data, idx_p, n, out.ctypes.data)
+    _check(rc, "oracle_attention_dense")
+    return out
+
+
+def attention_relational(spec, rel_inputs, extents, blockings, alpha=1.0, causal=None):
+    """Attention as one join-agg over relation buffers: per joined tuple the
+    online-softmax triple, merged per output key, recomposed as a / l.
+    Returns (out_relation float64 unrounded, present uint8 per output tuple)."""
+    lib = _load()
+    ins, out_letters = _parse(spec)
+    arrs = [np.ascontiguousarray(np.asarray(r, dtype=np.float64)) for r in rel_inputs]
+    for lt, a in zip(ins, arrs):
+        if a.size != relation_elems(lt, extents, blockings):
+            raise OracleError(f"relation {lt} has {a.size} elements")
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    out = np.zeros(relation_elems(out_letters, extents, blockings), dtype=np.float64)
+    n_tuples = 1
+    for c in out_letters:
+        n_tuples *= int(blockings.get(c, 1))
+    present = np.zeros(n_tuples, dtype=np.uint8)
+    ext, nb = _ext26(extents), _nblk26(blockings)
+    cs, ct = _causal(causal)
+    rc = lib.oracle_attention_relational(spec.encode(), alpha, cs, ct, _i64p(ext), _i32p(nb), ptrs,
+                                         out.ctypes.data, present.ctypes.data)
+    _check(rc, "oracle_attention_relational")
+    return out, present
+
+
+def softmax_merge(t1, t2):
+    """The merge of two online-softmax triples (m, l, a) -> (m, l, a)."""
+    lib = _load()
+    res = np.zeros(3, dtype=np.float64)
+    lib.oracle_softmax_merge(*(float(v) for v in t1), *(float(v) for v in t2), res.ctypes.data)
+    return tuple(float(v) for v in res)
 
 
 def round_to(x, dtype):
