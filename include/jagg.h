@@ -57,8 +57,13 @@ typedef enum {
 
 typedef enum { JAGG_F32 = 0, JAGG_BF16 = 1 } jagg_dtype;
 
-/* The aggregation of Def. 3.7 step (2); both are associative and commutative. */
-typedef enum { JAGG_AGG_NONE = 0, JAGG_AGG_SUM = 1, JAGG_AGG_MAX = 2 } jagg_agg;
+/* The aggregation of Def. 3.7 step (2); each is associative and commutative.
+ * JAGG_AGG_SOFTMAX ("TensorPlay Stax 05", Section 9.10: the online-softmax
+ * triple lets attention be tiled like a reduction) merges triples
+ * (m, l, a) as (M, l1 e^(m1-M) + l2 e^(m2-M), a1 e^(m1-M) + a2 e^(m2-M)),
+ * M = max(m1, m2), identity (-inf, 0, 0), and its recompose step writes
+ * a / l (0 where l = 0).  It pairs only with JAGG_G_ATTENTION. */
+typedef enum { JAGG_AGG_NONE = 0, JAGG_AGG_SUM = 1, JAGG_AGG_MAX = 2, JAGG_AGG_SOFTMAX = 3 } jagg_agg;
 
 /* Block function g applied, element by element, to the joined input values
  * x0, x1, x2 before aggregation.  With g = MUL and agg = SUM the spec is a
@@ -71,8 +76,22 @@ typedef enum {
   JAGG_G_EXP_SUB_DIV = 4, /* exp(x0 - x1) / x2                       */
   JAGG_G_RMS_SCALE = 5,   /* x0 / sqrt(x1 * beta + eps) * x2         */
   JAGG_G_SILU_MUL = 6,    /* x0 / (1 + exp(-x0)) * x1                */
-  JAGG_G_ADD = 7          /* x0 + x1 (+ x2)                          */
+  JAGG_G_ADD = 7,         /* x0 + x1 (+ x2)                          */
+  JAGG_G_ATTENTION = 8    /* with JAGG_AGG_SOFTMAX; see below        */
 } jagg_g;
+
+/* Attention as one join-agg (g = JAGG_G_ATTENTION, agg = JAGG_AGG_SOFTMAX).
+ * The spec is "Q,K,V->O" with the letter roles "X s D, X t D, X t E -> X s E":
+ * X (any number of letters) in all four operands, s in Q and O only, t in
+ * K and V only, one letter D in Q and K only, one letter E in V and O only.
+ * out[X,s,E] = sum_t softmax_t(alpha * sum_D Q[X,s,D] K[X,t,D]) V[X,t,E],
+ * over every t, or over t <= s when the causal pair is (s, t).  The join
+ * pairs each (X, s, E) block with the K/V blocks of every t block; f of a
+ * joined tuple is the triple of its t range, the aggregation merges the
+ * triples in join-list order.  Requirements (else JAGG_E_UNSUPPORTED): Q, K
+ * and V in bfloat16; D and E one block each, of equal padded extent 64 or
+ * 128, innermost in their operands; row strides and block sizes multiples of
+ * 8 elements; blocks under 2 GiB. */
 
 /* One join-agg spec.  out[o] = alpha * AGG over the reduced letters of
  * g(x0, ...).  `einsum` is "in0,in1,...->out" (1 to 3 inputs); operand

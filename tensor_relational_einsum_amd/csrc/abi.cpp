@@ -153,14 +153,17 @@ bool g_arity_ok(int g, int n) {
     case JAGG_G_EXP_SUB:
     case JAGG_G_SILU_MUL: return n == 2;
     case JAGG_G_EXP_SUB_DIV:
-    case JAGG_G_RMS_SCALE: return n == 3;
+    case JAGG_G_RMS_SCALE:
+    case JAGG_G_ATTENTION: return n == 3;
   }
   return false;
 }
 
 jagg_status check_spec(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p) {
-  if (sp->g < JAGG_G_MUL || sp->g > JAGG_G_ADD) return fail(ctx, JAGG_E_INVALID, "unknown g %d", int(sp->g));
-  if (sp->agg < JAGG_AGG_NONE || sp->agg > JAGG_AGG_MAX) return fail(ctx, JAGG_E_INVALID, "unknown aggregation");
+  if (sp->g < JAGG_G_MUL || sp->g > JAGG_G_ATTENTION) return fail(ctx, JAGG_E_INVALID, "unknown g %d", int(sp->g));
+  if (sp->agg < JAGG_AGG_NONE || sp->agg > JAGG_AGG_SOFTMAX) return fail(ctx, JAGG_E_INVALID, "unknown aggregation");
+  if ((sp->agg == JAGG_AGG_SOFTMAX) != (sp->g == JAGG_G_ATTENTION))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "the softmax-triple aggregation pairs only with g = ATTENTION");
   if (sp->out_dtype != JAGG_F32 && sp->out_dtype != JAGG_BF16) return fail(ctx, JAGG_E_INVALID, "unknown out dtype");
   if (!g_arity_ok(sp->g, p.n_in))
     return fail(ctx, JAGG_E_UNSUPPORTED, "g %d does not take %d inputs", int(sp->g), p.n_in);
@@ -761,6 +764,100 @@ jagg_status plan_ew(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, const ja
   return JAGG_OK;
 }
 
+// ------------------------------------------------------------ attention planning
+// Roles of "X s D, X t D, X t E -> X s E" (see jagg.h) and the kernel's
+// layout requirements; every violation is JAGG_E_UNSUPPORTED before launch.
+jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, const jagg_relation *const *ins,
+                           const jagg_relation *out, const int32_t *list, const int32_t *counts, AttnArgs &a,
+                           int &d) {
+  memset(&a, 0, sizeof(a));
+  const Spec &p = b.p;
+  std::string X;
+  char s = 0, t = 0, dl = 0, el = 0;
+  for (char c : p.order) {
+    const bool q = p.in[0].find(c) != std::string::npos, k = p.in[1].find(c) != std::string::npos;
+    const bool v = p.in[2].find(c) != std::string::npos, o = p.out.find(c) != std::string::npos;
+    if (q && k && v && o) X += c;
+    else if (q && !k && !v && o && !s) s = c;
+    else if (!q && k && v && !o && !t) t = c;
+    else if (q && k && !v && !o && !dl) dl = c;
+    else if (!q && !k && v && o && !el) el = c;
+    else return fail(ctx, JAGG_E_UNSUPPORTED, "attention letter '%c' has no role of X s D, X t D, X t E -> X s E", c);
+  }
+  if (!s || !t || !dl || !el) return fail(ctx, JAGG_E_UNSUPPORTED, "attention needs one s, t, D and E letter");
+  if (sp->causal_s && (sp->causal_s != s || sp->causal_t != t))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "the causal pair of attention must be (s, t) = (%c, %c)", s, t);
+  for (int j = 0; j < 3; ++j)
+    if (ins[j]->dt != JAGG_BF16) return fail(ctx, JAGG_E_UNSUPPORTED, "attention inputs must be bfloat16");
+  const jagg_relation &Q = *ins[0], &K = *ins[1], &V = *ins[2], &O = *out;
+  auto pos = [&](int j, char c) { return int(j < 3 ? p.in[j].find(c) : p.out.find(c)); };
+  if (pos(0, dl) != Q.r - 1 || pos(1, dl) != K.r - 1 || pos(2, el) != V.r - 1 || pos(3, el) != O.r - 1)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "D must be innermost in Q and K, E innermost in V and the output");
+  if (b.L.k[dl - 'a'] != 1 || b.L.k[el - 'a'] != 1)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "D and E must be one block each");
+  const int64_t nd = b.L.n[dl - 'a'], ne = b.L.n[el - 'a'];
+  if (nd != ne || (nd != 64 && nd != 128)) return fail(ctx, JAGG_E_UNSUPPORTED, "D = E must be 64 or 128");
+  d = int(nd);
+  a.sQ = inblock_s(Q, pos(0, s));
+  a.tK = inblock_s(K, pos(1, t));
+  a.tV = inblock_s(V, pos(2, t));
+  a.sO = inblock_s(O, pos(3, s));
+  const int64_t lim31 = (int64_t(1) << 31) - 1;
+  for (const jagg_relation *R : {&Q, &K, &V, &O})
+    if (R->be % 8 != 0 || R->be * esz_of(R->dt) > lim31)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "attention blocks must hold a multiple of 8 elements, under 2 GiB");
+  if (a.sQ % 8 || a.tK % 8 || a.tV % 8 || a.sO % 8)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "attention row strides must be multiples of 8 elements");
+  a.nx = int(X.size());
+  if (a.nx > kMaxLetters) return fail(ctx, JAGG_E_UNSUPPORTED, "too many batch letters");
+  int64_t nb = 1;
+  {  // batch letters in output order
+    int i = 0;
+    for (char c : p.out) {
+      if (X.find(c) == std::string::npos) continue;
+      const int64_t e = O.e[pos(3, c)];
+      a.xdiv[i] = make_fastdiv(uint32_t(e));
+      a.xQ[i] = inblock_s(Q, pos(0, c));
+      a.xK[i] = inblock_s(K, pos(1, c));
+      a.xV[i] = inblock_s(V, pos(2, c));
+      a.xO[i] = inblock_s(O, pos(3, c));
+      if (a.xQ[i] % 8 || a.xK[i] % 8 || a.xV[i] % 8 || a.xO[i] % 8)
+        return fail(ctx, JAGG_E_UNSUPPORTED, "attention batch strides must be multiples of 8 elements");
+      nb *= e;
+      ++i;
+    }
+  }
+  a.nbatch = int32_t(nb);
+  a.Q = Q.buf;
+  a.K = K.buf;
+  a.V = V.buf;
+  a.O = O.buf;
+  a.list = list;
+  a.counts = counts;
+  a.per_key = int32_t(b.join.per_key);
+  a.n_keys = int32_t(b.join.n_keys);
+  a.beQ = Q.be;
+  a.beK = K.be;
+  a.beV = V.be;
+  a.beO = O.be;
+  a.e_s = int32_t(O.e[pos(3, s)]);
+  a.e_t = int32_t(K.e[pos(1, t)]);
+  a.n_s = int32_t(b.L.n[s - 'a']);
+  a.n_t = int32_t(b.L.n[t - 'a']);
+  a.s_tiles = int32_t((a.e_s + 127) / 128);
+  a.div_st = make_fastdiv(uint32_t(a.s_tiles));
+  a.div_nb = make_fastdiv(uint32_t(a.nbatch));
+  a.div_Ws = make_fastdiv(uint32_t(tuple_w(O, pos(3, s))));
+  a.div_ks = make_fastdiv(uint32_t(O.k[pos(3, s)]));
+  a.div_Wt = make_fastdiv(uint32_t(tuple_w(K, pos(1, t))));
+  a.div_kt = make_fastdiv(uint32_t(K.k[pos(1, t)]));
+  a.scale_log2 = float(double(sp->alpha) * 1.4426950408889634);
+  a.reverse = sp->causal_s ? 1 : 0;
+  if (int64_t(a.nbatch) * a.n_keys * a.s_tiles > lim31)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "attention grid too large");
+  return JAGG_OK;
+}
+
 // ------------------------------------------------------------ contraction planning
 struct Group {
   std::string letters;  // in canonical order
@@ -1068,8 +1165,10 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   // inputs where every reduced letter is in both inputs and each input
   // contributes output letters of its own; any other aggregating spec is a
   // streaming reduce, and a spec without aggregation is a map.
-  enum { MAP, REDUCE, CONTRACT } kind = MAP;
-  if (spec->agg != JAGG_AGG_NONE) {
+  enum { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
+  if (spec->agg == JAGG_AGG_SOFTMAX) {
+    kind = ATTENTION;
+  } else if (spec->agg != JAGG_AGG_NONE) {
     kind = REDUCE;
     if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
       bool both = true, m_any = false, n_any = false;
@@ -1111,7 +1210,12 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   if (kind == CONTRACT) {
     if ((st = plan_contract(ctx, spec, b, use, out, list, counts, ca, dtype, akc, bkc, va, vb)) != JAGG_OK) return st;
   }
-  if (kind != CONTRACT && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK) return st;
+  AttnArgs at;
+  int att_d = 0;
+  if (kind == ATTENTION && (st = plan_attention(ctx, spec, b, use, out, list, counts, at, att_d)) != JAGG_OK)
+    return st;
+  if ((kind == MAP || kind == REDUCE) && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK)
+    return st;
   std::vector<RelayoutArgs> reblocks;
   std::vector<int> reblock_vec;
   for (int j = 0; j < n_in; ++j) {
@@ -1130,6 +1234,13 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   b.join.list = list;
   b.join.counts = counts;
   if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
+  if (kind == ATTENTION) {
+    const hipError_t e = launch_attention(at, att_d, spec->causal_s != 0, spec->out_dtype == JAGG_BF16, ctx->stream);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: attention d%d, %d keys x %d batch x %d s-tiles\n", spec->einsum, att_d, at.n_keys,
+              at.nbatch, at.s_tiles);
+    return after_launch(ctx, e, "attention");
+  }
   if (kind == CONTRACT) {
     // 256x256 tiles where the block is large enough and the grid still fills the chip
     const int F = dtype ? 8 : 4;

@@ -1,0 +1,332 @@
+// attention.hip -- attention as one join-agg: the online-softmax triple.
+//
+// "TensorPlay Stax 05", Section 9.10: the (m, l, a) triple of online softmax
+// lets attention be tiled like a reduction whose combine merges triples;
+// "Every Kernel Is a Join" Def. 3.7 then makes it one join-agg over blocked
+// Q, K, V: the join pairs each output (X, s, E) block with the K/V tuples of
+// every t block (only t-block <= s-block under a causal pair), f of a joined
+// tuple is the triple of its t range, the aggregation merges the triples of
+// one output key in join-list order, and the recompose writes a / l.  Here
+// the merge runs in registers as the workgroup walks the key's joined
+// tuples, so neither scores nor probabilities reach memory.
+//
+// CDNA4 mapping (v_mfma_f32_32x32x16_bf16; fragment lane l holds row/column
+// l % 32 and K values 8 * (l / 32) .. + 7):
+//  - Scores are computed transposed, S^T = K Q^T (M = t, N = s, K = D), so
+//    that lane l owns one query row s = l % 32 of its wavefront and 32 of
+//    the tile's 64 keys; lane l ^ 32 holds the other 32.  A row maximum is
+//    32 in-lane maxima and one cross-half exchange.
+//  - The output is accumulated transposed too, O^T = V^T P^T (M = E, N = s,
+//    K = t): lane l again owns row s, so rescaling by exp(m_old - m_new) is
+//    one scalar per lane, and P^T is the B operand straight from the score
+//    registers.  The score layout puts keys {0-3, 8-11} (+4 on the upper
+//    half) in a lane's first 8 values; the V^T fragment is read with the
+//    same key permutation through two ds_read_b64_tr_b16 (the sum over the
+//    16 keys of an MFMA step does not depend on their order).
+//  - Q fragments stay in registers for the whole walk; K and V tiles of 64
+//    keys are staged in LDS (rows padded by 16 / 64 bytes against bank
+//    conflicts) with two stages: the global loads of tile i+1 are in flight
+//    while tile i is computed, one barrier per tile.
+//  - Softmax works in base 2 (scores scaled by alpha * log2 e).
+//  - The 128 x E output tile goes through LDS so that rows leave as 16-byte
+//    stores.
+#include "device_common.h"
+#include "jagg_internal.h"
+
+namespace jagg {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = 128;  // query rows per workgroup (32 per wavefront)
+constexpr int kKeys = 64;   // keys per tile
+constexpr uint32_t kOut = 0x80000000u;  // byte offset past any block: the load reads zeros
+
+__device__ __forceinline__ f32x16 mma(const uint4 &a, const uint4 &b, const f32x16 &c) {
+  bf16x8 av, bv;
+  __builtin_memcpy(&av, &a, 16);
+  __builtin_memcpy(&bv, &b, 16);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ uint32_t fd_mod(uint32_t n, const FastDiv &f) { return n - fd_div(n, f) * f.d; }
+
+__device__ __forceinline__ uint4 tr_pair(const char *p0, const char *p1) {
+  typedef __attribute__((address_space(3))) i16x4 *lds_v4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(const_cast<char *>(p0)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(const_cast<char *>(p1)));
+  uint4 r;
+  __builtin_memcpy(&r.x, &lo, 8);
+  __builtin_memcpy(&r.z, &hi, 8);
+  return r;
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
+  constexpr int KP = D * 2 + 16;  // K tile row pitch (bytes)
+  constexpr int VP = D * 2 + 64;  // V tile row pitch
+  constexpr int KBYTES = kKeys * KP;
+  constexpr int STAGE = KBYTES + kKeys * VP;
+  constexpr int OESZ = OUT_BF16 ? 2 : 4;
+  constexpr int OP = D * OESZ + 16;  // output staging row pitch
+  constexpr int LDS = 2 * STAGE > kRows * OP ? 2 * STAGE : kRows * OP;
+  constexpr int CPR = D / 8;       // 16-byte chunks per K / V row
+  constexpr int RPP = 256 / CPR;   // rows per pass of the workgroup
+  constexpr int NP = kKeys / RPP;  // passes per tile
+  constexpr int KS = D / 16;       // MFMA steps over D
+  constexpr int ET = D / 32;       // 32-wide E tiles
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // workgroup -> (batch index inside the block, output key, s tile)
+  uint32_t w = blockIdx.x;
+  const uint32_t st = fd_mod(w, a.div_st);
+  w = fd_div(w, a.div_st);
+  const uint32_t kq = w % uint32_t(a.n_keys);
+  const uint32_t bi = w / uint32_t(a.n_keys);
+  const uint32_t key = a.reverse ? uint32_t(a.n_keys) - 1 - kq : kq;
+  const int32_t cnt = a.counts[key];
+  const int32_t *ents = a.list + int64_t(key) * a.per_key * 4;
+
+  // offsets of the batch index inside each block
+  int64_t oQ = 0, oK = 0, oV = 0, oO = 0;
+  {
+    uint32_t r = bi;
+    for (int i = a.nx - 1; i >= 0; --i) {
+      const uint32_t q = fd_div(r, a.xdiv[i]);
+      const int64_t dig = int64_t(r - q * a.xdiv[i].d);
+      r = q;
+      oQ += dig * a.xQ[i];
+      oK += dig * a.xK[i];
+      oV += dig * a.xV[i];
+      oO += dig * a.xO[i];
+    }
+  }
+  const int32_t S0 = int32_t(fd_mod(fd_div(key, a.div_Ws), a.div_ks)) * a.e_s;  // first s of the block
+  const int32_t s_tile0 = int32_t(st) * kRows;
+  const int32_t s_loc = s_tile0 + 32 * wave + l32;  // this lane's query row, inside the block
+  const int32_t s_glob = S0 + s_loc;
+  const bool row_ok = s_loc < a.e_s && s_glob < a.n_s;
+  const int32_t s_hi = (s_tile0 + kRows < a.e_s ? s_tile0 + kRows : a.e_s) - 1;
+  const int32_t wg_s_last = S0 + s_hi;                                     // last row of the workgroup
+  const int32_t wave_s_first = S0 + s_tile0 + 32 * wave;                   // first row of the wavefront
+  const int32_t wave_s_last = S0 + (s_tile0 + 32 * wave + 31 < s_hi ? s_tile0 + 32 * wave + 31 : s_hi);
+
+  // Q fragments (B operand of S^T = K Q^T), kept for the whole walk
+  uint4 qf[KS];
+  {
+    const int64_t qt = cnt > 0 ? ents[1] : 0;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(static_cast<const char *>(a.Q) + (qt * a.beQ + oQ) * 2, (a.beQ - oQ) * 2);
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      qf[k] = bload(rq, s_loc < a.e_s ? uint32_t((int64_t(s_loc) * a.sQ + 16 * k + 8 * hi) * 2) : kOut);
+  }
+
+  // tiles of the walk: joined tuples in t-block order, 64 keys at a time;
+  // under a causal pair the walk ends at the first tile past the last row
+  const int tpe = (a.e_t + kKeys - 1) / kKeys;
+  int n_it = cnt * tpe;
+  if (CAUSAL) {
+    n_it = 0;
+    for (int e = 0; e < cnt; ++e) {
+      const int32_t T0 = int32_t(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt)) * a.e_t;
+      if (T0 > wg_s_last) break;
+      int tt = 0;
+      while (tt < tpe && T0 + tt * kKeys <= wg_s_last) ++tt;
+      n_it += tt;
+      if (tt < tpe) break;
+    }
+  }
+
+  uint4 kr[NP], vr[NP];
+  auto load_tile = [&](int it) {
+    const int e = it / tpe, tt = it - e * tpe;
+    const int64_t kt = ents[e * 4 + 2], vt = ents[e * 4 + 3];
+    const __amdgpu_buffer_rsrc_t rk =
+        rsrc(static_cast<const char *>(a.K) + (kt * a.beK + oK) * 2, (a.beK - oK) * 2);
+    const __amdgpu_buffer_rsrc_t rv =
+        rsrc(static_cast<const char *>(a.V) + (vt * a.beV + oV) * 2, (a.beV - oV) * 2);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int row = p * RPP + tid / CPR, ch = tid % CPR;
+      const int t_loc = tt * kKeys + row;
+      const bool ok = t_loc < a.e_t;
+      kr[p] = bload(rk, ok ? uint32_t((int64_t(t_loc) * a.tK + ch * 8) * 2) : kOut);
+      vr[p] = bload(rv, ok ? uint32_t((int64_t(t_loc) * a.tV + ch * 8) * 2) : kOut);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char *ks = smem + stage * STAGE;
+    char *vs = ks + KBYTES;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int row = p * RPP + tid / CPR, ch = tid % CPR;
+      *reinterpret_cast<uint4 *>(ks + row * KP + ch * 16) = kr[p];
+      *reinterpret_cast<uint4 *>(vs + row * VP + ch * 16) = vr[p];
+    }
+  };
+
+  f32x16 acc[ET];
+#pragma unroll
+  for (int et = 0; et < ET; ++et)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[et][v] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  if (n_it > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  const int g = lane >> 4, s16 = lane & 15;
+  for (int it = 0; it < n_it; ++it) {
+    const bool more = it + 1 < n_it;
+    if (more) load_tile(it + 1);
+    const int e = it / tpe, tt = it - e * tpe;
+    const int32_t T0 =
+        int32_t(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt)) * a.e_t + tt * kKeys;
+    // keys [0, t_valid) of the tile exist
+    int32_t t_valid = a.e_t - tt * kKeys;
+    if (a.n_t - T0 < t_valid) t_valid = a.n_t - T0;
+    if (t_valid > kKeys) t_valid = kKeys;
+    if (!(CAUSAL && T0 > wave_s_last)) {
+      const char *ks = smem + (it & 1) * STAGE;
+      const char *vs = ks + KBYTES;
+      // S^T = K Q^T for the 64 keys x 32 rows of this wavefront
+      f32x16 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const uint4 kf = *reinterpret_cast<const uint4 *>(ks + (32 * mt + l32) * KP + 32 * k + 16 * hi);
+          sacc[mt] = mma(kf, qf[k], sacc[mt]);
+        }
+      // scale to base 2; drop missing keys and, under the causal pair, t > s
+      const bool full = t_valid == kKeys && !(CAUSAL && T0 + kKeys - 1 > wave_s_first);
+      float z[2][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = sacc[mt][v] * a.scale_log2;
+          if (!full) {
+            const int tl = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (tl >= t_valid || (CAUSAL && T0 + tl > s_glob)) x = -INFINITY;
+          }
+          z[mt][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // merge this tile's triple into the running one
+      const float m_new = fmaxf(m_run, mx);
+      const float base = m_new == -INFINITY ? 0.0f : m_new;
+      const float corr = __builtin_amdgcn_exp2f(m_run - base);
+      float sum = 0.0f;
+      uint4 pf[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(z[mt][8 * h + j] - base);
+            sum += p[j];
+          }
+          pf[2 * mt + h] = uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                 pack_bf16x2(p[6], p[7])};
+        }
+      l_run = l_run * corr + sum;
+      m_run = m_new;
+      if (!__all(corr == 1.0f)) {  // the running maximum moved for some row
+#pragma unroll
+        for (int et = 0; et < ET; ++et)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[et][v] *= corr;
+      }
+      // O^T += V^T P^T, with V^T read in the keys' score order
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        const int n = 32 * et + 16 * (g & 1) + 4 * (s16 & 3);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int kb = 16 * kk + 4 * (g >> 1) + (s16 >> 2);
+          const uint4 vf = tr_pair(vs + kb * VP + n * 2, vs + (kb + 8) * VP + n * 2);
+          acc[et] = mma(vf, pf[kk], acc[et]);
+        }
+      }
+    }
+    if (more) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // recompose: a / l for rows that exist and are inside the relation, 0 elsewhere
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = (row_ok && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
+  {
+    char *orow = smem + (32 * wave + l32) * OP;
+#pragma unroll
+    for (int et = 0; et < ET; ++et)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e0 = 32 * et + 8 * q + 4 * hi;
+        const float y0 = acc[et][4 * q] * inv, y1 = acc[et][4 * q + 1] * inv;
+        const float y2 = acc[et][4 * q + 2] * inv, y3 = acc[et][4 * q + 3] * inv;
+        if constexpr (OUT_BF16) {
+          *reinterpret_cast<uint2 *>(orow + e0 * 2) = uint2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        } else {
+          *reinterpret_cast<float4 *>(orow + e0 * 4) = make_float4(y0, y1, y2, y3);
+        }
+      }
+  }
+  __syncthreads();
+  constexpr int OCH = D * OESZ / 16;  // 16-byte chunks per output row
+  char *ob = static_cast<char *>(a.O) + (int64_t(key) * a.beO + oO) * OESZ;
+  for (int i = tid; i < kRows * OCH; i += 256) {
+    const int row = i / OCH, ch = i - row * OCH;
+    const int sl = s_tile0 + row;
+    if (sl < a.e_s)
+      *reinterpret_cast<uint4 *>(ob + int64_t(sl) * a.sO * OESZ + ch * 16) =
+          *reinterpret_cast<const uint4 *>(smem + row * OP + ch * 16);
+  }
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+static hipError_t go(const AttnArgs &a, hipStream_t st) {
+  const int64_t grid = int64_t(a.nbatch) * a.n_keys * a.s_tiles;
+  hipLaunchKernelGGL((attention_kernel<D, CAUSAL, OUT_BF16>), dim3(unsigned(grid)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs &a, int d, bool causal, bool out_bf16, hipStream_t st) {
+#define JAGG_ATT(DD, CC, OO) \
+  if (d == DD && causal == CC && out_bf16 == OO) return go<DD, CC, OO>(a, st);
+  JAGG_ATT(128, false, false) JAGG_ATT(128, false, true) JAGG_ATT(128, true, false) JAGG_ATT(128, true, true)
+  JAGG_ATT(64, false, false) JAGG_ATT(64, false, true) JAGG_ATT(64, true, false) JAGG_ATT(64, true, true)
+#undef JAGG_ATT
+  return hipErrorInvalidValue;
+}
+
+}  // namespace jagg

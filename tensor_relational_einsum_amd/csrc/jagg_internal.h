@@ -231,4 +231,33 @@ struct FlatArgs {
 hipError_t launch_flat_map(const FlatArgs &a, int g, hipStream_t st);  // 8 elements per vector
 hipError_t launch_flat_reduce(const FlatArgs &a, int vec, int lpr, int g, int agg, hipStream_t st);
 
+// ---------------------------------------------------------------- attention
+// One workgroup: 128 rows of s (32 per wavefront) of one output key and one
+// batch index inside the block; it walks the key's joined (K, V) tuples in
+// join-list order, 64 keys t at a time.
+struct AttnArgs {
+  const void *Q, *K, *V;
+  void *O;
+  const int32_t *list;
+  const int32_t *counts;
+  int32_t per_key;
+  int32_t n_keys;
+  int64_t beQ, beK, beV, beO;          // block elements
+  int32_t nx;                          // batch letters inside a block, innermost last
+  FastDiv xdiv[kMaxLetters];           // their block extents
+  int64_t xQ[kMaxLetters], xK[kMaxLetters], xV[kMaxLetters], xO[kMaxLetters];  // in-block strides
+  int32_t nbatch;                      // product of the batch block extents
+  int64_t sQ, sO, tK, tV;              // in-block strides of s (Q, O) and t (K, V)
+  int32_t e_s, e_t;                    // padded block extents of s and t
+  int32_t n_s, n_t;                    // extents of s and t
+  int32_t s_tiles;                     // ceil(e_s / 128)
+  FastDiv div_st, div_nb;              // division by s_tiles and by nbatch
+  FastDiv div_Ws, div_ks;              // kappa_s = (output tuple / Ws) % ks
+  FastDiv div_Wt, div_kt;              // kappa_t = (K tuple / Wt) % kt
+  float scale_log2;                    // alpha * log2(e)
+  int32_t reverse;                     // walk output keys from the last (causal balance)
+};
+// d: 64 or 128 (the padded D = E extent)
+hipError_t launch_attention(const AttnArgs &a, int d, bool causal, bool out_bf16, hipStream_t st);
+
 }  // namespace jagg
