@@ -40,18 +40,28 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 def spec_flops(st: I.Step, ext: dict) -> float:
     """Algorithmic FLOPs of a contraction spec: 2 per multiply-add over the
-    unpadded index space; under a causal pair only t <= s is counted."""
-    if not (st.g == "mul" and st.agg == "sum" and len(st.ins) == 2):
+    unpadded index space; under a causal pair only t <= s is counted.  Fused
+    attention counts its two products (scores and P V), as the unfused chain
+    does; softmax arithmetic is not counted."""
+    ins = st.spec.split("->")[0].split(",")
+    if st.g == "attention":
+        q, k, v = ins
+        groups = [set(q) | set(k), set(v) | set(st.spec.split("->")[1])]
+    elif st.g == "mul" and st.agg == "sum" and len(st.ins) == 2:
+        groups = [set("".join(ins))]
+    else:
         return 0.0
-    letters = set("".join(st.spec.split("->")[0].split(",")))
-    n = 1.0
-    for c in letters:
-        n *= ext[c]
-    if st.causal:
-        s, t = st.causal
-        S = ext[s]
-        n = n / (ext[s] * ext[t]) * (S * (S + 1) / 2)
-    return 2.0 * n
+    total = 0.0
+    for letters in groups:
+        n = 1.0
+        for c in letters:
+            n *= ext[c]
+        if st.causal:
+            s, t = st.causal
+            S = ext[s]
+            n = n / (ext[s] * ext[t]) * (S * (S + 1) / 2)
+        total += 2.0 * n
+    return total
 
 
 def spec_bytes(run: ChainRunner, st, ext: dict) -> float:
@@ -165,6 +175,7 @@ def cpu_baseline(w: I.Workload, dense: dict, target_s: float = 12.0) -> dict:
     vals["r1"] = I.draw(gen[0], [w.extents[c] for c in "bsh"], "normal", "bf16").to(torch.float64).numpy()
     vals["r2"] = vals["r1"]
     vals["O"] = I.draw(gen[1], [w.extents[c] for c in "bsqd"], "normal", "bf16").to(torch.float64).numpy()
+    # (r1, r2 and O are outputs of earlier steps: stand-ins of the same shape)
     specs = [st for st in w.chain if isinstance(st, I.Step) and spec_flops(st, w.extents) > 0 and not st.causal
              and all(n in vals for n in st.ins)]
     rng = np.random.default_rng(0)
@@ -199,7 +210,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama", choices=["llama", "attention", "multi_index", "matmul"])
+    ap.add_argument("--workload", default="llama",
+                    choices=["llama", "llama_chain", "attention", "attention_chain", "multi_index", "matmul"],
+                    help="llama / attention: fused attention; *_chain: the five-spec attention chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repartition", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,8 +224,9 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     ctx = jagg.Context(0)
-    w = {"llama": I.llama_block, "attention": I.attention_chain, "multi_index": I.multi_index,
-         "matmul": I.matmul_256}[args.workload]()
+    w = {"llama": lambda: I.llama_block(fused_attention=True), "llama_chain": I.llama_block,
+         "attention": lambda: I.attention_chain(fused=True), "attention_chain": I.attention_chain,
+         "multi_index": I.multi_index, "matmul": I.matmul_256}[args.workload]()
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     dense = I.generate(w)
     run = ChainRunner(ctx, w, dense)
@@ -235,7 +249,8 @@ def main():
             ent["TFLOP/s"] = round(f / (call_ms[i] * 1e-3) / 1e12, 2)
         ent["GB/s"] = round(by / (call_ms[i] * 1e-3) / 1e9, 1)
         breakdown.append(ent)
-        if isinstance(st, I.Step) and f and not st.causal and run.rel[st.ins[0]].dtype == "bf16":
+        if (isinstance(st, I.Step) and f and not st.causal and st.g == "mul"
+                and run.rel[st.ins[0]].dtype == "bf16"):
             dom_flops += f
             dom_ms += float(call_ms[i])
             dom_bytes += by
@@ -245,7 +260,7 @@ def main():
     in_dtype = run.rel[big.ins[0]].dtype
     if dom_launches:
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-        tr = counter_traffic() if args.workload == "llama" else None
+        tr = counter_traffic() if args.workload in ("llama", "llama_chain") else None
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": tr,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
@@ -255,8 +270,9 @@ def main():
     else:
         peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS
         achieved = value
+        kname = "attention_kernel<bf16>" if big.g == "attention" else f"contract_kernel<{in_dtype}>"
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": f"contract_kernel<{in_dtype}>"}
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": kname}
     rep = {}
     if not args.no_repartition:
         del run
@@ -273,7 +289,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
     cpu = None
-    if not args.no_cpu_baseline and args.workload == "llama":
+    if not args.no_cpu_baseline and args.workload in ("llama", "llama_chain"):
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, dense)
     out = {

@@ -104,13 +104,19 @@ def repartition_4d(shape=(32, 128, 64, 64)) -> Workload:
         chain=[Relayout("Y", "X", "acbd", {"a": 1, "b": 1, "c": 4, "d": 2})], seed=1002)
 
 
-def attention_chain(b=4, h=32, s=2048, d=128, nb=16) -> Workload:
-    """Unfused attention as join-aggs: QK^T, row MAX, row SUM of exp, normalize, PV.
-    No 1/sqrt(d) scale; Q, K, V bf16 N(0,1); s and t each in `nb` blocks."""
-    ext = {"b": b, "h": h, "s": s, "t": s, "d": d}
-    blk = {"b": 1, "h": 1, "s": nb, "t": nb, "d": 1}
+def attention_chain(b=4, h=32, s=2048, d=128, nb=16, fused=False) -> Workload:
+    """Attention as join-aggs.  Unfused: QK^T, row MAX, row SUM of exp,
+    normalize, PV (five specs).  Fused: one spec whose aggregation merges
+    online-softmax triples.  No 1/sqrt(d) scale; Q, K, V bf16 N(0,1); s and
+    t each in `nb` blocks."""
+    ext = {"b": b, "h": h, "s": s, "t": s, "d": d, "e": d}
+    blk = {"b": 1, "h": 1, "s": nb, "t": nb, "d": 1, "e": 1}
     tens = [("Q", "bhsd", "normal", "bf16", 1.0, 0.0, blk), ("K", "bhtd", "normal", "bf16", 1.0, 0.0, blk),
             ("V", "bhtd", "normal", "bf16", 1.0, 0.0, blk)]
+    if fused:
+        chain = [Step("O", "bhsd,bhtd,bhte->bhse", ["Q", "K", "V"], "attention", "softmax", "f32", blk)]
+        return Workload(name=f"attention_fused_b{b}_h{h}_s{s}_d{d}_bf16_st{nb}", extents=ext, tensors=tens,
+                        chain=chain, seed=1003)
     chain = [
         Step("S", "bhsd,bhtd->bhst", ["Q", "K"], "mul", "sum", "f32", blk),
         Step("M", "bhst->bhs", ["S"], "ident", "max", "f32", blk),
@@ -122,14 +128,18 @@ def attention_chain(b=4, h=32, s=2048, d=128, nb=16) -> Workload:
                     chain=chain, seed=1003)
 
 
-def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8) -> Workload:
+def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8,
+                fused_attention=False) -> Workload:
     """LLaMA-7B-shaped decoder block, every op a join-agg spec.
 
-    x (fp32) -> RMSNorm*g1 -> Q,K,V -> relayout to head-major -> causal
-    attention (scale 1/sqrt(d)) -> relayout back -> Wo -> +x -> RMSNorm*g2 ->
-    gate, up -> silu(gate)*up -> down -> +residual.  No RoPE, no biases.
+    x (fp32) -> RMSNorm*g1 -> Q,K,V -> causal attention (scale 1/sqrt(d)) ->
+    Wo -> +x -> RMSNorm*g2 -> gate, up -> silu(gate)*up -> down -> +residual.
+    No RoPE, no biases.  Attention is either the five-spec chain between
+    relayouts to head-major order and back, or one spec whose aggregation
+    merges online-softmax triples, read and written in the projections'
+    own layout (no relayout).
     """
-    ext = {"b": b, "s": s, "t": s, "h": hid, "q": heads, "d": d, "f": ffn}
+    ext = {"b": b, "s": s, "t": s, "h": hid, "q": heads, "d": d, "e": d, "f": ffn}
     proj = {"b": 1, "s": s_blk, "t": s_blk, "h": h_blk, "q": q_blk, "d": 1}
     att = {"b": 1, "q": 1, "s": s_blk, "t": s_blk, "d": 1}
     ffb = {"b": 1, "s": s_blk, "h": h_blk, "f": f_blk}
@@ -154,15 +164,24 @@ def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_b
         Step("Qp", "bsh,hqd->bsqd", ["r1", "Wq"], "mul", "sum", "bf16", proj),
         Step("Kp", "bth,hqd->btqd", ["r1", "Wk"], "mul", "sum", "bf16", proj),
         Step("Vp", "bth,hqd->btqd", ["r1", "Wv"], "mul", "sum", "bf16", proj),
-        Relayout("Q", "Qp", "bqsd", att),
-        Relayout("K", "Kp", "bqtd", att),
-        Relayout("V", "Vp", "bqtd", att),
-        Step("S", "bqsd,bqtd->bqst", ["Q", "K"], "mul", "sum", "f32", att, alpha=1.0 / math.sqrt(d), causal=c),
-        Step("M", "bqst->bqs", ["S"], "ident", "max", "f32", att, causal=c),
-        Step("L", "bqst,bqs->bqs", ["S", "M"], "exp_sub", "sum", "f32", att, causal=c),
-        Step("P", "bqst,bqs,bqs->bqst", ["S", "M", "L"], "exp_sub_div", "none", "bf16", att, causal=c),
-        Step("Oh", "bqst,bqtd->bqsd", ["P", "V"], "mul", "sum", "bf16", att, causal=c),
-        Relayout("O", "Oh", "bsqd", proj),
+    ]
+    if fused_attention:
+        fa = dict(proj, e=1)
+        chain += [Step("O", "bsqd,btqd,btqe->bsqe", ["Qp", "Kp", "Vp"], "attention", "softmax", "bf16", fa,
+                       alpha=1.0 / math.sqrt(d), causal=c)]
+    else:
+        chain += [
+            Relayout("Q", "Qp", "bqsd", att),
+            Relayout("K", "Kp", "bqtd", att),
+            Relayout("V", "Vp", "bqtd", att),
+            Step("S", "bqsd,bqtd->bqst", ["Q", "K"], "mul", "sum", "f32", att, alpha=1.0 / math.sqrt(d), causal=c),
+            Step("M", "bqst->bqs", ["S"], "ident", "max", "f32", att, causal=c),
+            Step("L", "bqst,bqs->bqs", ["S", "M"], "exp_sub", "sum", "f32", att, causal=c),
+            Step("P", "bqst,bqs,bqs->bqst", ["S", "M", "L"], "exp_sub_div", "none", "bf16", att, causal=c),
+            Step("Oh", "bqst,bqtd->bqsd", ["P", "V"], "mul", "sum", "bf16", att, causal=c),
+            Relayout("O", "Oh", "bsqd", proj),
+        ]
+    chain += [
         Step("A", "bsqd,qdh->bsh", ["O", "Wo"], "mul", "sum", "f32", proj),
         Step("x2", "bsh,bsh->bsh", ["x", "A"], "add", "none", "f32", proj),
         Step("ss2", "bsh->bs", ["x2"], "square", "sum", "f32", ffb),
@@ -173,7 +192,8 @@ def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_b
         Step("D", "bsf,fh->bsh", ["H", "Wd"], "mul", "sum", "f32", ffb),
         Step("y", "bsh,bsh->bsh", ["x2", "D"], "add", "none", "f32", ffb),
     ]
-    return Workload(name=f"llama7b_block_b{b}_s{s}_bf16", extents=ext, tensors=tens, chain=chain, seed=1004)
+    name = f"llama7b_block_b{b}_s{s}_bf16_" + ("fused_attention" if fused_attention else "attention_chain")
+    return Workload(name=name, extents=ext, tensors=tens, chain=chain, seed=1004)
 
 
 def multi_index(a=96, b=300, c=64, d=48, e=1000, blk=(5, 7, 4, 3, 6)) -> Workload:

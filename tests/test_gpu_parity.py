@@ -360,8 +360,11 @@ def oracle_chain(w, dense, stop=None):
             xs = []
             for name, lt in zip(st.ins, ins):
                 xs.append(vals[name])
-            y = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
-                        causal=st.causal)
+            if st.g == "attention":
+                y = O.attention_dense(st.spec, xs, w.extents, alpha=st.alpha, causal=st.causal)
+            else:
+                y = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
+                            causal=st.causal)
             vals[st.out] = O.round_to(y, st.out_dtype)
         else:
             src_letters = None
@@ -495,8 +498,12 @@ def sampled_spec_check(ctx, run, w, n_samples=400, seed=2):
         idx = rng.integers(0, got.numel(), size=n_samples)
         idx = np.concatenate([idx, [got.numel() - 1]])
         xs = [to_np(dense_of(n)) for n in st.ins]
-        want = O.round_to(O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta,
-                                  eps=st.eps, causal=st.causal, sample=idx), st.out_dtype)
+        if st.g == "attention":
+            want = O.attention_dense(st.spec, xs, w.extents, alpha=st.alpha, causal=st.causal, sample=idx)
+        else:
+            want = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
+                           causal=st.causal, sample=idx)
+        want = O.round_to(want, st.out_dtype)
         g = to_np(got).reshape(-1)[idx]
         if st.causal is not None and st.agg == "none" or (st.causal is not None and st.g == "mul" and
                                                           st.causal[1] in out_l):
@@ -510,7 +517,8 @@ def sampled_spec_check(ctx, run, w, n_samples=400, seed=2):
         if st.agg == "max":
             assert np.array_equal(g, want), f"{st.out}: MAX differs"
         else:
-            tol = F32_TOL if st.out_dtype == "f32" else BF16_OUT_TOL
+            # fused attention: probabilities enter P V rounded to bf16 (see test_gpu_attention)
+            tol = F32_TOL if st.out_dtype == "f32" and st.g != "attention" else BF16_OUT_TOL
             err = normwise_err(g, want)
             assert err < tol, f"{st.out} ({st.spec}): normwise error {err:.3e}"
 
@@ -533,6 +541,31 @@ def test_llama_block_small(ctx):
     sampled_spec_check(ctx, run, w, n_samples=200)
 
 
+def test_llama_block_small_fused_attention(ctx):
+    w = I.llama_block(b=1, s=256, hid=512, heads=4, d=128, ffn=1376, s_blk=2, h_blk=4, q_blk=2, f_blk=8,
+                      fused_attention=True)
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    want = oracle_chain(w, dense)
+    for name in ["ss1", "r1", "Qp", "Kp", "Vp", "O", "A", "x2", "r2", "G", "U", "H", "D", "y"]:
+        err = normwise_err(rel_dense(run.rel[name], w.extents), want[name])
+        assert err < CHAIN_TOL, f"{name}: normwise error {err:.3e}"
+    sampled_spec_check(ctx, run, w, n_samples=200)
+
+
+def test_llama_block_config_sampled_fused_attention(ctx):
+    """The full LLaMA-7B-shaped block with fused attention, as bench.py
+    times it: every spec checked on sampled outputs."""
+    w = I.llama_block(fused_attention=True)
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    run.run()
+    torch.cuda.synchronize()
+    sampled_spec_check(ctx, run, w, n_samples=300)
+
+
 def test_llama_block_config_sampled(ctx):
     """The full LLaMA-7B-shaped block (4 x 2048 tokens), each spec checked on
     sampled outputs, each relayout bit-exactly."""
@@ -545,7 +578,7 @@ def test_llama_block_config_sampled(ctx):
 
 
 def test_multi_index_and_attention_configs_per_spec(ctx):
-    for w in (I.multi_index(), I.attention_chain()):
+    for w in (I.multi_index(), I.attention_chain(), I.attention_chain(fused=True)):
         dense = I.generate(w)
         run = ChainRunner(ctx, w, dense)
         run.run()
