@@ -88,8 +88,8 @@ typedef enum {
  * over every t, or over t <= s when the causal pair is (s, t).  The join
  * pairs each (X, s, E) block with the K/V blocks of every t block; f of a
  * joined tuple is the triple of its t range, the aggregation merges the
- * triples in join-list order.  Requirements (else JAGG_E_UNSUPPORTED): Q, K
- * and V in bfloat16; D and E one block each, of equal padded extent 64 or
+ * triples in join-list order.  Requirements (else JAGG_E_UNSUPPORTED):
+ * alpha > 0; Q, K and V in bfloat16; D and E one block each, of equal padded extent 64 or
  * 128, innermost in their operands; row strides and block sizes multiples of
  * 8 elements; blocks under 2 GiB. */
 

@@ -853,6 +853,9 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
   a.div_kt = make_fastdiv(uint32_t(K.k[pos(1, t)]));
   a.scale_log2 = float(double(sp->alpha) * 1.4426950408889634);
   a.reverse = sp->causal_s ? 1 : 0;
+  a.xcd_group = a.nbatch % 8 == 0 ? 1 : 0;
+  a.div_group = make_fastdiv(uint32_t(a.n_keys * a.s_tiles));
+  if (!(sp->alpha > 0.0f)) return fail(ctx, JAGG_E_UNSUPPORTED, "attention needs a positive score scale alpha");
   if (int64_t(a.nbatch) * a.n_keys * a.s_tiles > lim31)
     return fail(ctx, JAGG_E_UNSUPPORTED, "attention grid too large");
   return JAGG_OK;

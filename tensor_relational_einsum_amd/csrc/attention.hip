@@ -95,8 +95,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // workgroup -> (batch index inside the block, output key, s tile)
+  // workgroup -> (batch index inside the block, output key, s tile).  With
+  // xcd_group, the workgroups of one batch index (which share its K and V)
+  // are numbered so that they all land on one XCD: dispatch deals
+  // workgroups to the 8 XCDs round-robin, each XCD with its own L2.
   uint32_t w = blockIdx.x;
+  if (a.xcd_group) {
+    const uint32_t xcd = w & 7u, local = w >> 3;
+    const uint32_t grp = fd_div(local, a.div_group);
+    w = (grp * 8u + xcd) * a.div_group.d + (local - grp * a.div_group.d);
+  }
   const uint32_t st = fd_mod(w, a.div_st);
   w = fd_div(w, a.div_st);
   const uint32_t kq = w % uint32_t(a.n_keys);

@@ -256,6 +256,8 @@ struct AttnArgs {
   FastDiv div_Wt, div_kt;              // kappa_t = (K tuple / Wt) % kt
   float scale_log2;                    // alpha * log2(e)
   int32_t reverse;                     // walk output keys from the last (causal balance)
+  int32_t xcd_group;                   // keep one batch index's workgroups on one XCD
+  FastDiv div_group;                   // workgroups per batch index (n_keys * s_tiles)
 };
 // d: 64 or 128 (the padded D = E extent)
 hipError_t launch_attention(const AttnArgs &a, int d, bool causal, bool out_bf16, hipStream_t st);
