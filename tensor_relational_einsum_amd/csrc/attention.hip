@@ -27,7 +27,8 @@
 //    keys are staged in LDS (rows padded by 16 / 64 bytes against bank
 //    conflicts) with two stages: the global loads of tile i+1 are in flight
 //    while tile i is computed, one barrier per tile.
-//  - Softmax works in base 2 (scores scaled by alpha * log2 e).
+//  - Softmax works in base 2: the maximum is taken on the raw scores and
+//    exp2(score * alpha log2 e - m) is one FMA and one exp (alpha > 0).
 //  - The 128 x E output tile goes through LDS so that rows leave as 16-byte
 //    stores.
 #include "device_common.h"
@@ -163,21 +164,31 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     }
   }
 
+  // K / V tile loads: each lane's byte offset inside a tile is fixed; the
+  // tile's origin goes into the (scalar) buffer base, and the buffer ends at
+  // the tuple's last valid row, so rows past it read zeros
+  uint32_t koff[NP], voff[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * RPP + tid / CPR, ch = tid % CPR;
+    koff[p] = uint32_t((int64_t(row) * a.tK + ch * 8) * 2);
+    voff[p] = uint32_t((int64_t(row) * a.tV + ch * 8) * 2);
+  }
   uint4 kr[NP], vr[NP];
   auto load_tile = [&](int it) {
     const int e = it / tpe, tt = it - e * tpe;
     const int64_t kt = ents[e * 4 + 2], vt = ents[e * 4 + 3];
+    const int64_t r0 = int64_t(tt) * kKeys;  // first row of the tile
+    const int64_t kbase = kt * a.beK + oK + r0 * a.tK, vbase = vt * a.beV + oV + r0 * a.tV;
+    const int64_t kend = oK + int64_t(a.e_t - 1) * a.tK + D, vend = oV + int64_t(a.e_t - 1) * a.tV + D;
     const __amdgpu_buffer_rsrc_t rk =
-        rsrc(static_cast<const char *>(a.K) + (kt * a.beK + oK) * 2, (a.beK - oK) * 2);
+        rsrc(static_cast<const char *>(a.K) + kbase * 2, (kt * a.beK + kend - kbase) * 2);
     const __amdgpu_buffer_rsrc_t rv =
-        rsrc(static_cast<const char *>(a.V) + (vt * a.beV + oV) * 2, (a.beV - oV) * 2);
+        rsrc(static_cast<const char *>(a.V) + vbase * 2, (vt * a.beV + vend - vbase) * 2);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int row = p * RPP + tid / CPR, ch = tid % CPR;
-      const int t_loc = tt * kKeys + row;
-      const bool ok = t_loc < a.e_t;
-      kr[p] = bload(rk, ok ? uint32_t((int64_t(t_loc) * a.tK + ch * 8) * 2) : kOut);
-      vr[p] = bload(rv, ok ? uint32_t((int64_t(t_loc) * a.tV + ch * 8) * 2) : kOut);
+      kr[p] = bload(rk, koff[p]);
+      vr[p] = bload(rv, voff[p]);
     }
   };
   auto store_tile = [&](int stage) {
@@ -204,6 +215,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   }
   __syncthreads();
   const int g = lane >> 4, s16 = lane & 15;
+  const float scale = a.scale_log2;  // > 0
   for (int it = 0; it < n_it; ++it) {
     const bool more = it + 1 < n_it;
     if (more) load_tile(it + 1);
@@ -230,25 +242,27 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
           const uint4 kf = *reinterpret_cast<const uint4 *>(ks + (32 * mt + l32) * KP + 32 * k + 16 * hi);
           sacc[mt] = mma(kf, qf[k], sacc[mt]);
         }
-      // scale to base 2; drop missing keys and, under the causal pair, t > s
+      // drop missing keys and, under the causal pair, t > s
       const bool full = t_valid == kKeys && !(CAUSAL && T0 + kKeys - 1 > wave_s_first);
-      float z[2][16];
+      if (!full) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int tl = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (tl >= t_valid || (CAUSAL && T0 + tl > s_glob)) sacc[mt][v] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[mt][v] * a.scale_log2;
-          if (!full) {
-            const int tl = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
-            if (tl >= t_valid || (CAUSAL && T0 + tl > s_glob)) x = -INFINITY;
-          }
-          z[mt][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // merge this tile's triple into the running one
-      const float m_new = fmaxf(m_run, mx);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[mt][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale;  // base-2 maximum of the tile (scale > 0)
+      // The reference m of the running triple moves only when the tile's
+      // maximum exceeds it by more than 8 (then p <= 2^8 always): the merge
+      // is exact for any common reference, and most tiles skip the rescale.
+      const float m_new = mx > m_run + 8.0f ? mx : m_run;
       const float base = m_new == -INFINITY ? 0.0f : m_new;
       const float corr = __builtin_amdgcn_exp2f(m_run - base);
       float sum = 0.0f;
@@ -260,20 +274,21 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
           float p[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(z[mt][8 * h + j] - base);
+            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * h + j], scale, -base));
             sum += p[j];
           }
           pf[2 * mt + h] = uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                  pack_bf16x2(p[6], p[7])};
         }
-      l_run = l_run * corr + sum;
-      m_run = m_new;
-      if (!__all(corr == 1.0f)) {  // the running maximum moved for some row
+      if (!__all(m_new == m_run)) {  // some row moved its reference
+        l_run *= corr;
 #pragma unroll
         for (int et = 0; et < ET; ++et)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[et][v] *= corr;
       }
+      l_run += sum;
+      m_run = m_new;
       // O^T += V^T P^T, with V^T read in the keys' score order
 #pragma unroll
       for (int et = 0; et < ET; ++et) {
