@@ -272,27 +272,36 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
   TB tb[1];
   ta[0].init(p.sAm, p.sAk);
   tb[0].init(p.sBn, p.sBk);
-  auto load_step = [&](int s, TA &xa, TB &xb) {
-    const int e = s / KT;
-    const int kt = s - e * KT;
-    const int32_t *ent = ents + e * 3;
-    const int64_t aid = ent[p.a_slot], bid = ent[p.b_slot];
-    const int k0 = kt * BK;
+  // the walk over (joined tuple, K-tile): the next load's position and tuple
+  // ids are kept ahead, so a tuple's ids are read one step before they are
+  // used and no step waits on a scalar load
+  int le = 0, lkt = 0;  // position of the next load
+  int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
+  int pe = 0, pk0 = 0;  // position of the load in flight (for the causal mask)
+  auto load_next = [&](TA &xa, TB &xb) {
+    const int k0 = lkt * BK;
+    pe = le;
+    pk0 = k0;
     const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
-    const T *pa = reinterpret_cast<const T *>(p.A) + aid * p.beA + ao;
-    const T *pb = reinterpret_cast<const T *>(p.B) + bid * p.beB + bo;
+    const T *pa = reinterpret_cast<const T *>(p.A) + la * p.beA + ao;
+    const T *pb = reinterpret_cast<const T *>(p.B) + lb * p.beB + bo;
     xa.load(tile_rsrc(pa, (p.beA - ao) * ESZ), p.M - m0, p.K - k0);
     xb.load(tile_rsrc(pb, (p.beB - bo) * ESZ), p.N - n0, p.K - k0);
+    if (++lkt == KT) {
+      lkt = 0;
+      if (++le < cnt) {
+        la = ents[le * 3 + p.a_slot];
+        lb = ents[le * 3 + p.b_slot];
+      }
+    }
   };
   // causal pair with t reduced: zero A where t > s, on the diagonal block only;
   // applied just before the LDS store so the loads stay in flight meanwhile
-  auto mask_step = [&](int s, TA &xa) {
+  auto mask_step = [&](TA &xa) {
     if (MASK && p.causal_red) {
-      const int e = s / KT;
-      const int k0 = (s - e * KT) * BK;
-      const int64_t aid = ents[e * 3 + p.a_slot];
+      const int64_t aid = ents[pe * 3 + p.a_slot];
       const int64_t kt_blk = (aid / p.ct_w) % p.ct_k;
-      if (kt_blk == ks) xa.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, k0);
+      if (kt_blk == ks) xa.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, pk0);
     }
   };
 
@@ -359,20 +368,20 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
       }
     }
   };
-  auto store_step = [&](int s, TA &xa, TB &xb, char *lds) {
-    mask_step(s, xa);
+  auto store_step = [&](TA &xa, TB &xb, char *lds) {
+    mask_step(xa);
     xa.store(lds);
     xb.store(lds + A_BYTES);
   };
 
-  load_step(0, ta[0], tb[0]);
-  store_step(0, ta[0], tb[0], smem);
+  load_next(ta[0], tb[0]);
+  store_step(ta[0], tb[0], smem);
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int cur = s & 1;
-    if (s + 1 < steps) load_step(s + 1, ta[0], tb[0]);
+    if (s + 1 < steps) load_next(ta[0], tb[0]);
     compute(smem + cur * STAGE);
-    if (s + 1 < steps) store_step(s + 1, ta[0], tb[0], smem + (cur ^ 1) * STAGE);
+    if (s + 1 < steps) store_step(ta[0], tb[0], smem + (cur ^ 1) * STAGE);
     __syncthreads();
   }
 
