@@ -90,7 +90,7 @@ def counter_traffic() -> float | None:
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernel source is still
     the one the counters were taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "llama_block_hbm_counters.md")
+    path = os.path.join(ROOT, "profiles", "llama_block_fused_attention_hbm_counters.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -260,7 +260,7 @@ def main():
     in_dtype = run.rel[big.ins[0]].dtype
     if dom_launches:
         achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-        tr = counter_traffic() if args.workload in ("llama", "llama_chain") else None
+        tr = counter_traffic() if args.workload == "llama" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": tr,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",

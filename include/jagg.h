@@ -58,8 +58,9 @@ typedef enum {
 typedef enum { JAGG_F32 = 0, JAGG_BF16 = 1 } jagg_dtype;
 
 /* The aggregation of Def. 3.7 step (2); each is associative and commutative.
- * JAGG_AGG_SOFTMAX ("TensorPlay Stax 05", Section 9.10: the online-softmax
- * triple lets attention be tiled like a reduction) merges triples
+ * JAGG_AGG_SOFTMAX ("Stax (5): Caching and Measurement", chapter summary on
+ * Section 9.10: the online-softmax triple lets attention be tiled like a
+ * reduction) merges triples
  * (m, l, a) as (M, l1 e^(m1-M) + l2 e^(m2-M), a1 e^(m1-M) + a2 e^(m2-M)),
  * M = max(m1, m2), identity (-inf, 0, 0), and its recompose step writes
  * a / l (0 where l = 0).  It pairs only with JAGG_G_ATTENTION. */

@@ -584,15 +584,15 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
 /* Attention as one join-agg: the online-softmax triple.                     */
 /* ------------------------------------------------------------------------ */
 /*
- * "TensorPlay Stax 05" (tensorplay.cn), Section 9.10 and its exercise on the
- * triple (m, l, a): online softmax lets attention be tiled like a reduction,
- * the merge of triples being associative and commutative; Section 9.5 /
- * Proposition 9.1 give the same semigroup on (m, d) pairs for a single-pass
- * softmax.  With "Every Kernel Is a Join" Def. 3.7, attention over blocked
- * Q, K, V is then one join-agg: f of a joined (Q, K, V) tuple is the triple
- * of its key range, the aggregation merges triples, and the recompose step
- * divides a by l.  The pages print no formula for the merge; the reading
- * taken here is the standard one:
+ * "Stax (5): Caching and Measurement", chapter summary (on its Section 9.10)
+ * and exercise 15 on the triple (m, l, a): online softmax lets attention be
+ * tiled like a reduction, the merge of triples being associative and
+ * commutative; the summary's Proposition 9.1 gives the same semigroup on
+ * (m, d) pairs for a single-pass softmax.  With "Every Kernel Is a Join"
+ * Def. 3.7, attention over blocked Q, K, V is then one join-agg: f of a
+ * joined (Q, K, V) tuple is the triple of its key range, the aggregation
+ * merges triples, and the recompose step divides a by l.  The pages print
+ * no formula for the merge; the reading taken here is the standard one:
  *   (m1, l1, a1) + (m2, l2, a2) = (M, l1 e^(m1-M) + l2 e^(m2-M),
  *                                    a1 e^(m1-M) + a2 e^(m2-M)),  M = max(m1, m2),
  * identity (-inf, 0, 0).

@@ -1,6 +1,7 @@
 // attention.hip -- attention as one join-agg: the online-softmax triple.
 //
-// "TensorPlay Stax 05", Section 9.10: the (m, l, a) triple of online softmax
+// "Stax (5): Caching and Measurement", chapter summary on Section 9.10 and
+// exercise 15: the (m, l, a) triple of online softmax
 // lets attention be tiled like a reduction whose combine merges triples;
 // "Every Kernel Is a Join" Def. 3.7 then makes it one join-agg over blocked
 // Q, K, V: the join pairs each output (X, s, E) block with the K/V tuples of

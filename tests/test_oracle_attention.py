@@ -1,6 +1,7 @@
 """Pins for the oracle's attention join-agg (the online-softmax triple).
 
-"TensorPlay Stax 05", Section 9.10 and its exercise on the triple (m, l, a):
+"Stax (5): Caching and Measurement", chapter summary on Section 9.10 and
+exercise 15 on the triple (m, l, a):
 attention is tiled like a reduction whose aggregation merges triples; with
 "Every Kernel Is a Join" Def. 3.7 that is one join-agg over blocked Q, K, V.
 The oracle's dense form is pinned to torch's softmax and matmul in float64
