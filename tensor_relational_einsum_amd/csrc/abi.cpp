@@ -882,6 +882,12 @@ bool group_stride(const Group &g, const std::string &lt, const jagg_relation &R,
   return true;
 }
 
+// M panels per group of the grouped tile order (measured best of 2/4/8/16)
+#ifndef JAGG_GROUP_M
+#define JAGG_GROUP_M 4
+#endif
+constexpr int kGroupM = JAGG_GROUP_M;
+
 jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, const jagg_relation *const *ins,
                           const jagg_relation *out, const int32_t *list, const int32_t *counts, ContractArgs &a,
                           int &dtype, bool &a_kc, bool &b_kc, int &va, int &vb) {
@@ -974,6 +980,28 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
   a.tiles_m = (a.M + 127) / 128;
   a.tiles_n = (a.N + 127) / 128;
   a.n_keys = b.join.n_keys;
+  // key grid for the grouped tile order: every blocked output letter is an M
+  // or N letter, the M ones before the N ones in the key's row-major order
+  {
+    int64_t km = 1, kn = 1;
+    bool ok = Gb.ext == 1, seen_n = false;
+    for (char c : p.out) {
+      const int32_t k = b.L.k[c - 'a'];
+      if (k == 1) continue;
+      const bool m = Gm.letters.find(c) != std::string::npos, n = Gn.letters.find(c) != std::string::npos;
+      if (m && !seen_n) km *= k;
+      else if (n) {
+        kn *= k;
+        seen_n = true;
+      } else {
+        ok = false;
+      }
+    }
+    if (ok && km * kn == a.n_keys && km < (1 << 20) && kn < (1 << 20)) {
+      a.km = int32_t(km);
+      a.kn = int32_t(kn);
+    }
+  }
   a.div_s = a.div_t = make_fastdiv(1);
   // blocks addressed through 32-bit buffer offsets
   if (RA.be * esz_of(RA.dt) >= (int64_t(1) << 31) || RB.be * esz_of(RB.dt) >= (int64_t(1) << 31))
@@ -1252,6 +1280,7 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
     // per-XCD renumbering pays where several tiles of one output block share panels
     const int bm = big ? 256 : 128;
     ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
+    ca.group_m = (ca.remap && ca.km > 0 && ca.batch == 1) ? kGroupM : 0;
     const int ob = spec->out_dtype == JAGG_BF16;
     const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream)
                                : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream);

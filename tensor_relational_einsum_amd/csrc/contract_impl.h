@@ -247,12 +247,30 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     const int64_t G = gridDim.x;
     if (p.remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
   }
-  const int tn = int(w % p.tiles_n);
-  w /= p.tiles_n;
-  const int tm = int(w % p.tiles_m);
-  w /= p.tiles_m;
-  const int bt = int(w % p.batch);
-  const int64_t key = w / p.batch;
+  int tn, tm, bt;
+  int64_t key;
+  if (p.group_m) {
+    // Tiles of all output keys form one grid of M panels x N panels, walked
+    // column-major in groups of group_m M panels: the tiles that run
+    // together (a contiguous range on each XCD) cover a compact block of
+    // panels, so their operand slices are shared through L2.
+    const int64_t Mp = int64_t(p.km) * p.tiles_m, Np = int64_t(p.kn) * p.tiles_n;
+    const int64_t per_group = int64_t(p.group_m) * Np;
+    const int64_t g = w / per_group, r = w - g * per_group;
+    const int64_t rows = Mp - g * p.group_m < p.group_m ? Mp - g * p.group_m : p.group_m;
+    const int64_t pm = g * p.group_m + r % rows, pn = r / rows;
+    key = (pm / p.tiles_m) * p.kn + pn / p.tiles_n;
+    tm = int(pm % p.tiles_m);
+    tn = int(pn % p.tiles_n);
+    bt = 0;
+  } else {
+    tn = int(w % p.tiles_n);
+    w /= p.tiles_n;
+    tm = int(w % p.tiles_m);
+    w /= p.tiles_m;
+    bt = int(w % p.batch);
+    key = w / p.batch;
+  }
 
   const int32_t cnt = p.counts[key];
   if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier

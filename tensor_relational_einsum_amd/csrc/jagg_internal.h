@@ -128,6 +128,10 @@ struct ContractArgs {
   int32_t e_s, e_t;
   FastDiv div_s, div_t;         // division by e_s / e_t
   int32_t remap;                // renumber workgroups per XCD (tiles share operand panels)
+  // grouped tile order over the global panel grid, when the output key is
+  // (M-letter blocks) x (N-letter blocks) in that order and batch == 1:
+  // km, kn = key blocks along M and N; group_m = M panels per group (0: off)
+  int32_t km, kn, group_m;
 };
 // out_bf16: 0 f32 / 1 bf16 output; a_kc / b_kc: operand contiguous along K;
 // va / vb: vector width (elements) of global loads (16 bytes or one element);
