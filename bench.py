@@ -101,7 +101,8 @@ def counter_traffic() -> float | None:
     if "traffic_bytes_per_launch" not in vals or "kernel_source_sha256_16" not in vals:
         return None
     h = hashlib.sha256()
-    for rel in ("tensor_relational_einsum_amd/csrc/contract_impl.h", "tensor_relational_einsum_amd/csrc/contract_bf16.hip"):
+    for rel in ("tensor_relational_einsum_amd/csrc/contract_impl.h", "tensor_relational_einsum_amd/csrc/contract_dma.h",
+                "tensor_relational_einsum_amd/csrc/contract_bf16.hip"):
         h.update(open(os.path.join(ROOT, rel), "rb").read())
     if h.hexdigest()[:16] != vals["kernel_source_sha256_16"]:
         return None
@@ -265,7 +266,8 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": tr,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": round(dom_bytes / dom_launches),
-                "kernel": "contract_kernel<bf16> (projection / FFN specs)", "launches_per_step": dom_launches,
+                "kernel": "contract_dma_kernel<bf16> (projection / FFN specs, 256x256 tiles)",
+                "launches_per_step": dom_launches,
                 "avg_launch_ms": round(dom_ms / dom_launches, 4)}
     else:
         peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS

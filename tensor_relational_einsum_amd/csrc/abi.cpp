@@ -1282,8 +1282,12 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
     ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
     ca.group_m = (ca.remap && ca.km > 0 && ca.batch == 1) ? kGroupM : 0;
     const int ob = spec->out_dtype == JAGG_BF16;
-    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream)
-                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream);
+    const char *which = "";
+    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which)
+                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", spec->einsum, which, (long long)ca.n_keys,
+              ca.batch);
     return after_launch(ctx, e, "contract");
   }
   const char *which = "";

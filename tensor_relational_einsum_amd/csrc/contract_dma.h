@@ -1,0 +1,327 @@
+// contract_dma.h -- bf16 block contraction with a deep LDS pipeline fed by
+// buffer loads that write LDS directly.
+//
+// Same computation as contract_kernel ("Every Kernel Is a Join", Sec. 1 and
+// Examples 3.8/3.9: a join on the shared inner index, then SUM over the
+// joined tuples; one workgroup owns one output tile of one output key and
+// accumulates every joined tuple's product in registers), for the case that
+// dominates projection-heavy chains: bf16 operands read as 16-byte vectors,
+// 256 x 256 output tiles, no causal pair on the reduced letter.
+//
+// CDNA4 mapping
+//  - 4 wavefronts, one per SIMD, each owning a 128 x 128 quarter of the tile
+//    (16 accumulators of 32 x 32 in AGPRs).  Per K chunk of 16 a wavefront
+//    reads 8 fragments for 16 MFMAs: half the LDS bytes per MFMA of a
+//    128 x 64 wavefront tile.
+//  - The K walk (joined tuple, K-tile of 32) is served by NS LDS stages of
+//    A[256 x 32] and B[256 x 32] (32 KB each, NS = 4 by default); a step's
+//    loads are issued NS - 2 steps before the step that consumes them.  No
+//    VGPRs hold data in flight.
+//  - buffer_load_dwordx4 ... lds: each wavefront instruction fills 1 KB of
+//    LDS contiguously, lane l at byte 16*l; which global vector lands in each
+//    16-byte slot is chosen through the lane's offset.  The tiles are stored
+//    unpadded with an XOR swizzle of 16-byte slots so that the fragment reads
+//    below hit all 64 banks:
+//      K-contiguous [256 rows][4 slots]: slot q of row r at q ^ ((r >> 2) & 3)
+//      M/N-contiguous [32 K rows][32 slots]: slot c of row k at c ^ (4 * (k & 3))
+//  - Out-of-range lanes (rows past the block edge, the K tail) pass an offset
+//    past the buffer's end and write zeros, as the plain buffer load does.
+//  - Each step is two phases of 16 MFMAs around one barrier; the fragment
+//    reads of the next chunk and the step's loads are issued between the
+//    MFMAs, so the in-order wavefront issues them in the MFMA shadow.
+//    Issuing the loads as a burst after the barrier instead cost ~10% (the
+//    vector memory path backs up and stalls MFMA issue).
+//  - Waits: before the barrier a wavefront waits for its own loads of the
+//    stage the next phase reads (vmcnt counts vector loads in issue order)
+//    and for its LDS reads; the barrier then makes every wavefront's loads of
+//    that stage visible and every read of the stage about to be refilled
+//    complete.
+#pragma once
+
+#ifndef JAGG_DMA_STAGES
+#define JAGG_DMA_STAGES 4
+#endif
+
+#include "contract_impl.h"
+
+namespace jagg {
+
+typedef __attribute__((address_space(3))) void *lds_dma_ptr;
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four scalar words: base, stride 0, byte count, and the
+// gfx950 word-3 flags (raw buffer, 32-bit data format); lanes whose offset
+// lies at or past `bytes` read zeros.
+__device__ __forceinline__ i32x4_rsrc dma_rsrc(const void *base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_rsrc r;
+  r.x = int(uint32_t(a));
+  r.y = int(uint32_t(a >> 32) & 0xffffu);
+  r.z = int(bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One 16-byte buffer load per lane into LDS: the wavefront's 64 vectors land
+// contiguously at `lds` (lane l at lds + 16 l).  Written as inline assembly
+// so that the compiler's wait-count pass does not track it: its per-object
+// tracking of LDS-writing loads loses precision across the loop back edge
+// and would wait for every stage on the first step of each unrolled pass.
+// The kernel waits for these loads itself (vmcnt, in issue order).
+__device__ __forceinline__ void dma16(i32x4_rsrc rs, uint32_t voff, const char *lds) {
+  const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_dma_ptr)(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
+
+constexpr int kDmaBK = 32;                 // K elements per step
+constexpr int kDmaRowBytes = kDmaBK * 2;   // bytes of one K-contiguous row
+constexpr int kDmaTileBytes = 256 * kDmaRowBytes;  // one operand tile (16 KB)
+
+// One operand's DMA loads: 256 rows (M or N) by 32 K values; R*4 slots over
+// NT threads, NI instructions each.
+template <bool KC, int NT>
+struct DmaOperand {
+  static constexpr int SLOTS = 256 * 4;
+  static constexpr int NI = SLOTS / NT;
+  static_assert(SLOTS % NT == 0 && NT % 64 == 0, "tile does not split over the wavefronts");
+  uint32_t off[NI];   // byte offset from the step's origin, or kOob for rows past the edge
+  int32_t kidx[NI];   // K index of the lane's vector inside the step
+
+  // wave: wavefront index; lane: lane index; rows_left: valid rows (M or N)
+  __device__ __forceinline__ void init(int wave, int lane, int rows_left, int64_t s_row, int64_t s_k) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int P = (i * (NT / 64) + wave) * 64 + lane;  // 16-byte LDS slot this lane fills
+      int row, k;
+      if (KC) {
+        const int r = P >> 2, q = (P & 3) ^ ((r >> 2) & 3);
+        row = r;
+        k = q * 8;
+      } else {
+        const int kr = P >> 5, c = (P & 31) ^ ((kr & 3) << 2);
+        row = c * 8;
+        k = kr;
+      }
+      kidx[i] = k;
+      off[i] = row < rows_left ? uint32_t((int64_t(row) * s_row + int64_t(k) * s_k) * 2) : kOob;
+    }
+  }
+
+  // issue load i of one step into `lds` (this operand's 16 KB of a stage)
+  __device__ __forceinline__ void issue(int i, i32x4_rsrc rs, int k_left, char *lds, int wave_s) const {
+    dma16(rs, kidx[i] < k_left ? off[i] : kOob, lds + (i * (NT / 64) + wave_s) * 1024);
+  }
+};
+
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_kernel(
+    const ContractArgs p) {
+  // 4 wavefronts, one per SIMD, each owning a 128 x 128 quarter of the tile
+  constexpr int NT = 256, WAVES_N = 2;
+  constexpr int WTM = 128, WTN = 128, TM = WTM / 32, TN = WTN / 32;
+  constexpr int BM = 256, BN = 256, BK = kDmaBK;
+  constexpr int L = DmaOperand<A_KC, NT>::NI + DmaOperand<B_KC, NT>::NI;  // loads per step per thread
+  static_assert(NS >= 3 && NS <= 5, "stage count");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * 2 * kDmaTileBytes];
+  auto stage = [&](int s) { return smem + (s % NS) * (2 * kDmaTileBytes); };
+
+  int tn, tm, bt;
+  int64_t key;
+  decode_tile(p, tm, tn, bt, key);
+  const int32_t cnt = p.counts[key];
+  if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier
+  // the join list is read-only for the kernel's lifetime: reading it through
+  // the constant address space keeps the tuple-id reads on the scalar unit
+  typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+  const const_i32p ents = (const_i32p)(p.list + key * int64_t(p.per_key) * 3);
+
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KT = (p.K + BK - 1) / BK;
+  const int steps = cnt * KT;
+  const int64_t a_org = int64_t(bt) * p.sAb + int64_t(m0) * p.sAm;
+  const int64_t b_org = int64_t(bt) * p.sBb + int64_t(n0) * p.sBn;
+  int64_t ks = 0;
+  if (p.causal_out) ks = (key / p.cs_w) % p.cs_k;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  DmaOperand<A_KC, NT> da;
+  DmaOperand<B_KC, NT> db;
+  da.init(wave, lane, p.M - m0, p.sAm, p.sAk);
+  db.init(wave, lane, p.N - n0, p.sBn, p.sBk);
+
+  // the walk over (joined tuple, K-tile): position and tuple ids of the next
+  // step to load; past the last step the loads use an empty resource (every
+  // lane reads zeros) so that every step issues the same number of loads
+  int ld = 0, le = 0, lkt = 0;
+  int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
+  i32x4_rsrc rs_a, rs_b;  // resources of the step being loaded
+  int k_left = 0;
+  char *ld_buf = smem;
+  auto prep = [&](char *buf) {
+    const int k0 = lkt * BK;
+    const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
+    const uint16_t *pa = reinterpret_cast<const uint16_t *>(p.A) + la * p.beA + ao;
+    const uint16_t *pb = reinterpret_cast<const uint16_t *>(p.B) + lb * p.beB + bo;
+    const bool live = ld < steps;
+    rs_a = dma_rsrc(pa, live ? (p.beA - ao) * 2 : 0);
+    rs_b = dma_rsrc(pb, live ? (p.beB - bo) * 2 : 0);
+    k_left = p.K - k0;
+    ld_buf = buf;
+  };
+  auto dma_a = [&](int i) { da.issue(i, rs_a, k_left, ld_buf, wave_s); };
+  auto dma_b = [&](int i) { db.issue(i, rs_b, k_left, ld_buf + kDmaTileBytes, wave_s); };
+  auto advance = [&]() {
+    ++ld;
+    if (++lkt == KT) {
+      lkt = 0;
+      if (++le < cnt) {
+        la = ents[le * 3 + p.a_slot];
+        lb = ents[le * 3 + p.b_slot];
+      }
+    }
+  };
+  constexpr int NA = DmaOperand<A_KC, NT>::NI, NB = DmaOperand<B_KC, NT>::NI;
+
+  const int wm = (wave / WAVES_N) * WTM, wn = (wave % WAVES_N) * WTN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  // fragment addresses inside a stage (bytes), per K chunk kc of 16
+  //  K-contiguous: row wm + 32 i + lrow, slot (2 kc + lhalf) ^ ((lrow >> 2) & 3)
+  //  M/N-contiguous (transposing reads): lane s of 16-lane group g reads K row
+  //  16 kc + 8 (g >> 1) + (s >> 2), columns col0 + 16 (g & 1) + 4 (s & 3)
+  const int g16 = lane >> 4, s16 = lane & 15;
+  auto kc_addr = [&](int row0, int kc) {
+    return (row0 + lrow) * kDmaRowBytes + (((2 * kc + lhalf) ^ ((lrow >> 2) & 3)) << 4);
+  };
+  auto rc_addr = [&](int col0) {
+    const int kr = 8 * (g16 >> 1) + (s16 >> 2);
+    const int slot = (col0 >> 3) + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+    return kr * 512 + ((slot ^ ((kr & 3) << 2)) << 4) + 8 * (s16 & 1);
+  };
+  int a_addr[A_KC ? 2 : TM], b_addr[B_KC ? 2 : TN];
+  if constexpr (A_KC) {
+    a_addr[0] = kc_addr(wm, 0);
+    a_addr[1] = kc_addr(wm, 1);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_addr[i] = rc_addr(wm + 32 * i);
+  }
+  if constexpr (B_KC) {
+    b_addr[0] = kc_addr(wn, 0) + kDmaTileBytes;
+    b_addr[1] = kc_addr(wn, 1) + kDmaTileBytes;
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_addr[j] = rc_addr(wn + 32 * j) + kDmaTileBytes;
+  }
+
+  typedef __attribute__((address_space(3))) i16x4 *lds_v4;
+  auto frag_kc = [&](const char *base, int addr, int i) {
+    return *reinterpret_cast<const uint4 *>(base + addr + i * 32 * kDmaRowBytes);
+  };
+  auto frag_rc = [&](const char *base, int addr, int kc) {
+    char *p0 = const_cast<char *>(base) + addr + kc * 16 * 512;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0 + 4 * 512));
+    uint4 r;
+    __builtin_memcpy(&r.x, &lo, 8);
+    __builtin_memcpy(&r.z, &hi, 8);
+    return r;
+  };
+  // fragments of one K chunk of 16: TM of A, TN of B
+  struct Frags {
+    uint4 a[TM], b[TN];
+  };
+  // fragment x of chunk kc: x < TM is A's fragment x, else B's fragment x - TM
+  auto read_frag = [&](const char *S, int kc, Frags &f, int x) {
+    if (x < TM) {
+      if constexpr (A_KC) f.a[x] = frag_kc(S, a_addr[kc], x);
+      else f.a[x] = frag_rc(S, a_addr[x], kc);
+    } else {
+      if constexpr (B_KC) f.b[x - TM] = frag_kc(S, b_addr[kc], x - TM);
+      else f.b[x - TM] = frag_rc(S, b_addr[x - TM], kc);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Step s (stage s mod NS), with chunk 0 of its stage already in f0:
+  //   phase A: MFMAs of chunk 0, with the reads of chunk 1 and the second
+  //     half of step s+NS-2's loads (into stage s-2) between them;
+  //   wait for this wavefront's loads of stage s+1 and for its LDS reads,
+  //     barrier (stage s+1 now visible to all; every read of stage s-1,
+  //     last read in step s-1, complete);
+  //   phase B: MFMAs of chunk 1, with the reads of chunk 0 of stage s+1 and
+  //     the first half of step s+NS-1's loads (into stage s-1) between them.
+  // One wavefront per SIMD issues in order, so memory instructions placed
+  // between MFMAs issue in the MFMA shadow instead of stalling it; spreading
+  // the loads over the step also keeps the vector memory path from being
+  // flooded right after the barrier.  Scheduling barriers pin the order.
+  // Stage s-2 is free since step s-1's barrier and stage s-1 since step s's.
+  // Past the last step the reads see zero fill or stale data that no MFMA
+  // consumes.
+  static_assert(TM * TN == 16 && TM + TN <= 8 && NA <= 4 && NB <= 4, "interleave pattern");
+  auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
+      if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
+      if (k >= 8 && (k & 1) == 0 && (k - 8) / 2 < 4) dma((k - 8) / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  Frags f0, f1;
+  // prologue: steps 0..NS-3 whole, the first half of step NS-2
+  for (int s = 0; s < NS - 2; ++s) {
+    prep(stage(s));
+#pragma unroll
+    for (int i = 0; i < NA; ++i) dma_a(i);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma_b(i);
+    advance();
+  }
+  prep(stage(NS - 2));
+#pragma unroll
+  for (int i = 0; i < NA; ++i) dma_a(i);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 3) * (NA + NB) + NA) : "memory");
+#pragma unroll
+  for (int x = 0; x < TM + TN; ++x) read_frag(stage(0), 0, f0, x);
+  for (int s = 0; s < steps; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    phase(f0, stage(s), 1, f1, [&](int i) {
+      if (i < NB) dma_b(i);
+    });
+    advance();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 3) * (NA + NB)) : "memory");
+    prep(stage(s + NS - 1));
+    phase(f1, stage(s + 1), 0, f0, [&](int i) {
+      if (i < NA) dma_a(i);
+    });
+  }
+
+  // the zero-fill loads past the last step may still be in flight: let them
+  // land before the workgroup's LDS can be handed to another workgroup
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+}
+
+template <int OB, bool AK, bool BKC>
+static hipError_t launch_dma(const ContractArgs &a, hipStream_t st) {
+  ContractArgs b = a;
+  b.tiles_m = (a.M + 255) / 256;
+  b.tiles_n = (a.N + 255) / 256;
+  const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
+  hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES>), dim3(unsigned(grid)), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+}  // namespace jagg

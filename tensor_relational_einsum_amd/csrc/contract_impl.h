@@ -25,9 +25,10 @@
 //    turns four 4-element row pieces into four 4-element K columns; for
 //    fp32 M/N-contiguous tiles one ds_read_b32 per MFMA.
 //  - Two LDS stages: the global loads of step s+1 are in flight while the
-//    MFMAs of step s run; one barrier per step.  (Measured on MI355X, the
-//    kernel is bound by its LDS-read / MFMA interleave rather than by global
-//    latency: keeping every K-step's tile L2-resident gains only ~6%.)
+//    MFMAs of step s run; one barrier per step.  This kernel serves fp32,
+//    one-element loads, causal masks on the reduced letter and small tiles;
+//    bf16 256 x 256 tiles over 16-byte vectors go to the LDS-pipelined
+//    kernel of contract_dma.h.
 //  - Workgroups are renumbered so that consecutive tiles of one output row
 //    panel land on the same XCD (dispatch round-robins workgroups over the
 //    8 XCDs, each with its own L2).
@@ -225,30 +226,15 @@ struct Mma<float> {
   }
 };
 
-template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
-          bool MASK>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
-  constexpr int NT = WAVES_M * WAVES_N * 64;
-  constexpr int ESZ = int(sizeof(T));
-  constexpr int BK = kSlab / ESZ;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int KCH = ESZ == 2 ? BK / 16 : BK / 8;  // fragment chunks per K-tile
-  using TA = Tile<T, A_KC, BM, VA, NT>;
-  using TB = Tile<T, B_KC, BN, VB, NT>;
-  constexpr int A_BYTES = tile_bytes<A_KC, BM, ESZ>(), B_BYTES = tile_bytes<B_KC, BN, ESZ>();
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-  // workgroup -> tile; where neighbouring tiles share operand panels, the
-  // numbering gives each XCD a contiguous run of tiles
+// workgroup -> (tile row, tile column, batch index, output key).  Where
+// neighbouring tiles share operand panels, the numbering gives each XCD a
+// contiguous run of tiles (dispatch round-robins workgroups over the 8 XCDs).
+__device__ __forceinline__ void decode_tile(const ContractArgs &p, int &tm, int &tn, int &bt, int64_t &key) {
   int64_t w = blockIdx.x;
   {
     const int64_t G = gridDim.x;
     if (p.remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
   }
-  int tn, tm, bt;
-  int64_t key;
   if (p.group_m) {
     // Tiles of all output keys form one grid of M panels x N panels, walked
     // column-major in groups of group_m M panels: the tiles that run
@@ -271,6 +257,61 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     bt = int(w % p.batch);
     key = w / p.batch;
   }
+}
+
+// Epilogue: scale, causal mask, convert, store the TM x TN fragments of one
+// wavefront (fragment element v of lane l: row 8*(v/4) + 4*(l/32) + v%4,
+// column l%32).  m0 / n0: tile origin plus the wavefront's offset.
+template <int OUT_BF16, int TM, int TN>
+__device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                           int bt, int64_t key, int64_t ks, int m0, int n0, int lane) {
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  char *Cb = reinterpret_cast<char *>(p.C);
+  const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
+  int64_t kt_out = 0;
+  if (p.causal_out) kt_out = (key / p.ct_w) % p.ct_k;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + i * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
+        const int n = n0 + j * 32 + lrow;
+        if (m < p.M && n < p.N) {
+          float x = p.alpha * acc[i][j][v];
+          if (p.causal_out) {
+            const int64_t sg = ks * p.e_s + (uint32_t(m) - fd_div(uint32_t(m), p.div_s) * p.div_s.d);
+            const int64_t tg = kt_out * p.e_t + (uint32_t(n) - fd_div(uint32_t(n), p.div_t) * p.div_t.d);
+            if (tg > sg) x = 0.0f;
+          }
+          const int64_t off = cbase + int64_t(m) * p.sCm + n;
+          if (OUT_BF16)
+            reinterpret_cast<uint16_t *>(Cb)[off] = f32_to_bf16(x);
+          else
+            reinterpret_cast<float *>(Cb)[off] = x;
+        }
+      }
+}
+
+template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
+          bool MASK>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int ESZ = int(sizeof(T));
+  constexpr int BK = kSlab / ESZ;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int KCH = ESZ == 2 ? BK / 16 : BK / 8;  // fragment chunks per K-tile
+  using TA = Tile<T, A_KC, BM, VA, NT>;
+  using TB = Tile<T, B_KC, BN, VB, NT>;
+  constexpr int A_BYTES = tile_bytes<A_KC, BM, ESZ>(), B_BYTES = tile_bytes<B_KC, BN, ESZ>();
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  int tn, tm, bt;
+  int64_t key;
+  decode_tile(p, tm, tn, bt, key);
 
   const int32_t cnt = p.counts[key];
   if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier
@@ -403,34 +444,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     __syncthreads();
   }
 
-  // epilogue: scale, mask, convert, store (row = 8*(v/4) + 4*half + v%4, col = lane%32)
-  const int32_t out_id = ents[0];
-  char *Cb = reinterpret_cast<char *>(p.C);
-  const int64_t cbase = int64_t(out_id) * p.beC + int64_t(bt) * p.sCb;
-  int64_t kt_out = 0;
-  if (p.causal_out) kt_out = (key / p.ct_w) % p.ct_k;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm + i * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
-        const int n = n0 + wn + j * 32 + lrow;
-        if (m < p.M && n < p.N) {
-          float x = p.alpha * acc[i][j][v];
-          if (p.causal_out) {
-            const int64_t sg = ks * p.e_s + (uint32_t(m) - fd_div(uint32_t(m), p.div_s) * p.div_s.d);
-            const int64_t tg = kt_out * p.e_t + (uint32_t(n) - fd_div(uint32_t(n), p.div_t) * p.div_t.d);
-            if (tg > sg) x = 0.0f;
-          }
-          const int64_t off = cbase + int64_t(m) * p.sCm + n;
-          if (OUT_BF16)
-            reinterpret_cast<uint16_t *>(Cb)[off] = f32_to_bf16(x);
-          else
-            reinterpret_cast<float *>(Cb)[off] = x;
-        }
-      }
+  store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
 }
 
 template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false>

@@ -135,11 +135,12 @@ struct ContractArgs {
 };
 // out_bf16: 0 f32 / 1 bf16 output; a_kc / b_kc: operand contiguous along K;
 // va / vb: vector width (elements) of global loads (16 bytes or one element);
-// big: 256x256 tiles (8 wavefronts) instead of 128x128 (4 wavefronts).
+// big: 256x256 tiles (8 wavefronts) instead of 128x128 (4 wavefronts);
+// *which names the kernel that ran (for tracing).
 hipError_t launch_contract_bf16(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
-                                hipStream_t st);
+                                hipStream_t st, const char **which);
 hipError_t launch_contract_f32(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
-                               hipStream_t st);
+                               hipStream_t st, const char **which);
 
 // ---------------------------------------------------------------- map / reduce
 struct EwArgs {

@@ -187,6 +187,47 @@ def test_contraction_parity(ctx, spec, ext, blk, idt, odt):
     assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
 
 
+# The LDS-pipelined 256x256 kernel: at least 256 such tiles, 16-byte vectors,
+# bf16 operands.  Blocks of 264 rows (one full tile and a ragged 8-row tail),
+# two joined tuples per output key of 104 K values each (three full K-steps of
+# 32 and a tail of 8), every operand orientation.
+LDS_PIPELINE_CASES = [
+    # spec, extents, blockings, out dtype, causal
+    ("ij,jk->ik", dict(i=2112, j=208, k=2112), dict(i=8, j=2, k=8), "f32", None),
+    ("ij,kj->ik", dict(i=2112, j=208, k=2112), dict(i=8, j=2, k=8), "bf16", None),
+    ("ji,jk->ik", dict(i=2112, j=208, k=2112), dict(i=8, j=2, k=8), "f32", None),
+    ("ji,kj->ik", dict(i=2112, j=208, k=2112), dict(i=8, j=2, k=8), "f32", None),
+    # one long K walk per key (K = 528: 16 full steps and a tail of 16)
+    ("ij,jk->ik", dict(i=2112, j=528, k=2112), dict(i=8, j=1, k=8), "bf16", None),
+    # causal pair in the output (mask applied in the epilogue)
+    ("bhsd,bhtd->bhst", dict(b=2, h=4, s=1056, t=1056, d=128), dict(b=1, h=1, s=4, t=4, d=1), "f32", ("s", "t")),
+]
+
+
+@pytest.mark.parametrize("spec,ext,blk,odt,causal", LDS_PIPELINE_CASES)
+def test_contraction_lds_pipeline(trace_ctx, capfd, spec, ext, blk, odt, causal):
+    n_in = len(spec.split("->")[0].split(","))
+    got, want, got_rel, pad, _ = run_spec_case(trace_ctx, spec, ext, blk, in_dtypes=["bf16"] * n_in, out_dtype=odt,
+                                               causal=causal, alpha=0.5 if causal else 1.0)
+    assert "lds pipeline" in capfd.readouterr().err, "the case must run the LDS-pipelined kernel"
+    if causal is not None:
+        # tuples above the block diagonal are absent from the output relation
+        # and never written; compare the present ones
+        s_, t_ = causal
+        out = spec.split("->")[1]
+        e = -(-ext[s_] // blk[s_])
+        idx = np.indices(got.shape)
+        mask = (idx[out.index(t_)] // e) <= (idx[out.index(s_)] // e)
+        got, want = np.where(mask, got, 0.0), np.where(mask, want, 0.0)
+        kidx = np.indices([blk[c] for c in out]).reshape(len(out), -1)
+        present = kidx[out.index(t_)] <= kidx[out.index(s_)]
+        pad = (pad.reshape(present.size, -1) & present[:, None]).reshape(-1)
+    tol = F32_TOL if odt == "f32" else BF16_OUT_TOL
+    err = normwise_err(got, want)
+    assert err < tol, f"normwise error {err:.3e}"
+    assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
+
+
 EW_CASES = [
     # spec, g, agg, extents, blockings, in dtypes, out dtype, positive inputs, causal
     ("bhst->bhs", "ident", "max", dict(b=2, h=3, s=40, t=300), dict(b=1, h=1, s=3, t=4), ["f32"], "f32", (), None),
