@@ -252,6 +252,114 @@ int64_t largest_divisor_le(int64_t n, int64_t cap) {
   return 1;
 }
 
+// LDS-transposing plan for a digit permutation: the innermost dim is shared
+// (stride 1 on both sides) but short, so one side would move it in short
+// runs.  Dims whose source stride continues the source run are added to the
+// box until the run reaches ~1 KB (the source chain), then dims continuing
+// the destination run likewise (the destination chain); the box is read in
+// source runs and written in destination runs.  Returns false when no such
+// box of 1, 2, 4, 8 or 16 vectors per thread exists.
+#ifndef JAGG_RELAYOUT_LDS
+#define JAGG_RELAYOUT_LDS 1
+#endif
+#ifndef JAGG_RELAYOUT_LANES_DST
+#define JAGG_RELAYOUT_LANES_DST 0
+#endif
+constexpr bool kRelayoutLds = JAGG_RELAYOUT_LDS;
+#ifndef JAGG_RELAYOUT_RUN_CAP
+#define JAGG_RELAYOUT_RUN_CAP 2048
+#endif
+constexpr int64_t kRelayoutRunCap = JAGG_RELAYOUT_RUN_CAP;  // longest run a chain builds (bytes)
+static bool plan_relayout_lds(const std::vector<Dim> &dims, int esz, int v, RelayoutArgs &a) {
+  if (dims.size() < 2) return false;
+  const Dim inner = dims.back();
+  if (inner.src != 1 || inner.dst != 1 || inner.ext % v != 0 || inner.ext * esz >= 512) return false;
+  std::vector<Dim> work(dims.begin(), dims.end() - 1);
+  auto chain = [&](bool by_src, std::vector<Dim> &out) {
+    int64_t run = inner.ext;
+    while (run * esz < std::min<int64_t>(1024, kRelayoutRunCap) && int(out.size()) < kMaxChain) {
+      int pick = -1;
+      for (size_t i = 0; i < work.size(); ++i)
+        if ((by_src ? work[i].src : work[i].dst) == run) pick = int(i);
+      if (pick < 0) break;
+      Dim d = work[pick];
+      const int64_t f = largest_divisor_le(d.ext, std::max<int64_t>(1, kRelayoutRunCap / esz / run));
+      if (f <= 1) break;
+      Dim t = d;
+      t.ext = f;
+      out.push_back(t);
+      if (f < d.ext) {
+        work[pick].ext = d.ext / f;
+        work[pick].src *= f;
+        work[pick].dst *= f;
+      } else {
+        work.erase(work.begin() + pick);
+      }
+      run *= f;
+    }
+    return run;
+  };
+  std::vector<Dim> cs, cd;
+  const int64_t s_run = chain(true, cs);
+  const int64_t d_run = chain(false, cd);
+  if (s_run * esz < 512 || d_run * esz < 512) return false;
+  int64_t ncs = 1, ncd = 1;
+  for (auto &d : cs) ncs *= d.ext;
+  for (auto &d : cd) ncd *= d.ext;
+  const int64_t vecs = inner.ext * ncs * ncd / v;
+  if (vecs % 256 != 0) return false;
+  const int64_t nv = vecs / 256;
+  if (nv != 1 && nv != 2 && nv != 4 && nv != 8 && nv != 16) return false;
+  // LDS: ncd source runs of s_run elements, each padded so that runs lie
+  // inner-bytes apart modulo 256 (destination-order reads of 16 lanes then
+  // cover distinct banks)
+  const int64_t run_b = s_run * esz, in_b = inner.ext * esz;
+  int64_t pad_b = 0;
+  if (in_b < 256)
+    while ((run_b + pad_b) % 256 != in_b % 256) pad_b += 16;
+  const int64_t pitch = (run_b + pad_b) / esz;
+  if (pitch * ncd * esz > 65536) return false;
+  // in-box offsets must fit 32 bits
+  int64_t smax = s_run, dmax = d_run;
+  for (auto &d : cd) smax += (d.ext - 1) * d.src;
+  for (auto &d : cs) dmax += (d.ext - 1) * d.dst;
+  if (smax >= (int64_t(1) << 31) || dmax >= (int64_t(1) << 31)) return false;
+  std::vector<Dim> outer;
+  for (auto &d : work)
+    if (d.ext > 1) outer.push_back(d);
+  std::sort(outer.begin(), outer.end(), [](const Dim &x, const Dim &y) { return x.dst > y.dst; });
+  if (int(outer.size()) > kMaxLdsOuter) return false;
+  int64_t n_tiles = 1;
+  for (auto &d : outer) n_tiles *= d.ext;
+  if (n_tiles >= (int64_t(1) << 32)) return false;
+  a.lds = 1;
+  a.lds_nv = int32_t(nv);
+  a.lds_v = v;
+  a.lds_inner = int32_t(inner.ext);
+  a.lds_pitch = int32_t(pitch);
+  a.lds_R = make_fastdiv(uint32_t(s_run / v));
+  a.lds_Rd = make_fastdiv(uint32_t(d_run / v));
+  a.lds_iv = make_fastdiv(uint32_t(inner.ext / v));
+  a.n_cs = int32_t(cs.size());
+  a.n_cd = int32_t(cd.size());
+  for (int i = 0; i < kMaxChain; ++i) {
+    const bool s_on = i < int(cs.size()), d_on = i < int(cd.size());
+    a.cs_div[i] = make_fastdiv(s_on ? uint32_t(cs[i].ext) : 1u);
+    a.cs_dst[i] = s_on ? cs[i].dst : 0;
+    a.cd_div[i] = make_fastdiv(d_on ? uint32_t(cd[i].ext) : 1u);
+    a.cd_src[i] = d_on ? cd[i].src : 0;
+  }
+  a.lds_bytes = int32_t(pitch * ncd * esz);
+  a.n_tile = int(outer.size());
+  for (size_t i = 0; i < outer.size(); ++i)
+    a.tile[i] = {outer[i].ext, outer[i].src, outer[i].dst, -1, 0, make_fastdiv(uint32_t(outer[i].ext))};
+  for (int i = int(outer.size()); i < kMaxLdsOuter; ++i) a.tile[i] = {1, 0, 0, -1, 0, make_fastdiv(1)};
+  a.n_lane = 0;
+  a.n_tiles = n_tiles;
+  a.lanes = 256;
+  return true;
+}
+
 jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_relation &D, RelayoutArgs &a,
                           int &vec_bytes) {
   memset(&a, 0, sizeof(a));
@@ -342,6 +450,22 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
     if (ok) break;
   }
   vec_bytes = v * esz;
+  a.src = S.buf;
+  a.dst = D.buf;
+  if (kRelayoutLds && n_chk == 0 && v * esz == 16 && plan_relayout_lds(dims, esz, v, a)) {
+    if (ctx->trace) {
+      fprintf(stderr, "[jagg] relayout %s -> %s: lds transpose, %d vectors/thread, %d B LDS, %lld boxes | run %d x %d, runs %u / %u vectors |",
+              S.letters, D.letters, a.lds_nv, a.lds_bytes, (long long)a.n_tiles, a.lds_inner, a.lds_v, a.lds_R.d,
+              a.lds_Rd.d);
+      for (int i = 0; i < a.n_cs; ++i) fprintf(stderr, " S(%u d%lld)", a.cs_div[i].d, (long long)a.cs_dst[i]);
+      for (int i = 0; i < a.n_cd; ++i) fprintf(stderr, " D(%u s%lld)", a.cd_div[i].d, (long long)a.cd_src[i]);
+      for (int i = 0; i < a.n_tile; ++i)
+        fprintf(stderr, " T(%lld s%lld d%lld)", (long long)a.tile[i].ext, (long long)a.tile[i].src,
+                (long long)a.tile[i].dst);
+      fprintf(stderr, "\n");
+    }
+    return JAGG_OK;
+  }
   // lane dims: the vectorised inner dim, then dims that extend contiguity
   std::vector<Dim> lane, rest(dims.begin(), dims.end() - 1);
   int64_t lanes = 1;
@@ -366,7 +490,7 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
   while (lanes < 256 && !rest.empty()) {
     int pick = -1;
     for (size_t i = 0; i < rest.size(); ++i)
-      if (src_run > 0 && rest[i].src == src_run) pick = int(i);
+      if (!JAGG_RELAYOUT_LANES_DST && src_run > 0 && rest[i].src == src_run) pick = int(i);
     if (pick < 0) {
       int64_t best = -1;
       for (size_t i = 0; i < rest.size(); ++i)

@@ -11,6 +11,8 @@ constexpr int kMaxLetters = 8;   // per relation
 constexpr int kMaxIn = 3;        // inputs per spec
 constexpr int kMaxDims = 24;     // relayout dims after splitting (<= 3 per letter)
 constexpr int kMaxChk = 8;       // relayout letters whose range must be checked
+constexpr int kMaxChain = 3;     // dims per run chain of the LDS-transposing relayout
+constexpr int kMaxLdsOuter = 8;  // outer (box) dims of the LDS-transposing relayout
 
 // Unsigned 32-bit division by a run-time invariant d >= 1 through a
 // multiply-high, after Granlund and Montgomery, "Division by Invariant
@@ -75,6 +77,21 @@ struct RelayoutArgs {
   FastDiv irr_div[kMaxChk];    // division by the source block extent
   int64_t irr_K[kMaxChk];      // source tuple stride of the letter (elements)
   int64_t irr_E[kMaxChk];      // source in-block stride of the letter
+  // LDS transpose (lds != 0): the tile dims above are the outer loop; each
+  // workgroup moves one box of lds_nv * 256 vectors of lds_v elements.  The
+  // box is the shared innermost run (lds_inner elements) extended two ways:
+  // by the source chain (dims continuing the source run, to lds_R vectors)
+  // and by the destination chain (dims continuing the destination run, to
+  // lds_Rd vectors).  LDS holds it as source runs of lds_pitch elements.
+  int32_t lds;
+  int32_t lds_nv;
+  int32_t lds_v, lds_inner, lds_pitch;
+  FastDiv lds_R, lds_Rd, lds_iv;  // vectors per source run / destination run / inner run
+  int32_t n_cs, n_cd;             // dims of the source chain / destination chain
+  FastDiv cs_div[kMaxChain], cd_div[kMaxChain];
+  int64_t cs_dst[kMaxChain];      // destination stride of each source-chain dim
+  int64_t cd_src[kMaxChain];      // source stride of each destination-chain dim
+  int32_t lds_bytes;
 };
 
 // vec_bytes: 16, 8, 4 or 2; elem_bytes 2 or 4.

@@ -200,8 +200,134 @@ static hipError_t go_affine(const RelayoutArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// A digit permutation whose shared innermost run is short on one side (the
+// destination's contiguous order walks letters the source strides over, as
+// in a transposition of two letters): each workgroup reads one in-tile box
+// in source order (runs of at least ~1 KB), parks it in LDS, and writes it
+// in destination order (runs of at least ~1 KB).  LDS runs are padded so
+// the destination-order reads of 16 consecutive lanes hit distinct banks.
+// The in-tile offsets are the same for every box, so each thread decodes
+// its NV load and store offsets once.
+template <typename V, int VE, int NV>
+__global__ __launch_bounds__(256) void relayout_lds_kernel(const RelayoutArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lbuf[];
+  constexpr int ESZ = int(sizeof(V)) / VE;  // offsets below count elements
+  const int tid = threadIdx.x;
+  const int64_t vl = a.lds_v, inner = a.lds_inner, pitch = a.lds_pitch;
+  // chain parameters, read once; unused chain slots are identity (divide by
+  // one, stride zero), so the decodes below run without branches
+  FastDiv cdv[kMaxChain], csv[kMaxChain];
+  int64_t cds[kMaxChain], csd[kMaxChain];
+#pragma unroll
+  for (int d = 0; d < kMaxChain; ++d) {
+    cdv[d] = a.cd_div[d];
+    cds[d] = a.cd_src[d];
+    csv[d] = a.cs_div[d];
+    csd[d] = a.cs_dst[d];
+  }
+  const FastDiv fR = a.lds_R, fRd = a.lds_Rd, fiv = a.lds_iv;
+  int32_t ld_src[NV], ld_lds[NV], st_lds[NV], st_dst[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const uint32_t q = uint32_t(k * 256 + tid);
+    // load order: source run `run`, vector `pos` in it; the run's source
+    // offset comes from the destination-chain digits
+    const uint32_t run = fd_div(q, fR), pos = q - run * fR.d;
+    int64_t o = 0;
+    uint32_t r = run;
+#pragma unroll
+    for (int d = 0; d < kMaxChain; ++d) {
+      const uint32_t qq = fd_div(r, cdv[d]);
+      o += int64_t(r - qq * cdv[d].d) * cds[d];
+      r = qq;
+    }
+    ld_src[k] = int32_t(pos * vl + o);
+    ld_lds[k] = int32_t(pos * vl + run * pitch);
+    // store order: destination run `r2`, vector `dpos` in it; the run's
+    // destination offset comes from the source-chain digits
+    const uint32_t r2 = fd_div(q, fRd), dpos = q - r2 * fRd.d;
+    o = 0;
+    r = r2;
+#pragma unroll
+    for (int d = 0; d < kMaxChain; ++d) {
+      const uint32_t qq = fd_div(r, csv[d]);
+      o += int64_t(r - qq * csv[d].d) * csd[d];
+      r = qq;
+    }
+    st_dst[k] = int32_t(dpos * vl + o);
+    const uint32_t dr = fd_div(dpos, fiv), iv = dpos - dr * fiv.d;
+    st_lds[k] = int32_t(iv * vl + r2 * inner + dr * pitch);
+  }
+  // outer dims (tile dims, outermost first)
+  int64_t os[kMaxLdsOuter], od[kMaxLdsOuter];
+  FastDiv ov[kMaxLdsOuter];
+#pragma unroll
+  for (int d = 0; d < kMaxLdsOuter; ++d) {
+    os[d] = a.tile[d].src;
+    od[d] = a.tile[d].dst;
+    ov[d] = a.tile[d].div;
+  }
+  // the planner lists the outer dims first and pads the rest with identity
+  // dims (extent one, stride zero), so the decode runs without branches
+  auto base = [&](uint32_t t, int64_t &bs, int64_t &bd) {
+    uint32_t r = t;
+    bs = 0;
+    bd = 0;
+#pragma unroll
+    for (int d = kMaxLdsOuter - 1; d >= 0; --d) {
+      const uint32_t q = fd_div(r, ov[d]);
+      const int64_t dig = int64_t(r - q * ov[d].d);
+      r = q;
+      bs += dig * os[d];
+      bd += dig * od[d];
+    }
+  };
+  // LDS offsets in vectors (every box offset is a multiple of the vector),
+  // so the LDS accesses are known 16-byte aligned and stay single b128 ops
+  V *lvec = reinterpret_cast<V *>(lbuf);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    ld_lds[k] /= VE;
+    st_lds[k] /= VE;
+  }
+  const char *src = reinterpret_cast<const char *>(a.src);
+  char *dst = reinterpret_cast<char *>(a.dst);
+  const uint32_t nt = uint32_t(a.n_tiles);
+  // one box per pass: its loads go straight into LDS (each box is its own
+  // workgroup where the grid allows, so the hardware overlaps one box's
+  // loads with another's stores; a register prefetch of the next box made
+  // the compiler wait on each load in turn and ran 2.4x slower)
+  for (uint32_t t = blockIdx.x; t < nt; t += gridDim.x) {
+    int64_t bs, bd;
+    base(t, bs, bd);
+    V v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = *reinterpret_cast<const V *>(src + (bs + ld_src[k]) * ESZ);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) lvec[ld_lds[k]] = v[k];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = lvec[st_lds[k]];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) *reinterpret_cast<V *>(dst + (bd + st_dst[k]) * ESZ) = v[k];
+    __syncthreads();
+  }
+}
+
 template <typename V, int VE>
 static hipError_t go(const RelayoutArgs &a, hipStream_t st) {
+  if (a.lds) {
+    const int64_t grid = a.n_tiles < (int64_t(1) << 20) ? a.n_tiles : (int64_t(1) << 20);
+    switch (a.lds_nv) {
+      case 1: hipLaunchKernelGGL((relayout_lds_kernel<V, VE, 1>), dim3(unsigned(grid)), dim3(256), a.lds_bytes, st, a); break;
+      case 2: hipLaunchKernelGGL((relayout_lds_kernel<V, VE, 2>), dim3(unsigned(grid)), dim3(256), a.lds_bytes, st, a); break;
+      case 4: hipLaunchKernelGGL((relayout_lds_kernel<V, VE, 4>), dim3(unsigned(grid)), dim3(256), a.lds_bytes, st, a); break;
+      case 8: hipLaunchKernelGGL((relayout_lds_kernel<V, VE, 8>), dim3(unsigned(grid)), dim3(256), a.lds_bytes, st, a); break;
+      case 16: hipLaunchKernelGGL((relayout_lds_kernel<V, VE, 16>), dim3(unsigned(grid)), dim3(256), a.lds_bytes, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (a.n_chk == 0 && a.n_tiles < (int64_t(1) << 31)) {
     switch (a.n_tile) {
       case 1: return go_affine<V, VE, 1>(a, st);

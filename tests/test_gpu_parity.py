@@ -96,6 +96,26 @@ def test_repartition_config_4d(ctx):
                    seed=w.seed)
 
 
+# Digit permutations whose shared innermost run is short: the LDS-transposing
+# relayout (source-order reads, destination-order writes through LDS).
+LDS_RELAYOUT_CASES = [
+    # the 4-D config: d runs of 64 B in the destination, b and c exchanged
+    ((32, 128, 64, 64), "abcd", dict(a=4, b=8, c=1, d=1), "acbd", dict(a=1, b=1, c=4, d=2), "bf16"),
+    # head-major relayout of a projection output (8 x 2048 tokens, 16 heads of 128)
+    ((8, 2048, 16, 128), "bsqd", dict(b=1, s=16, q=4, d=1), "bqsd", dict(b=1, q=1, s=16, d=1), "bf16"),
+    ((16, 64, 32, 32), "abcd", dict(a=2, b=4, c=1, d=1), "acbd", dict(a=1, b=1, c=2, d=1), "f32"),
+    ((4, 32, 64, 8), "abcd", dict(a=1, b=2, c=1, d=1), "acbd", dict(a=1, b=1, c=2, d=1), "f32"),
+]
+
+
+@pytest.mark.parametrize("shape,src_l,src_b,dst_l,dst_b,dtype", LDS_RELAYOUT_CASES)
+def test_repartition_lds_transpose(trace_ctx, capfd, shape, src_l, src_b, dst_l, dst_b, dtype):
+    check_relayout(trace_ctx, shape, src_l, src_b, dst_l, dst_b, dtype)
+    lines = [ln for ln in capfd.readouterr().err.splitlines() if f"relayout {src_l} -> {dst_l}:" in ln]
+    print("\n".join(lines))
+    assert lines and "lds transpose" in lines[0], "the forward relayout must take the LDS-transposing kernel"
+
+
 # ----------------------------------------------------------------- join lists
 
 JOIN_CASES = [
