@@ -262,9 +262,6 @@ int64_t largest_divisor_le(int64_t n, int64_t cap) {
 #ifndef JAGG_RELAYOUT_LDS
 #define JAGG_RELAYOUT_LDS 1
 #endif
-#ifndef JAGG_RELAYOUT_LANES_DST
-#define JAGG_RELAYOUT_LANES_DST 0
-#endif
 constexpr bool kRelayoutLds = JAGG_RELAYOUT_LDS;
 #ifndef JAGG_RELAYOUT_RUN_CAP
 #define JAGG_RELAYOUT_RUN_CAP 2048
@@ -490,7 +487,7 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
   while (lanes < 256 && !rest.empty()) {
     int pick = -1;
     for (size_t i = 0; i < rest.size(); ++i)
-      if (!JAGG_RELAYOUT_LANES_DST && src_run > 0 && rest[i].src == src_run) pick = int(i);
+      if (src_run > 0 && rest[i].src == src_run) pick = int(i);
     if (pick < 0) {
       int64_t best = -1;
       for (size_t i = 0; i < rest.size(); ++i)
