@@ -109,6 +109,23 @@ def counter_traffic() -> float | None:
     return float(vals["traffic_bytes_per_launch"])
 
 
+def timed_graph(run: ChainRunner, steps: int) -> float:
+    """Mean ms per step when the whole chain is replayed as one recorded
+    graph (the same launches; no per-call host work in between)."""
+    g = run.capture()
+    for _ in range(2):
+        g.launch()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(run.ctx.stream)
+    for _ in range(steps):
+        g.launch()
+    b.record(run.ctx.stream)
+    torch.cuda.synchronize()
+    g.close()
+    return a.elapsed_time(b) / steps
+
+
 def timed_chain(run: ChainRunner, steps: int, warmup: int):
     stream = run.ctx.stream
     n = len(run.calls)
@@ -224,7 +241,10 @@ def main():
               "(the sharding design is described, not built); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    ctx = jagg.Context(0)
+    # a stream of its own (default priority): graph capture cannot record the null stream
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    ctx = jagg.Context(0, stream)
     w = {"llama": lambda: I.llama_block(fused_attention=True), "llama_chain": I.llama_block,
          "attention": lambda: I.attention_chain(fused=True), "attention_chain": I.attention_chain,
          "multi_index": I.multi_index, "matmul": I.matmul_256}[args.workload]()
@@ -233,6 +253,7 @@ def main():
     run = ChainRunner(ctx, w, dense)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     step_ms, per_call, wall = timed_chain(run, args.steps, args.warmup)
+    graph_ms = timed_graph(run, args.steps)
     ms = float(np.mean(step_ms))
     steps = [st for st in w.chain]
     flops = sum(spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0 for st in steps)
@@ -299,7 +320,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": in_dtype, "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": w.name, "extents": w.extents, "step_flops": flops, "wall_s": round(wall, 3)},
-        "roofline": roof, "cpu_baseline": cpu, "repartition": rep, "breakdown": breakdown,
+        "roofline": roof, "cpu_baseline": cpu, "repartition": rep,
+        "graph": {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 3),
+                  "note": "the same chain replayed as one recorded HIP graph (jagg_capture_begin/end)"},
+        "breakdown": breakdown,
     }
     print(json.dumps(out))
 

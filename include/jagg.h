@@ -190,6 +190,31 @@ jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_let
 jagg_status jagg_join_list(jagg_ctx *ctx, const jagg_spec *spec, const int64_t *extents_by_letter,
                            const int32_t *blockings, int32_t *dev_list, int32_t *dev_counts);
 
+/* Graph capture of a call chain.  "Every Kernel Is a Join" (Ding et al.),
+ * Sec. 5.1, makes the executable artifact a graph of GPU kernels run
+ * directly; "Stax (5): Caching and Measurement", Section 11.3, notes that
+ * the host cost of a call grows with the number of kernels launched and
+ * that replaying a recorded graph removes the per-launch term.
+ *
+ * jagg_capture_begin starts recording the context's stream (relaxed mode:
+ * other host threads may allocate meanwhile); every later jagg_einsum /
+ * jagg_repartition on this context is recorded, not run, until
+ * jagg_capture_end, which instantiates the recording into *out.  The
+ * recorded launches keep the device pointers they were given (relations,
+ * workspaces): the caller keeps those buffers alive and unmoved for the
+ * graph's lifetime and may change their contents between launches.
+ * jagg_graph_launch replays the graph on the context's stream
+ * (asynchronously, like every call); jagg_graph_destroy frees it.  The
+ * library records no memset or allocation, so replays are exact repeats of
+ * the recorded launches.  Errors: JAGG_E_INVALID for a NULL handle or an
+ * end without a begin, JAGG_E_DEVICE when HIP refuses the capture (e.g. the
+ * stream is already being captured); a failed capture leaves *out unset. */
+typedef struct jagg_graph jagg_graph;
+jagg_status jagg_capture_begin(jagg_ctx *ctx);
+jagg_status jagg_capture_end(jagg_ctx *ctx, jagg_graph **out);
+jagg_status jagg_graph_launch(jagg_ctx *ctx, const jagg_graph *g);
+jagg_status jagg_graph_destroy(jagg_graph *g);
+
 const char *jagg_status_str(jagg_status s);
 /* Detail of the last error on this context (empty string if none). */
 const char *jagg_last_error(const jagg_ctx *ctx);

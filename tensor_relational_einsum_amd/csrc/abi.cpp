@@ -28,6 +28,12 @@ struct jagg_ctx {
   std::string err;
   bool trace;
   bool debug_sync;
+  bool capturing;  // between jagg_capture_begin and jagg_capture_end
+};
+
+struct jagg_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
 };
 
 struct jagg_relation {
@@ -716,7 +722,7 @@ hipError_t launch_ew(jagg_ctx *ctx, const EwArgs &a, int agg, const char **which
 
 jagg_status after_launch(jagg_ctx *ctx, hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
-  if (ctx->debug_sync) {
+  if (ctx->debug_sync && !ctx->capturing) {
     e = hipStreamSynchronize(ctx->stream);
     if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
   }
@@ -1188,6 +1194,7 @@ jagg_status jagg_ctx_create(int device, void *hip_stream, jagg_ctx **out) {
   c->stream = reinterpret_cast<hipStream_t>(hip_stream);
   c->trace = env_or("JAGG_TRACE")[0] == '1';
   c->debug_sync = env_or("JAGG_DEBUG_SYNC")[0] == '1';
+  c->capturing = false;
   *out = c;
   return JAGG_OK;
 }
@@ -1195,6 +1202,47 @@ jagg_status jagg_ctx_create(int device, void *hip_stream, jagg_ctx **out) {
 jagg_status jagg_ctx_destroy(jagg_ctx *ctx) {
   if (!ctx) return JAGG_E_INVALID;
   delete ctx;
+  return JAGG_OK;
+}
+
+jagg_status jagg_capture_begin(jagg_ctx *ctx) {
+  if (!ctx) return JAGG_E_INVALID;
+  if (ctx->capturing) return fail(ctx, JAGG_E_INVALID, "capture already begun on this context");
+  const hipError_t e = hipStreamBeginCapture(ctx->stream, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "capture begin: %s", hipGetErrorString(e));
+  ctx->capturing = true;
+  return JAGG_OK;
+}
+
+jagg_status jagg_capture_end(jagg_ctx *ctx, jagg_graph **out) {
+  if (!ctx || !out) return JAGG_E_INVALID;
+  if (!ctx->capturing) return fail(ctx, JAGG_E_INVALID, "capture end without a begin");
+  ctx->capturing = false;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(ctx->stream, &g);
+  if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "capture end: %s", hipGetErrorString(e));
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(g);
+    return fail(ctx, JAGG_E_DEVICE, "graph instantiate: %s", hipGetErrorString(e));
+  }
+  *out = new jagg_graph{g, x};
+  return JAGG_OK;
+}
+
+jagg_status jagg_graph_launch(jagg_ctx *ctx, const jagg_graph *g) {
+  if (!ctx || !g) return JAGG_E_INVALID;
+  const hipError_t e = hipGraphLaunch(g->exec, ctx->stream);
+  if (e != hipSuccess) return fail(ctx, JAGG_E_DEVICE, "graph launch: %s", hipGetErrorString(e));
+  return JAGG_OK;
+}
+
+jagg_status jagg_graph_destroy(jagg_graph *g) {
+  if (!g) return JAGG_E_INVALID;
+  hipGraphExecDestroy(g->exec);
+  hipGraphDestroy(g->graph);
+  delete g;
   return JAGG_OK;
 }
 

@@ -458,7 +458,10 @@ static hipError_t launch_tile(const ContractArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// big: 256x256 tiles, 8 wavefronts of 128x64; small: 128x128, 4 of 64x64.
+// big: 256x256 tiles, 8 wavefronts of 128x64; small: 128x128, 4 of 64x64, or
+// 128x64 (4 of 64x32) where 64-wide tiles pad N less than 128-wide ones (e.g.
+// N = 167: three 64-wide tiles keep 87% of the MFMA work useful, two
+// 128-wide ones 65%).
 template <typename T, int OB, bool AK, bool BKC>
 static hipError_t launch_layout(const ContractArgs &a, int va, int vb, bool big, hipStream_t st) {
   constexpr int F = 16 / int(sizeof(T));
@@ -469,9 +472,13 @@ static hipError_t launch_layout(const ContractArgs &a, int va, int vb, bool big,
   }
   if (va == F && vb == F) {
     if (big) return launch_tile<T, OB, AK, BKC, F, F, 256, 256, 2, 4>(a, st);
+    if ((a.N + 63) / 64 * 64 < (a.N + 127) / 128 * 128) return launch_tile<T, OB, AK, BKC, F, F, 128, 64, 2, 2>(a, st);
     return launch_tile<T, OB, AK, BKC, F, F, 128, 128, 2, 2>(a, st);
   }
-  if (va == F && vb == 1) return launch_tile<T, OB, AK, BKC, F, 1, 128, 128, 2, 2>(a, st);
+  if (va == F && vb == 1) {
+    if ((a.N + 63) / 64 * 64 < (a.N + 127) / 128 * 128) return launch_tile<T, OB, AK, BKC, F, 1, 128, 64, 2, 2>(a, st);
+    return launch_tile<T, OB, AK, BKC, F, 1, 128, 128, 2, 2>(a, st);
+  }
   if (va == 1 && vb == F) return launch_tile<T, OB, AK, BKC, 1, F, 128, 128, 2, 2>(a, st);
   if (va == 1 && vb == 1) return launch_tile<T, OB, AK, BKC, 1, 1, 128, 128, 2, 2>(a, st);
   return hipErrorInvalidValue;

@@ -24,7 +24,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "shape mismatch", -3: "bad blocki
 
 EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
            "jagg_relation_destroy", "jagg_repartition", "jagg_einsum_workspace", "jagg_einsum", "jagg_join_shape",
-           "jagg_join_list", "jagg_status_str", "jagg_last_error"]
+           "jagg_join_list", "jagg_capture_begin", "jagg_capture_end", "jagg_graph_launch", "jagg_graph_destroy",
+           "jagg_status_str", "jagg_last_error"]
 
 
 class JaggError(RuntimeError):
@@ -67,6 +68,10 @@ def lib():
                                   ctypes.c_size_t]
         L.jagg_join_shape.argtypes = [ctypes.POINTER(jagg_spec), i64p, i32p, i64p, i64p]
         L.jagg_join_list.argtypes = [vp, ctypes.POINTER(jagg_spec), i64p, i32p, vp, vp]
+        L.jagg_capture_begin.argtypes = [vp]
+        L.jagg_capture_end.argtypes = [vp, ctypes.POINTER(vp)]
+        L.jagg_graph_launch.argtypes = [vp, vp]
+        L.jagg_graph_destroy.argtypes = [vp]
         L.jagg_status_str.argtypes = [ctypes.c_int]
         L.jagg_status_str.restype = ctypes.c_char_p
         L.jagg_last_error.argtypes = [vp]
@@ -174,6 +179,41 @@ class Relation:
                 self.handle = None
         except Exception:
             pass
+
+
+class Graph:
+    """A recorded chain of calls on one context (jagg_capture_begin ..
+    jagg_capture_end); launch() replays it on the context's stream.  The
+    relations and workspaces the recorded calls used must stay alive."""
+
+    def __init__(self, ctx: Context, handle):
+        self.ctx, self.handle = ctx, handle
+
+    def launch(self):
+        self.ctx._check(lib().jagg_graph_launch(self.ctx.handle, self.handle))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().jagg_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def capture(ctx: Context, record) -> Graph:
+    """Records every call `record()` makes on `ctx` into a graph."""
+    ctx._check(lib().jagg_capture_begin(ctx.handle))
+    try:
+        record()
+    finally:
+        h = ctypes.c_void_p()
+        rc = lib().jagg_capture_end(ctx.handle, ctypes.byref(h))
+    ctx._check(rc)
+    return Graph(ctx, h)
 
 
 def repartition(ctx: Context, src: Relation, dst: Relation) -> Relation:

@@ -53,6 +53,11 @@ class ChainRunner:
             else:
                 jagg.repartition(self.ctx, obj[0], obj[1])
 
+    def capture(self) -> jagg.Graph:
+        """The whole chain recorded into one graph (every buffer it uses is
+        already allocated, so replays repeat the same launches)."""
+        return jagg.capture(self.ctx, self.run)
+
     def run_step(self, i: int):
         kind, obj, _ = self.calls[i]
         if kind == "einsum":

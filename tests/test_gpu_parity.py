@@ -194,6 +194,10 @@ CONTRACT_CASES = [
     ("bhst,bhtd->bhsd", dict(b=2, h=3, s=256, t=256, d=128), dict(b=1, h=1, s=2, t=2, d=1), "bf16", "f32"),
     ("bsh,hqd->bsqd", dict(b=2, s=256, h=512, q=4, d=128), dict(b=1, s=2, h=4, q=2, d=1), "bf16", "bf16"),
     ("bsf,fh->bsh", dict(b=2, s=128, f=688, h=256), dict(b=1, s=1, f=8, h=2), "bf16", "f32"),
+    # N = 167 per block: 128x64 tiles (three 64-wide column tiles, the last ragged)
+    ("ij,jk->ik", dict(i=300, j=96, k=334), dict(i=2, j=3, k=2), "f32", "f32"),
+    ("ij,kj->ik", dict(i=300, j=96, k=334), dict(i=2, j=3, k=2), "bf16", "bf16"),
+    ("abcd,cde->abe", dict(a=20, b=43, c=16, d=32, e=334), dict(a=1, b=1, c=1, d=2, e=2), "f32", "f32"),
 ]
 
 
