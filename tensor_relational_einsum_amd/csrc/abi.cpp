@@ -1074,6 +1074,10 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
   auto vec_ok = [&](bool kc, int64_t rows, int64_t sRow, int64_t sK, int64_t sBat, int64_t be) {
     const int64_t contig = kc ? Gk.ext : rows;
     const int64_t other = kc ? sRow : sK;
+    // fp32 operand contiguous along M or N: vectors may straddle the row end
+    // (the extra lanes only feed output rows/columns that are never stored)
+    // and start at any element (4-byte aligned)
+    if (!kc && !dtype) return true;
     return contig % F == 0 && other % F == 0 && sBat % F == 0 && be % F == 0;
   };
   va = vec_ok(a_kc, Gm.ext, sAm, sAk, sAb, RA.be) ? F : 1;
