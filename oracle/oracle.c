@@ -25,6 +25,12 @@
  *   - blocking of an index of extent n into k blocks: block extent
  *     e = ceil(n/k); block kappa covers [kappa*e, min((kappa+1)*e, n)); a
  *     blocking whose last block would be empty is rejected.
+ *   - interval blocking (the `_iv` entry points): the caller lists the
+ *     bounds 0 = b_0 < b_1 < ... < b_k = n of one index (Sec. 3.3 lets an
+ *     index be split only at legal positions, e.g. the ends of packed
+ *     sequences); block kappa covers [b_kappa, b_kappa+1), and every block is
+ *     padded to the longest interval.  bnd26 holds 26 rows of ORIV+1 bounds,
+ *     one per letter; a row whose first entry is negative means uniform.
  *   - storage of a relation: tuples in row-major order of the block
  *     coordinates, in the relation's own letter order; each block dense and
  *     row-major over the padded extents e; padding holds +0.
@@ -226,17 +232,29 @@ int oracle_dense(const char *spec, int g, int agg, double alpha, double beta, do
 /* Relation geometry (Def. 3.1 intervals, padded blocks).                    */
 /* ------------------------------------------------------------------------ */
 
+/* Interval blockings (Sec. 3.2: a shardable index is decomposed into
+ * intervals; Ex. 3.10: the intervals may sit at data-dependent positions,
+ * such as the ends of packed sequences).  A letter blocked by explicit
+ * bounds 0 = b_0 < b_1 < ... < b_k = n has block kappa = [b_kappa,
+ * b_kappa+1); every block is stored padded to the longest one.  Bounds are
+ * passed as 26 rows of ORIV + 1 entries, row L for letter 'a' + L; a row
+ * whose first entry is negative leaves that letter uniformly blocked. */
+#define ORIV 64
+
 typedef struct {
   int r;
   char letters[27];
   int64_t n[26];      /* extents, by position in `letters` */
   int64_t k[26];      /* block counts */
   int64_t e[26];      /* padded block extents */
+  int iv[26];         /* 1: blocked by the explicit bounds below */
+  int64_t bnd[26][ORIV + 1];
   int64_t n_tuples;
   int64_t block_elems;
 } orel;
 
-static int make_rel(const char *letters, const int64_t *ext26, const int32_t *nblk26, orel *R) {
+static int make_rel_iv(const char *letters, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                       orel *R) {
   memset(R, 0, sizeof(*R));
   R->r = (int)strlen(letters);
   if (R->r > 26) return OR_BAD_SPEC;
@@ -248,8 +266,21 @@ static int make_rel(const char *letters, const int64_t *ext26, const int32_t *nb
     R->n[a] = ext26[L];
     R->k[a] = nblk26[L];
     if (R->n[a] < 1 || R->k[a] < 1 || R->k[a] > R->n[a]) return OR_BAD_BLOCKING;
-    R->e[a] = (R->n[a] + R->k[a] - 1) / R->k[a];
-    if ((R->k[a] - 1) * R->e[a] >= R->n[a]) return OR_BAD_BLOCKING; /* empty last block */
+    const int64_t *b = bnd26 ? bnd26 + (size_t)L * (ORIV + 1) : NULL;
+    if (b && b[0] >= 0) {
+      if (R->k[a] > ORIV || b[0] != 0 || b[R->k[a]] != R->n[a]) return OR_BAD_BLOCKING;
+      R->iv[a] = 1;
+      R->e[a] = 0;
+      for (int64_t q = 0; q < R->k[a]; ++q) {
+        if (b[q + 1] <= b[q]) return OR_BAD_BLOCKING; /* empty or reversed interval */
+        R->bnd[a][q] = b[q];
+        if (b[q + 1] - b[q] > R->e[a]) R->e[a] = b[q + 1] - b[q];
+      }
+      R->bnd[a][R->k[a]] = R->n[a];
+    } else {
+      R->e[a] = (R->n[a] + R->k[a] - 1) / R->k[a];
+      if ((R->k[a] - 1) * R->e[a] >= R->n[a]) return OR_BAD_BLOCKING; /* empty last block */
+    }
     R->n_tuples *= R->k[a];
     R->block_elems *= R->e[a];
   }
@@ -261,32 +292,46 @@ static void tuple_coords(const orel *R, int64_t t, int64_t *kappa) {
   for (int a = R->r - 1; a >= 0; --a) { kappa[a] = t % R->k[a]; t /= R->k[a]; }
 }
 
-static int64_t lo_of(const orel *R, int a, int64_t kappa) { return kappa * R->e[a]; }
+/* the interval [lo, hi) of block kappa of the letter at position a */
+static int64_t lo_of(const orel *R, int a, int64_t kappa) { return R->iv[a] ? R->bnd[a][kappa] : kappa * R->e[a]; }
 static int64_t hi_of(const orel *R, int a, int64_t kappa) {
+  if (R->iv[a]) return R->bnd[a][kappa + 1];
   int64_t h = (kappa + 1) * R->e[a];
   return h < R->n[a] ? h : R->n[a];
+}
+
+/* the block of the letter at position a that holds global coordinate x */
+static int64_t block_of(const orel *R, int a, int64_t x) {
+  if (!R->iv[a]) return x / R->e[a];
+  int64_t q = 0;
+  while (R->bnd[a][q + 1] <= x) ++q;
+  return q;
 }
 
 /* value at global coordinates x (by letter) inside tuple `tid` (block coords kap) */
 static double rel_at(const orel *R, const double *buf, int64_t tid, const int64_t *kap, const int64_t *x) {
   int64_t off = 0;
-  for (int a = 0; a < R->r; ++a) off = off * R->e[a] + (x[R->letters[a] - 'a'] - kap[a] * R->e[a]);
+  for (int a = 0; a < R->r; ++a) off = off * R->e[a] + (x[R->letters[a] - 'a'] - lo_of(R, a, kap[a]));
   return buf[tid * R->block_elems + off];
 }
 
-int oracle_relation_elems(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *elems) {
+int oracle_relation_elems_iv(const char *letters, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                             int64_t *elems) {
   orel R;
-  int rc = make_rel(letters, ext26, nblk26, &R);
+  int rc = make_rel_iv(letters, ext26, nblk26, bnd26, &R);
   if (rc) return rc;
   *elems = R.n_tuples * R.block_elems;
   return OR_OK;
 }
+int oracle_relation_elems(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *elems) {
+  return oracle_relation_elems_iv(letters, ext26, nblk26, NULL, elems);
+}
 
 /* dense (row-major) -> relation storage, padding = +0; elements of `esz` bytes */
-int oracle_to_relation(const void *dense, int esz, const char *letters, const int64_t *ext26,
-                       const int32_t *nblk26, void *rel) {
+int oracle_to_relation_iv(const void *dense, int esz, const char *letters, const int64_t *ext26,
+                          const int32_t *nblk26, const int64_t *bnd26, void *rel) {
   orel R;
-  int rc = make_rel(letters, ext26, nblk26, &R);
+  int rc = make_rel_iv(letters, ext26, nblk26, bnd26, &R);
   if (rc) return rc;
   memset(rel, 0, (size_t)(R.n_tuples * R.block_elems) * (size_t)esz);
   int64_t dstride[26], s = 1;
@@ -297,9 +342,9 @@ int oracle_to_relation(const void *dense, int esz, const char *letters, const in
     for (int64_t w = 0; w < R.block_elems; ++w) {
       int64_t rem = w, doff = 0, valid = 1;
       for (int a = R.r - 1; a >= 0; --a) {
-        int64_t x = kappa[a] * R.e[a] + rem % R.e[a];
+        int64_t x = lo_of(&R, a, kappa[a]) + rem % R.e[a];
         rem /= R.e[a];
-        if (x >= R.n[a]) { valid = 0; break; }
+        if (x >= hi_of(&R, a, kappa[a])) { valid = 0; break; }
         doff += x * dstride[a];
       }
       if (valid)
@@ -310,10 +355,15 @@ int oracle_to_relation(const void *dense, int esz, const char *letters, const in
 }
 
 /* relation storage -> dense (row-major); padding is dropped */
-int oracle_from_relation(const void *rel, int esz, const char *letters, const int64_t *ext26,
-                         const int32_t *nblk26, void *dense) {
+int oracle_to_relation(const void *dense, int esz, const char *letters, const int64_t *ext26,
+                       const int32_t *nblk26, void *rel) {
+  return oracle_to_relation_iv(dense, esz, letters, ext26, nblk26, NULL, rel);
+}
+/* relation storage -> dense (row-major); padding is skipped */
+int oracle_from_relation_iv(const void *rel, int esz, const char *letters, const int64_t *ext26,
+                            const int32_t *nblk26, const int64_t *bnd26, void *dense) {
   orel R;
-  int rc = make_rel(letters, ext26, nblk26, &R);
+  int rc = make_rel_iv(letters, ext26, nblk26, bnd26, &R);
   if (rc) return rc;
   int64_t dstride[26], s = 1;
   for (int a = R.r - 1; a >= 0; --a) { dstride[a] = s; s *= R.n[a]; }
@@ -323,9 +373,9 @@ int oracle_from_relation(const void *rel, int esz, const char *letters, const in
     for (int64_t w = 0; w < R.block_elems; ++w) {
       int64_t rem = w, doff = 0, valid = 1;
       for (int a = R.r - 1; a >= 0; --a) {
-        int64_t x = kappa[a] * R.e[a] + rem % R.e[a];
+        int64_t x = lo_of(&R, a, kappa[a]) + rem % R.e[a];
         rem /= R.e[a];
-        if (x >= R.n[a]) { valid = 0; break; }
+        if (x >= hi_of(&R, a, kappa[a])) { valid = 0; break; }
         doff += x * dstride[a];
       }
       if (valid)
@@ -334,12 +384,16 @@ int oracle_from_relation(const void *rel, int esz, const char *letters, const in
   }
   return OR_OK;
 }
+int oracle_from_relation(const void *rel, int esz, const char *letters, const int64_t *ext26,
+                         const int32_t *nblk26, void *dense) {
+  return oracle_from_relation_iv(rel, esz, letters, ext26, nblk26, NULL, dense);
+}
 
 /* Repartition: densify the source, then re-block into the destination's
  * letter order and blocking.  Works on raw element bytes, so it is exact. */
-int oracle_repartition(const void *src, int esz, const char *src_letters, const int32_t *src_nblk26,
-                       void *dst, const char *dst_letters, const int32_t *dst_nblk26,
-                       const int64_t *ext26) {
+int oracle_repartition_iv(const void *src, int esz, const char *src_letters, const int32_t *src_nblk26,
+                          const int64_t *src_bnd26, void *dst, const char *dst_letters, const int32_t *dst_nblk26,
+                          const int64_t *dst_bnd26, const int64_t *ext26) {
   if (strlen(src_letters) != strlen(dst_letters)) return OR_BAD_SHAPE;
   for (const char *c = src_letters; *c; ++c)
     if (!strchr(dst_letters, *c)) return OR_BAD_SHAPE;
@@ -347,7 +401,7 @@ int oracle_repartition(const void *src, int esz, const char *src_letters, const 
   for (const char *c = src_letters; *c; ++c) n *= ext26[*c - 'a'];
   char *dense_src = malloc((size_t)n * esz), *dense_dst = malloc((size_t)n * esz);
   if (!dense_src || !dense_dst) { free(dense_src); free(dense_dst); return OR_BAD_SHAPE; }
-  int rc = oracle_from_relation(src, esz, src_letters, ext26, src_nblk26, dense_src);
+  int rc = oracle_from_relation_iv(src, esz, src_letters, ext26, src_nblk26, src_bnd26, dense_src);
   if (!rc) {
     /* permute the dense tensor from the source letter order to the destination's */
     int r = (int)strlen(src_letters);
@@ -362,10 +416,15 @@ int oracle_repartition(const void *src, int esz, const char *src_letters, const 
       }
       memcpy(dense_dst + (size_t)i * esz, dense_src + (size_t)soff * esz, esz);
     }
-    rc = oracle_to_relation(dense_dst, esz, dst_letters, ext26, dst_nblk26, dst);
+    rc = oracle_to_relation_iv(dense_dst, esz, dst_letters, ext26, dst_nblk26, dst_bnd26, dst);
   }
   free(dense_src); free(dense_dst);
   return rc;
+}
+int oracle_repartition(const void *src, int esz, const char *src_letters, const int32_t *src_nblk26,
+                       void *dst, const char *dst_letters, const int32_t *dst_nblk26,
+                       const int64_t *ext26) {
+  return oracle_repartition_iv(src, esz, src_letters, src_nblk26, NULL, dst, dst_letters, dst_nblk26, NULL, ext26);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -389,8 +448,8 @@ static int cmp_combo(const void *a, const void *b) {
  * keeping each combination whose key intervals agree on every letter the
  * inputs share (and, with causal letters, that holds some t <= s).
  * Returns a malloc'd array of combos sorted in canonical order. */
-static int join(const ospec *p, const orel *in, const orel *out, const int64_t *ext26, const int32_t *nblk26,
-                int causal_s, int causal_t, combo **res, int64_t *n_res) {
+static int join(const ospec *p, const orel *in, const orel *out, int causal_s, int causal_t, combo **res,
+                int64_t *n_res) {
   int64_t total = 1;
   for (int j = 0; j < p->n_in; ++j) total *= in[j].n_tuples;
   combo *list = malloc(sizeof(combo) * (size_t)(total ? total : 1));
@@ -420,13 +479,19 @@ static int join(const ospec *p, const orel *in, const orel *out, const int64_t *
     int64_t out_id = 0;
     for (int a = 0; a < out->r; ++a) {
       int L = out->letters[a] - 'a';
-      out_id = out_id * out->k[a] + lo[L] / out->e[a];
+      out_id = out_id * out->k[a] + block_of(out, a, lo[L]);
     }
+    /* reduced letters: block coordinates as the first input holding each one sees them */
     int64_t red_key = 0;
     for (int a = 0; a < p->n_reduced; ++a) {
       int L = p->reduced[a] - 'a';
-      int64_t e = (ext26[L] + nblk26[L] - 1) / nblk26[L];
-      red_key = red_key * nblk26[L] + lo[L] / e;
+      for (int j = 0; j < p->n_in; ++j) {
+        const char *q = strchr(in[j].letters, 'a' + L);
+        if (!q) continue;
+        int ia = (int)(q - in[j].letters);
+        red_key = red_key * in[j].k[ia] + block_of(&in[j], ia, lo[L]);
+        break;
+      }
     }
     list[n].out_id = out_id;
     list[n].red_key = red_key;
@@ -439,26 +504,27 @@ static int join(const ospec *p, const orel *in, const orel *out, const int64_t *
   return OR_OK;
 }
 
-static int build_rels(const ospec *p, const int64_t *ext26, const int32_t *nblk26, orel *in, orel *out) {
+static int build_rels(const ospec *p, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26, orel *in,
+                      orel *out) {
   int rc;
   for (int j = 0; j < p->n_in; ++j)
-    if ((rc = make_rel(p->in[j], ext26, nblk26, &in[j]))) return rc;
-  return make_rel(p->out, ext26, nblk26, out);
+    if ((rc = make_rel_iv(p->in[j], ext26, nblk26, bnd26, &in[j]))) return rc;
+  return make_rel_iv(p->out, ext26, nblk26, bnd26, out);
 }
 
 /* Join list only: entries [out_id, in_id_0, ..., in_id_{n-1}] (int64), in
  * canonical order.  Pass list == NULL to get the count. */
-int oracle_join_list(const char *spec, const int64_t *ext26, const int32_t *nblk26, int causal_s,
-                     int causal_t, int64_t *list, int64_t cap, int64_t *n_entries) {
+int oracle_join_list_iv(const char *spec, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                        int causal_s, int causal_t, int64_t *list, int64_t cap, int64_t *n_entries) {
   ospec p;
   int rc = parse_spec(spec, &p);
   if (rc) return rc;
   if ((causal_s >= 0) != (causal_t >= 0)) return OR_BAD_SPEC;
   orel in[OR_MAX_IN], out;
-  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, ext26, nblk26, causal_s, causal_t, &c, &n))) return rc;
+  if ((rc = join(&p, in, &out, causal_s, causal_t, &c, &n))) return rc;
   *n_entries = n;
   if (list) {
     if (cap < n) { free(c); return OR_BAD_SHAPE; }
@@ -470,23 +536,27 @@ int oracle_join_list(const char *spec, const int64_t *ext26, const int32_t *nblk
   free(c);
   return OR_OK;
 }
+int oracle_join_list(const char *spec, const int64_t *ext26, const int32_t *nblk26, int causal_s,
+                     int causal_t, int64_t *list, int64_t cap, int64_t *n_entries) {
+  return oracle_join_list_iv(spec, ext26, nblk26, NULL, causal_s, causal_t, list, cap, n_entries);
+}
 
 /* Relational evaluation.  Inputs are relation buffers (double values) in the
  * operands' letter orders under `nblk26`; the output relation buffer gets the
  * aggregated blocks, +0 in its padding, unrounded.  `present` (optional, one
  * byte per output tuple) marks the output keys that the join produced. */
-int oracle_relational(const char *spec, int g, int agg, double alpha, double beta, double eps,
-                      int causal_s, int causal_t, const int64_t *ext26, const int32_t *nblk26,
-                      const double *const *in_rel, double *out_rel, uint8_t *present) {
+int oracle_relational_iv(const char *spec, int g, int agg, double alpha, double beta, double eps,
+                         int causal_s, int causal_t, const int64_t *ext26, const int32_t *nblk26,
+                         const int64_t *bnd26, const double *const *in_rel, double *out_rel, uint8_t *present) {
   ospec p;
   int rc = parse_spec(spec, &p);
   if (rc) return rc;
   if ((rc = check_common(&p, g, agg, causal_s, causal_t))) return rc;
   orel in[OR_MAX_IN], out;
-  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, ext26, nblk26, causal_s, causal_t, &c, &n))) return rc;
+  if ((rc = join(&p, in, &out, causal_s, causal_t, &c, &n))) return rc;
 
   memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
   if (present) memset(present, 0, (size_t)out.n_tuples);
@@ -524,7 +594,7 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
         }
         /* position inside the padded output block */
         int64_t w = 0;
-        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - kout[a] * out.e[a]);
+        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - lo_of(&out, a, kout[a]));
         double acc = agg == AGG_MAX ? -INFINITY : 0.0;
         int any = 0;
         for (int64_t r = 0; r < red_box; ++r) {
@@ -541,7 +611,7 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
             tuple_coords(&in[j], c[ci].in_id[j], kappa);
             for (int a = 0; a < in[j].r; ++a) {
               int L = in[j].letters[a] - 'a';
-              off = off * in[j].e[a] + (x[L] - kappa[a] * in[j].e[a]);
+              off = off * in[j].e[a] + (x[L] - lo_of(&in[j], a, kappa[a]));
             }
             v[j] = in_rel[j][c[ci].in_id[j] * in[j].block_elems + off];
           }
@@ -578,6 +648,12 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
   }
   free(agg_blk); free(touched); free(c);
   return OR_OK;
+}
+int oracle_relational(const char *spec, int g, int agg, double alpha, double beta, double eps,
+                      int causal_s, int causal_t, const int64_t *ext26, const int32_t *nblk26,
+                      const double *const *in_rel, double *out_rel, uint8_t *present) {
+  return oracle_relational_iv(spec, g, agg, alpha, beta, eps, causal_s, causal_t, ext26, nblk26, NULL, in_rel,
+                              out_rel, present);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -718,9 +794,9 @@ void oracle_softmax_merge(double m1, double l1, double a1, double m2, double l2,
  * of equal output key in canonical order (step 2), then write a / l into the
  * output relation (step 3).  Inputs are relation buffers of doubles; the D
  * letters must be one block each (a triple needs whole scores). */
-int oracle_attention_relational(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
-                                const int32_t *nblk26, const double *const *in_rel, double *out_rel,
-                                uint8_t *present) {
+int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s, int causal_t,
+                                   const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                                   const double *const *in_rel, double *out_rel, uint8_t *present) {
   ospec p;
   oroles r;
   int rc = parse_spec(spec, &p);
@@ -731,10 +807,10 @@ int oracle_attention_relational(const char *spec, double alpha, int causal_s, in
   for (int a = 0; a < r.nd; ++a)
     if (nblk26[r.d[a] - 'a'] != 1) return OR_UNSUPPORTED;
   orel in[OR_MAX_IN], out;
-  if ((rc = build_rels(&p, ext26, nblk26, in, &out))) return rc;
+  if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, ext26, nblk26, causal ? r.s : -1, causal ? r.t : -1, &c, &n))) return rc;
+  if ((rc = join(&p, in, &out, causal ? r.s : -1, causal ? r.t : -1, &c, &n))) return rc;
   memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
   if (present) memset(present, 0, (size_t)out.n_tuples);
   double *tm = malloc(sizeof(double) * (size_t)out.block_elems * 3);
@@ -766,7 +842,7 @@ int oracle_attention_relational(const char *spec, double alpha, int causal_s, in
           rem /= hi[L] - lo[L];
         }
         int64_t w = 0;
-        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - kout[a] * out.e[a]);
+        for (int a = 0; a < out.r; ++a) w = w * out.e[a] + (x[out.letters[a] - 'a'] - lo_of(&out, a, kout[a]));
         /* f: the triple of this tuple's key range (two passes: max, then sums) */
         double m = -INFINITY, l = 0.0, acc = 0.0;
         for (int pass = 0; pass < 2; ++pass) {
@@ -818,6 +894,12 @@ int oracle_attention_relational(const char *spec, double alpha, int causal_s, in
   free(c);
   return OR_OK;
 }
+int oracle_attention_relational(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
+                                const int32_t *nblk26, const double *const *in_rel, double *out_rel,
+                                uint8_t *present) {
+  return oracle_attention_relational_iv(spec, alpha, causal_s, causal_t, ext26, nblk26, NULL, in_rel, out_rel,
+                                        present);
+}
 
 /* ------------------------------------------------------------------------ */
 /* Rounding to the stored type, once, round-to-nearest-even.                 */
@@ -843,10 +925,14 @@ void oracle_round(double *x, int64_t n, int dtype) {
 }
 
 /* padded block extents of a relation, in its letter order */
-int oracle_block_shape(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *e) {
+int oracle_block_shape_iv(const char *letters, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                          int64_t *e) {
   orel R;
-  int rc = make_rel(letters, ext26, nblk26, &R);
+  int rc = make_rel_iv(letters, ext26, nblk26, bnd26, &R);
   if (rc) return rc;
   for (int a = 0; a < R.r; ++a) e[a] = R.e[a];
   return OR_OK;
+}
+int oracle_block_shape(const char *letters, const int64_t *ext26, const int32_t *nblk26, int64_t *e) {
+  return oracle_block_shape_iv(letters, ext26, nblk26, NULL, e);
 }

@@ -55,11 +55,11 @@ def _load():
         lib.oracle_dense.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                      ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                      i64p, dpp, i64p, ctypes.c_int64, ctypes.c_void_p]
-        lib.oracle_relational.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-                                          ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int,
-                                          i64p, i32p, dpp, ctypes.c_void_p, ctypes.c_void_p]
-        lib.oracle_join_list.argtypes = [ctypes.c_char_p, i64p, i32p, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_void_p, ctypes.c_int64, i64p]
+        lib.oracle_relational_iv.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                             ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                             i64p, i32p, i64p, dpp, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_join_list_iv.argtypes = [ctypes.c_char_p, i64p, i32p, i64p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_int64, i64p]
         lib.oracle_relation_elems.argtypes = [ctypes.c_char_p, i64p, i32p, i64p]
         lib.oracle_to_relation.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i64p, i32p,
                                            ctypes.c_void_p]
@@ -68,11 +68,20 @@ def _load():
         lib.oracle_repartition.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i32p,
                                            ctypes.c_void_p, ctypes.c_char_p, i32p, i64p]
         lib.oracle_block_shape.argtypes = [ctypes.c_char_p, i64p, i32p, i64p]
+        lib.oracle_relation_elems_iv.argtypes = [ctypes.c_char_p, i64p, i32p, i64p, i64p]
+        lib.oracle_to_relation_iv.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i64p, i32p, i64p,
+                                              ctypes.c_void_p]
+        lib.oracle_from_relation_iv.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i64p, i32p, i64p,
+                                                ctypes.c_void_p]
+        lib.oracle_repartition_iv.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p, i32p, i64p,
+                                              ctypes.c_void_p, ctypes.c_char_p, i32p, i64p, i64p]
+        lib.oracle_block_shape_iv.argtypes = [ctypes.c_char_p, i64p, i32p, i64p, i64p]
         lib.oracle_attention_dense.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int, i64p,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i64p,
                                                ctypes.c_int64, ctypes.c_void_p]
-        lib.oracle_attention_relational.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int,
-                                                    i64p, i32p, dpp, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_attention_relational_iv.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int,
+                                                       ctypes.c_int, i64p, i32p, i64p, dpp, ctypes.c_void_p,
+                                                       ctypes.c_void_p]
         lib.oracle_softmax_merge.argtypes = [ctypes.c_double] * 6 + [ctypes.c_void_p]
         lib.oracle_softmax_merge.restype = None
         lib.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
@@ -88,11 +97,31 @@ def _ext26(extents: dict) -> np.ndarray:
     return a
 
 
+MAX_INTERVALS = 64  # ORIV in oracle.c
+
+
 def _nblk26(blockings: dict) -> np.ndarray:
+    """Block count per letter.  A blocking value is a count (uniform blocks)
+    or a list of interval bounds [0, b_1, ..., n] (k = len - 1 blocks)."""
     a = np.ones(26, dtype=np.int32)
     for k, v in blockings.items():
-        a[ord(k) - 97] = int(v)
+        a[ord(k) - 97] = len(v) - 1 if isinstance(v, (list, tuple)) else int(v)
     return a
+
+
+def _bnd26(blockings: dict) -> np.ndarray:
+    """26 rows of MAX_INTERVALS+1 bounds; a row starting with -1 is uniform."""
+    a = np.full((26, MAX_INTERVALS + 1), -1, dtype=np.int64)
+    for k, v in blockings.items():
+        if isinstance(v, (list, tuple)):
+            if len(v) - 1 > MAX_INTERVALS:
+                raise OracleError(f"letter {k}: more than {MAX_INTERVALS} intervals")
+            a[ord(k) - 97, :len(v)] = [int(b) for b in v]
+    return a
+
+
+def _has_iv(blockings: dict) -> bool:
+    return any(isinstance(v, (list, tuple)) for v in blockings.values())
 
 
 def _i64p(a):
@@ -158,8 +187,9 @@ def dense(spec, inputs, extents, g="mul", agg="sum", alpha=1.0, beta=0.0, eps=0.
 def relation_elems(letters, extents, blockings) -> int:
     lib = _load()
     n = np.zeros(1, dtype=np.int64)
-    ext, nb = _ext26(extents), _nblk26(blockings)
-    _check(lib.oracle_relation_elems(letters.encode(), _i64p(ext), _i32p(nb), _i64p(n)), "relation_elems")
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
+    _check(lib.oracle_relation_elems_iv(letters.encode(), _i64p(ext), _i32p(nb), _i64p(bd), _i64p(n)),
+           "relation_elems")
     return int(n[0])
 
 
@@ -167,8 +197,8 @@ def block_shape(letters, extents, blockings):
     """Padded block extents, in the relation's letter order."""
     lib = _load()
     e = np.zeros(max(1, len(letters)), dtype=np.int64)
-    ext, nb = _ext26(extents), _nblk26(blockings)
-    _check(lib.oracle_block_shape(letters.encode(), _i64p(ext), _i32p(nb), _i64p(e)), "block_shape")
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
+    _check(lib.oracle_block_shape_iv(letters.encode(), _i64p(ext), _i32p(nb), _i64p(bd), _i64p(e)), "block_shape")
     return tuple(int(v) for v in e[:len(letters)])
 
 
@@ -178,9 +208,9 @@ def to_relation(x, letters, extents, blockings):
     x = np.ascontiguousarray(x)
     n = relation_elems(letters, extents, blockings)
     out = np.zeros(n, dtype=x.dtype)
-    ext, nb = _ext26(extents), _nblk26(blockings)
-    _check(lib.oracle_to_relation(x.ctypes.data, x.dtype.itemsize, letters.encode(), _i64p(ext), _i32p(nb),
-                                  out.ctypes.data), "to_relation")
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
+    _check(lib.oracle_to_relation_iv(x.ctypes.data, x.dtype.itemsize, letters.encode(), _i64p(ext), _i32p(nb),
+                                     _i64p(bd), out.ctypes.data), "to_relation")
     return out
 
 
@@ -190,9 +220,9 @@ def from_relation(rel, letters, extents, blockings):
     rel = np.ascontiguousarray(rel)
     shape = tuple(int(extents[c]) for c in letters)
     out = np.zeros(shape, dtype=rel.dtype)
-    ext, nb = _ext26(extents), _nblk26(blockings)
-    _check(lib.oracle_from_relation(rel.ctypes.data, rel.dtype.itemsize, letters.encode(), _i64p(ext),
-                                    _i32p(nb), out.ctypes.data), "from_relation")
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
+    _check(lib.oracle_from_relation_iv(rel.ctypes.data, rel.dtype.itemsize, letters.encode(), _i64p(ext),
+                                       _i32p(nb), _i64p(bd), out.ctypes.data), "from_relation")
     return out
 
 
@@ -204,9 +234,10 @@ def repartition(src, src_letters, src_blockings, dst_letters, dst_blockings, ext
     dst = np.zeros(n, dtype=src.dtype)
     ext = _ext26(extents)
     sb, db = _nblk26(src_blockings), _nblk26(dst_blockings)
-    _check(lib.oracle_repartition(src.ctypes.data, src.dtype.itemsize, src_letters.encode(), _i32p(sb),
-                                  dst.ctypes.data, dst_letters.encode(), _i32p(db), _i64p(ext)),
-           "repartition")
+    sv, dv = _bnd26(src_blockings), _bnd26(dst_blockings)
+    _check(lib.oracle_repartition_iv(src.ctypes.data, src.dtype.itemsize, src_letters.encode(), _i32p(sb),
+                                     _i64p(sv), dst.ctypes.data, dst_letters.encode(), _i32p(db), _i64p(dv),
+                                     _i64p(ext)), "repartition")
     return dst
 
 
@@ -214,13 +245,14 @@ def join_list(spec, extents, blockings, causal=None):
     """Canonical join list: int64 array [n_entries, 1 + n_in] of [out_id, in_ids...]."""
     lib = _load()
     ins, _ = _parse(spec)
-    ext, nb = _ext26(extents), _nblk26(blockings)
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
     cs, ct = _causal(causal)
     n = np.zeros(1, dtype=np.int64)
-    _check(lib.oracle_join_list(spec.encode(), _i64p(ext), _i32p(nb), cs, ct, None, 0, _i64p(n)), "join_list")
+    _check(lib.oracle_join_list_iv(spec.encode(), _i64p(ext), _i32p(nb), _i64p(bd), cs, ct, None, 0, _i64p(n)),
+           "join_list")
     lst = np.zeros((int(n[0]), 1 + len(ins)), dtype=np.int64)
-    _check(lib.oracle_join_list(spec.encode(), _i64p(ext), _i32p(nb), cs, ct, lst.ctypes.data, int(n[0]),
-                                _i64p(n)), "join_list")
+    _check(lib.oracle_join_list_iv(spec.encode(), _i64p(ext), _i32p(nb), _i64p(bd), cs, ct, lst.ctypes.data,
+                                   int(n[0]), _i64p(n)), "join_list")
     return lst
 
 
@@ -241,12 +273,12 @@ def relational(spec, rel_inputs, extents, blockings, g="mul", agg="sum", alpha=1
     out = np.zeros(n_out, dtype=np.float64)
     n_tuples = 1
     for c in out_letters:
-        n_tuples *= int(blockings.get(c, 1))
+        n_tuples *= int(_nblk26(blockings)[ord(c) - 97])
     present = np.zeros(n_tuples, dtype=np.uint8)
-    ext, nb = _ext26(extents), _nblk26(blockings)
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
     cs, ct = _causal(causal)
-    rc = lib.oracle_relational(spec.encode(), G_CODES[g], AGG_CODES[agg], alpha, beta, eps, cs, ct,
-                               _i64p(ext), _i32p(nb), ptrs, out.ctypes.data, present.ctypes.data)
+    rc = lib.oracle_relational_iv(spec.encode(), G_CODES[g], AGG_CODES[agg], alpha, beta, eps, cs, ct,
+                                  _i64p(ext), _i32p(nb), _i64p(bd), ptrs, out.ctypes.data, present.ctypes.data)
     _check(rc, "oracle_relational")
     return out, present
 
@@ -294,12 +326,12 @@ def attention_relational(spec, rel_inputs, extents, blockings, alpha=1.0, causal
     out = np.zeros(relation_elems(out_letters, extents, blockings), dtype=np.float64)
     n_tuples = 1
     for c in out_letters:
-        n_tuples *= int(blockings.get(c, 1))
+        n_tuples *= int(_nblk26(blockings)[ord(c) - 97])
     present = np.zeros(n_tuples, dtype=np.uint8)
-    ext, nb = _ext26(extents), _nblk26(blockings)
+    ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
     cs, ct = _causal(causal)
-    rc = lib.oracle_attention_relational(spec.encode(), alpha, cs, ct, _i64p(ext), _i32p(nb), ptrs,
-                                         out.ctypes.data, present.ctypes.data)
+    rc = lib.oracle_attention_relational_iv(spec.encode(), alpha, cs, ct, _i64p(ext), _i32p(nb), _i64p(bd), ptrs,
+                                            out.ctypes.data, present.ctypes.data)
     _check(rc, "oracle_attention_relational")
     return out, present
 
