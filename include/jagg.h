@@ -140,6 +140,39 @@ jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, con
 jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64_t *extents,
                                  const int32_t *nblocks, jagg_dtype dtype, void *dev_buf, size_t buf_bytes,
                                  jagg_relation **out);
+/* Interval-blocked relations.  "Every Kernel Is a Join" (Ding et al.):
+ * a key is an interval per index (Def. 3.1), and Sec. 3.3 lets an index be
+ * cut only at legal positions -- Example 3.10 splits a packed sequence
+ * index only at the ends of its sequences, and the query heads of grouped-
+ * query attention along with their key-value heads.  So the blocks of one
+ * letter may differ in length.
+ *
+ * bounds[i] is NULL for a uniformly blocked letter (as above), or points
+ * to nblocks[i] + 1 strictly increasing positions 0 = b_0 < ... < b_k =
+ * extents[i]; block kappa then covers [b_kappa, b_kappa+1).  Every block of
+ * such a letter is padded to the longest interval, max(b_kappa+1 - b_kappa),
+ * and the storage convention is otherwise the one above.  At most 32
+ * intervals per letter (JAGG_E_UNSUPPORTED beyond); bounds that do not run
+ * from 0 to the extent or do not increase give JAGG_E_BLOCKING.  The bounds
+ * are copied; the caller keeps ownership of the arrays.  bounds == NULL is
+ * the uniform case for every letter.
+ *
+ * jagg_repartition converts between any two blockings, interval or uniform.
+ * jagg_einsum takes interval-blocked inputs when every relation holding such
+ * a letter (the output included) carries the same bounds and `blockings`
+ * names their count; a letter blocked differently in two relations is
+ * repartitioned by the caller first.  The block kernels compute the padding
+ * positions as well, so the spec's value must be +0 wherever an interval
+ * letter sits in padding: g = MUL, IDENT, SQUARE or SILU_MUL; ADD only when
+ * every input holds every interval letter; RMS_SCALE only when its first
+ * input does; MAX only over uniformly blocked letters; no ATTENTION and no
+ * causal pair on interval letters (JAGG_E_UNSUPPORTED otherwise). */
+jagg_status jagg_relation_bytes_iv(const char *letters, const int64_t *extents, const int32_t *nblocks,
+                                   const int64_t *const *bounds, jagg_dtype dtype, size_t *bytes);
+jagg_status jagg_relation_create_iv(jagg_ctx *ctx, const char *letters, const int64_t *extents,
+                                    const int32_t *nblocks, const int64_t *const *bounds, jagg_dtype dtype,
+                                    void *dev_buf, size_t buf_bytes, jagg_relation **out);
+
 /* Frees the metadata only, never dev_buf. */
 jagg_status jagg_relation_destroy(jagg_relation *rel);
 

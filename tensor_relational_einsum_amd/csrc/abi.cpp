@@ -48,6 +48,9 @@ struct jagg_relation {
   size_t bytes;
   int64_t n_tuples;
   int64_t be;  // elements per block
+  // interval-blocked letters: iv[i] = 1 and bnd[i][0..k[i]] the bounds
+  int32_t iv[kMaxLetters];
+  int64_t bnd[kMaxLetters][kMaxIv + 1];
 };
 
 namespace {
@@ -68,14 +71,32 @@ int esz_of(jagg_dtype d) { return d == JAGG_BF16 ? 2 : 4; }
 
 // ------------------------------------------------------------ geometry
 // Fills block extents, tuple count and block size; checks the blocking.
-jagg_status geometry(jagg_ctx *ctx, int r, const int64_t *n, const int32_t *k, int64_t *e, int64_t *n_tuples,
-                     int64_t *be) {
+// bnd (optional): bnd[i] NULL for a uniform letter, else its k[i]+1 bounds
+// 0 = b_0 < ... < b_k = n; such a letter's blocks pad to the longest interval.
+jagg_status geometry(jagg_ctx *ctx, int r, const int64_t *n, const int32_t *k, const int64_t *const *bnd,
+                     int64_t *e, int64_t *n_tuples, int64_t *be) {
   int64_t nt = 1, b = 1;
   for (int i = 0; i < r; ++i) {
     if (n[i] < 1) return fail(ctx, JAGG_E_SHAPE, "extent %d of dimension %d must be >= 1", int(n[i]), i);
     if (k[i] < 1 || k[i] > n[i])
       return fail(ctx, JAGG_E_BLOCKING, "block count %d of dimension %d is outside [1, %lld]", k[i], i,
                   (long long)n[i]);
+    if (bnd && bnd[i]) {
+      const int64_t *q = bnd[i];
+      if (k[i] > kMaxIv) return fail(ctx, JAGG_E_UNSUPPORTED, "dimension %d: more than %d intervals", i, kMaxIv);
+      if (q[0] != 0 || q[k[i]] != n[i])
+        return fail(ctx, JAGG_E_BLOCKING, "dimension %d: bounds must run from 0 to %lld", i, (long long)n[i]);
+      e[i] = 0;
+      for (int j = 0; j < k[i]; ++j) {
+        if (q[j + 1] <= q[j])
+          return fail(ctx, JAGG_E_BLOCKING, "dimension %d: bounds must increase strictly (%lld, %lld)", i,
+                      (long long)q[j], (long long)q[j + 1]);
+        e[i] = std::max(e[i], q[j + 1] - q[j]);
+      }
+      nt *= k[i];
+      b *= e[i];
+      continue;
+    }
     e[i] = (n[i] + k[i] - 1) / k[i];
     if ((k[i] - 1) * e[i] >= n[i])
       return fail(ctx, JAGG_E_BLOCKING, "dimension %d: %lld cut into %d blocks of %lld leaves the last empty", i,
@@ -729,7 +750,75 @@ jagg_status after_launch(jagg_ctx *ctx, hipError_t e, const char *what) {
   return JAGG_OK;
 }
 
+bool has_intervals(const jagg_relation &R) {
+  for (int q = 0; q < R.r; ++q)
+    if (R.iv[q]) return true;
+  return false;
+}
+
+// Interval relayout plan: per destination letter its destination geometry
+// and where its index lands in the source; the bounds of interval letters go
+// to a shared pool.  Vectors run along the innermost destination letter when
+// it is innermost in the source too and every bound of it, on both sides, is
+// a multiple of the width (so no vector straddles a block or padding edge).
+jagg_status plan_relayout_iv(jagg_ctx *ctx, const jagg_relation &S, const jagg_relation &D, IvRelayoutArgs &a,
+                             int &vec_bytes) {
+  memset(&a, 0, sizeof(a));
+  a.src = S.buf;
+  a.dst = D.buf;
+  a.r = D.r;
+  int pool = 0;
+  auto put = [&](const jagg_relation &R, int q) -> int {
+    if (!R.iv[q]) return -1;
+    if (pool + R.k[q] + 1 > kIvPool) return -2;
+    const int off = pool;
+    for (int i = 0; i <= R.k[q]; ++i) a.pool[pool++] = int32_t(R.bnd[q][i]);
+    return off;
+  };
+  for (int p = 0; p < D.r; ++p) {
+    const int q = int(strchr(S.letters, D.letters[p]) - S.letters);
+    IvRelayoutDim &d = a.d[p];
+    d.dk = make_fastdiv(uint32_t(D.k[p]));
+    d.de = make_fastdiv(uint32_t(D.e[p]));
+    d.n = int32_t(D.n[p]);
+    d.d_bnd = put(D, p);
+    d.s_bnd = put(S, q);
+    if (d.d_bnd == -2 || d.s_bnd == -2)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "more than %d interval bounds in one repartition", kIvPool);
+    d.s_k = S.k[q];
+    d.s_e = make_fastdiv(uint32_t(S.e[q]));
+    d.s_tw = uint32_t(tuple_w(S, q) * S.be);
+    d.s_ew = uint32_t(inblock_s(S, q));
+  }
+  a.n_pool = pool;
+  const int esz = esz_of(D.dt);
+  const int pi = D.r - 1;
+  const int qi = int(strchr(S.letters, D.letters[pi]) - S.letters);
+  int v = 16 / esz;
+  for (; v > 1; v >>= 1) {
+    bool ok = qi == S.r - 1 && D.n[pi] % v == 0 && D.e[pi] % v == 0 && S.e[qi] % v == 0;
+    for (int i = 0; ok && D.iv[pi] && i <= D.k[pi]; ++i) ok = D.bnd[pi][i] % v == 0;
+    for (int i = 0; ok && S.iv[qi] && i <= S.k[qi]; ++i) ok = S.bnd[qi][i] % v == 0;
+    if (ok) break;
+  }
+  a.v = v;
+  a.n_vec = uint32_t(D.n_tuples * D.be / v);
+  a.be_v = make_fastdiv(uint32_t(D.be / v));
+  vec_bytes = v * esz;
+  if (ctx->trace)
+    fprintf(stderr, "[jagg] relayout %s -> %s: intervals, %d-element vectors, %u vectors, %d bounds\n", S.letters,
+            D.letters, v, a.n_vec, pool);
+  return JAGG_OK;
+}
+
 jagg_status do_repartition(jagg_ctx *ctx, const jagg_relation &S, const jagg_relation &D) {
+  if (has_intervals(S) || has_intervals(D)) {
+    IvRelayoutArgs ia;
+    int vb = 0;
+    jagg_status st = plan_relayout_iv(ctx, S, D, ia, vb);
+    if (st != JAGG_OK) return st;
+    return after_launch(ctx, launch_relayout_iv(ia, vb, ctx->stream), "interval relayout");
+  }
   RelayoutArgs a;
   int vb = 0;
   jagg_status st = plan_relayout(ctx, S, D, a, vb);
@@ -741,13 +830,100 @@ jagg_status do_repartition(jagg_ctx *ctx, const jagg_relation &S, const jagg_rel
 struct Bound {
   Spec p;
   LetterInfo L;
-  const jagg_relation *in[kMaxIn];
+  const jagg_relation *in[kMaxIn];  // the inputs as the kernels see them (see shadow)
+  // Interval-blocked letters (iv_letter[c]) run as uniform letters of
+  // extent k * e (e the longest interval): every block is a full uniform
+  // block whose padding holds +0, and the shadows below carry that view.
+  bool iv_letter[26];
+  const int64_t *iv_bnd[26];
+  jagg_relation shadow[kMaxIn];
   bool needs_reblock[kMaxIn];
   size_t list_bytes, counts_bytes, reblock_bytes[kMaxIn], total;
   JoinArgs join;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Interval letters of a spec: every relation holding such a letter must
+// carry the same bounds, and the requested block count must be theirs (a
+// relation blocked otherwise is repartitioned by the caller first).  The
+// kernels then compute the padding too, so only specs whose value is +0
+// wherever an interval letter sits in its padding are taken: g = MUL, IDENT,
+// SQUARE or SILU_MUL (a zero factor), ADD when every input holds every
+// interval letter, RMS_SCALE when its first input does; MAX only over
+// uniform letters; no attention and no causal pair on interval letters.
+jagg_status bind_intervals(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const *in, int n_in, Bound &b) {
+  bool any = false;
+  for (int c = 0; c < 26; ++c) {
+    b.iv_letter[c] = false;
+    b.iv_bnd[c] = nullptr;
+  }
+  for (int j = 0; j < n_in; ++j)
+    for (int q = 0; q < in[j]->r; ++q)
+      if (in[j]->iv[q]) {
+        b.iv_letter[b.p.in[j][q] - 'a'] = true;
+        any = true;
+      }
+  for (int j = 0; j < n_in; ++j) b.in[j] = in[j];
+  if (!any) return JAGG_OK;
+  for (int j = 0; j < n_in; ++j) {
+    const jagg_relation *R = in[j];
+    for (int q = 0; q < R->r; ++q) {
+      const int c = b.p.in[j][q] - 'a';
+      if (!b.iv_letter[c]) continue;
+      if (!R->iv[q])
+        return fail(ctx, JAGG_E_BLOCKING, "letter '%c' is interval-blocked in one input and uniform in input %d",
+                    'a' + c, j);
+      if (R->k[q] != b.L.k[c])
+        return fail(ctx, JAGG_E_BLOCKING, "letter '%c' holds %d intervals, the spec asks %d blocks", 'a' + c, R->k[q],
+                    b.L.k[c]);
+      if (!b.iv_bnd[c]) {
+        b.iv_bnd[c] = R->bnd[q];
+      } else if (memcmp(b.iv_bnd[c], R->bnd[q], sizeof(int64_t) * size_t(R->k[q] + 1)) != 0) {
+        return fail(ctx, JAGG_E_BLOCKING, "letter '%c' has different bounds in two inputs", 'a' + c);
+      }
+    }
+  }
+  auto is_iv = [&](char c) { return b.iv_letter[c - 'a']; };
+  if (sp->g == JAGG_G_ATTENTION)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "attention over interval-blocked letters is not supported");
+  if (sp->causal_s && (is_iv(sp->causal_s) || is_iv(sp->causal_t)))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "causal letters must be uniformly blocked");
+  if (sp->g == JAGG_G_EXP_SUB || sp->g == JAGG_G_EXP_SUB_DIV)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "g %d is not zero on padding; interval letters need it", int(sp->g));
+  if (sp->agg == JAGG_AGG_MAX)
+    for (char c : b.p.reduced)
+      if (is_iv(c)) return fail(ctx, JAGG_E_UNSUPPORTED, "MAX over the interval-blocked letter '%c'", c);
+  for (int c = 0; c < 26; ++c) {
+    if (!b.iv_letter[c]) continue;
+    const int first = sp->g == JAGG_G_RMS_SCALE ? 1 : (sp->g == JAGG_G_ADD ? n_in : 0);
+    for (int j = 0; j < first; ++j)
+      if (b.p.in[j].find(char('a' + c)) == std::string::npos)
+        return fail(ctx, JAGG_E_UNSUPPORTED, "g %d needs the interval-blocked letter '%c' in input %d", int(sp->g),
+                    'a' + c, j);
+  }
+  for (int j = 0; j < n_in; ++j) {
+    jagg_relation &T = b.shadow[j];
+    T = *in[j];
+    for (int q = 0; q < T.r; ++q)
+      if (T.iv[q]) {
+        T.n[q] = int64_t(T.k[q]) * T.e[q];
+        T.iv[q] = 0;
+      }
+    b.in[j] = &T;
+  }
+  for (int c = 0; c < 26; ++c)
+    if (b.iv_letter[c]) {
+      for (int j = 0; j < n_in; ++j) {
+        const size_t q = b.p.in[j].find(char('a' + c));
+        if (q != std::string::npos) {
+          b.L.n[c] = b.shadow[j].n[q];
+          break;
+        }
+      }
+    }
+  return JAGG_OK;
+}
 
 jagg_status bind(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const *in, int n_in,
                  const int32_t *blockings, Bound &b) {
@@ -782,6 +958,7 @@ jagg_status bind(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const 
       if (R->k[q] != b.L.k[c]) b.needs_reblock[j] = true;
     }
   }
+  if ((st = bind_intervals(ctx, sp, in, n_in, b)) != JAGG_OK) return st;
   // the requested blocking must be valid for every letter
   for (char c : b.p.order) {
     const int i = c - 'a';
@@ -1250,21 +1427,32 @@ jagg_status jagg_graph_destroy(jagg_graph *g) {
   return JAGG_OK;
 }
 
-jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, const int32_t *nblocks, jagg_dtype dtype,
-                                size_t *bytes) {
+jagg_status jagg_relation_bytes_iv(const char *letters, const int64_t *extents, const int32_t *nblocks,
+                                   const int64_t *const *bounds, jagg_dtype dtype, size_t *bytes) {
   if (!letters || !extents || !nblocks || !bytes) return JAGG_E_INVALID;
   if (dtype != JAGG_F32 && dtype != JAGG_BF16) return JAGG_E_INVALID;
   const int r = int(strlen(letters));
   if (r < 1 || r > kMaxLetters) return JAGG_E_UNSUPPORTED;
   int64_t e[kMaxLetters], nt, be;
-  jagg_status st = geometry(nullptr, r, extents, nblocks, e, &nt, &be);
+  jagg_status st = geometry(nullptr, r, extents, nblocks, bounds, e, &nt, &be);
   if (st != JAGG_OK) return st;
   *bytes = size_t(nt * be) * size_t(esz_of(dtype));
   return JAGG_OK;
 }
 
+jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, const int32_t *nblocks, jagg_dtype dtype,
+                                size_t *bytes) {
+  return jagg_relation_bytes_iv(letters, extents, nblocks, nullptr, dtype, bytes);
+}
+
 jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64_t *extents, const int32_t *nblocks,
                                  jagg_dtype dtype, void *dev_buf, size_t buf_bytes, jagg_relation **out) {
+  return jagg_relation_create_iv(ctx, letters, extents, nblocks, nullptr, dtype, dev_buf, buf_bytes, out);
+}
+
+jagg_status jagg_relation_create_iv(jagg_ctx *ctx, const char *letters, const int64_t *extents,
+                                    const int32_t *nblocks, const int64_t *const *bounds, jagg_dtype dtype,
+                                    void *dev_buf, size_t buf_bytes, jagg_relation **out) {
   if (!ctx || !letters || !extents || !nblocks || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
   *out = nullptr;
   if (dtype != JAGG_F32 && dtype != JAGG_BF16) return fail(ctx, JAGG_E_INVALID, "unknown dtype %d", int(dtype));
@@ -1284,8 +1472,15 @@ jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64
     R.n[i] = extents[i];
     R.k[i] = nblocks[i];
   }
-  jagg_status st = geometry(ctx, r, R.n, R.k, R.e, &R.n_tuples, &R.be);
+  jagg_status st = geometry(ctx, r, R.n, R.k, bounds, R.e, &R.n_tuples, &R.be);
   if (st != JAGG_OK) return st;
+  memset(R.iv, 0, sizeof(R.iv));
+  memset(R.bnd, 0, sizeof(R.bnd));
+  for (int i = 0; i < r; ++i)
+    if (bounds && bounds[i]) {
+      R.iv[i] = 1;
+      for (int j = 0; j <= R.k[i]; ++j) R.bnd[i][j] = bounds[i][j];
+    }
   const int64_t elems = R.n_tuples * R.be;
   if (elems >= (int64_t(1) << 31)) return fail(ctx, JAGG_E_UNSUPPORTED, "relation of %lld elements exceeds 2^31", (long long)elems);
   const size_t need = size_t(elems) * size_t(esz_of(dtype));
@@ -1343,14 +1538,26 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   if (out->r != int(b.p.out.size()))
     return fail(ctx, JAGG_E_SHAPE, "out relation has %d dimensions, output '%s' names %d", out->r, b.p.out.c_str(),
                 int(b.p.out.size()));
+  jagg_relation out_view = *out;  // interval letters as uniform ones, like the inputs
   for (int q = 0; q < out->r; ++q) {
     const int c = b.p.out[q] - 'a';
-    if (out->n[q] != b.L.n[c])
+    if (out->iv[q] != int32_t(b.iv_letter[c]))
+      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' must be %s-blocked like the inputs", 'a' + c,
+                  b.iv_letter[c] ? "interval" : "uniformly");
+    if (out->iv[q]) {
+      if (out->k[q] != b.L.k[c] ||
+          memcmp(out->bnd[q], b.iv_bnd[c], sizeof(int64_t) * size_t(out->k[q] + 1)) != 0)
+        return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has other bounds than the inputs", 'a' + c);
+      out_view.n[q] = int64_t(out->k[q]) * out->e[q];
+      out_view.iv[q] = 0;
+    }
+    if (out_view.n[q] != b.L.n[c])
       return fail(ctx, JAGG_E_SHAPE, "out letter '%c' has extent %lld, expected %lld", 'a' + c, (long long)out->n[q],
                   (long long)b.L.n[c]);
     if (out->k[q] != b.L.k[c])
       return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has %d blocks, the spec asks %d", 'a' + c, out->k[q], b.L.k[c]);
   }
+  out = &out_view;
   if (out->dt != spec->out_dtype) return fail(ctx, JAGG_E_SHAPE, "out relation dtype differs from spec->out_dtype");
   {
     const char *ob = static_cast<const char *>(out->buf);
@@ -1395,12 +1602,12 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   jagg_relation tmp[kMaxIn];
   const jagg_relation *use[kMaxIn];
   for (int j = 0; j < n_in; ++j) {
-    use[j] = in[j];
+    use[j] = b.in[j];
     if (!b.needs_reblock[j]) continue;
     jagg_relation &T = tmp[j];
-    T = *in[j];
+    T = *b.in[j];
     for (int q = 0; q < T.r; ++q) T.k[q] = b.L.k[b.p.in[j][q] - 'a'];
-    if ((st = geometry(ctx, T.r, T.n, T.k, T.e, &T.n_tuples, &T.be)) != JAGG_OK) return st;
+    if ((st = geometry(ctx, T.r, T.n, T.k, nullptr, T.e, &T.n_tuples, &T.be)) != JAGG_OK) return st;
     T.buf = ws + off;
     T.bytes = b.reblock_bytes[j];
     off += b.reblock_bytes[j];
@@ -1426,7 +1633,7 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
     if (!b.needs_reblock[j]) continue;
     RelayoutArgs ra;
     int vbytes = 0;
-    if ((st = plan_relayout(ctx, *in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
+    if ((st = plan_relayout(ctx, *b.in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
     reblocks.push_back(ra);
     reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
   }

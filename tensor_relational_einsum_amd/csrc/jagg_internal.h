@@ -13,6 +13,8 @@ constexpr int kMaxDims = 24;     // relayout dims after splitting (<= 3 per lett
 constexpr int kMaxChk = 8;       // relayout letters whose range must be checked
 constexpr int kMaxChain = 3;     // dims per run chain of the LDS-transposing relayout
 constexpr int kMaxLdsOuter = 8;  // outer (box) dims of the LDS-transposing relayout
+constexpr int kMaxIv = 32;       // intervals of one interval-blocked letter
+constexpr int kIvPool = 192;     // interval bounds one interval relayout carries
 
 // Unsigned 32-bit division by a run-time invariant d >= 1 through a
 // multiply-high, after Granlund and Montgomery, "Division by Invariant
@@ -96,6 +98,40 @@ struct RelayoutArgs {
 
 // vec_bytes: 16, 8, 4 or 2; elem_bytes 2 or 4.
 hipError_t launch_relayout(const RelayoutArgs &a, int vec_bytes, int elem_bytes, hipStream_t st);
+
+// ---------------------------------------------------------------- interval relayout
+// Copy between relations where some letter is blocked by a list of bounds
+// (non-uniform intervals).  One thread moves one vector of the destination:
+// it decodes the destination tuple and in-block coordinates, forms each
+// letter's global index x from the destination interval, writes +0 where x
+// falls in the block's padding, and otherwise finds the source block of x
+// (division for a uniform letter, a search of the bounds for an interval
+// letter) and reads the vector there.
+struct IvRelayoutDim {   // one letter, destination order
+  FastDiv dk, de;        // destination block count, padded block extent
+  int32_t d_bnd;         // pool offset of the destination bounds, -1 if uniform
+  int32_t n;             // extent of the letter
+  int32_t s_bnd;         // pool offset of the source bounds, -1 if uniform
+  int32_t s_k;           // source block count
+  FastDiv s_e;           // source padded block extent
+  uint32_t s_tw;         // source offset of one block step (elements)
+  uint32_t s_ew;         // source in-block stride (elements)
+};
+
+struct IvRelayoutArgs {
+  const void *src;
+  void *dst;
+  int32_t r;
+  IvRelayoutDim d[kMaxLetters];
+  uint32_t n_vec;        // destination vectors
+  FastDiv be_v;          // destination block size, in vectors
+  int32_t v;             // elements per vector
+  int32_t n_pool;
+  int32_t pool[kIvPool];
+};
+
+// vec_bytes: 16, 8, 4 or 2 (a multiple of elem_bytes).
+hipError_t launch_relayout_iv(const IvRelayoutArgs &a, int vec_bytes, hipStream_t st);
 
 // ---------------------------------------------------------------- join
 struct JoinArgs {

@@ -345,6 +345,90 @@ static hipError_t go(const RelayoutArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- interval letters
+// "Every Kernel Is a Join", Def. 3.1 and Sec. 3.3: a key is an interval per
+// index, and an index may be cut only at legal positions (the ends of packed
+// sequences), so blocks of one letter can differ in length; storage pads
+// each to the longest.  The affine digit walk above needs nesting uniform
+// blocks, so these copies take this kernel: per destination vector, decode
+// the coordinates, zero-fill padding, locate the source block of each
+// index (a division, or a search of that letter's bounds held in LDS).
+// A vector never straddles a block or padding edge: the host picks the width
+// so that every bound of the innermost letter is a multiple of it.
+template <typename V>
+__global__ __launch_bounds__(256) void relayout_iv_kernel(const IvRelayoutArgs a) {
+  __shared__ int32_t bnd[kIvPool];
+  for (int i = threadIdx.x; i < a.n_pool; i += blockDim.x) bnd[i] = a.pool[i];
+  __syncthreads();
+  const V *src = static_cast<const V *>(a.src);
+  V *dst = static_cast<V *>(a.dst);
+  const uint32_t vshift = a.v == 1 ? 0 : (a.v == 2 ? 1 : (a.v == 4 ? 2 : 3));
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_vec; i += gridDim.x * blockDim.x) {
+    const uint32_t t0 = fd_div(i, a.be_v);
+    uint32_t w = (i - t0 * a.be_v.d) << vshift;  // element offset inside the destination block
+    uint32_t t = t0;
+    uint32_t soff = 0;
+    bool valid = true;
+#pragma unroll
+    for (int p = kMaxLetters - 1; p >= 0; --p) {
+      if (p >= a.r) continue;
+      const IvRelayoutDim &d = a.d[p];
+      const uint32_t wq = fd_div(w, d.de), tq = fd_div(t, d.dk);
+      const uint32_t wp = w - wq * d.de.d, kp = t - tq * d.dk.d;
+      w = wq;
+      t = tq;
+      uint32_t lo, hi;
+      if (d.d_bnd >= 0) {
+        lo = uint32_t(bnd[d.d_bnd + kp]);
+        hi = uint32_t(bnd[d.d_bnd + kp + 1]);
+      } else {
+        lo = kp * d.de.d;
+        hi = min(lo + d.de.d, uint32_t(d.n));
+      }
+      const uint32_t x = lo + wp;
+      valid = valid && x < hi;
+      uint32_t ks, slo;
+      if (d.s_bnd >= 0) {
+        // largest ks with bound[ks] <= x, over ks in [0, s_k); s_k <= kMaxIv
+        ks = 0;
+#pragma unroll
+        for (int step = kMaxIv / 2; step >= 1; step >>= 1)
+          if (ks + step < uint32_t(d.s_k) && uint32_t(bnd[d.s_bnd + ks + step]) <= x) ks += step;
+        slo = uint32_t(bnd[d.s_bnd + ks]);
+      } else {
+        ks = fd_div(x, d.s_e);
+        slo = ks * d.s_e.d;
+      }
+      soff += ks * d.s_tw + (x - slo) * d.s_ew;
+    }
+    V val;
+    if (valid) {
+      val = src[soff >> vshift];
+    } else {
+      memset(&val, 0, sizeof(V));
+    }
+    dst[i] = val;
+  }
+}
+
+template <typename V>
+hipError_t go_iv(const IvRelayoutArgs &a, hipStream_t st) {
+  const int64_t want = (int64_t(a.n_vec) + 255) / 256;
+  const int grid = int(want < 8192 ? (want > 0 ? want : 1) : 8192);
+  relayout_iv_kernel<V><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_relayout_iv(const IvRelayoutArgs &a, int vec_bytes, hipStream_t st) {
+  switch (vec_bytes) {
+    case 16: return go_iv<uint4>(a, st);
+    case 8: return go_iv<uint2>(a, st);
+    case 4: return go_iv<uint32_t>(a, st);
+    case 2: return go_iv<uint16_t>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_relayout(const RelayoutArgs &a, int vec_bytes, int elem_bytes, hipStream_t st) {
   if (elem_bytes == 2) {
     switch (vec_bytes) {

@@ -23,7 +23,7 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "shape mismatch", -3: "bad blocki
           -5: "workspace too small", -6: "device error"}
 
 EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
-           "jagg_relation_destroy", "jagg_repartition", "jagg_einsum_workspace", "jagg_einsum", "jagg_join_shape",
+           "jagg_relation_bytes_iv", "jagg_relation_create_iv", "jagg_relation_destroy", "jagg_repartition", "jagg_einsum_workspace", "jagg_einsum", "jagg_join_shape",
            "jagg_join_list", "jagg_capture_begin", "jagg_capture_end", "jagg_graph_launch", "jagg_graph_destroy",
            "jagg_status_str", "jagg_last_error"]
 
@@ -60,6 +60,11 @@ def lib():
         L.jagg_relation_bytes.argtypes = [ctypes.c_char_p, i64p, i32p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         L.jagg_relation_create.argtypes = [vp, ctypes.c_char_p, i64p, i32p, ctypes.c_int, vp, ctypes.c_size_t,
                                            ctypes.POINTER(vp)]
+        i64pp = ctypes.POINTER(i64p)
+        L.jagg_relation_bytes_iv.argtypes = [ctypes.c_char_p, i64p, i32p, i64pp, ctypes.c_int,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+        L.jagg_relation_create_iv.argtypes = [vp, ctypes.c_char_p, i64p, i32p, i64pp, ctypes.c_int, vp,
+                                              ctypes.c_size_t, ctypes.POINTER(vp)]
         L.jagg_relation_destroy.argtypes = [vp]
         L.jagg_repartition.argtypes = [vp, vp, vp]
         L.jagg_einsum_workspace.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p,
@@ -138,9 +143,30 @@ class Context:
             pass
 
 
+def block_count(b) -> int:
+    """A blocking value is a block count or a list of interval bounds."""
+    return len(b) - 1 if isinstance(b, (list, tuple)) else int(b)
+
+
+def _bounds(blocks):
+    """(count array, bounds pointer array, keep-alive) for per-letter blocking
+    values; a NULL bounds pointer marks a uniformly blocked letter."""
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    keep, ptrs = [], []
+    for b in blocks:
+        if isinstance(b, (list, tuple)):
+            arr = _i64(b)
+            keep.append(arr)
+            ptrs.append(ctypes.cast(arr, p64))
+        else:
+            ptrs.append(p64())
+    return _i32([block_count(b) for b in blocks]), (p64 * len(ptrs))(*ptrs), keep
+
+
 def relation_bytes(letters, extents, nblocks, dtype) -> int:
     out = ctypes.c_size_t()
-    rc = lib().jagg_relation_bytes(letters.encode(), _i64(extents), _i32(nblocks), DT[dtype], ctypes.byref(out))
+    counts, bnd, _keep = _bounds(nblocks)
+    rc = lib().jagg_relation_bytes_iv(letters.encode(), _i64(extents), counts, bnd, DT[dtype], ctypes.byref(out))
     if rc != 0:
         raise JaggError(rc, f"relation {letters} {list(extents)} / {list(nblocks)}")
     return out.value
@@ -148,29 +174,36 @@ def relation_bytes(letters, extents, nblocks, dtype) -> int:
 
 class Relation:
     """Tensor relation over a flat torch device buffer (padded blocks in
-    canonical tuple order).  ``extents`` / ``nblocks`` follow ``letters``."""
+    canonical tuple order).  ``extents`` / ``nblocks`` follow ``letters``; an
+    entry of ``nblocks`` is a block count or a list of interval bounds."""
 
     def __init__(self, ctx: Context, letters: str, extents, nblocks, dtype: str, buffer: torch.Tensor | None = None):
         self.ctx, self.letters, self.dtype = ctx, letters, dtype
         self.extents = [int(v) for v in extents]
-        self.nblocks = [int(v) for v in nblocks]
-        nbytes = relation_bytes(letters, self.extents, self.nblocks, dtype)
+        self.bounds = [[int(x) for x in b] if isinstance(b, (list, tuple)) else None for b in nblocks]
+        self.nblocks = [block_count(b) for b in nblocks]
+        nbytes = relation_bytes(letters, self.extents, self._blocks(), dtype)
         if buffer is None:
             buffer = torch.empty(nbytes // ESZ[dtype], dtype=TORCH_DT[dtype], device=f"cuda:{ctx.device}")
         self.data = buffer
         self.nbytes = nbytes
         h = ctypes.c_void_p()
-        ctx._check(lib().jagg_relation_create(ctx.handle, letters.encode(), _i64(self.extents), _i32(self.nblocks),
-                                              DT[dtype], ctypes.c_void_p(buffer.data_ptr()),
-                                              buffer.numel() * buffer.element_size(), ctypes.byref(h)))
+        counts, bnd, _keep = _bounds(self._blocks())
+        ctx._check(lib().jagg_relation_create_iv(ctx.handle, letters.encode(), _i64(self.extents), counts, bnd,
+                                                 DT[dtype], ctypes.c_void_p(buffer.data_ptr()),
+                                                 buffer.numel() * buffer.element_size(), ctypes.byref(h)))
         self.handle = h
+
+    def _blocks(self):
+        return [b if b is not None else k for b, k in zip(self.bounds, self.nblocks)]
 
     @property
     def block_shape(self):
-        return [-(-n // k) for n, k in zip(self.extents, self.nblocks)]
+        return [max(y - x for x, y in zip(b, b[1:])) if b is not None else -(-n // k)
+                for n, k, b in zip(self.extents, self.nblocks, self.bounds)]
 
     def blocking(self) -> dict:
-        return dict(zip(self.letters, self.nblocks))
+        return dict(zip(self.letters, self._blocks()))
 
     def __del__(self):
         try:
@@ -257,7 +290,7 @@ class EinsumCall:
         self.ctx, self.einsum = ctx, einsum
         self.spec = make_spec(einsum, g, agg, out_dtype, alpha, beta, eps, causal)
         self.inputs = list(inputs)
-        self.blk = _i32([blockings.get(c, 1) for c in order])
+        self.blk = _i32([block_count(blockings.get(c, 1)) for c in order])
         self.in_arr = (ctypes.c_void_p * len(self.inputs))(*[r.handle.value for r in self.inputs])
         if out is None:
             ext = {}

@@ -44,6 +44,26 @@ def test_relation_bytes_matches_oracle_geometry(letters, ext, blk, dtype):
     assert got == want
 
 
+@pytest.mark.parametrize("letters,ext,blk,dtype", [
+    ("sd", (4096, 128), ([0, 1024, 2560, 4096], 1), "bf16"),   # packed sequences (Example 3.10)
+    ("ij", (11, 6), ([0, 3, 4, 11], [0, 1, 6]), "f32"),
+    ("abc", (7, 5, 6), (2, [0, 2, 5], 3), "f32"),
+    ("h", (32,), ([4 * m for m in range(9)],), "bf16"),
+])
+def test_interval_relation_bytes_match_oracle_geometry(letters, ext, blk, dtype):
+    got = jagg.relation_bytes(letters, ext, blk, dtype)
+    want = O.relation_elems(letters, dict(zip(letters, ext)), dict(zip(letters, blk))) * jagg.ESZ[dtype]
+    assert got == want
+
+
+def test_interval_relation_bytes_reject_bad_bounds():
+    for bnd, status in (([1, 4, 8], -3), ([0, 4, 7], -3), ([0, 4, 4, 8], -3), ([0, 5, 3, 8], -3),
+                        (list(range(33)) + [64], -4)):
+        with pytest.raises(jagg.JaggError) as e:
+            jagg.relation_bytes("a", (max(8, bnd[-1]) if status == -4 else 8,), (bnd,), "f32")
+        assert e.value.status == status, bnd
+
+
 def test_relation_bytes_rejects_bad_blockings():
     with pytest.raises(jagg.JaggError) as e:
         jagg.relation_bytes("a", (10,), (6,), "f32")  # last block empty
