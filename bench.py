@@ -10,8 +10,9 @@ already resident in HBM when the timed region starts.
 Prints one JSON line: value = algorithmic TFLOP/s of the step (contraction
 FLOPs, causal attention counted element-wise), a roofline entry for the
 dominant kernel (the bf16 MFMA contraction of the projection / FFN specs),
-the repartition GB/s of the 8192^2 and 4-D reblocking workloads, and the
-CPU oracle timed on a bounded sample of the same specs.
+the repartition GB/s of the 8192^2, 4-D and packed-sequence (interval)
+reblocking workloads, and the CPU oracle timed on a bounded sample of the
+same specs.
 """
 from __future__ import annotations
 
@@ -162,7 +163,9 @@ def repartition_rate(ctx, w: I.Workload, reps: int, scratch) -> dict:
     run = ChainRunner(ctx, w, dense)
     st = w.chain[0]
     src, dst = run.rel[st.src], run.rel[st.out]
-    nbytes = 2.0 * math.prod(src.extents) * jagg.ESZ[src.dtype]
+    # algorithmic bytes: every element read once, every destination slot
+    # (padding of interval blocks included) written once
+    nbytes = float(math.prod(src.extents) * jagg.ESZ[src.dtype] + dst.nbytes)
     for _ in range(3):
         jagg.repartition(ctx, src, dst)
     times = []
@@ -302,7 +305,9 @@ def main():
         torch.cuda.empty_cache()
         scratch = torch.zeros(512 << 20 >> 2, dtype=torch.float32, device="cuda")
         rep = {"8192x8192": repartition_rate(ctx, I.repartition_2d(), 15, scratch),
-               "32x128x64x64": repartition_rate(ctx, I.repartition_4d(), 15, scratch)}
+               "32x128x64x64": repartition_rate(ctx, I.repartition_4d(), 15, scratch),
+               "packed_to_uniform": repartition_rate(ctx, I.repartition_packed(), 15, scratch),
+               "uniform_to_packed": repartition_rate(ctx, I.repartition_packed(to_packed=True), 15, scratch)}
         del scratch
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")

@@ -750,6 +750,11 @@ jagg_status after_launch(jagg_ctx *ctx, hipError_t e, const char *what) {
   return JAGG_OK;
 }
 
+#ifndef JAGG_IV_ROWS
+#define JAGG_IV_ROWS 1
+#endif
+constexpr bool kIvRows = JAGG_IV_ROWS;
+
 bool has_intervals(const jagg_relation &R) {
   for (int q = 0; q < R.r; ++q)
     if (R.iv[q]) return true;
@@ -805,9 +810,14 @@ jagg_status plan_relayout_iv(jagg_ctx *ctx, const jagg_relation &S, const jagg_r
   a.n_vec = uint32_t(D.n_tuples * D.be / v);
   a.be_v = make_fastdiv(uint32_t(D.be / v));
   vec_bytes = v * esz;
+  // rows of at least a wave's worth of vectors take the row form
+  a.row_vecs = uint32_t(D.e[pi] / v);
+  a.rows = kIvRows && a.row_vecs >= 64;
+  a.n_rows = uint32_t(D.n_tuples * (D.be / D.e[pi]));
+  a.rows_pt = make_fastdiv(uint32_t(D.be / D.e[pi]));
   if (ctx->trace)
-    fprintf(stderr, "[jagg] relayout %s -> %s: intervals, %d-element vectors, %u vectors, %d bounds\n", S.letters,
-            D.letters, v, a.n_vec, pool);
+    fprintf(stderr, "[jagg] relayout %s -> %s: intervals, %d-element vectors, %u vectors, %d bounds%s\n", S.letters,
+            D.letters, v, a.n_vec, pool, a.rows ? ", rows" : "");
   return JAGG_OK;
 }
 

@@ -101,12 +101,14 @@ hipError_t launch_relayout(const RelayoutArgs &a, int vec_bytes, int elem_bytes,
 
 // ---------------------------------------------------------------- interval relayout
 // Copy between relations where some letter is blocked by a list of bounds
-// (non-uniform intervals).  One thread moves one vector of the destination:
-// it decodes the destination tuple and in-block coordinates, forms each
-// letter's global index x from the destination interval, writes +0 where x
-// falls in the block's padding, and otherwise finds the source block of x
-// (division for a uniform letter, a search of the bounds for an interval
-// letter) and reads the vector there.
+// (non-uniform intervals).  For each destination vector: decode the
+// destination tuple and in-block coordinates, form each letter's global
+// index x from the destination interval, write +0 where x falls in the
+// block's padding, and otherwise find the source block of x (division for a
+// uniform letter, a search of the bounds for an interval letter) and read
+// the vector there.  Row form: a wave decodes the outer letters of a row
+// (one block extent of the innermost destination letter) once and streams
+// the row; vector form (short rows): a thread decodes each vector.
 struct IvRelayoutDim {   // one letter, destination order
   FastDiv dk, de;        // destination block count, padded block extent
   int32_t d_bnd;         // pool offset of the destination bounds, -1 if uniform
@@ -126,6 +128,12 @@ struct IvRelayoutArgs {
   uint32_t n_vec;        // destination vectors
   FastDiv be_v;          // destination block size, in vectors
   int32_t v;             // elements per vector
+  // row form (rows != 0): a row is one block extent of the innermost
+  // destination letter; a wave decodes a row once and streams its vectors
+  int32_t rows;
+  uint32_t n_rows;
+  FastDiv rows_pt;       // rows per destination tuple
+  uint32_t row_vecs;     // vectors per row
   int32_t n_pool;
   int32_t pool[kIvPool];
 };

@@ -355,6 +355,50 @@ static hipError_t go(const RelayoutArgs &a, hipStream_t st) {
 // index (a division, or a search of that letter's bounds held in LDS).
 // A vector never straddles a block or padding edge: the host picks the width
 // so that every bound of the innermost letter is a multiple of it.
+// source offset (elements) of destination vector i, or -1 for padding
+__device__ __forceinline__ int64_t iv_source(const IvRelayoutArgs &a, const int32_t *bnd, uint32_t i,
+                                             uint32_t vshift) {
+  const uint32_t t0 = fd_div(i, a.be_v);
+  uint32_t w = (i - t0 * a.be_v.d) << vshift;  // element offset inside the destination block
+  uint32_t t = t0;
+  uint32_t soff = 0;
+  bool valid = true;
+#pragma unroll
+  for (int p = kMaxLetters - 1; p >= 0; --p) {
+    if (p >= a.r) continue;
+    const IvRelayoutDim &d = a.d[p];
+    const uint32_t wq = fd_div(w, d.de), tq = fd_div(t, d.dk);
+    const uint32_t wp = w - wq * d.de.d, kp = t - tq * d.dk.d;
+    w = wq;
+    t = tq;
+    uint32_t lo, hi;
+    if (d.d_bnd >= 0) {
+      lo = uint32_t(bnd[d.d_bnd + kp]);
+      hi = uint32_t(bnd[d.d_bnd + kp + 1]);
+    } else {
+      lo = kp * d.de.d;
+      hi = min(lo + d.de.d, uint32_t(d.n));
+    }
+    const uint32_t x = lo + wp;
+    valid = valid && x < hi;
+    uint32_t ks, slo;
+    if (d.s_bnd >= 0) {
+      // largest ks with bound[ks] <= x, over ks in [0, s_k); s_k <= kMaxIv
+      ks = 0;
+#pragma unroll
+      for (int step = kMaxIv / 2; step >= 1; step >>= 1)
+        if (ks + step < uint32_t(d.s_k) && uint32_t(bnd[d.s_bnd + ks + step]) <= x) ks += step;
+      slo = uint32_t(bnd[d.s_bnd + ks]);
+    } else {
+      ks = fd_div(x, d.s_e);
+      slo = ks * d.s_e.d;
+    }
+    soff += ks * d.s_tw + (x - slo) * d.s_ew;
+  }
+  return valid ? int64_t(soff) : int64_t(-1);
+}
+
+// Vector form (short rows): one destination vector per thread and pass.
 template <typename V>
 __global__ __launch_bounds__(256) void relayout_iv_kernel(const IvRelayoutArgs a) {
   __shared__ int32_t bnd[kIvPool];
@@ -364,18 +408,44 @@ __global__ __launch_bounds__(256) void relayout_iv_kernel(const IvRelayoutArgs a
   V *dst = static_cast<V *>(a.dst);
   const uint32_t vshift = a.v == 1 ? 0 : (a.v == 2 ? 1 : (a.v == 4 ? 2 : 3));
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_vec; i += gridDim.x * blockDim.x) {
-    const uint32_t t0 = fd_div(i, a.be_v);
-    uint32_t w = (i - t0 * a.be_v.d) << vshift;  // element offset inside the destination block
-    uint32_t t = t0;
+    const int64_t so = iv_source(a, bnd, i, vshift);
+    V val;
+    memset(&val, 0, sizeof(V));
+    if (so >= 0) val = src[uint32_t(so) >> vshift];
+    dst[i] = val;
+  }
+}
+
+// vectors in flight per lane in the row form
+constexpr int kIvUnroll = 4;
+
+// Row form: with long rows along the innermost destination letter, a wave
+// decodes the outer letters of one row once (uniform values) and its lanes
+// stream the row, mapping only the innermost index per vector.
+template <typename V>
+__global__ __launch_bounds__(256) void relayout_iv_rows_kernel(const IvRelayoutArgs a) {
+  __shared__ int32_t bnd[kIvPool];
+  for (int i = threadIdx.x; i < a.n_pool; i += blockDim.x) bnd[i] = a.pool[i];
+  __syncthreads();
+  const V *src = static_cast<const V *>(a.src);
+  V *dst = static_cast<V *>(a.dst);
+  const uint32_t vshift = a.v == 1 ? 0 : (a.v == 2 ? 1 : (a.v == 4 ? 2 : 3));
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (uint32_t row = blockIdx.x * 4 + wave; row < a.n_rows; row += gridDim.x * 4) {
+    uint32_t t = fd_div(row, a.rows_pt);
+    uint32_t w = row - t * a.rows_pt.d;
     uint32_t soff = 0;
     bool valid = true;
+    uint32_t lo_in = 0, hi_in = 0, k_in = 0, tw_in = 0, ew_in = 0;
+    int32_t sb_in = -1;
+    FastDiv se_in = a.d[0].s_e;
 #pragma unroll
     for (int p = kMaxLetters - 1; p >= 0; --p) {
       if (p >= a.r) continue;
       const IvRelayoutDim &d = a.d[p];
-      const uint32_t wq = fd_div(w, d.de), tq = fd_div(t, d.dk);
-      const uint32_t wp = w - wq * d.de.d, kp = t - tq * d.dk.d;
-      w = wq;
+      const uint32_t tq = fd_div(t, d.dk);
+      const uint32_t kp = t - tq * d.dk.d;
       t = tq;
       uint32_t lo, hi;
       if (d.d_bnd >= 0) {
@@ -385,11 +455,22 @@ __global__ __launch_bounds__(256) void relayout_iv_kernel(const IvRelayoutArgs a
         lo = kp * d.de.d;
         hi = min(lo + d.de.d, uint32_t(d.n));
       }
-      const uint32_t x = lo + wp;
+      if (p == a.r - 1) {  // innermost: mapped per vector below
+        lo_in = lo;
+        hi_in = hi;
+        sb_in = d.s_bnd;
+        k_in = uint32_t(d.s_k);
+        se_in = d.s_e;
+        tw_in = d.s_tw;
+        ew_in = d.s_ew;
+        continue;
+      }
+      const uint32_t wq = fd_div(w, d.de);
+      const uint32_t x = lo + (w - wq * d.de.d);
+      w = wq;
       valid = valid && x < hi;
       uint32_t ks, slo;
       if (d.s_bnd >= 0) {
-        // largest ks with bound[ks] <= x, over ks in [0, s_k); s_k <= kMaxIv
         ks = 0;
 #pragma unroll
         for (int step = kMaxIv / 2; step >= 1; step >>= 1)
@@ -401,18 +482,46 @@ __global__ __launch_bounds__(256) void relayout_iv_kernel(const IvRelayoutArgs a
       }
       soff += ks * d.s_tw + (x - slo) * d.s_ew;
     }
-    V val;
-    if (valid) {
-      val = src[soff >> vshift];
-    } else {
-      memset(&val, 0, sizeof(V));
+    V *drow = dst + size_t(row) * a.row_vecs;
+    for (uint32_t j0 = 0; j0 < a.row_vecs; j0 += 64 * kIvUnroll) {
+      V val[kIvUnroll];
+#pragma unroll
+      for (int u = 0; u < kIvUnroll; ++u) {
+        const uint32_t j = j0 + u * 64 + lane;
+        const uint32_t x = lo_in + (j << vshift);
+        memset(&val[u], 0, sizeof(V));
+        if (valid && j < a.row_vecs && x < hi_in) {
+          uint32_t ks, slo;
+          if (sb_in >= 0) {
+            ks = 0;
+#pragma unroll
+            for (int step = kMaxIv / 2; step >= 1; step >>= 1)
+              if (ks + step < k_in && uint32_t(bnd[sb_in + ks + step]) <= x) ks += step;
+            slo = uint32_t(bnd[sb_in + ks]);
+          } else {
+            ks = fd_div(x, se_in);
+            slo = ks * se_in.d;
+          }
+          val[u] = src[(soff + ks * tw_in + (x - slo) * ew_in) >> vshift];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kIvUnroll; ++u) {
+        const uint32_t j = j0 + u * 64 + lane;
+        if (j < a.row_vecs) drow[j] = val[u];
+      }
     }
-    dst[i] = val;
   }
 }
 
 template <typename V>
 hipError_t go_iv(const IvRelayoutArgs &a, hipStream_t st) {
+  if (a.rows) {
+    const int64_t want = (int64_t(a.n_rows) + 3) / 4;
+    const int grid = int(want < 8192 ? (want > 0 ? want : 1) : 8192);
+    relayout_iv_rows_kernel<V><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   const int64_t want = (int64_t(a.n_vec) + 255) / 256;
   const int grid = int(want < 8192 ? (want > 0 ? want : 1) : 8192);
   relayout_iv_kernel<V><<<grid, 256, 0, st>>>(a);

@@ -104,6 +104,23 @@ def repartition_4d(shape=(32, 128, 64, 64)) -> Workload:
         chain=[Relayout("Y", "X", "acbd", {"a": 1, "b": 1, "c": 4, "d": 2})], seed=1002)
 
 
+PACKED_ENDS = (0, 1024, 2560, 4096)  # three sequences packed into 4096 positions
+
+
+def repartition_packed(b=8, s=4096, h=4096, bounds=PACKED_ENDS, to_packed=False) -> Workload:
+    """'bsh' bf16 N(0,1): token blocks cut at the ends of packed sequences
+    ("Every Kernel Is a Join", Sec. 3.3, Example 3.10: three sequences ending
+    at 1024, 2560 and 4096) <-> four uniform token blocks."""
+    ext = {"b": b, "s": s, "h": h}
+    packed, uniform = {"s": list(bounds)}, {"s": 4}
+    src, dst = (uniform, packed) if to_packed else (packed, uniform)
+    name = "uniform_to_packed" if to_packed else "packed_to_uniform"
+    return Workload(
+        name=f"repartition_bsh_{b}x{s}x{h}_bf16_{name}", extents=ext,
+        tensors=[("X", "bsh", "normal", "bf16", 1.0, 0.0, src)],
+        chain=[Relayout("Y", "X", "bsh", dst)], seed=1004)
+
+
 def attention_chain(b=4, h=32, s=2048, d=128, nb=16, fused=False) -> Workload:
     """Attention as join-aggs.  Unfused: QK^T, row MAX, row SUM of exp,
     normalize, PV (five specs).  Fused: one spec whose aggregation merges

@@ -85,6 +85,10 @@ RELAYOUT_CASES = [
     ((7, 5, 6), "abc", dict(a=2, b=[0, 2, 5], c=3), "cab", dict(a=[0, 1, 7], b=1, c=[0, 4, 6]), "bf16"),
     # query heads blocked as intervals derived from 8 key-value heads
     ((32, 256, 128), "hsd", dict(h=[4 * m for m in range(9)]), "hsd", dict(h=2, s=2), "bf16"),
+    # long rows along the innermost letter: a wave streams each row
+    ((2, 1000, 1024), "bsh", dict(s=[0, 100, 356, 1000]), "sbh", dict(s=3, b=2), "bf16"),
+    ((300, 2048), "sh", dict(s=2, h=[0, 512, 2048]), "sh", dict(s=[0, 7, 300], h=[0, 1000, 2048]), "f32"),
+    ((64, 1001), "ab", dict(b=[0, 500, 1001]), "ab", dict(a=2, b=1), "f32"),
     # one interval per letter, and 32 intervals (the limit)
     ((5, 9), "ab", dict(a=[0, 5], b=[0, 9]), "ba", dict(a=5, b=3), "f32"),
     ((64, 40), "ab", dict(a=list(range(0, 32)) + [64]), "ab", dict(a=3, b=[0, 8, 40]), "f32"),
@@ -100,6 +104,13 @@ def test_packed_sequence_relayout_uses_vectors(ctx, capfd):
     check_relayout(ctx, (4096, 256), "sd", dict(s=1), "sd", dict(s=PACKED), "bf16")
     lines = [ln for ln in capfd.readouterr().err.splitlines() if "relayout sd -> sd: intervals" in ln]
     assert lines and all("8-element vectors" in ln for ln in lines), lines
+
+
+def test_packed_sequence_long_rows_use_row_form(ctx, capfd):
+    check_relayout(ctx, (2, 4096, 1024), "bsh", dict(s=1), "bsh", dict(s=PACKED), "bf16")
+    check_relayout(ctx, (2, 4096, 1024), "bsh", dict(s=PACKED), "bsh", dict(s=4), "bf16")
+    lines = [ln for ln in capfd.readouterr().err.splitlines() if "relayout bsh -> bsh: intervals" in ln]
+    assert lines and all("8-element vectors" in ln and ln.endswith(", rows") for ln in lines), lines
 
 
 def test_gqa_interval_heads_equal_split_heads(ctx):
