@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256) void flat_map_kernel(const FlatArgs a) {
 // tuples are taken EU at a time: the EU vectors a lane needs from them are
 // loaded together and then combined in join-list order, so the result is
 // deterministic.
-template <int V, int G, int AGG, int EU, int DT0>
+// VU: row steps loaded together (1, or 4 where a row holds at least four)
+template <int V, int G, int AGG, int EU, int DT0, int VU>
 __global__ __launch_bounds__(256) void flat_reduce_kernel(const FlatArgs a, int lpr_log2) {
   const uint32_t key = fd_div(blockIdx.x, a.div_chunks);
   const uint32_t chunk = blockIdx.x - key * uint32_t(a.chunks);
@@ -282,35 +283,46 @@ __global__ __launch_bounds__(256) void flat_reduce_kernel(const FlatArgs a, int 
           rs[u][j] = block_rsrc(a.in[j].p, (j < a.n_in) ? ent[1 + j] : 0, (j < a.n_in) ? a.in[j].block_bytes : 0);
       }
       nonempty = nonempty || maxlim > 0;
-      for (int32_t v = sub * V; v < maxlim; v += step) {
-        Raw<V> raw[EU][kMaxIn];
+      // VU steps of the row are loaded together (all EU tuples each), then
+      // combined step by step, tuple by tuple: the same order as one step
+      // at a time
+      for (int32_t v0 = sub * V; v0 < maxlim; v0 += step * VU) {
+        Raw<V> raw[VU][EU][kMaxIn];
 #pragma unroll
-        for (int u = 0; u < EU; ++u) {
+        for (int vv = 0; vv < VU; ++vv) {
+          const int32_t v = v0 + vv * step;
 #pragma unroll
-          for (int j = 0; j < kMaxIn; ++j) {
-            if (j == 0 || (j < a.n_in && a.in[j].inner)) {
-              const uint32_t e = q * uint32_t(a.in[j].row_mul) + uint32_t(v);
-              raw_load<V>(raw[u][j], rs[u][j], e, v < lim[u], j == 0 ? DT0 : a.in[j].dt, 1);
+          for (int u = 0; u < EU; ++u) {
+#pragma unroll
+            for (int j = 0; j < kMaxIn; ++j) {
+              if (j == 0 || (j < a.n_in && a.in[j].inner)) {
+                const uint32_t e = q * uint32_t(a.in[j].row_mul) + uint32_t(v);
+                raw_load<V>(raw[vv][u][j], rs[u][j], e, v < lim[u], j == 0 ? DT0 : a.in[j].dt, 1);
+              }
             }
           }
         }
 #pragma unroll
-        for (int u = 0; u < EU; ++u) {
-          float x[kMaxIn][V];
+        for (int vv = 0; vv < VU; ++vv) {
+          const int32_t v = v0 + vv * step;
 #pragma unroll
-          for (int j = 0; j < kMaxIn; ++j) {
-            if (j == 0 || (j < a.n_in && a.in[j].inner)) {
-              raw_to_f32<V>(raw[u][j], j == 0 ? DT0 : a.in[j].dt, 1, x[j]);
-            } else {
+          for (int u = 0; u < EU; ++u) {
+            float x[kMaxIn][V];
 #pragma unroll
-              for (int w = 0; w < V; ++w) x[j][w] = bc[j];
+            for (int j = 0; j < kMaxIn; ++j) {
+              if (j == 0 || (j < a.n_in && a.in[j].inner)) {
+                raw_to_f32<V>(raw[vv][u][j], j == 0 ? DT0 : a.in[j].dt, 1, x[j]);
+              } else {
+#pragma unroll
+                for (int w = 0; w < V; ++w) x[j][w] = bc[j];
+              }
             }
-          }
-          const int32_t keep = lim[u] - v;
+            const int32_t keep = lim[u] - v;
 #pragma unroll
-          for (int w = 0; w < V; ++w) {
-            const float gv = g_fn<G>(x[0][w], x[1][w], x[2][w], a.beta, a.eps);
-            if (w < keep) acc = AGG == 2 ? fmaxf(acc, gv) : acc + gv;
+            for (int w = 0; w < V; ++w) {
+              const float gv = g_fn<G>(x[0][w], x[1][w], x[2][w], a.beta, a.eps);
+              if (w < keep) acc = AGG == 2 ? fmaxf(acc, gv) : acc + gv;
+            }
           }
         }
       }
@@ -342,30 +354,38 @@ hipError_t map_go(const FlatArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int V, int G>
+template <int V, int G, int VU>
 hipError_t reduce_go(const FlatArgs &a, int lg, int agg, hipStream_t st) {
   const dim3 grid(unsigned(a.n_keys) * unsigned(a.chunks));
   if (a.in[0].dt) {
-    if (agg == 2) hipLaunchKernelGGL((flat_reduce_kernel<V, G, 2, kReduceEU, 1>), grid, dim3(256), 0, st, a, lg);
-    else hipLaunchKernelGGL((flat_reduce_kernel<V, G, 1, kReduceEU, 1>), grid, dim3(256), 0, st, a, lg);
+    if (agg == 2) hipLaunchKernelGGL((flat_reduce_kernel<V, G, 2, kReduceEU, 1, VU>), grid, dim3(256), 0, st, a, lg);
+    else hipLaunchKernelGGL((flat_reduce_kernel<V, G, 1, kReduceEU, 1, VU>), grid, dim3(256), 0, st, a, lg);
   } else {
-    if (agg == 2) hipLaunchKernelGGL((flat_reduce_kernel<V, G, 2, kReduceEU, 0>), grid, dim3(256), 0, st, a, lg);
-    else hipLaunchKernelGGL((flat_reduce_kernel<V, G, 1, kReduceEU, 0>), grid, dim3(256), 0, st, a, lg);
+    if (agg == 2) hipLaunchKernelGGL((flat_reduce_kernel<V, G, 2, kReduceEU, 0, VU>), grid, dim3(256), 0, st, a, lg);
+    else hipLaunchKernelGGL((flat_reduce_kernel<V, G, 1, kReduceEU, 0, VU>), grid, dim3(256), 0, st, a, lg);
   }
   return hipGetLastError();
+}
+
+template <int V, int G>
+hipError_t reduce_vu(const FlatArgs &a, int lg, int agg, hipStream_t st) {
+  // rows of four or more steps load four steps at once; shorter rows would
+  // only issue out-of-range loads
+  if (a.e_red >= 4 * (V << lg)) return reduce_go<V, G, 4>(a, lg, agg, st);
+  return reduce_go<V, G, 1>(a, lg, agg, st);
 }
 
 template <int V>
 hipError_t reduce_g(const FlatArgs &a, int lg, int g, int agg, hipStream_t st) {
   switch (g) {
-    case 0: return reduce_go<V, 0>(a, lg, agg, st);
-    case 1: return reduce_go<V, 1>(a, lg, agg, st);
-    case 2: return reduce_go<V, 2>(a, lg, agg, st);
-    case 3: return reduce_go<V, 3>(a, lg, agg, st);
-    case 4: return reduce_go<V, 4>(a, lg, agg, st);
-    case 5: return reduce_go<V, 5>(a, lg, agg, st);
-    case 6: return reduce_go<V, 6>(a, lg, agg, st);
-    case 7: return reduce_go<V, 7>(a, lg, agg, st);
+    case 0: return reduce_vu<V, 0>(a, lg, agg, st);
+    case 1: return reduce_vu<V, 1>(a, lg, agg, st);
+    case 2: return reduce_vu<V, 2>(a, lg, agg, st);
+    case 3: return reduce_vu<V, 3>(a, lg, agg, st);
+    case 4: return reduce_vu<V, 4>(a, lg, agg, st);
+    case 5: return reduce_vu<V, 5>(a, lg, agg, st);
+    case 6: return reduce_vu<V, 6>(a, lg, agg, st);
+    case 7: return reduce_vu<V, 7>(a, lg, agg, st);
   }
   return hipErrorInvalidValue;
 }
