@@ -678,14 +678,20 @@ int oracle_relational(const char *spec, int g, int agg, double alpha, double bet
  * letters in Q and K only (contracted into the scores), E letters in V and
  * the output only.  score(s, t) = alpha * sum_D Q K; t > s is dropped under
  * a causal pair (s, t).
+ *
+ * Grouped-query attention (Sec. 3.3, Example 3.10: query heads 4m..4m+3 use
+ * key-value head m): further letters in Q and the output only are query-
+ * group letters G, "X G s D, X t D, X t E -> X G s E"; the rows of one group
+ * share K and V.  With a causal pair s is its first letter; without one, the
+ * last such letter of the spec (the choice changes nothing then).
  */
 typedef struct {
-  char x[27], d[27], e[27];
-  int nx, nd, ne;
+  char x[27], d[27], e[27], g[27];
+  int nx, nd, ne, ng;
   int s, t; /* letter indices 0..25 */
 } oroles;
 
-static int attention_roles(const ospec *p, oroles *r) {
+static int attention_roles(const ospec *p, int causal_s, oroles *r) {
   memset(r, 0, sizeof(*r));
   r->s = r->t = -1;
   if (p->n_in != 3) return OR_UNSUPPORTED;
@@ -694,13 +700,20 @@ static int attention_roles(const ospec *p, oroles *r) {
     int q = strchr(p->in[0], c) != NULL, k = strchr(p->in[1], c) != NULL;
     int v = strchr(p->in[2], c) != NULL, o = strchr(p->out, c) != NULL;
     if (q && k && v && o) r->x[r->nx++] = c;
-    else if (q && !k && !v && o) { if (r->s >= 0) return OR_UNSUPPORTED; r->s = c - 'a'; }
+    else if (q && !k && !v && o) r->g[r->ng++] = c; /* s or a query-group letter */
     else if (!q && k && v && !o) { if (r->t >= 0) return OR_UNSUPPORTED; r->t = c - 'a'; }
     else if (q && k && !v && !o) r->d[r->nd++] = c;
     else if (!q && !k && v && o) r->e[r->ne++] = c;
     else return OR_UNSUPPORTED;
   }
-  if (r->s < 0 || r->t < 0 || r->nd == 0 || r->ne == 0) return OR_UNSUPPORTED;
+  if (r->ng == 0) return OR_UNSUPPORTED;
+  if (causal_s >= 0) {
+    if (!memchr(r->g, 'a' + causal_s, (size_t)r->ng)) return OR_BAD_SPEC;
+    r->s = causal_s;
+  } else {
+    r->s = r->g[r->ng - 1] - 'a';
+  }
+  if (r->t < 0 || r->nd == 0 || r->ne == 0) return OR_UNSUPPORTED;
   return OR_OK;
 }
 
@@ -740,7 +753,7 @@ int oracle_attention_dense(const char *spec, double alpha, int causal_s, int cau
   oroles r;
   int rc = parse_spec(spec, &p);
   if (rc) return rc;
-  if ((rc = attention_roles(&p, &r))) return rc;
+  if ((rc = attention_roles(&p, causal_s, &r))) return rc;
   const int causal = causal_s >= 0;
   if (causal && (causal_s != r.s || causal_t != r.t)) return OR_BAD_SPEC;
   int64_t out_total = 1;
@@ -801,7 +814,7 @@ int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s,
   oroles r;
   int rc = parse_spec(spec, &p);
   if (rc) return rc;
-  if ((rc = attention_roles(&p, &r))) return rc;
+  if ((rc = attention_roles(&p, causal_s, &r))) return rc;
   const int causal = causal_s >= 0;
   if (causal && (causal_s != r.s || causal_t != r.t)) return OR_BAD_SPEC;
   for (int a = 0; a < r.nd; ++a)

@@ -192,3 +192,49 @@ def test_rejects_malformed_attention():
         O.attention_dense("bsd,btd,bse->bse", [Q, K, rand((2, 4, 3), 4)], ext)
     with pytest.raises(O.OracleError):  # causal letters that are not (s, t)
         O.attention_dense(SPEC, [Q, K, V], ext, causal=("t", "s"))
+
+
+# Grouped-query attention ("Every Kernel Is a Join", Sec. 3.3, Example 3.10):
+# query heads 4m..4m+3 use key-value head m.  Written with a query-group
+# letter r that appears in Q and the output only: "grsd,gtd,gte->grse".
+GQA = "grsd,gtd,gte->grse"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_dense_equals_attention_with_repeated_kv_heads(causal):
+    g, r, S, D, E = 3, 4, 9, 8, 5
+    Q, K, V = rand((g, r, S, D), 41), rand((g, S, D), 42), rand((g, S, E), 43)
+    ext = dict(g=g, r=r, s=S, t=S, d=D, e=E)
+    got = O.attention_dense(GQA, [Q, K, V], ext, alpha=0.4, causal=("s", "t") if causal else None)
+    # torch: flatten the query heads, repeat each kv head for its group
+    Kr, Vr = np.repeat(K, r, axis=0), np.repeat(V, r, axis=0)
+    want = torch_attention(Q.reshape(g * r, S, D), Kr, Vr, 0.4, causal).reshape(g, r, S, E)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_relational_by_kv_head_equals_dense(causal):
+    """Blocking the kv-head letter g into unit intervals gives one joined
+    (Q, K, V) combination per kv head and s/t block pair; the query group
+    follows its kv head (Example 3.10)."""
+    g, r, S, D, E = 4, 2, 10, 4, 3
+    Q, K, V = rand((g, r, S, D), 44), rand((g, S, D), 45), rand((g, S, E), 46)
+    ext = dict(g=g, r=r, s=S, t=S, d=D, e=E)
+    blk = dict(g=4, r=1, s=3, t=3)
+    c = ("s", "t") if causal else None
+    want = O.attention_dense(GQA, [Q, K, V], ext, alpha=0.7, causal=c)
+    rels = [O.to_relation(x, lt, ext, blk) for x, lt in zip((Q, K, V), ("grsd", "gtd", "gte"))]
+    got, present = O.attention_relational(GQA, rels, ext, blk, alpha=0.7, causal=c)
+    assert present.all()
+    np.testing.assert_allclose(O.from_relation(got, "grse", ext, blk), want, rtol=1e-12, atol=1e-13)
+    # the query-group letter written innermost-but-one or outermost changes nothing
+    Qt = np.ascontiguousarray(Q.transpose(1, 0, 2, 3))
+    got2 = O.attention_dense("rgsd,gtd,gte->rgse", [Qt, K, V], ext, alpha=0.7, causal=c)
+    np.testing.assert_allclose(got2.transpose(1, 0, 2, 3), want, rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_causal_letter_must_be_a_query_letter():
+    ext = dict(g=2, r=2, s=4, t=4, d=3, e=3)
+    Q, K, V = rand((2, 2, 4, 3), 47), rand((2, 4, 3), 48), rand((2, 4, 3), 49)
+    with pytest.raises(O.OracleError):
+        O.attention_dense(GQA, [Q, K, V], ext, causal=("g", "t"))
