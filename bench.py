@@ -232,7 +232,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama",
-                    choices=["llama", "llama_chain", "attention", "attention_chain", "multi_index", "matmul"],
+                    choices=["llama", "llama_chain", "attention", "attention_chain", "attention_gqa", "multi_index",
+                             "matmul"],
                     help="llama / attention: fused attention; *_chain: the five-spec attention chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repartition", action="store_true")
@@ -250,6 +251,7 @@ def main():
     ctx = jagg.Context(0, stream)
     w = {"llama": lambda: I.llama_block(fused_attention=True), "llama_chain": I.llama_block,
          "attention": lambda: I.attention_chain(fused=True), "attention_chain": I.attention_chain,
+         "attention_gqa": I.attention_gqa,
          "multi_index": I.multi_index, "matmul": I.matmul_256}[args.workload]()
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     dense = I.generate(w)

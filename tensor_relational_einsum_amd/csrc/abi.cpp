@@ -1086,25 +1086,42 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
                            int &d) {
   memset(&a, 0, sizeof(a));
   const Spec &p = b.p;
-  std::string X;
+  // X: letters of every operand; G: letters of Q and the output only, i.e.
+  // s and any query-group letters of grouped-query attention ("Every Kernel
+  // Is a Join", Example 3.10: query heads 4m..4m+3 share key-value head m),
+  // which run as batch letters whose K and V strides are 0
+  std::string X, G;
   char s = 0, t = 0, dl = 0, el = 0;
   for (char c : p.order) {
     const bool q = p.in[0].find(c) != std::string::npos, k = p.in[1].find(c) != std::string::npos;
     const bool v = p.in[2].find(c) != std::string::npos, o = p.out.find(c) != std::string::npos;
     if (q && k && v && o) X += c;
-    else if (q && !k && !v && o && !s) s = c;
+    else if (q && !k && !v && o) G += c;
     else if (!q && k && v && !o && !t) t = c;
     else if (q && k && !v && !o && !dl) dl = c;
     else if (!q && !k && v && o && !el) el = c;
-    else return fail(ctx, JAGG_E_UNSUPPORTED, "attention letter '%c' has no role of X s D, X t D, X t E -> X s E", c);
+    else return fail(ctx, JAGG_E_UNSUPPORTED, "attention letter '%c' has no role of X G s D, X t D, X t E -> X G s E", c);
   }
-  if (!s || !t || !dl || !el) return fail(ctx, JAGG_E_UNSUPPORTED, "attention needs one s, t, D and E letter");
-  if (sp->causal_s && (sp->causal_s != s || sp->causal_t != t))
-    return fail(ctx, JAGG_E_UNSUPPORTED, "the causal pair of attention must be (s, t) = (%c, %c)", s, t);
+  if (G.empty() || !t || !dl || !el) return fail(ctx, JAGG_E_UNSUPPORTED, "attention needs one s, t, D and E letter");
   for (int j = 0; j < 3; ++j)
     if (ins[j]->dt != JAGG_BF16) return fail(ctx, JAGG_E_UNSUPPORTED, "attention inputs must be bfloat16");
   const jagg_relation &Q = *ins[0], &K = *ins[1], &V = *ins[2], &O = *out;
   auto pos = [&](int j, char c) { return int(j < 3 ? p.in[j].find(c) : p.out.find(c)); };
+  if (sp->causal_s) {
+    if (G.find(sp->causal_s) == std::string::npos || sp->causal_t != t)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "the causal pair of attention must be (a query letter, %c)", t);
+    s = sp->causal_s;
+  } else {  // the row letter: the innermost of G in Q
+    for (char c : G)
+      if (!s || inblock_s(Q, pos(0, c)) < inblock_s(Q, pos(0, s))) s = c;
+  }
+  const std::string grp = [&] {
+    std::string r;
+    for (char c : G)
+      if (c != s) r += c;
+    return r;
+  }();
+  X += grp;
   if (pos(0, dl) != Q.r - 1 || pos(1, dl) != K.r - 1 || pos(2, el) != V.r - 1 || pos(3, el) != O.r - 1)
     return fail(ctx, JAGG_E_UNSUPPORTED, "D must be innermost in Q and K, E innermost in V and the output");
   if (b.L.k[dl - 'a'] != 1 || b.L.k[el - 'a'] != 1)
@@ -1131,9 +1148,10 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
       if (X.find(c) == std::string::npos) continue;
       const int64_t e = O.e[pos(3, c)];
       a.xdiv[i] = make_fastdiv(uint32_t(e));
+      const bool shared_kv = grp.find(c) != std::string::npos;  // a query-group letter
       a.xQ[i] = inblock_s(Q, pos(0, c));
-      a.xK[i] = inblock_s(K, pos(1, c));
-      a.xV[i] = inblock_s(V, pos(2, c));
+      a.xK[i] = shared_kv ? 0 : inblock_s(K, pos(1, c));
+      a.xV[i] = shared_kv ? 0 : inblock_s(V, pos(2, c));
       a.xO[i] = inblock_s(O, pos(3, c));
       if (a.xQ[i] % 8 || a.xK[i] % 8 || a.xV[i] % 8 || a.xO[i] % 8)
         return fail(ctx, JAGG_E_UNSUPPORTED, "attention batch strides must be multiples of 8 elements");

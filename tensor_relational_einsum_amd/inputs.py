@@ -145,6 +145,22 @@ def attention_chain(b=4, h=32, s=2048, d=128, nb=16, fused=False) -> Workload:
                     chain=chain, seed=1003)
 
 
+def attention_gqa(b=4, kv=8, group=4, s=2048, d=128, nb=16) -> Workload:
+    """Causal grouped-query attention as one join-agg ("Every Kernel Is a
+    Join", Example 3.10: 32 query heads over 8 key-value heads, query heads
+    4m..4m+3 on kv head m).  Q 'bgrsd' (g kv head, r member of its group),
+    K and V 'bgtd'; the kv heads in unit intervals, s and t in `nb` blocks;
+    scale 1/sqrt(d); bf16 N(0,1)."""
+    ext = {"b": b, "g": kv, "r": group, "s": s, "t": s, "d": d, "e": d}
+    blk = {"b": 1, "g": kv, "r": 1, "s": nb, "t": nb, "d": 1, "e": 1}
+    tens = [("Q", "bgrsd", "normal", "bf16", 1.0, 0.0, blk), ("K", "bgtd", "normal", "bf16", 1.0, 0.0, blk),
+            ("V", "bgtd", "normal", "bf16", 1.0, 0.0, blk)]
+    chain = [Step("O", "bgrsd,bgtd,bgte->bgrse", ["Q", "K", "V"], "attention", "softmax", "bf16", blk,
+                  alpha=1.0 / math.sqrt(d), causal=("s", "t"))]
+    return Workload(name=f"attention_gqa_causal_b{b}_kv{kv}x{group}_s{s}_d{d}_bf16_st{nb}", extents=ext,
+                    tensors=tens, chain=chain, seed=1005)
+
+
 def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8,
                 fused_attention=False) -> Workload:
     """LLaMA-7B-shaped decoder block, every op a join-agg spec.

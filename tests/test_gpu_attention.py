@@ -67,6 +67,16 @@ CASES = [
      ("s", "t"), "bf16"),
     # more keys than queries
     ("hsd,htd,hte->hse", dict(h=2, s=128, t=384, d=64, e=64), dict(h=1, s=1, t=3, d=1, e=1), None, "f32"),
+    # grouped-query attention ("Every Kernel Is a Join", Example 3.10): 32 query
+    # heads over 8 key-value heads, the kv heads in unit intervals; the query
+    # group letter r appears in Q and the output only
+    ("grsd,gtd,gte->grse", dict(g=8, r=4, s=512, t=512, d=128, e=128), dict(g=8, r=1, s=2, t=2, d=1, e=1),
+     ("s", "t"), "bf16"),
+    ("grsd,gtd,gte->grse", dict(g=2, r=3, s=200, t=200, d=64, e=64), dict(g=2, r=3, s=2, t=2, d=1, e=1), None,
+     "f32"),
+    # the projection layout with the group inside: s is the row letter, r a batch letter
+    ("bsgrd,btgd,btge->bsgre", dict(b=2, s=256, t=256, g=2, r=4, d=128, e=128),
+     dict(b=1, s=2, t=2, g=2, r=2, d=1, e=1), ("s", "t"), "bf16"),
 ]
 
 
@@ -105,3 +115,9 @@ def test_attention_rejects_unsupported(ctx):
         jagg.EinsumCall(ctx, "hsd,htd,hte->hse", rels, blk, g="attention", agg="softmax").run()
     with pytest.raises(jagg.JaggError):  # the triple aggregation pairs only with g = attention
         jagg.EinsumCall(ctx, "hsd,htd,hte->hse", rels, blk, g="mul", agg="softmax").run()
+    ext = dict(g=2, r=2, s=64, t=64, d=64, e=64)
+    blk = dict(g=1, r=1, s=1, t=1, d=1, e=1)
+    xs = [I.draw(g, [ext[c] for c in lt], "normal", "bf16") for g, lt in zip(gens, ("grsd", "gtd", "gte"))]
+    rels = [jagg.from_dense(ctx, x.to("cuda"), lt, blk) for x, lt in zip(xs, ("grsd", "gtd", "gte"))]
+    with pytest.raises(jagg.JaggError):  # a causal pair whose first letter is a kv letter
+        jagg.EinsumCall(ctx, "grsd,gtd,gte->grse", rels, blk, g="attention", agg="softmax", causal=("g", "t")).run()
