@@ -448,8 +448,8 @@ static int cmp_combo(const void *a, const void *b) {
  * keeping each combination whose key intervals agree on every letter the
  * inputs share (and, with causal letters, that holds some t <= s).
  * Returns a malloc'd array of combos sorted in canonical order. */
-static int join(const ospec *p, const orel *in, const orel *out, int causal_s, int causal_t, combo **res,
-                int64_t *n_res) {
+static int join(const ospec *p, const orel *in, const orel *out, int causal_s, int causal_t, int seg_s, int seg_t,
+                combo **res, int64_t *n_res) {
   int64_t total = 1;
   for (int j = 0; j < p->n_in; ++j) total *= in[j].n_tuples;
   combo *list = malloc(sizeof(combo) * (size_t)(total ? total : 1));
@@ -475,6 +475,8 @@ static int join(const ospec *p, const orel *in, const orel *out, int causal_s, i
     }
     if (!keep) continue;
     if (causal_s >= 0 && lo[causal_t] > hi[causal_s] - 1) continue;
+    /* segment pair: s and t must lie in the same interval */
+    if (seg_s >= 0 && (lo[seg_s] != lo[seg_t] || hi[seg_s] != hi[seg_t])) continue;
     /* output key: the intervals of the output letters, as a tuple id */
     int64_t out_id = 0;
     for (int a = 0; a < out->r; ++a) {
@@ -524,7 +526,7 @@ int oracle_join_list_iv(const char *spec, const int64_t *ext26, const int32_t *n
   if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, causal_s, causal_t, &c, &n))) return rc;
+  if ((rc = join(&p, in, &out, causal_s, causal_t, -1, -1, &c, &n))) return rc;
   *n_entries = n;
   if (list) {
     if (cap < n) { free(c); return OR_BAD_SHAPE; }
@@ -556,7 +558,7 @@ int oracle_relational_iv(const char *spec, int g, int agg, double alpha, double 
   if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, causal_s, causal_t, &c, &n))) return rc;
+  if ((rc = join(&p, in, &out, causal_s, causal_t, -1, -1, &c, &n))) return rc;
 
   memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
   if (present) memset(present, 0, (size_t)out.n_tuples);
@@ -746,9 +748,19 @@ static double att_score(const ospec *p, const oroles *r, const int64_t *ext26, c
  * over the t that are kept (all, or t <= s under a causal pair, which must
  * name the s and t roles); 0 when none is.  Outputs at the row-major flat
  * indices in `idx` (all when idx == NULL). */
-int oracle_attention_dense(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
-                           const double *Q, const double *K, const double *V, const int64_t *idx, int64_t n_out,
-                           double *out) {
+/* the segment (interval of seg_bnd) holding position x */
+static int64_t segment_of(const int64_t *seg_bnd, int seg_k, int64_t x) {
+  int64_t q = 0;
+  while (q + 1 < seg_k && seg_bnd[q + 1] <= x) ++q;
+  return q;
+}
+
+/* Packed sequences (Sec. 3.3, Example 3.10): with a segment pair (s, t) and
+ * bounds seg_bnd[0..seg_k] (0 = b_0 < ... < b_k = extent of s and t), a
+ * query position attends only to key positions of its own segment. */
+int oracle_attention_dense_seg(const char *spec, double alpha, int causal_s, int causal_t, int seg_s, int seg_t,
+                               const int64_t *seg_bnd, int seg_k, const int64_t *ext26, const double *Q,
+                               const double *K, const double *V, const int64_t *idx, int64_t n_out, double *out) {
   ospec p;
   oroles r;
   int rc = parse_spec(spec, &p);
@@ -756,6 +768,14 @@ int oracle_attention_dense(const char *spec, double alpha, int causal_s, int cau
   if ((rc = attention_roles(&p, causal_s, &r))) return rc;
   const int causal = causal_s >= 0;
   if (causal && (causal_s != r.s || causal_t != r.t)) return OR_BAD_SPEC;
+  const int seg = seg_s >= 0;
+  if ((seg_s >= 0) != (seg_t >= 0)) return OR_BAD_SPEC;
+  if (seg) {
+    if (seg_s != r.s || seg_t != r.t || ext26[r.s] != ext26[r.t] || seg_k < 1 || !seg_bnd) return OR_BAD_SPEC;
+    if (seg_bnd[0] != 0 || seg_bnd[seg_k] != ext26[r.s]) return OR_BAD_BLOCKING;
+    for (int q = 0; q < seg_k; ++q)
+      if (seg_bnd[q + 1] <= seg_bnd[q]) return OR_BAD_BLOCKING;
+  }
   int64_t out_total = 1;
   for (int a = 0; a < p.out_len; ++a) out_total *= ext26[p.out[a] - 'a'];
   if (!idx) n_out = out_total;
@@ -771,9 +791,11 @@ int oracle_attention_dense(const char *spec, double alpha, int causal_s, int cau
       rem /= ext26[L];
     }
     const int64_t s = x[r.s];
+    const int64_t sg = seg ? segment_of(seg_bnd, seg_k, s) : 0;
     double m = -INFINITY;
     for (int64_t t = 0; t < T; ++t) {
       if (causal && t > s) continue;
+      if (seg && segment_of(seg_bnd, seg_k, t) != sg) continue;
       x[r.t] = t;
       double sc = att_score(&p, &r, ext26, Q, K, x, alpha);
       if (sc > m) m = sc;
@@ -781,6 +803,7 @@ int oracle_attention_dense(const char *spec, double alpha, int causal_s, int cau
     double l = 0.0, acc = 0.0;
     for (int64_t t = 0; t < T; ++t) {
       if (causal && t > s) continue;
+      if (seg && segment_of(seg_bnd, seg_k, t) != sg) continue;
       x[r.t] = t;
       double w = exp(att_score(&p, &r, ext26, Q, K, x, alpha) - m);
       l += w;
@@ -789,6 +812,13 @@ int oracle_attention_dense(const char *spec, double alpha, int causal_s, int cau
     out[q] = l > 0.0 ? acc / l : 0.0;
   }
   return OR_OK;
+}
+
+int oracle_attention_dense(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
+                           const double *Q, const double *K, const double *V, const int64_t *idx, int64_t n_out,
+                           double *out) {
+  return oracle_attention_dense_seg(spec, alpha, causal_s, causal_t, -1, -1, NULL, 0, ext26, Q, K, V, idx, n_out,
+                                    out);
 }
 
 /* the merge of two triples (the aggregation of the attention join-agg) */
@@ -807,9 +837,9 @@ void oracle_softmax_merge(double m1, double l1, double a1, double m2, double l2,
  * of equal output key in canonical order (step 2), then write a / l into the
  * output relation (step 3).  Inputs are relation buffers of doubles; the D
  * letters must be one block each (a triple needs whole scores). */
-int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s, int causal_t,
-                                   const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
-                                   const double *const *in_rel, double *out_rel, uint8_t *present) {
+int oracle_attention_relational_seg(const char *spec, double alpha, int causal_s, int causal_t, int seg_s,
+                                    int seg_t, const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                                    const double *const *in_rel, double *out_rel, uint8_t *present) {
   ospec p;
   oroles r;
   int rc = parse_spec(spec, &p);
@@ -823,7 +853,9 @@ int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s,
   if ((rc = build_rels(&p, ext26, nblk26, bnd26, in, &out))) return rc;
   combo *c;
   int64_t n;
-  if ((rc = join(&p, in, &out, causal ? r.s : -1, causal ? r.t : -1, &c, &n))) return rc;
+  if ((seg_s >= 0) != (seg_t >= 0)) return OR_BAD_SPEC;
+  if (seg_s >= 0 && (seg_s != r.s || seg_t != r.t)) return OR_BAD_SPEC;
+  if ((rc = join(&p, in, &out, causal ? r.s : -1, causal ? r.t : -1, seg_s, seg_t, &c, &n))) return rc;
   memset(out_rel, 0, sizeof(double) * (size_t)(out.n_tuples * out.block_elems));
   if (present) memset(present, 0, (size_t)out.n_tuples);
   double *tm = malloc(sizeof(double) * (size_t)out.block_elems * 3);
@@ -906,6 +938,12 @@ int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s,
   free(tm);
   free(c);
   return OR_OK;
+}
+int oracle_attention_relational_iv(const char *spec, double alpha, int causal_s, int causal_t,
+                                   const int64_t *ext26, const int32_t *nblk26, const int64_t *bnd26,
+                                   const double *const *in_rel, double *out_rel, uint8_t *present) {
+  return oracle_attention_relational_seg(spec, alpha, causal_s, causal_t, -1, -1, ext26, nblk26, bnd26, in_rel,
+                                         out_rel, present);
 }
 int oracle_attention_relational(const char *spec, double alpha, int causal_s, int causal_t, const int64_t *ext26,
                                 const int32_t *nblk26, const double *const *in_rel, double *out_rel,

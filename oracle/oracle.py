@@ -79,9 +79,13 @@ def _load():
         lib.oracle_attention_dense.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int, i64p,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i64p,
                                                ctypes.c_int64, ctypes.c_void_p]
-        lib.oracle_attention_relational_iv.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int,
-                                                       ctypes.c_int, i64p, i32p, i64p, dpp, ctypes.c_void_p,
-                                                       ctypes.c_void_p]
+        lib.oracle_attention_relational_seg.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int,
+                                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, i64p, i32p, i64p,
+                                                        dpp, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_attention_dense_seg.argtypes = [ctypes.c_char_p, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, i64p, ctypes.c_int, i64p,
+                                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, i64p,
+                                                   ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_softmax_merge.argtypes = [ctypes.c_double] * 6 + [ctypes.c_void_p]
         lib.oracle_softmax_merge.restype = None
         lib.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
@@ -283,9 +287,11 @@ def relational(spec, rel_inputs, extents, blockings, g="mul", agg="sum", alpha=1
     return out, present
 
 
-def attention_dense(spec, inputs, extents, alpha=1.0, causal=None, sample=None):
+def attention_dense(spec, inputs, extents, alpha=1.0, causal=None, sample=None, segments=None):
     """Attention by its definition: out[X,s,E] = sum_t softmax_t(alpha sum_D Q K) V
-    (unrounded float64); roles as in oracle.c.  ``sample``: flat output indices."""
+    (unrounded float64); roles as in oracle.c.  ``sample``: flat output indices.
+    ``segments``: (s, t, bounds) -- packed sequences: s attends only to the
+    t of its own interval of ``bounds``."""
     lib = _load()
     ins, out_letters = _parse(spec)
     if len(ins) != 3:
@@ -306,15 +312,23 @@ def attention_dense(spec, inputs, extents, alpha=1.0, causal=None, sample=None):
         idx = np.ascontiguousarray(np.asarray(sample, dtype=np.int64))
         out = np.zeros(idx.shape[0], dtype=np.float64)
         idx_p, n = _i64p(idx), idx.shape[0]
-    rc = lib.oracle_attention_dense(spec.encode(), alpha, cs, ct, _i64p(ext), arrs[0].ctypes.data,
-                                    arrs[1].ctypes.data, arrs[2].ctypes.data, idx_p, n, out.ctypes.data)
+    ss, st, sb, sk = -1, -1, np.zeros(1, dtype=np.int64), 0
+    if segments is not None:
+        ss, st = ord(segments[0]) - 97, ord(segments[1]) - 97
+        sb = np.ascontiguousarray(np.asarray(segments[2], dtype=np.int64))
+        sk = sb.size - 1
+    rc = lib.oracle_attention_dense_seg(spec.encode(), alpha, cs, ct, ss, st, _i64p(sb), sk, _i64p(ext),
+                                        arrs[0].ctypes.data, arrs[1].ctypes.data, arrs[2].ctypes.data, idx_p, n,
+                                        out.ctypes.data)
     _check(rc, "oracle_attention_dense")
     return out
 
 
-def attention_relational(spec, rel_inputs, extents, blockings, alpha=1.0, causal=None):
+def attention_relational(spec, rel_inputs, extents, blockings, alpha=1.0, causal=None, segment=None):
     """Attention as one join-agg over relation buffers: per joined tuple the
     online-softmax triple, merged per output key, recomposed as a / l.
+    ``segment``: (s, t) -- the join keeps only combinations whose s and t
+    intervals coincide (packed sequences blocked at their ends).
     Returns (out_relation float64 unrounded, present uint8 per output tuple)."""
     lib = _load()
     ins, out_letters = _parse(spec)
@@ -330,8 +344,9 @@ def attention_relational(spec, rel_inputs, extents, blockings, alpha=1.0, causal
     present = np.zeros(n_tuples, dtype=np.uint8)
     ext, nb, bd = _ext26(extents), _nblk26(blockings), _bnd26(blockings)
     cs, ct = _causal(causal)
-    rc = lib.oracle_attention_relational_iv(spec.encode(), alpha, cs, ct, _i64p(ext), _i32p(nb), _i64p(bd), ptrs,
-                                            out.ctypes.data, present.ctypes.data)
+    ss, st = _causal(segment)
+    rc = lib.oracle_attention_relational_seg(spec.encode(), alpha, cs, ct, ss, st, _i64p(ext), _i32p(nb), _i64p(bd),
+                                             ptrs, out.ctypes.data, present.ctypes.data)
     _check(rc, "oracle_attention_relational")
     return out, present
 

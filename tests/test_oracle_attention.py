@@ -238,3 +238,62 @@ def test_gqa_causal_letter_must_be_a_query_letter():
     Q, K, V = rand((2, 2, 4, 3), 47), rand((2, 4, 3), 48), rand((2, 4, 3), 49)
     with pytest.raises(O.OracleError):
         O.attention_dense(GQA, [Q, K, V], ext, causal=("g", "t"))
+
+
+# Packed sequences ("Every Kernel Is a Join", Sec. 3.3, Example 3.10): three
+# sequences packed end to end; attention never crosses a sequence boundary,
+# so the sequence index is cut only at the sequence ends, and the join pairs
+# each query block with the key block of the same sequence.
+PACK = [0, 5, 7, 16]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_segments_dense_equals_attention_per_sequence(causal):
+    B, S, D, E = 2, PACK[-1], 6, 4
+    Q, K, V = rand((B, S, D), 51), rand((B, S, D), 52), rand((B, S, E), 53)
+    ext = dict(b=B, s=S, t=S, d=D, e=E)
+    got = O.attention_dense(SPEC, [Q, K, V], ext, alpha=0.5, causal=("s", "t") if causal else None,
+                            segments=("s", "t", PACK))
+    for lo, hi in zip(PACK, PACK[1:]):
+        want = torch_attention(Q[:, lo:hi], K[:, lo:hi], V[:, lo:hi], 0.5, causal)
+        np.testing.assert_allclose(got[:, lo:hi], want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_segments_relational_on_sequence_intervals_equals_dense(causal):
+    B, S, D, E = 2, PACK[-1], 4, 3
+    Q, K, V = rand((B, S, D), 54), rand((B, S, D), 55), rand((B, S, E), 56)
+    ext = dict(b=B, s=S, t=S, d=D, e=E)
+    blk = dict(b=2, s=PACK, t=PACK)
+    c = ("s", "t") if causal else None
+    want = O.attention_dense(SPEC, [Q, K, V], ext, alpha=0.3, causal=c, segments=("s", "t", PACK))
+    rels = [O.to_relation(x, lt, ext, blk) for x, lt in zip((Q, K, V), ("bsd", "btd", "bte"))]
+    got, present = O.attention_relational(SPEC, rels, ext, blk, alpha=0.3, causal=c, segment=("s", "t"))
+    assert present.all()
+    np.testing.assert_allclose(O.from_relation(got, "bse", ext, blk), want, rtol=1e-12, atol=1e-13)
+    # padding rows of the short sequences stay +0
+    pad = O.to_relation(np.ones((B, S, E)), "bse", ext, blk) == 0
+    assert pad.any() and np.all(got[pad] == 0.0)
+
+
+def test_segments_on_uniform_blocks_are_block_local_attention():
+    B, S, D, E = 1, 12, 4, 4
+    Q, K, V = rand((B, S, D), 57), rand((B, S, D), 58), rand((B, S, E), 59)
+    ext = dict(b=B, s=S, t=S, d=D, e=E)
+    blk = dict(s=3, t=3)
+    rels = [O.to_relation(x, lt, ext, blk) for x, lt in zip((Q, K, V), ("bsd", "btd", "bte"))]
+    got, _ = O.attention_relational(SPEC, rels, ext, blk, alpha=0.6, segment=("s", "t"))
+    want = O.attention_dense(SPEC, [Q, K, V], ext, alpha=0.6, segments=("s", "t", [0, 4, 8, 12]))
+    np.testing.assert_allclose(O.from_relation(got, "bse", ext, blk), want, rtol=1e-12, atol=1e-13)
+    for lo in (0, 4, 8):
+        np.testing.assert_allclose(want[:, lo:lo + 4], torch_attention(Q[:, lo:lo + 4], K[:, lo:lo + 4],
+                                                                      V[:, lo:lo + 4], 0.6, False), rtol=1e-12)
+
+
+def test_segments_reject_other_letters_and_bad_bounds():
+    ext = dict(b=1, s=6, t=6, d=3, e=3)
+    Q, K, V = rand((1, 6, 3), 60), rand((1, 6, 3), 61), rand((1, 6, 3), 62)
+    with pytest.raises(O.OracleError):  # the pair must be (s, t)
+        O.attention_dense(SPEC, [Q, K, V], ext, segments=("b", "t", [0, 1]))
+    with pytest.raises(O.OracleError):  # bounds must end at the extent
+        O.attention_dense(SPEC, [Q, K, V], ext, segments=("s", "t", [0, 2, 5]))
