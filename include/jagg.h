@@ -105,7 +105,17 @@ typedef enum {
  * combination whose t-block starts after its s-block ends, terms with t > s
  * are left out of the aggregation, and an output element whose own t > s is
  * written as 0.  A causal pair needs s and t of equal extent and block
- * count. */
+ * count.
+ * seg_s / seg_t: 0 for none, else a segment pair (s, t): only elements whose
+ * s and t lie in the same block take part, and the join keeps only the
+ * combinations whose s and t blocks coincide.  "Every Kernel Is a Join",
+ * Sec. 3.3, Example 3.10: three sequences packed into one index, attention
+ * never crossing a sequence end, the index cut only at those ends -- with s
+ * and t blocked by the sequences' bounds (jagg_relation_create_iv) each
+ * query attends to its own sequence only; on uniform blocks it is
+ * block-local attention.  Taken by g = JAGG_G_ATTENTION only, with (s, t)
+ * its query and key letters, blocked alike (same bounds, or the same count
+ * of uniform blocks); a causal pair, if any, must be the same (s, t). */
 typedef struct {
   const char *einsum;
   jagg_g g;
@@ -116,6 +126,8 @@ typedef struct {
   float eps;   /* parameter of JAGG_G_RMS_SCALE */
   char causal_s;
   char causal_t;
+  char seg_s;
+  char seg_t;
 } jagg_spec;
 
 typedef struct jagg_ctx jagg_ctx;
@@ -165,8 +177,11 @@ jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64
  * positions as well, so the spec's value must be +0 wherever an interval
  * letter sits in padding: g = MUL, IDENT, SQUARE or SILU_MUL; ADD only when
  * every input holds every interval letter; RMS_SCALE only when its first
- * input does; MAX only over uniformly blocked letters; no ATTENTION and no
- * causal pair on interval letters (JAGG_E_UNSUPPORTED otherwise). */
+ * input does; MAX only over uniformly blocked letters; a causal pair on
+ * interval letters only with attention under the same segment pair.
+ * ATTENTION takes interval blocking on its (s, t) letters under a segment
+ * pair (packed sequences; see jagg_spec), masking each block by its own
+ * interval's length (JAGG_E_UNSUPPORTED otherwise). */
 jagg_status jagg_relation_bytes_iv(const char *letters, const int64_t *extents, const int32_t *nblocks,
                                    const int64_t *const *bounds, jagg_dtype dtype, size_t *bytes);
 jagg_status jagg_relation_create_iv(jagg_ctx *ctx, const char *letters, const int64_t *extents,

@@ -205,6 +205,16 @@ jagg_status check_spec(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p) {
     if (p.out.find(sp->causal_s) == std::string::npos)
       return fail(ctx, JAGG_E_UNSUPPORTED, "causal letter s must be an output letter");
   }
+  if ((sp->seg_s != 0) != (sp->seg_t != 0)) return fail(ctx, JAGG_E_INVALID, "a segment pair needs both letters");
+  if (sp->seg_s) {
+    if (sp->seg_s == sp->seg_t) return fail(ctx, JAGG_E_INVALID, "segment letters must differ");
+    if (p.order.find(sp->seg_s) == std::string::npos || p.order.find(sp->seg_t) == std::string::npos)
+      return fail(ctx, JAGG_E_INVALID, "segment letters are not in the spec");
+    if (sp->g != JAGG_G_ATTENTION)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "a segment pair is taken by attention only");
+    if (sp->causal_s && (sp->causal_s != sp->seg_s || sp->causal_t != sp->seg_t))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "the causal pair must be the segment pair");
+  }
   return JAGG_OK;
 }
 
@@ -249,16 +259,21 @@ jagg_status plan_join(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p, const L
   }
   a.per_key = int32_t(per_key);
   a.n_keys = n_keys;
-  if (sp->causal_s) {
-    const int cs = sp->causal_s - 'a', ct = sp->causal_t - 'a';
+  // a causal or segment pair (s, t): locate both letters' block coordinates
+  const char ps = sp->causal_s ? sp->causal_s : sp->seg_s, pt = sp->causal_s ? sp->causal_t : sp->seg_t;
+  if (ps) {
+    const int cs = ps - 'a', ct = pt - 'a';
     if (L.n[cs] != L.n[ct] || L.k[cs] != L.k[ct])
-      return fail(ctx, JAGG_E_UNSUPPORTED, "causal letters need equal extents and block counts");
-    a.causal = 1;
+      return fail(ctx, JAGG_E_UNSUPPORTED, "causal or segment letters need equal extents and block counts");
+    if (p.out.find(ps) == std::string::npos)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "the first letter of a causal or segment pair must be an output letter");
+    a.causal = sp->causal_s ? 1 : 0;
+    a.seg = sp->seg_s ? 1 : 0;
     a.s_red = 0;
-    a.s_idx = int32_t(p.out.find(sp->causal_s));
-    const size_t to = p.out.find(sp->causal_t);
+    a.s_idx = int32_t(p.out.find(ps));
+    const size_t to = p.out.find(pt);
     a.t_red = to == std::string::npos;
-    a.t_idx = int32_t(a.t_red ? p.reduced.find(sp->causal_t) : to);
+    a.t_idx = int32_t(a.t_red ? p.reduced.find(pt) : to);
     a.e_s = (L.n[cs] + L.k[cs] - 1) / L.k[cs];
     a.e_t = (L.n[ct] + L.k[ct] - 1) / L.k[ct];
     a.n_s = L.n[cs];
@@ -861,7 +876,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // wherever an interval letter sits in its padding are taken: g = MUL, IDENT,
 // SQUARE or SILU_MUL (a zero factor), ADD when every input holds every
 // interval letter, RMS_SCALE when its first input does; MAX only over
-// uniform letters; no attention and no causal pair on interval letters.
+// uniform letters; no causal pair on interval letters.  Attention takes
+// intervals on its segment pair only (packed sequences): its kernel masks
+// each block by the length of its own interval.
 jagg_status bind_intervals(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const *in, int n_in, Bound &b) {
   bool any = false;
   for (int c = 0; c < 26; ++c) {
@@ -895,22 +912,34 @@ jagg_status bind_intervals(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relati
     }
   }
   auto is_iv = [&](char c) { return b.iv_letter[c - 'a']; };
-  if (sp->g == JAGG_G_ATTENTION)
-    return fail(ctx, JAGG_E_UNSUPPORTED, "attention over interval-blocked letters is not supported");
-  if (sp->causal_s && (is_iv(sp->causal_s) || is_iv(sp->causal_t)))
-    return fail(ctx, JAGG_E_UNSUPPORTED, "causal letters must be uniformly blocked");
-  if (sp->g == JAGG_G_EXP_SUB || sp->g == JAGG_G_EXP_SUB_DIV)
-    return fail(ctx, JAGG_E_UNSUPPORTED, "g %d is not zero on padding; interval letters need it", int(sp->g));
-  if (sp->agg == JAGG_AGG_MAX)
-    for (char c : b.p.reduced)
-      if (is_iv(c)) return fail(ctx, JAGG_E_UNSUPPORTED, "MAX over the interval-blocked letter '%c'", c);
-  for (int c = 0; c < 26; ++c) {
-    if (!b.iv_letter[c]) continue;
-    const int first = sp->g == JAGG_G_RMS_SCALE ? 1 : (sp->g == JAGG_G_ADD ? n_in : 0);
-    for (int j = 0; j < first; ++j)
-      if (b.p.in[j].find(char('a' + c)) == std::string::npos)
-        return fail(ctx, JAGG_E_UNSUPPORTED, "g %d needs the interval-blocked letter '%c' in input %d", int(sp->g),
-                    'a' + c, j);
+  if (sp->g == JAGG_G_ATTENTION) {
+    // packed sequences: intervals only on the segment pair (s, t), which the
+    // attention kernel masks by each block's own length
+    if (!sp->seg_s)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "attention over interval-blocked letters needs a segment pair (s, t)");
+    for (int c = 0; c < 26; ++c)
+      if (b.iv_letter[c] && c != sp->seg_s - 'a' && c != sp->seg_t - 'a')
+        return fail(ctx, JAGG_E_UNSUPPORTED, "attention: '%c' is interval-blocked but not a segment letter", 'a' + c);
+    const int cs = sp->seg_s - 'a', ct = sp->seg_t - 'a';
+    if (!is_iv(sp->seg_s) || !is_iv(sp->seg_t) || b.L.k[cs] != b.L.k[ct] ||
+        memcmp(b.iv_bnd[cs], b.iv_bnd[ct], sizeof(int64_t) * size_t(b.L.k[cs] + 1)) != 0)
+      return fail(ctx, JAGG_E_BLOCKING, "segment letters must be blocked by the same bounds");
+  } else {
+    if (sp->causal_s && (is_iv(sp->causal_s) || is_iv(sp->causal_t)))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "causal letters must be uniformly blocked");
+    if (sp->g == JAGG_G_EXP_SUB || sp->g == JAGG_G_EXP_SUB_DIV)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "g %d is not zero on padding; interval letters need it", int(sp->g));
+    if (sp->agg == JAGG_AGG_MAX)
+      for (char c : b.p.reduced)
+        if (is_iv(c)) return fail(ctx, JAGG_E_UNSUPPORTED, "MAX over the interval-blocked letter '%c'", c);
+    for (int c = 0; c < 26; ++c) {
+      if (!b.iv_letter[c]) continue;
+      const int first = sp->g == JAGG_G_RMS_SCALE ? 1 : (sp->g == JAGG_G_ADD ? n_in : 0);
+      for (int j = 0; j < first; ++j)
+        if (b.p.in[j].find(char('a' + c)) == std::string::npos)
+          return fail(ctx, JAGG_E_UNSUPPORTED, "g %d needs the interval-blocked letter '%c' in input %d", int(sp->g),
+                      'a' + c, j);
+    }
   }
   for (int j = 0; j < n_in; ++j) {
     jagg_relation &T = b.shadow[j];
@@ -1107,10 +1136,11 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
     if (ins[j]->dt != JAGG_BF16) return fail(ctx, JAGG_E_UNSUPPORTED, "attention inputs must be bfloat16");
   const jagg_relation &Q = *ins[0], &K = *ins[1], &V = *ins[2], &O = *out;
   auto pos = [&](int j, char c) { return int(j < 3 ? p.in[j].find(c) : p.out.find(c)); };
-  if (sp->causal_s) {
-    if (G.find(sp->causal_s) == std::string::npos || sp->causal_t != t)
-      return fail(ctx, JAGG_E_UNSUPPORTED, "the causal pair of attention must be (a query letter, %c)", t);
-    s = sp->causal_s;
+  const char pair_s = sp->causal_s ? sp->causal_s : sp->seg_s, pair_t = sp->causal_s ? sp->causal_t : sp->seg_t;
+  if (pair_s) {
+    if (G.find(pair_s) == std::string::npos || pair_t != t)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "the causal / segment pair of attention must be (a query letter, %c)", t);
+    s = pair_s;
   } else {  // the row letter: the innermost of G in Q
     for (char c : G)
       if (!s || inblock_s(Q, pos(0, c)) < inblock_s(Q, pos(0, s))) s = c;
@@ -1185,6 +1215,11 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
   a.div_kt = make_fastdiv(uint32_t(K.k[pos(1, t)]));
   a.scale_log2 = float(double(sp->alpha) * 1.4426950408889634);
   a.reverse = sp->causal_s ? 1 : 0;
+  a.iv = 0;
+  if (b.iv_letter[s - 'a']) {  // packed sequences (bind_intervals checked the segment pair)
+    a.iv = 1;
+    for (int i = 0; i <= b.L.k[s - 'a']; ++i) a.bnd[i] = int32_t(b.iv_bnd[s - 'a'][i]);
+  }
   a.xcd_group = a.nbatch % 8 == 0 ? 1 : 0;
   a.div_group = make_fastdiv(uint32_t(a.n_keys * a.s_tiles));
   if (!(sp->alpha > 0.0f)) return fail(ctx, JAGG_E_UNSUPPORTED, "attention needs a positive score scale alpha");

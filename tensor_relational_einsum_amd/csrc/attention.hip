@@ -129,11 +129,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
       oO += dig * a.xO[i];
     }
   }
-  const int32_t S0 = int32_t(fd_mod(fd_div(key, a.div_Ws), a.div_ks)) * a.e_s;  // first s of the block
+  // the block's interval of s (and, for a key tuple, of t): uniform blocks
+  // of e, or the bounds of packed sequences
+  const uint32_t kap_s = fd_mod(fd_div(key, a.div_Ws), a.div_ks);
+  const int32_t S0 = a.iv ? a.bnd[kap_s] : int32_t(kap_s) * a.e_s;  // first s of the block
+  const int32_t S_end = a.iv ? a.bnd[kap_s + 1] : a.n_s;            // rows from here on do not exist
   const int32_t s_tile0 = int32_t(st) * kRows;
   const int32_t s_loc = s_tile0 + 32 * wave + l32;  // this lane's query row, inside the block
   const int32_t s_glob = S0 + s_loc;
-  const bool row_ok = s_loc < a.e_s && s_glob < a.n_s;
+  const bool row_ok = s_loc < a.e_s && s_glob < S_end;
+  auto t_lo = [&](uint32_t kap) { return a.iv ? a.bnd[kap] : int32_t(kap) * a.e_t; };
+  auto t_end = [&](uint32_t kap) { return a.iv ? a.bnd[kap + 1] : a.n_t; };
   const int32_t s_hi = (s_tile0 + kRows < a.e_s ? s_tile0 + kRows : a.e_s) - 1;
   const int32_t wg_s_last = S0 + s_hi;                                     // last row of the workgroup
   const int32_t wave_s_first = S0 + s_tile0 + 32 * wave;                   // first row of the wavefront
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   if (CAUSAL) {
     n_it = 0;
     for (int e = 0; e < cnt; ++e) {
-      const int32_t T0 = int32_t(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt)) * a.e_t;
+      const int32_t T0 = t_lo(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt));
       if (T0 > wg_s_last) break;
       int tt = 0;
       while (tt < tpe && T0 + tt * kKeys <= wg_s_last) ++tt;
@@ -221,11 +227,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     const bool more = it + 1 < n_it;
     if (more) load_tile(it + 1);
     const int e = it / tpe, tt = it - e * tpe;
-    const int32_t T0 =
-        int32_t(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt)) * a.e_t + tt * kKeys;
+    const uint32_t kap_t = fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt);
+    const int32_t T0 = t_lo(kap_t) + tt * kKeys;
     // keys [0, t_valid) of the tile exist
     int32_t t_valid = a.e_t - tt * kKeys;
-    if (a.n_t - T0 < t_valid) t_valid = a.n_t - T0;
+    if (t_end(kap_t) - T0 < t_valid) t_valid = t_end(kap_t) - T0;
     if (t_valid > kKeys) t_valid = kKeys;
     if (!(CAUSAL && T0 > wave_s_last)) {
       const char *ks = smem + (it & 1) * STAGE;

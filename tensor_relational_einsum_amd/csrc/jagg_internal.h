@@ -154,8 +154,10 @@ struct JoinArgs {
   int64_t w_red[kMaxIn][26];           // tuple-id weight of each reduced letter's block coordinate
   int32_t per_key;
   int64_t n_keys;
-  // causal pair: letter s / t located as (is_reduced, index)
-  int32_t causal;
+  // causal or segment pair: letter s / t located as (is_reduced, index);
+  // causal keeps t-blocks starting before the s-block ends, seg keeps only
+  // the t-block equal to the s-block
+  int32_t causal, seg;
   int32_t s_red, s_idx, t_red, t_idx;
   int64_t e_s, e_t, n_s;
   int32_t *list;
@@ -324,6 +326,10 @@ struct AttnArgs {
   int32_t reverse;                     // walk output keys from the last (causal balance)
   int32_t xcd_group;                   // keep one batch index's workgroups on one XCD
   FastDiv div_group;                   // workgroups per batch index (n_keys * s_tiles)
+  // packed sequences: s and t blocked by the same bounds (segment pair);
+  // block kappa holds positions [bnd[kappa], bnd[kappa + 1])
+  int32_t iv;
+  int32_t bnd[kMaxIv + 1];
 };
 // d: 64 or 128 (the padded D = E extent)
 hipError_t launch_attention(const AttnArgs &a, int d, bool causal, bool out_bf16, hipStream_t st);

@@ -9,7 +9,9 @@
 // coordinates of its letters.  One wavefront lists the combinations of one
 // output key (the reduced letters' block coordinates, row-major in order of
 // first appearance), compacting with a ballot where a causal pair drops
-// some of them, so the list is deterministic.
+// some of them, so the list is deterministic.  A segment pair (packed
+// sequences, Example 3.10) keeps only the combinations whose s and t blocks
+// coincide.
 #include "device_common.h"
 #include "jagg_internal.h"
 
@@ -31,8 +33,8 @@ __global__ __launch_bounds__(256) void join_kernel(const JoinArgs a) {
     rem = q;
 #pragma unroll
     for (int j = 0; j < kMaxIn; ++j) base[j] += kap * a.w_out[j][i];
-    if (a.causal && !a.s_red && a.s_idx == i) ks = kap;
-    if (a.causal && !a.t_red && a.t_idx == i) kt_out = kap;
+    if ((a.causal || a.seg) && !a.s_red && a.s_idx == i) ks = kap;
+    if ((a.causal || a.seg) && !a.t_red && a.t_idx == i) kt_out = kap;
   }
   const int stride = 1 + a.n_in;
   int32_t *out = a.list + key * int64_t(a.per_key) * stride;
@@ -49,8 +51,9 @@ __global__ __launch_bounds__(256) void join_kernel(const JoinArgs a) {
       rr = q;
 #pragma unroll
       for (int j = 0; j < kMaxIn; ++j) tid[j] += kap * a.w_red[j][i];
-      if (a.causal && a.t_red && a.t_idx == i) kt = kap;
+      if ((a.causal || a.seg) && a.t_red && a.t_idx == i) kt = kap;
     }
+    if (a.seg && keep) keep = kt == ks;  // segment pair: the same block only
     if (a.causal && keep) {
       const int64_t lo_t = kt * a.e_t;
       int64_t hi_s = (ks + 1) * a.e_s;

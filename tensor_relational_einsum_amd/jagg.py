@@ -37,7 +37,8 @@ class JaggError(RuntimeError):
 class jagg_spec(ctypes.Structure):
     _fields_ = [("einsum", ctypes.c_char_p), ("g", ctypes.c_int), ("agg", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("eps", ctypes.c_float),
-                ("causal_s", ctypes.c_char), ("causal_t", ctypes.c_char)]
+                ("causal_s", ctypes.c_char), ("causal_t", ctypes.c_char), ("seg_s", ctypes.c_char),
+                ("seg_t", ctypes.c_char)]
 
 
 _lib = None
@@ -104,7 +105,8 @@ def parse(einsum: str):
     return ins, out, order
 
 
-def make_spec(einsum, g="mul", agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, eps=0.0, causal=None) -> jagg_spec:
+def make_spec(einsum, g="mul", agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, eps=0.0, causal=None,
+              segment=None) -> jagg_spec:
     s = jagg_spec()
     s._einsum_bytes = einsum.encode()  # keep the string alive with the struct
     s.einsum = s._einsum_bytes
@@ -112,6 +114,8 @@ def make_spec(einsum, g="mul", agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, 
     s.alpha, s.beta, s.eps = alpha, beta, eps
     s.causal_s = causal[0].encode() if causal else b"\0"
     s.causal_t = causal[1].encode() if causal else b"\0"
+    s.seg_s = segment[0].encode() if segment else b"\0"
+    s.seg_t = segment[1].encode() if segment else b"\0"
     return s
 
 
@@ -285,10 +289,10 @@ class EinsumCall:
 
     def __init__(self, ctx: Context, einsum: str, inputs, blockings: dict, out: Relation | None = None, g="mul",
                  agg="sum", out_dtype="f32", alpha=1.0, beta=0.0, eps=0.0, causal=None,
-                 workspace: torch.Tensor | None = None):
+                 workspace: torch.Tensor | None = None, segment=None):
         ins, out_letters, order = parse(einsum)
         self.ctx, self.einsum = ctx, einsum
-        self.spec = make_spec(einsum, g, agg, out_dtype, alpha, beta, eps, causal)
+        self.spec = make_spec(einsum, g, agg, out_dtype, alpha, beta, eps, causal, segment)
         self.inputs = list(inputs)
         self.blk = _i32([block_count(blockings.get(c, 1)) for c in order])
         self.in_arr = (ctypes.c_void_p * len(self.inputs))(*[r.handle.value for r in self.inputs])

@@ -230,3 +230,90 @@ def test_interval_relation_rejects_bad_bounds(ctx):
             jagg.Relation(ctx, "a", [8], [bnd], "f32")
     with pytest.raises(jagg.JaggError):  # 33 intervals
         jagg.Relation(ctx, "a", [64], [list(range(33)) + [64]], "f32")
+
+
+# ----------------------------------------------------------- packed attention
+# Example 3.10: attention never crosses a sequence end; with s and t blocked
+# at the sequence ends and a segment pair (s, t), each query block joins the
+# key block of its own sequence only, and the kernel masks each block by its
+# own interval's length.
+
+def run_packed_attention(ctx, spec, ext, blk, bounds, causal, odt, seed=11):
+    ins, out = spec.split("->")
+    ins = ins.split(",")
+    xs = [I.draw(g, [ext[c] for c in lt], "normal", "bf16") for g, lt in zip(I.streams(seed, 3), ins)]
+    rels = [upload(ctx, x, lt, blk) for x, lt in zip(xs, ins)]
+    alpha = 1.0 / ext["d"] ** 0.5
+    call = jagg.EinsumCall(ctx, spec, rels, blk, g="attention", agg="softmax", out_dtype=odt, alpha=alpha,
+                           causal=causal, segment=("s", "t"))
+    call.out.data.fill_(5)
+    call.run()
+    torch.cuda.synchronize()
+    got_rel = to_np(call.out.data)
+    xs64 = [to_np(x) for x in xs]
+    want = O.round_to(O.attention_dense(spec, xs64, ext, alpha=alpha, causal=causal, segments=("s", "t", bounds)),
+                      odt)
+    got = O.from_relation(got_rel, out, ext, blk)
+    pad = padding_mask(out, ext, blk)
+    assert np.all(got_rel[pad] == 0.0), "padding rows of short sequences must be +0"
+    return got, want, got_rel, xs64
+
+
+PACKED_ATT = [
+    # spec, extents, blockings (s and t alike), causal, out dtype
+    ("bhsd,bhtd,bhte->bhse", dict(b=1, h=2, s=1000, t=1000, d=128, e=128), [0, 200, 456, 1000], ("s", "t"), "bf16"),
+    ("bhsd,bhtd,bhte->bhse", dict(b=2, h=1, s=600, t=600, d=64, e=64), [0, 64, 300, 301, 600], None, "f32"),
+    # grouped-query attention over packed sequences: both halves of Example 3.10
+    ("grsd,gtd,gte->grse", dict(g=2, r=4, s=700, t=700, d=128, e=128), [0, 129, 700], ("s", "t"), "bf16"),
+]
+
+
+@pytest.mark.parametrize("spec,ext,bounds,causal,odt", PACKED_ATT)
+def test_packed_sequence_attention(ctx, spec, ext, bounds, causal, odt):
+    blk = {c: 1 for c in ext}
+    blk.update(s=bounds, t=bounds)
+    if spec.startswith("grsd"):
+        blk["g"] = ext["g"]
+    got, want, got_rel, xs64 = run_packed_attention(ctx, spec, ext, blk, bounds, causal, odt)
+    err = normwise_err(got, want)
+    assert err < BF16_OUT_TOL, f"normwise error {err:.3e}"
+
+
+def test_packed_attention_matches_relational_oracle(ctx):
+    """The GPU walk and the oracle's segment join / triple merge / recompose
+    agree relation to relation, padding included (a small case: the
+    relational oracle runs on one host thread)."""
+    spec, bounds = "hsd,htd,hte->hse", [0, 44, 300]
+    ext = dict(h=1, s=300, t=300, d=64, e=64)
+    blk = dict(h=1, s=bounds, t=bounds)
+    got, want, got_rel, xs64 = run_packed_attention(ctx, spec, ext, blk, bounds, ("s", "t"), "f32")
+    assert normwise_err(got, want) < BF16_OUT_TOL
+    rels = [O.to_relation(x, lt, ext, blk) for x, lt in zip(xs64, ("hsd", "htd", "hte"))]
+    want_rel, present = O.attention_relational(spec, rels, ext, blk, alpha=1.0 / 8.0, causal=("s", "t"),
+                                               segment=("s", "t"))
+    assert present.all()
+    assert normwise_err(got_rel, O.round_to(want_rel, "f32")) < BF16_OUT_TOL
+
+
+def test_segment_pair_on_uniform_blocks_is_block_local(ctx):
+    ext = dict(h=2, s=512, t=512, d=64, e=64)
+    blk = dict(h=1, s=4, t=4)
+    got, want, _, _ = run_packed_attention(ctx, "hsd,htd,hte->hse", ext, blk, [0, 128, 256, 384, 512], None, "f32")
+    assert normwise_err(got, want) < BF16_OUT_TOL
+
+
+def test_segment_pair_rejects(ctx):
+    ext = dict(h=1, s=256, t=256, d=64, e=64)
+    bnd = [0, 100, 256]
+    mk = lambda lt, b: jagg.relation_like(ctx, lt, ext, b, "bf16")
+    q, k, v = mk("hsd", dict(s=bnd)), mk("htd", dict(t=bnd)), mk("hte", dict(t=bnd))
+    spec = "hsd,htd,hte->hse"
+    with pytest.raises(jagg.JaggError):  # interval s and t without a segment pair
+        jagg.EinsumCall(ctx, spec, [q, k, v], dict(s=bnd, t=bnd), g="attention", agg="softmax").run()
+    k2, v2 = mk("htd", dict(t=[0, 128, 256])), mk("hte", dict(t=[0, 128, 256]))
+    with pytest.raises(jagg.JaggError):  # s and t cut at different places
+        jagg.EinsumCall(ctx, spec, [q, k2, v2], dict(s=bnd, t=[0, 128, 256]), g="attention", agg="softmax",
+                        segment=("s", "t")).run()
+    with pytest.raises(jagg.JaggError):  # a segment pair outside attention
+        a, b = mk("st", dict(s=2, t=2)), mk("td", dict(t=2))
+        jagg.EinsumCall(ctx, "st,td->sd", [a, b], dict(s=2, t=2), segment=("s", "t")).run()
