@@ -57,7 +57,18 @@ def spec_flops(st: I.Step, ext: dict) -> float:
         n = 1.0
         for c in letters:
             n *= ext[c]
-        if st.causal:
+        if st.segment:
+            # (s, t) pairs inside each segment only (t <= s under a causal pair)
+            s, t = st.segment
+            b = st.blockings[s]
+            if isinstance(b, list):
+                lens = [y - x for x, y in zip(b, b[1:])]
+            else:
+                e = -(-ext[s] // b)
+                lens = [min(e, ext[s] - q * e) for q in range(b)]
+            pairs = sum(L * (L + 1) / 2 if st.causal else L * L for L in lens)
+            n = n / (ext[s] * ext[t]) * pairs
+        elif st.causal:
             s, t = st.causal
             S = ext[s]
             n = n / (ext[s] * ext[t]) * (S * (S + 1) / 2)
@@ -232,8 +243,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama",
-                    choices=["llama", "llama_chain", "attention", "attention_chain", "attention_gqa", "multi_index",
-                             "matmul"],
+                    choices=["llama", "llama_chain", "attention", "attention_chain", "attention_gqa",
+                             "attention_packed", "multi_index", "matmul"],
                     help="llama / attention: fused attention; *_chain: the five-spec attention chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repartition", action="store_true")
@@ -251,7 +262,7 @@ def main():
     ctx = jagg.Context(0, stream)
     w = {"llama": lambda: I.llama_block(fused_attention=True), "llama_chain": I.llama_block,
          "attention": lambda: I.attention_chain(fused=True), "attention_chain": I.attention_chain,
-         "attention_gqa": I.attention_gqa,
+         "attention_gqa": I.attention_gqa, "attention_packed": I.attention_packed,
          "multi_index": I.multi_index, "matmul": I.matmul_256}[args.workload]()
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     dense = I.generate(w)

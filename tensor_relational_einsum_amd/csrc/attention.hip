@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   auto t_lo = [&](uint32_t kap) { return a.iv ? a.bnd[kap] : int32_t(kap) * a.e_t; };
   auto t_end = [&](uint32_t kap) { return a.iv ? a.bnd[kap + 1] : a.n_t; };
   const int32_t s_hi = (s_tile0 + kRows < a.e_s ? s_tile0 + kRows : a.e_s) - 1;
-  const int32_t wg_s_last = S0 + s_hi;                                     // last row of the workgroup
+  // last existing row of the workgroup (rows past the block's interval are padding)
+  const int32_t wg_s_last = S0 + s_hi < S_end - 1 ? S0 + s_hi : S_end - 1;
   const int32_t wave_s_first = S0 + s_tile0 + 32 * wave;                   // first row of the wavefront
   const int32_t wave_s_last = S0 + (s_tile0 + 32 * wave + 31 < s_hi ? s_tile0 + 32 * wave + 31 : s_hi);
 
@@ -158,8 +159,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   // tiles of the walk: joined tuples in t-block order, 64 keys at a time;
   // under a causal pair the walk ends at the first tile past the last row
   const int tpe = (a.e_t + kKeys - 1) / kKeys;
-  int n_it = cnt * tpe;
-  if (CAUSAL) {
+  // a tile of padding rows only (a short packed sequence) walks nothing and
+  // writes zeros
+  int n_it = S0 + s_tile0 < S_end ? cnt * tpe : 0;
+  if (CAUSAL && n_it > 0) {
     n_it = 0;
     for (int e = 0; e < cnt; ++e) {
       const int32_t T0 = t_lo(fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt));

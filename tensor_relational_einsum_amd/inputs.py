@@ -56,6 +56,7 @@ class Step:
     beta: float = 0.0
     eps: float = 0.0
     causal: tuple | None = None
+    segment: tuple | None = None  # (s, t): attention within blocks only (packed sequences)
 
 
 @dataclass
@@ -159,6 +160,23 @@ def attention_gqa(b=4, kv=8, group=4, s=2048, d=128, nb=16) -> Workload:
                   alpha=1.0 / math.sqrt(d), causal=("s", "t"))]
     return Workload(name=f"attention_gqa_causal_b{b}_kv{kv}x{group}_s{s}_d{d}_bf16_st{nb}", extents=ext,
                     tensors=tens, chain=chain, seed=1005)
+
+
+def attention_packed(b=2, kv=8, group=4, ends=PACKED_ENDS, d=128) -> Workload:
+    """Causal grouped-query attention over packed sequences ("Every Kernel
+    Is a Join", Example 3.10: 32 query heads over 8 kv heads; three
+    sequences packed into 4096 positions, ending at 1024, 2560 and 4096).
+    s and t are cut at the sequence ends and paired as a segment, so each
+    query attends within its own sequence; bf16 N(0,1), scale 1/sqrt(d)."""
+    n = ends[-1]
+    ext = {"b": b, "g": kv, "r": group, "s": n, "t": n, "d": d, "e": d}
+    blk = {"b": 1, "g": kv, "r": 1, "s": list(ends), "t": list(ends), "d": 1, "e": 1}
+    tens = [("Q", "bgrsd", "normal", "bf16", 1.0, 0.0, blk), ("K", "bgtd", "normal", "bf16", 1.0, 0.0, blk),
+            ("V", "bgtd", "normal", "bf16", 1.0, 0.0, blk)]
+    chain = [Step("O", "bgrsd,bgtd,bgte->bgrse", ["Q", "K", "V"], "attention", "softmax", "bf16", blk,
+                  alpha=1.0 / math.sqrt(d), causal=("s", "t"), segment=("s", "t"))]
+    return Workload(name=f"attention_packed_causal_b{b}_kv{kv}x{group}_seq{'-'.join(map(str, ends[1:]))}_d{d}_bf16",
+                    extents=ext, tensors=tens, chain=chain, seed=1006)
 
 
 def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8,

@@ -27,7 +27,8 @@ class ChainRunner:
             if isinstance(st, Step):
                 ins = [self.rel[n] for n in st.ins]
                 call = jagg.EinsumCall(ctx, st.spec, ins, st.blockings, g=st.g, agg=st.agg, out_dtype=st.out_dtype,
-                                       alpha=st.alpha, beta=st.beta, eps=st.eps, causal=st.causal, workspace=ws)
+                                       alpha=st.alpha, beta=st.beta, eps=st.eps, causal=st.causal, workspace=ws,
+                                       segment=st.segment)
                 if ws is None or call.workspace.numel() > ws.numel():
                     ws = call.workspace
                 self.rel[st.out] = call.out
