@@ -294,6 +294,83 @@ __device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (
       }
 }
 
+// Epilogue through LDS: the wavefronts write their scaled (and causally
+// masked) fragments into a BM x BN tile in LDS, then the workgroup writes the
+// tile out row by row in 16-byte vectors, so a store instruction covers whole
+// row runs instead of one element per lane.  Rows are padded by 16 bytes so
+// the fragment writes (32 lanes along a row, the other 32 four rows down)
+// spread over the banks.  Vector stores need every row start 16-byte aligned
+// in the output block; otherwise each element goes out on its own, still in
+// row order.
+template <int OUT_BF16, int TM, int TN, int BM, int BN, int NT>
+__device__ __forceinline__ void store_tile_lds(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                               int bt, int64_t key, int64_t ks, int m0, int n0, int wm, int wn,
+                                               int lane, char *smem) {
+  constexpr int OSZ = OUT_BF16 ? 2 : 4;
+  constexpr int PITCH = BN * OSZ + 16;
+  constexpr int VE = 16 / OSZ;      // elements per 16-byte vector
+  constexpr int VPR = BN / VE;      // vectors per tile row
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  int64_t kt_out = 0;
+  if (p.causal_out) kt_out = (key / p.ct_w) % p.ct_k;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ml = wm + i * 32 + (v >> 2) * 8 + lhalf * 4 + (v & 3);
+        const int nl = wn + j * 32 + lrow;
+        float x = p.alpha * acc[i][j][v];
+        if (p.causal_out) {
+          const int m = m0 + ml, n = n0 + nl;
+          const int64_t sg = ks * p.e_s + (uint32_t(m) - fd_div(uint32_t(m), p.div_s) * p.div_s.d);
+          const int64_t tg = kt_out * p.e_t + (uint32_t(n) - fd_div(uint32_t(n), p.div_t) * p.div_t.d);
+          if (tg > sg) x = 0.0f;
+        }
+        if (OUT_BF16)
+          *reinterpret_cast<uint16_t *>(smem + ml * PITCH + nl * 2) = f32_to_bf16(x);
+        else
+          *reinterpret_cast<float *>(smem + ml * PITCH + nl * 4) = x;
+      }
+  __syncthreads();
+  char *Cb = reinterpret_cast<char *>(p.C);
+  const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
+  const bool vec_ok = (cbase % VE) == 0 && (p.sCm % VE) == 0;
+  if (vec_ok) {
+    for (int i = threadIdx.x; i < BM * VPR; i += NT) {
+      const int r = i / VPR, cv = i - r * VPR;
+      const int m = m0 + r, n = n0 + cv * VE;
+      if (m >= p.M || n >= p.N) continue;
+      const char *src = smem + r * PITCH + cv * 16;
+      char *dst = Cb + (cbase + int64_t(m) * p.sCm + n) * OSZ;
+      if (n + VE <= p.N) {
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+      } else {
+        for (int e = 0; e < p.N - n; ++e) {
+          if (OUT_BF16) reinterpret_cast<uint16_t *>(dst)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+          else reinterpret_cast<float *>(dst)[e] = reinterpret_cast<const float *>(src)[e];
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < BM * BN; i += NT) {
+      const int r = i / BN, c = i - r * BN;
+      const int m = m0 + r, n = n0 + c;
+      if (m >= p.M || n >= p.N) continue;
+      const int64_t off = cbase + int64_t(m) * p.sCm + n;
+      if (OUT_BF16)
+        reinterpret_cast<uint16_t *>(Cb)[off] = *reinterpret_cast<const uint16_t *>(smem + r * PITCH + c * 2);
+      else
+        reinterpret_cast<float *>(Cb)[off] = *reinterpret_cast<const float *>(smem + r * PITCH + c * 4);
+    }
+  }
+}
+
+#ifndef JAGG_LDS_EPILOGUE
+#define JAGG_LDS_EPILOGUE 1
+#endif
+
 template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
           bool MASK>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
@@ -444,7 +521,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     __syncthreads();
   }
 
-  store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+  if constexpr (JAGG_LDS_EPILOGUE && BM * (BN * (OUT_BF16 ? 2 : 4) + 16) <= 2 * STAGE) {
+    // the loop's last barrier has passed: the stages are free
+    store_tile_lds<OUT_BF16, TM, TN, BM, BN, NT>(p, acc, ents[0], bt, key, ks, m0, n0, wm, wn, lane, smem);
+  } else {
+    store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+  }
 }
 
 template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false>
