@@ -1215,6 +1215,7 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
   a.div_kt = make_fastdiv(uint32_t(K.k[pos(1, t)]));
   a.scale_log2 = float(double(sp->alpha) * 1.4426950408889634);
   a.reverse = sp->causal_s ? 1 : 0;
+  a.div_per_s = make_fastdiv(uint32_t(a.n_keys / O.k[pos(3, s)]));
   a.iv = 0;
   if (b.iv_letter[s - 'a']) {  // packed sequences (bind_intervals checked the segment pair)
     a.iv = 1;

@@ -111,7 +111,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   w = fd_div(w, a.div_st);
   const uint32_t kq = w % uint32_t(a.n_keys);
   const uint32_t bi = w / uint32_t(a.n_keys);
-  const uint32_t key = a.reverse ? uint32_t(a.n_keys) - 1 - kq : kq;
+  uint32_t key = kq;
+  if (a.reverse) {
+    // causal: a key's work grows with its s-block, so launch the keys by
+    // s-block, heaviest first (key = (hi * ks + kappa_s) * Ws + lo)
+    const uint32_t sb = fd_div(kq, a.div_per_s), rest = kq - sb * a.div_per_s.d;
+    const uint32_t hi = fd_div(rest, a.div_Ws), lo = rest - hi * a.div_Ws.d;
+    key = (hi * a.div_ks.d + (a.div_ks.d - 1 - sb)) * a.div_Ws.d + lo;
+  }
   const int32_t cnt = a.counts[key];
   const int32_t *ents = a.list + int64_t(key) * a.per_key * 4;
 

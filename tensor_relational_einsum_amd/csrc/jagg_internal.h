@@ -323,7 +323,8 @@ struct AttnArgs {
   FastDiv div_Ws, div_ks;              // kappa_s = (output tuple / Ws) % ks
   FastDiv div_Wt, div_kt;              // kappa_t = (K tuple / Wt) % kt
   float scale_log2;                    // alpha * log2(e)
-  int32_t reverse;                     // walk output keys from the last (causal balance)
+  int32_t reverse;                     // causal: launch keys by s-block, heaviest first
+  FastDiv div_per_s;                   // keys per s-block value (n_keys / ks)
   int32_t xcd_group;                   // keep one batch index's workgroups on one XCD
   FastDiv div_group;                   // workgroups per batch index (n_keys * s_tiles)
   // packed sequences: s and t blocked by the same bounds (segment pair);
