@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     const uint32_t grp = fd_div(local, a.div_group);
     w = (grp * 8u + xcd) * a.div_group.d + (local - grp * a.div_group.d);
   }
-  const uint32_t st = fd_mod(w, a.div_st);
+  uint32_t st = fd_mod(w, a.div_st);
+  if (a.reverse) st = a.div_st.d - 1 - st;  // causal: later row tiles walk more keys, so they go first
   w = fd_div(w, a.div_st);
   const uint32_t kq = w % uint32_t(a.n_keys);
   const uint32_t bi = w / uint32_t(a.n_keys);
