@@ -21,7 +21,10 @@ hipError_t launch_contract_bf16(const ContractArgs &a, int out_bf16, bool a_kc, 
     }
 #undef JAGG_DMA
   }
-  *which = big ? "bf16 256x256" : (a.N + 63) / 64 * 64 < (a.N + 127) / 128 * 128 ? "bf16 128x64" : "bf16 128x128";
+  *which = big ? "bf16 256x256"
+                : (a.N + 63) / 64 * 64 < (a.N + 127) / 128 * 128 ? "bf16 128x64"
+                : (!out_bf16 && va == 8 && vb == 8 && !a.causal_red && short_walk<uint16_t>(a)) ? "bf16 128x128 one stage"
+                : "bf16 128x128";
   return launch_typed<uint16_t>(a, out_bf16, a_kc, b_kc, va, vb, big, st);
 }
 }  // namespace jagg

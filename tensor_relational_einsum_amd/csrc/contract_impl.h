@@ -370,9 +370,16 @@ __device__ __forceinline__ void store_tile_lds(const ContractArgs &p, const f32x
 #ifndef JAGG_LDS_EPILOGUE
 #define JAGG_LDS_EPILOGUE 1
 #endif
+#ifndef JAGG_SHORT_WALK
+#define JAGG_SHORT_WALK 1
+#endif
+constexpr bool kShortWalk = JAGG_SHORT_WALK;
 
+// NSTG: LDS stages.  Two overlap the loads of step s+1 with step s; one
+// (for walks of one or two steps, e.g. a score block with K = 128) halves the
+// LDS so that twice as many workgroups share a CU and overlap each other.
 template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
-          bool MASK>
+          bool MASK, int NSTG>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
   constexpr int ESZ = int(sizeof(T));
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
   using TB = Tile<T, B_KC, BN, VB, NT>;
   constexpr int A_BYTES = tile_bytes<A_KC, BM, ESZ>(), B_BYTES = tile_bytes<B_KC, BN, ESZ>();
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[NSTG * STAGE];
 
   int tn, tm, bt;
   int64_t key;
@@ -510,18 +517,28 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
     xb.store(lds + A_BYTES);
   };
 
-  load_next(ta[0], tb[0]);
-  store_step(ta[0], tb[0], smem);
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < steps) load_next(ta[0], tb[0]);
-    compute(smem + cur * STAGE);
-    if (s + 1 < steps) store_step(ta[0], tb[0], smem + (cur ^ 1) * STAGE);
+  if constexpr (NSTG == 1) {
+    for (int s = 0; s < steps; ++s) {
+      load_next(ta[0], tb[0]);
+      store_step(ta[0], tb[0], smem);
+      __syncthreads();
+      compute(smem);
+      __syncthreads();
+    }
+  } else {
+    load_next(ta[0], tb[0]);
+    store_step(ta[0], tb[0], smem);
     __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < steps) load_next(ta[0], tb[0]);
+      compute(smem + cur * STAGE);
+      if (s + 1 < steps) store_step(ta[0], tb[0], smem + (cur ^ 1) * STAGE);
+      __syncthreads();
+    }
   }
 
-  if constexpr (JAGG_LDS_EPILOGUE && BM * (BN * (OUT_BF16 ? 2 : 4) + 16) <= 2 * STAGE) {
+  if constexpr (JAGG_LDS_EPILOGUE && BM * (BN * (OUT_BF16 ? 2 : 4) + 16) <= NSTG * STAGE) {
     // the loop's last barrier has passed: the stages are free
     store_tile_lds<OUT_BF16, TM, TN, BM, BN, NT>(p, acc, ents[0], bt, key, ks, m0, n0, wm, wn, lane, smem);
   } else {
@@ -529,15 +546,25 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
   }
 }
 
-template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false>
+template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false,
+          int NSTG = 2>
 static hipError_t launch_tile(const ContractArgs &a, hipStream_t st) {
   ContractArgs b = a;
   b.tiles_m = (a.M + BM - 1) / BM;
   b.tiles_n = (a.N + BN - 1) / BN;
   const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
-  hipLaunchKernelGGL((contract_kernel<T, OB, AK, BKC, VA, VB, BM, BN, WM, WN, MASK>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((contract_kernel<T, OB, AK, BKC, VA, VB, BM, BN, WM, WN, MASK, NSTG>), dim3(unsigned(grid)),
                      dim3(WM * WN * 64), 0, st, b);
   return hipGetLastError();
+}
+
+// walks of at most two K-steps per output tile with an fp32 output take the
+// one-stage kernel (score blocks with K = 128: 622 -> 535 us for 4x32x2048^2;
+// a bf16 output does better with two stages and the LDS epilogue)
+template <typename T>
+inline bool short_walk(const ContractArgs &a) {
+  constexpr int BK = kSlab / int(sizeof(T));
+  return kShortWalk && int64_t(a.per_key) * ((a.K + BK - 1) / BK) <= 2;
 }
 
 // big: 256x256 tiles, 8 wavefronts of 128x64; small: 128x128, 4 of 64x64, or
@@ -555,6 +582,7 @@ static hipError_t launch_layout(const ContractArgs &a, int va, int vb, bool big,
   if (va == F && vb == F) {
     if (big) return launch_tile<T, OB, AK, BKC, F, F, 256, 256, 2, 4>(a, st);
     if ((a.N + 63) / 64 * 64 < (a.N + 127) / 128 * 128) return launch_tile<T, OB, AK, BKC, F, F, 128, 64, 2, 2>(a, st);
+    if (OB == 0 && short_walk<T>(a)) return launch_tile<T, OB, AK, BKC, F, F, 128, 128, 2, 2, false, 1>(a, st);
     return launch_tile<T, OB, AK, BKC, F, F, 128, 128, 2, 2>(a, st);
   }
   if (va == F && vb == 1) {

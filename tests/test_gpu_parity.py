@@ -252,6 +252,29 @@ def test_contraction_lds_pipeline(trace_ctx, capfd, spec, ext, blk, odt, causal)
     assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
 
 
+# score-shaped specs whose walk is one or two K-steps with an fp32 output:
+# the one-stage kernel (two stages and the LDS epilogue for a bf16 output)
+SHORT_WALK_CASES = [
+    ("bhsd,bhtd->bhst", dict(b=2, h=3, s=256, t=256, d=128), dict(b=1, h=1, s=2, t=2, d=1), "f32", "one stage"),
+    ("bhsd,bhtd->bhst", dict(b=1, h=2, s=200, t=328, d=128), dict(b=1, h=1, s=2, t=3, d=1), "f32", "one stage"),
+    ("bhsd,bhtd->bhst", dict(b=1, h=2, s=200, t=328, d=64), dict(b=1, h=1, s=2, t=3, d=1), "f32", "one stage"),
+    ("bhsd,bhtd->bhst", dict(b=2, h=3, s=256, t=256, d=128), dict(b=1, h=1, s=2, t=2, d=1), "bf16", "128x128"),
+]
+
+
+@pytest.mark.parametrize("spec,ext,blk,odt,kernel", SHORT_WALK_CASES)
+def test_contraction_short_walk(trace_ctx, capfd, spec, ext, blk, odt, kernel):
+    got, want, got_rel, pad, _ = run_spec_case(trace_ctx, spec, ext, blk, in_dtypes=["bf16", "bf16"], out_dtype=odt)
+    err_lines = [ln for ln in capfd.readouterr().err.splitlines() if ": contract " in ln]
+    assert err_lines and kernel in err_lines[-1], err_lines
+    if kernel == "128x128":
+        assert "one stage" not in err_lines[-1]
+    tol = F32_TOL if odt == "f32" else BF16_OUT_TOL
+    err = normwise_err(got, want)
+    assert err < tol, f"normwise error {err:.3e}"
+    assert np.all(got_rel[pad] == 0.0), "output padding must be +0"
+
+
 EW_CASES = [
     # spec, g, agg, extents, blockings, in dtypes, out dtype, positive inputs, causal
     ("bhst->bhs", "ident", "max", dict(b=2, h=3, s=40, t=300), dict(b=1, h=1, s=3, t=4), ["f32"], "f32", (), None),
