@@ -11,8 +11,10 @@ Prints one JSON line: value = algorithmic TFLOP/s of the step (contraction
 FLOPs, causal attention counted element-wise), a roofline entry for the
 dominant kernel (the bf16 MFMA contraction of the projection / FFN specs),
 the repartition GB/s of the 8192^2, 4-D and packed-sequence (interval)
-reblocking workloads, and the CPU oracle timed on a bounded sample of the
-same specs.
+reblocking workloads, the other measured workloads (256^3 matmul, the
+attention chain and its fused, grouped-query and packed-sequence forms, the
+multi-index fp32 contraction) with per-spec rates, and the CPU oracle timed
+on a bounded sample of the block's specs.
 """
 from __future__ import annotations
 
@@ -194,6 +196,37 @@ def repartition_rate(ctx, w: I.Workload, reps: int, scratch) -> dict:
             "GB/s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS}
 
 
+def other_config(ctx, w: I.Workload, steps: int = 5, warmup: int = 2) -> dict:
+    """One of the other measured workloads, timed like the main one (events
+    around every call on the context stream): step time, rate, fraction of
+    the peak that bounds it, and per-spec rates."""
+    dense = I.generate(w)
+    run = ChainRunner(ctx, w, dense)
+    step_ms, per_call, _ = timed_chain(run, steps, warmup)
+    ms = float(np.mean(step_ms))
+    call_ms = per_call.mean(axis=0)
+    flops = sum(spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0 for st in w.chain)
+    big = max((st for st in w.chain if isinstance(st, I.Step)), key=lambda st: spec_flops(st, w.extents))
+    in_dtype = run.rel[big.ins[0]].dtype
+    peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS
+    specs = []
+    for i, st in enumerate(w.chain):
+        by = spec_bytes(run, st, w.extents)
+        f = spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0
+        e = {"name": st.out, "op": st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}",
+             "ms": round(float(call_ms[i]), 4), "GB/s": round(by / (call_ms[i] * 1e-3) / 1e9, 1),
+             "frac_hbm": round(by / (call_ms[i] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3)}
+        if f:
+            e["TFLOP/s"] = round(f / (call_ms[i] * 1e-3) / 1e12, 2)
+        specs.append(e)
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"workload": w.name, "ms_per_step": round(ms, 4), "TFLOP/s": round(tf, 3), "dtype": in_dtype,
+           "frac_mfma_peak": round(tf / peak, 4), "peak_TFLOP/s": peak, "specs": specs}
+    del run, dense
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(w: I.Workload, dense: dict, target_s: float = 12.0) -> dict:
     """The oracle, as it stands, on a bounded sample of the block's
     contraction specs: sampled outputs of each projection / FFN spec, scaled
@@ -248,6 +281,8 @@ def main():
                     help="llama / attention: fused attention; *_chain: the five-spec attention chain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-repartition", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the other workloads (matmul, attention chain and fused forms, multi-index)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -322,6 +357,15 @@ def main():
                "packed_to_uniform": repartition_rate(ctx, I.repartition_packed(), 15, scratch),
                "uniform_to_packed": repartition_rate(ctx, I.repartition_packed(to_packed=True), 15, scratch)}
         del scratch
+    others = {}
+    if not args.no_other_configs and args.workload == "llama":
+        print("[bench] timing the other workloads", file=sys.stderr, flush=True)
+        for name, mk in (("matmul_256_fp32", I.matmul_256), ("attention_chain", I.attention_chain),
+                         ("attention_fused", lambda: I.attention_chain(fused=True)),
+                         ("attention_gqa_causal", I.attention_gqa), ("attention_packed_causal", I.attention_packed),
+                         ("multi_index_fp32", I.multi_index)):
+            others[name] = other_config(ctx, mk())
+            torch.cuda.empty_cache()
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -338,7 +382,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": in_dtype, "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": w.name, "extents": w.extents, "step_flops": flops, "wall_s": round(wall, 3)},
-        "roofline": roof, "cpu_baseline": cpu, "repartition": rep,
+        "roofline": roof, "cpu_baseline": cpu, "repartition": rep, "other_configs": others,
         "graph": {"ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 3),
                   "note": "the same chain replayed as one recorded HIP graph (jagg_capture_begin/end)"},
         "breakdown": breakdown,
