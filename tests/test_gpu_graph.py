@@ -78,3 +78,37 @@ def test_graph_capture_errors(sctx):
         sctx._check(jagg.lib().jagg_capture_begin(sctx.handle))
     sctx._check(jagg.lib().jagg_capture_end(sctx.handle, jagg.ctypes.byref(h)))  # an empty graph is fine
     jagg.Graph(sctx, h).close()
+
+
+def test_graph_packed_attention_with_interval_relayouts(sctx):
+    """Packed-sequence GQA attention (segment pair over interval-blocked s and
+    t) and the interval relayouts around it, recorded and replayed."""
+    w = I.attention_packed(b=1, kv=2, group=2, ends=(0, 100, 356, 512), d=64)
+    with torch.cuda.stream(sctx.stream):
+        dense = I.generate(w)
+        run = ChainRunner(sctx, w, dense)
+        q = run.rel["Q"]
+        uni = jagg.relation_like(sctx, q.letters, dict(zip(q.letters, q.extents)), dict(s=4), q.dtype)
+        back = jagg.relation_like(sctx, q.letters, dict(zip(q.letters, q.extents)), q.blocking(), q.dtype)
+
+        def chain():
+            run.run()
+            jagg.repartition(sctx, q, uni)
+            jagg.repartition(sctx, uni, back)
+
+        chain()
+        torch.cuda.synchronize()
+        want_o, want_b = run.rel["O"].data.clone(), back.data.clone()
+        assert torch.equal(want_b, q.data)
+        g = jagg.capture(sctx, chain)
+        for rep in range(3):
+            run.rel["O"].data.fill_(7)
+            back.data.fill_(7)
+            g.launch()
+            torch.cuda.synchronize()
+            assert torch.equal(run.rel["O"].data, want_o), f"replay {rep}: attention output differs"
+            assert torch.equal(back.data, want_b), f"replay {rep}: interval relayout round trip differs"
+            chain()
+            torch.cuda.synchronize()
+            assert torch.equal(run.rel["O"].data, want_o)
+        g.close()
