@@ -164,7 +164,8 @@ jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64
  * extents[i]; block kappa then covers [b_kappa, b_kappa+1).  Every block of
  * such a letter is padded to the longest interval, max(b_kappa+1 - b_kappa),
  * and the storage convention is otherwise the one above.  At most 32
- * intervals per letter (JAGG_E_UNSUPPORTED beyond); bounds that do not run
+ * intervals per letter, and at most 192 bounds over both relations of one
+ * repartition (JAGG_E_UNSUPPORTED beyond); bounds that do not run
  * from 0 to the extent or do not increase give JAGG_E_BLOCKING.  The bounds
  * are copied; the caller keeps ownership of the arrays.  bounds == NULL is
  * the uniform case for every letter.
