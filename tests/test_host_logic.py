@@ -1,0 +1,79 @@
+"""Host-side logic with no GPU: the benchmark's algorithmic work counts, the
+binding's marshalling of interval blockings, and the workload recipes.
+
+FLOP counts are checked against closed forms written out here: 2 per
+multiply-add over the unpadded index space; a causal pair keeps the
+S(S+1)/2 pairs t <= s; a segment pair keeps the pairs inside each segment.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from tensor_relational_einsum_amd import inputs as I  # noqa: E402
+from tensor_relational_einsum_amd import jagg  # noqa: E402
+
+
+def test_contraction_flops():
+    st = I.Step("C", "ij,jk->ik", ["A", "B"], "mul", "sum", "f32", {})
+    assert bench.spec_flops(st, dict(i=3, j=5, k=7)) == 2 * 3 * 5 * 7
+    st = I.Step("M", "ij->i", ["A"], "ident", "max", "f32", {})
+    assert bench.spec_flops(st, dict(i=3, j=5)) == 0.0  # not a contraction
+
+
+def test_attention_flops_plain_causal_and_segmented():
+    ext = dict(b=2, h=3, s=10, t=10, d=4, e=4)
+    spec = "bhsd,bhtd,bhte->bhse"
+    full = I.Step("O", spec, ["Q", "K", "V"], "attention", "softmax", "f32", {})
+    assert bench.spec_flops(full, ext) == 2 * (2 * 2 * 3 * 10 * 10 * 4)
+    causal = I.Step("O", spec, ["Q", "K", "V"], "attention", "softmax", "f32", {}, causal=("s", "t"))
+    assert bench.spec_flops(causal, ext) == 2 * (2 * 2 * 3 * (10 * 11 // 2) * 4)
+    bnd = [0, 3, 4, 10]  # segments of 3, 1, 6
+    seg = I.Step("O", spec, ["Q", "K", "V"], "attention", "softmax", "f32", dict(s=bnd, t=bnd), causal=("s", "t"),
+                 segment=("s", "t"))
+    pairs = 3 * 4 // 2 + 1 + 6 * 7 // 2
+    assert bench.spec_flops(seg, ext) == 2 * (2 * 2 * 3 * pairs * 4)
+    seg_nc = I.Step("O", spec, ["Q", "K", "V"], "attention", "softmax", "f32", dict(s=bnd, t=bnd),
+                    segment=("s", "t"))
+    assert bench.spec_flops(seg_nc, ext) == 2 * (2 * 2 * 3 * (9 + 1 + 36) * 4)
+    uni = I.Step("O", spec, ["Q", "K", "V"], "attention", "softmax", "f32", dict(s=3, t=3), segment=("s", "t"))
+    assert bench.spec_flops(uni, ext) == 2 * (2 * 2 * 3 * (16 + 16 + 4) * 4)  # blocks of 4, 4, 2
+
+
+def test_gqa_flops_count_every_query_head():
+    w = I.attention_gqa(b=1, kv=2, group=3, s=8, d=4, nb=2)
+    st = w.chain[0]
+    # 6 query heads, causal 8 x 9 / 2 pairs, two products of D = E = 4
+    assert bench.spec_flops(st, w.extents) == 2 * (2 * 6 * 36 * 4)
+
+
+def test_packed_recipe_follows_the_sequence_ends():
+    w = I.attention_packed()
+    st = w.chain[0]
+    assert st.blockings["s"] == [0, 1024, 2560, 4096] == st.blockings["t"]
+    assert st.segment == ("s", "t") and st.causal == ("s", "t")
+    assert w.extents["s"] == 4096
+    rp = I.repartition_packed()
+    assert rp.tensors[0][-1] == {"s": [0, 1024, 2560, 4096]} and rp.chain[0].blockings == {"s": 4}
+
+
+def test_blocking_values_marshal_counts_and_bounds():
+    assert jagg.block_count(4) == 4 and jagg.block_count([0, 3, 9]) == 2
+    counts, bnd, keep = jagg._bounds([2, [0, 5, 7, 11], 1])
+    assert list(counts) == [2, 3, 1]
+    assert not bnd[0] and not bnd[2]          # uniform letters pass NULL
+    assert [bnd[1][i] for i in range(4)] == [0, 5, 7, 11]
+    assert len(keep) == 1
+
+
+@pytest.mark.parametrize("bounds", [[0, 5, 7, 11], [0, 11]])
+def test_interval_relation_size_through_the_binding(bounds):
+    # 'ij': i blocked by bounds (padded to the longest interval), j uniform in 2 of 3
+    blocks = len(bounds) - 1
+    longest = max(b - a for a, b in zip(bounds, bounds[1:]))
+    assert jagg.relation_bytes("ij", [11, 6], [bounds, 2], "f32") == 4 * blocks * longest * 2 * 3
+    assert jagg.relation_bytes("ij", [11, 6], [bounds, 2], "bf16") == 2 * blocks * longest * 2 * 3
