@@ -343,7 +343,7 @@ namespace {
 #define JAGG_FLAT_MAP_U 2
 #endif
 #ifndef JAGG_FLAT_REDUCE_EU
-#define JAGG_FLAT_REDUCE_EU 2
+#define JAGG_FLAT_REDUCE_EU 1
 #endif
 constexpr int kMapU = JAGG_FLAT_MAP_U;          // vectors per thread per pass (map)
 constexpr int kReduceEU = JAGG_FLAT_REDUCE_EU;  // joined tuples loaded together (row reduce)
