@@ -350,7 +350,14 @@ constexpr int kReduceEU = JAGG_FLAT_REDUCE_EU;  // joined tuples loaded together
 
 template <int G>
 hipError_t map_go(const FlatArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((flat_map_kernel<G, kMapU>), dim3(unsigned(a.n_keys) * unsigned(a.chunks)), dim3(256), 0, st, a);
+  // every input varying along the row: four vectors per thread in one pass
+  // (SiLU-up and residual adds 1-2% faster); with a row-constant input two
+  // per pass, twice (an RMS scale 10% faster that way)
+  bool all_inner = true;
+  for (int j = 0; j < a.n_in; ++j) all_inner = all_inner && a.in[j].inner;
+  const dim3 grid(unsigned(a.n_keys) * unsigned(a.chunks));
+  if (all_inner) hipLaunchKernelGGL((flat_map_kernel<G, 2 * kMapU>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((flat_map_kernel<G, kMapU>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
