@@ -226,6 +226,30 @@ struct Mma<float> {
   }
 };
 
+// One K chunk over a wavefront's TM x TN accumulators.  For fp32 the four
+// MFMAs of a chunk go round the accumulators (sub-step x of every
+// accumulator before sub-step x + 1 of any), so consecutive MFMAs do not wait
+// on each other's results; each accumulator still adds its products in the
+// same order.
+template <typename T, int TM, int TN>
+__device__ __forceinline__ void mma_chunk(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b) {
+  if constexpr (sizeof(T) == 4) {
+    auto part = [](const uint4 &v, int x) { return __uint_as_float(x == 0 ? v.x : x == 1 ? v.y : x == 2 ? v.z : v.w); };
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(part(a[i], x), part(b[j], x), acc[i][j], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], a[i], b[j]);
+  }
+}
+
 // workgroup -> (tile row, tile column, batch index, output key).  Where
 // neighbouring tiles share operand panels, the numbering gives each XCD a
 // contiguous run of tiles (dispatch round-robins workgroups over the 8 XCDs).
@@ -299,9 +323,9 @@ __device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (
 // tile out row by row in 16-byte vectors, so a store instruction covers whole
 // row runs instead of one element per lane.  Rows are padded by 16 bytes so
 // the fragment writes (32 lanes along a row, the other 32 four rows down)
-// spread over the banks.  Vector stores need every row start 16-byte aligned
-// in the output block; otherwise each element goes out on its own, still in
-// row order.
+// spread over the banks.  The caller guarantees that every row start is
+// 16-byte aligned in the output block (elsewhere the fragments are stored
+// directly: the LDS pass would buy nothing).
 template <int OUT_BF16, int TM, int TN, int BM, int BN, int NT>
 __device__ __forceinline__ void store_tile_lds(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
                                                int bt, int64_t key, int64_t ks, int m0, int n0, int wm, int wn,
@@ -336,33 +360,19 @@ __device__ __forceinline__ void store_tile_lds(const ContractArgs &p, const f32x
   __syncthreads();
   char *Cb = reinterpret_cast<char *>(p.C);
   const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
-  const bool vec_ok = (cbase % VE) == 0 && (p.sCm % VE) == 0;
-  if (vec_ok) {
-    for (int i = threadIdx.x; i < BM * VPR; i += NT) {
-      const int r = i / VPR, cv = i - r * VPR;
-      const int m = m0 + r, n = n0 + cv * VE;
-      if (m >= p.M || n >= p.N) continue;
-      const char *src = smem + r * PITCH + cv * 16;
-      char *dst = Cb + (cbase + int64_t(m) * p.sCm + n) * OSZ;
-      if (n + VE <= p.N) {
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-      } else {
-        for (int e = 0; e < p.N - n; ++e) {
-          if (OUT_BF16) reinterpret_cast<uint16_t *>(dst)[e] = reinterpret_cast<const uint16_t *>(src)[e];
-          else reinterpret_cast<float *>(dst)[e] = reinterpret_cast<const float *>(src)[e];
-        }
+  for (int i = threadIdx.x; i < BM * VPR; i += NT) {
+    const int r = i / VPR, cv = i - r * VPR;
+    const int m = m0 + r, n = n0 + cv * VE;
+    if (m >= p.M || n >= p.N) continue;
+    const char *src = smem + r * PITCH + cv * 16;
+    char *dst = Cb + (cbase + int64_t(m) * p.sCm + n) * OSZ;
+    if (n + VE <= p.N) {
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    } else {
+      for (int e = 0; e < p.N - n; ++e) {
+        if (OUT_BF16) reinterpret_cast<uint16_t *>(dst)[e] = reinterpret_cast<const uint16_t *>(src)[e];
+        else reinterpret_cast<float *>(dst)[e] = reinterpret_cast<const float *>(src)[e];
       }
-    }
-  } else {
-    for (int i = threadIdx.x; i < BM * BN; i += NT) {
-      const int r = i / BN, c = i - r * BN;
-      const int m = m0 + r, n = n0 + c;
-      if (m >= p.M || n >= p.N) continue;
-      const int64_t off = cbase + int64_t(m) * p.sCm + n;
-      if (OUT_BF16)
-        reinterpret_cast<uint16_t *>(Cb)[off] = *reinterpret_cast<const uint16_t *>(smem + r * PITCH + c * 2);
-      else
-        reinterpret_cast<float *>(Cb)[off] = *reinterpret_cast<const float *>(smem + r * PITCH + c * 4);
     }
   }
 }
@@ -493,10 +503,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
 #pragma unroll
       for (int kc = 0; kc < KCH; ++kc) {
         if (kc + 1 < KCH) read_frags(kc + 1, af[(kc + 1) & 1], bfr[(kc + 1) & 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[kc & 1][i], bfr[kc & 1][j]);
+        mma_chunk<T, TM, TN>(acc, af[kc & 1], bfr[kc & 1]);
       }
     } else {
       // 16 MFMAs per chunk give the reads of the next chunk room without a
@@ -504,10 +511,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
 #pragma unroll
       for (int kc = 0; kc < KCH; ++kc) {
         read_frags(kc, af[0], bfr[0]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[0][i], bfr[0][j]);
+        mma_chunk<T, TM, TN>(acc, af[0], bfr[0]);
       }
     }
   };
@@ -539,11 +543,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const C
   }
 
   if constexpr (JAGG_LDS_EPILOGUE && BM * (BN * (OUT_BF16 ? 2 : 4) + 16) <= NSTG * STAGE) {
-    // the loop's last barrier has passed: the stages are free
-    store_tile_lds<OUT_BF16, TM, TN, BM, BN, NT>(p, acc, ents[0], bt, key, ks, m0, n0, wm, wn, lane, smem);
-  } else {
-    store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+    // the loop's last barrier has passed: the stages are free.  The LDS pass
+    // pays only where output rows start 16-byte aligned (row stores); else
+    // the fragments go out directly (the test is uniform over the workgroup)
+    constexpr int VE = OUT_BF16 ? 8 : 4;
+    if ((ents[0] * p.beC + int64_t(bt) * p.sCb) % VE == 0 && p.sCm % VE == 0) {
+      store_tile_lds<OUT_BF16, TM, TN, BM, BN, NT>(p, acc, ents[0], bt, key, ks, m0, n0, wm, wn, lane, smem);
+      return;
+    }
   }
+  store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
 }
 
 template <typename T, int OB, bool AK, bool BKC, int VA, int VB, int BM, int BN, int WM, int WN, bool MASK = false,
