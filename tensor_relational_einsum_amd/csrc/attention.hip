@@ -121,7 +121,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     key = (hi * a.div_ks.d + (a.div_ks.d - 1 - sb)) * a.div_Ws.d + lo;
   }
   const int32_t cnt = a.counts[key];
-  const int32_t *ents = a.list + int64_t(key) * a.per_key * 4;
+  // the join list is read-only for the kernel's lifetime: reading it through
+  // the constant address space keeps the tuple-id reads on the scalar unit.
+  // A vector load there would make the walk wait (vmcnt counts in issue
+  // order) for the next tile's K / V loads issued just before it.
+  typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+  const const_i32p ents = (const_i32p)(a.list + int64_t(key) * a.per_key * 4);
 
   // offsets of the batch index inside each block
   int64_t oQ = 0, oK = 0, oV = 0, oO = 0;
@@ -231,6 +236,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     load_tile(0);
     store_tile(0);
   }
+  // Every global load so far (Q fragments, first tile) has landed: said
+  // explicitly (vmcnt(0)), the compiler's wait counting enters the loop with
+  // nothing pending and does not make the S^T MFMAs of each tile wait for
+  // the next tile's loads, which it would otherwise treat as possibly
+  // carrying Q
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   const int g = lane >> 4, s16 = lane & 15;
   const float scale = a.scale_log2;  // > 0
@@ -253,13 +264,22 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.0f;
+      // K fragments two MFMAs ahead of their use, as the V fragments below
+      auto kread = [&](int q) {
+        return *reinterpret_cast<const uint4 *>(ks + (32 * (q & 1) + l32) * KP + 32 * (q >> 1) + 16 * hi);
+      };
+      {
+        uint4 kring[3];
+        kring[0] = kread(0);
+        kring[1] = kread(1);
 #pragma unroll
-      for (int k = 0; k < KS; ++k)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const uint4 kf = *reinterpret_cast<const uint4 *>(ks + (32 * mt + l32) * KP + 32 * k + 16 * hi);
-          sacc[mt] = mma(kf, qf[k], sacc[mt]);
+        for (int q = 0; q < 2 * KS; ++q) {
+          if (q + 2 < 2 * KS) kring[(q + 2) % 3] = kread(q + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc[q & 1] = mma(kring[q % 3], qf[q >> 1], sacc[q & 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
       // drop missing keys and, under the causal pair, t > s
       const bool full = t_valid == kKeys && !(CAUSAL && T0 + kKeys - 1 > wave_s_first);
       if (!full) {
@@ -307,16 +327,23 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
       }
       l_run += sum;
       m_run = m_new;
-      // O^T += V^T P^T, with V^T read in the keys' score order
+      // O^T += V^T P^T, with V^T read in the keys' score order; the V
+      // fragments are read two MFMAs ahead of their use (a ring of three),
+      // so the LDS latency hides behind the MFMAs in between
+      auto vread = [&](int q) {
+        const int n = 32 * (q >> 2) + 16 * (g & 1) + 4 * (s16 & 3);
+        const int kb = 16 * (q & 3) + 4 * (g >> 1) + (s16 >> 2);
+        return tr_pair(vs + kb * VP + n * 2, vs + (kb + 8) * VP + n * 2);
+      };
+      uint4 vring[3];
+      vring[0] = vread(0);
+      vring[1] = vread(1);
 #pragma unroll
-      for (int et = 0; et < ET; ++et) {
-        const int n = 32 * et + 16 * (g & 1) + 4 * (s16 & 3);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kb = 16 * kk + 4 * (g >> 1) + (s16 >> 2);
-          const uint4 vf = tr_pair(vs + kb * VP + n * 2, vs + (kb + 8) * VP + n * 2);
-          acc[et] = mma(vf, pf[kk], acc[et]);
-        }
+      for (int q = 0; q < 4 * ET; ++q) {
+        if (q + 2 < 4 * ET) vring[(q + 2) % 3] = vread(q + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[q >> 2] = mma(vring[q % 3], pf[q & 3], acc[q >> 2]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (more) store_tile((it + 1) & 1);
