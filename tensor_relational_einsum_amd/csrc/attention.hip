@@ -197,11 +197,30 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     koff[p] = uint32_t((int64_t(row) * a.tK + ch * 8) * 2);
     voff[p] = uint32_t((int64_t(row) * a.tV + ch * 8) * 2);
   }
+  // tuple ids and key range of one tile of the walk; the loop reads them one
+  // iteration ahead, so the scalar loads overlap the LDS stores and the
+  // barrier instead of stalling the top of an iteration
+  struct TileIds {
+    int64_t kt, vt;           // K and V tuple ids
+    int32_t tt, T0, t_valid;  // tile inside the tuple, its first key, keys [0, t_valid) that exist
+  };
+  auto tile_ids = [&](int it) {
+    const int e = it / tpe;
+    TileIds r;
+    r.tt = it - e * tpe;
+    r.kt = ents[e * 4 + 2];
+    r.vt = ents[e * 4 + 3];
+    const uint32_t kap = fd_mod(fd_div(uint32_t(r.kt), a.div_Wt), a.div_kt);
+    r.T0 = t_lo(kap) + r.tt * kKeys;
+    int32_t tv = a.e_t - r.tt * kKeys;
+    if (t_end(kap) - r.T0 < tv) tv = t_end(kap) - r.T0;
+    r.t_valid = tv > kKeys ? kKeys : tv;
+    return r;
+  };
   uint4 kr[NP], vr[NP];
-  auto load_tile = [&](int it) {
-    const int e = it / tpe, tt = it - e * tpe;
-    const int64_t kt = ents[e * 4 + 2], vt = ents[e * 4 + 3];
-    const int64_t r0 = int64_t(tt) * kKeys;  // first row of the tile
+  auto load_tile = [&](const TileIds &ti) {
+    const int64_t kt = ti.kt, vt = ti.vt;
+    const int64_t r0 = int64_t(ti.tt) * kKeys;  // first row of the tile
     const int64_t kbase = kt * a.beK + oK + r0 * a.tK, vbase = vt * a.beV + oV + r0 * a.tV;
     const int64_t kend = oK + int64_t(a.e_t - 1) * a.tK + D, vend = oV + int64_t(a.e_t - 1) * a.tV + D;
     const __amdgpu_buffer_rsrc_t rk =
@@ -232,10 +251,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     for (int v = 0; v < 16; ++v) acc[et][v] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
+  TileIds cur{}, nxt{};  // the tile being computed, the one being loaded
   if (n_it > 0) {
-    load_tile(0);
+    cur = tile_ids(0);
+    load_tile(cur);
     store_tile(0);
   }
+  if (n_it > 1) nxt = tile_ids(1);
   // Every global load so far (Q fragments, first tile) has landed: said
   // explicitly (vmcnt(0)), the compiler's wait counting enters the loop with
   // nothing pending and does not make the S^T MFMAs of each tile wait for
@@ -247,14 +269,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   const float scale = a.scale_log2;  // > 0
   for (int it = 0; it < n_it; ++it) {
     const bool more = it + 1 < n_it;
-    if (more) load_tile(it + 1);
-    const int e = it / tpe, tt = it - e * tpe;
-    const uint32_t kap_t = fd_mod(fd_div(uint32_t(ents[e * 4 + 2]), a.div_Wt), a.div_kt);
-    const int32_t T0 = t_lo(kap_t) + tt * kKeys;
-    // keys [0, t_valid) of the tile exist
-    int32_t t_valid = a.e_t - tt * kKeys;
-    if (t_end(kap_t) - T0 < t_valid) t_valid = t_end(kap_t) - T0;
-    if (t_valid > kKeys) t_valid = kKeys;
+    if (more) load_tile(nxt);
+    const int32_t T0 = cur.T0, t_valid = cur.t_valid;
     if (!(CAUSAL && T0 > wave_s_last)) {
       const char *ks = smem + (it & 1) * STAGE;
       const char *vs = ks + KBYTES;
@@ -346,6 +362,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    cur = nxt;
+    if (it + 2 < n_it) nxt = tile_ids(it + 2);
     if (more) store_tile((it + 1) & 1);
     __syncthreads();
   }
