@@ -388,9 +388,14 @@ constexpr bool kShortWalk = JAGG_SHORT_WALK;
 // NSTG: LDS stages.  Two overlap the loads of step s+1 with step s; one
 // (for walks of one or two steps, e.g. a score block with K = 128) halves the
 // LDS so that twice as many workgroups share a CU and overlap each other.
+// The one-stage kernel is bound by its output writes: it asks the compiler
+// for a register allocation that lets four wavefronts share a SIMD (its LDS
+// allows four workgroups per CU), which keeps more stores in flight than the
+// three its default allocation allows.
 template <typename T, int OUT_BF16, bool A_KC, bool B_KC, int VA, int VB, int BM, int BN, int WAVES_M, int WAVES_N,
           bool MASK, int NSTG>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void contract_kernel(const ContractArgs p) {
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64)
+__attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(const ContractArgs p) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
   constexpr int ESZ = int(sizeof(T));
   constexpr int BK = kSlab / ESZ;
