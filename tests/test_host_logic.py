@@ -77,3 +77,18 @@ def test_interval_relation_size_through_the_binding(bounds):
     longest = max(b - a for a, b in zip(bounds, bounds[1:]))
     assert jagg.relation_bytes("ij", [11, 6], [bounds, 2], "f32") == 4 * blocks * longest * 2 * 3
     assert jagg.relation_bytes("ij", [11, 6], [bounds, 2], "bf16") == 2 * blocks * longest * 2 * 3
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The executor has one-GPU scope: bench.py exits with a message before
+    touching a device when asked for several GPUs or started under a
+    multi-rank launcher."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "exactly one GPU" in r.stderr
+    env = dict(os.environ, WORLD_SIZE="4")
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")], capture_output=True, text=True,
+                       timeout=300, env=env)
+    assert r.returncode == 2 and "exactly one GPU" in r.stderr
