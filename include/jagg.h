@@ -1,10 +1,10 @@
 /*
  * jagg.h -- C ABI of the join-agg einsum executor for AMD MI355X (gfx950).
  *
- * A tensor is held as a *tensor relation*: a set of (sub_tensor_key,
- * sub_tensor) tuples, one per block of a blocking of every index ("Every
- * Kernel Is a Join", Ding et al., Sec. 1 and Sec. 3.2; keys are tensor types,
- * Def. 3.1).  An einsum spec is executed as a join-agg spec (Def. 3.6) by the
+ * A tensor is held as a *tensor relation*: one tuple per block of a
+ * blocking of every index, each tuple pairing the block's key (its interval
+ * along every index) with the dense block itself ("Every Kernel Is a Join",
+ * Ding et al., Sec. 1 and Sec. 3.2; keys are tensor types, Def. 3.1).  An einsum spec is executed as a join-agg spec (Def. 3.6) by the
  * three steps of Def. 3.7: join the input tuples whose keys agree on every
  * shared index, apply a block function to each joined tuple, combine the
  * results of equal output key with an associative and commutative
@@ -102,10 +102,16 @@ typedef enum {
  * operand, and every output letter must occur in some input.
  * causal_s / causal_t: 0 for none, else two letters (s, t) of the spec; then
  * only elements with t <= s take part: the join drops every tuple
- * combination whose t-block starts after its s-block ends, terms with t > s
- * are left out of the aggregation, and an output element whose own t > s is
- * written as 0.  A causal pair needs s and t of equal extent and block
- * count.
+ * combination whose t-block starts after its s-block ends and terms with
+ * t > s are left out of the aggregation.  When both s and t are output
+ * letters, an output tuple whose t-block lies after its s-block has no
+ * joined tuple and is absent from the output relation: its storage slot is
+ * neither written nor read by any kernel (it keeps whatever the buffer held,
+ * so a buffer cleared once when allocated keeps +0 there), while inside a
+ * present tuple every element with t > s is written as 0.  A spec under the
+ * same causal pair never reads an absent tuple; any other consumer (a
+ * repartition, a spec without the pair) reads the slot's bytes as they are.
+ * A causal pair needs s and t of equal extent and block count.
  * seg_s / seg_t: 0 for none, else a segment pair (s, t): only elements whose
  * s and t lie in the same block take part, and the join keeps only the
  * combinations whose s and t blocks coincide.  "Every Kernel Is a Join",
@@ -178,8 +184,9 @@ jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64
  * positions as well, so the spec's value must be +0 wherever an interval
  * letter sits in padding: g = MUL, IDENT, SQUARE or SILU_MUL; ADD only when
  * every input holds every interval letter; RMS_SCALE only when its first
- * input does; MAX only over uniformly blocked letters; a causal pair on
- * interval letters only with attention under the same segment pair.
+ * input does and eps > 0 (padded rows compute 0 * rsqrt(eps)); MAX only
+ * over uniformly blocked letters; a causal pair on interval letters only
+ * with attention under the same segment pair.
  * ATTENTION takes interval blocking on its (s, t) letters under a segment
  * pair (packed sequences; see jagg_spec), masking each block by its own
  * interval's length (JAGG_E_UNSUPPORTED otherwise). */

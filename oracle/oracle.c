@@ -11,8 +11,8 @@
  * Computations in Einsummable" (Ding et al.).
  *   - Def. 3.1  tensor type: per index a half-open interval [lower, upper).
  *   - Def. 3.2  tiling: index sets cover the tensor and are pairwise disjoint.
- *   - Sec. 1 / Sec. 3.2  tensor relation: a set of (sub_tensor_key, sub_tensor)
- *               pairs; the key is the tensor type of the sub-tensor.
+ *   - Sec. 1 / Sec. 3.2  tensor relation: the blocks of a tensor, each held
+ *               with its key, the block's tensor type.
  *   - Def. 3.6  join-agg spec; Def. 3.7 implementation = join, aggregate with
  *               an associative and commutative op, recompose.
  *   - Sec. 3.3  one function specification per combination of intervals.

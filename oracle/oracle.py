@@ -365,3 +365,25 @@ def round_to(x, dtype):
     y = np.array(x, dtype=np.float64, copy=True, order="C")
     lib.oracle_round(y.ctypes.data, y.size, DTYPE_CODES[dtype])
     return y
+
+
+def contract(spec, a, b, extents):
+    """A two-operand contraction (g = MUL, aggregation SUM over the letters
+    absent from the output), unrounded float64: the dense form of a
+    contraction, out[o] = sum_r a[...] b[...] ("Every Kernel Is a Join",
+    Sec. 1: a matmul is the join on the inner index followed by SUM).  The
+    library routine numpy.einsum evaluates it in float64 (its BLAS path); it
+    is the same value as ``dense`` up to float64 rounding and is used where
+    the loops of ``dense`` would be too slow (whole token prefixes of a
+    projection)."""
+    ins, out_letters = _parse(spec)
+    if len(ins) != 2:
+        raise OracleError("contract takes two operands")
+    xs = []
+    for lt, x in zip(ins, (a, b)):
+        x = np.asarray(x, dtype=np.float64)
+        want = tuple(int(extents.get(c, -1)) for c in lt)
+        if x.shape != want:
+            raise OracleError(f"input {lt} has shape {x.shape}, expected {want}")
+        xs.append(x)
+    return np.einsum(spec, xs[0], xs[1], optimize=True)

@@ -875,7 +875,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // kernels then compute the padding too, so only specs whose value is +0
 // wherever an interval letter sits in its padding are taken: g = MUL, IDENT,
 // SQUARE or SILU_MUL (a zero factor), ADD when every input holds every
-// interval letter, RMS_SCALE when its first input does; MAX only over
+// interval letter, RMS_SCALE when its first input does and eps > 0; MAX only over
 // uniform letters; no causal pair on interval letters.  Attention takes
 // intervals on its segment pair only (packed sequences): its kernel masks
 // each block by the length of its own interval.
@@ -932,6 +932,10 @@ jagg_status bind_intervals(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relati
     if (sp->agg == JAGG_AGG_MAX)
       for (char c : b.p.reduced)
         if (is_iv(c)) return fail(ctx, JAGG_E_UNSUPPORTED, "MAX over the interval-blocked letter '%c'", c);
+    // padded rows of an RMS scale see x0 = 0 and a sum of squares of 0:
+    // 0 * rsqrt(eps) is +0 only for eps > 0
+    if (sp->g == JAGG_G_RMS_SCALE && !(sp->eps > 0.0f))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "RMS_SCALE over interval-blocked letters needs eps > 0");
     for (int c = 0; c < 26; ++c) {
       if (!b.iv_letter[c]) continue;
       const int first = sp->g == JAGG_G_RMS_SCALE ? 1 : (sp->g == JAGG_G_ADD ? n_in : 0);
@@ -1700,6 +1704,7 @@ jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
     if ((st = plan_relayout(ctx, *b.in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
     reblocks.push_back(ra);
     reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
+    if (ctx->trace) fprintf(stderr, "[jagg] %s: reblock input %d into the workspace\n", spec->einsum, j);
   }
   // launches
   for (size_t i = 0; i < reblocks.size(); ++i)

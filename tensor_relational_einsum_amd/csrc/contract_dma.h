@@ -2,8 +2,8 @@
 // buffer loads that write LDS directly.
 //
 // Same computation as contract_kernel ("Every Kernel Is a Join", Sec. 1 and
-// Examples 3.8/3.9: a join on the shared inner index, then SUM over the
-// joined tuples; one workgroup owns one output tile of one output key and
+// Examples 3.8/3.9: blocks matched on the contracted index, their products
+// added per output block; one workgroup owns one output tile of one output key and
 // accumulates every joined tuple's product in registers), for the case that
 // dominates projection-heavy chains: bf16 operands read as 16-byte vectors,
 // 256 x 256 output tiles, no causal pair on the reduced letter.

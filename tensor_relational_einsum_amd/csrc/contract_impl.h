@@ -1,9 +1,9 @@
 // contract_impl.h -- MFMA block contraction with the SUM aggregation fused.
 //
-// "Every Kernel Is a Join" (Ding et al.), Sec. 1 and Examples 3.8/3.9: a
-// matrix multiply is a join on the shared inner index followed by a SUM;
-// every joined tuple multiplies one block of each input and the products of
-// equal output key are added (Def. 3.7 step 2).  One workgroup owns one
+// "Every Kernel Is a Join" (Ding et al.), Sec. 1 and Examples 3.8/3.9: in a
+// product of two blocked matrices, the pairs of blocks that agree on the
+// contracted index are matched, each pair is multiplied, and the partial
+// products landing on one output block are added (Def. 3.7 step 2).  One workgroup owns one
 // BM x BN tile of one output block (and one batch index) and walks every
 // joined tuple of that output key and the K-tiles of each, accumulating in
 // fp32 registers; the tile is written once, so the aggregation never goes

@@ -181,14 +181,16 @@ class Relation:
     canonical tuple order).  ``extents`` / ``nblocks`` follow ``letters``; an
     entry of ``nblocks`` is a block count or a list of interval bounds."""
 
-    def __init__(self, ctx: Context, letters: str, extents, nblocks, dtype: str, buffer: torch.Tensor | None = None):
+    def __init__(self, ctx: Context, letters: str, extents, nblocks, dtype: str, buffer: torch.Tensor | None = None,
+                 zeroed: bool = False):
         self.ctx, self.letters, self.dtype = ctx, letters, dtype
         self.extents = [int(v) for v in extents]
         self.bounds = [[int(x) for x in b] if isinstance(b, (list, tuple)) else None for b in nblocks]
         self.nblocks = [block_count(b) for b in nblocks]
         nbytes = relation_bytes(letters, self.extents, self._blocks(), dtype)
         if buffer is None:
-            buffer = torch.empty(nbytes // ESZ[dtype], dtype=TORCH_DT[dtype], device=f"cuda:{ctx.device}")
+            alloc = torch.zeros if zeroed else torch.empty
+            buffer = alloc(nbytes // ESZ[dtype], dtype=TORCH_DT[dtype], device=f"cuda:{ctx.device}")
         self.data = buffer
         self.nbytes = nbytes
         h = ctypes.c_void_p()
@@ -200,11 +202,6 @@ class Relation:
 
     def _blocks(self):
         return [b if b is not None else k for b, k in zip(self.bounds, self.nblocks)]
-
-    @property
-    def block_shape(self):
-        return [max(y - x for x, y in zip(b, b[1:])) if b is not None else -(-n // k)
-                for n, k, b in zip(self.extents, self.nblocks, self.bounds)]
 
     def blocking(self) -> dict:
         return dict(zip(self.letters, self._blocks()))
@@ -301,8 +298,11 @@ class EinsumCall:
             for lt, r in zip(ins, self.inputs):
                 for c, n in zip(lt, r.extents):
                     ext[c] = n
+            # under a causal pair on two output letters the tuples above the
+            # block diagonal are absent and never written: clear them once
+            absent = causal is not None and causal[0] in out_letters and causal[1] in out_letters
             out = Relation(ctx, out_letters, [ext[c] for c in out_letters], [blockings.get(c, 1) for c in out_letters],
-                           out_dtype)
+                           out_dtype, zeroed=absent)
         self.out = out
         need = ctypes.c_size_t()
         ctx._check(lib().jagg_einsum_workspace(ctx.handle, ctypes.byref(self.spec), self.in_arr, len(self.inputs),

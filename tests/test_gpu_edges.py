@@ -108,3 +108,74 @@ def test_large_repartition_in_full(ctx):
     assert np.array_equal(bits(src.data), want_src)
     want = O.repartition(want_src, src_l, src_b, dst_l, dst_b, ext)
     assert np.array_equal(bits(dst.data), want)
+
+
+# Causal outputs: a tuple whose t-block lies after its s-block has no joined
+# tuple and is absent from the output relation.  Its slot must be left as it
+# was (never written, never read), while every present tuple -- the masked
+# elements t > s of the diagonal tuples and the padding included -- is exact.
+CAUSAL_OUT_CASES = [
+    # spec, g, agg, extents, blockings, in dtypes, out dtype, positive inputs
+    ("bqsd,bqtd->bqst", "mul", "sum", dict(b=1, q=2, s=300, t=300, d=64), dict(b=1, q=1, s=3, t=3, d=1),
+     ["bf16", "bf16"], "f32", ()),
+    # the LDS-pipelined kernel (256 x 256 tiles) with the mask in its epilogue
+    ("bhsd,bhtd->bhst", "mul", "sum", dict(b=2, h=4, s=1056, t=1056, d=128), dict(b=1, h=1, s=4, t=4, d=1),
+     ["bf16", "bf16"], "f32", ()),
+    ("qst,qs,qs->qst", "exp_sub_div", "none", dict(q=3, s=200, t=200), dict(q=1, s=4, t=4), ["f32", "f32", "f32"],
+     "bf16", (2,)),
+    ("qst,qs,qs->qst", "exp_sub_div", "none", dict(q=3, s=256, t=256), dict(q=1, s=4, t=4), ["f32", "f32", "f32"],
+     "bf16", (2,)),
+]
+
+
+@pytest.mark.parametrize("spec,g,agg,ext,blk,idts,odt,pos", CAUSAL_OUT_CASES)
+def test_causal_absent_tuples_are_never_written(ctx, spec, g, agg, ext, blk, idts, odt, pos):
+    ins, out = spec.split("->")
+    ins = ins.split(",")
+    xs = []
+    for j, (lt, gen, dt) in enumerate(zip(ins, I.streams(41, len(ins)), idts)):
+        x = I.draw(gen, [ext[c] for c in lt], "normal", dt)
+        if j in pos:
+            x = (x.float().abs() + 0.5).to(x.dtype)
+        xs.append(x)
+    rels = [jagg.from_dense(ctx, x.to("cuda"), lt, blk) for x, lt in zip(xs, ins)]
+    call = jagg.EinsumCall(ctx, spec, rels, blk, g=g, agg=agg, out_dtype=odt, causal=("s", "t"))
+    # the binding clears a causal output once when it allocates it
+    assert torch.count_nonzero(call.out.data).item() == 0
+    call.out.data.fill_(float("nan"))
+    call.run()
+    torch.cuda.synchronize()
+    got_rel = to_np(call.out.data)
+    want = O.round_to(O.dense(spec, [to_np(x) for x in xs], ext, g=g, agg=agg, causal=("s", "t")), odt)
+    want_rel = O.to_relation(want, out, ext, blk)
+    # which tuples are present: t-block <= s-block
+    kidx = np.indices([blk[c] for c in out]).reshape(len(out), -1)
+    present = kidx[out.index("t")] <= kidx[out.index("s")]
+    per = got_rel.size // present.size
+    got_t, want_t = got_rel.reshape(present.size, per), want_rel.reshape(present.size, per)
+    assert np.all(np.isnan(got_t[~present])), "an absent tuple's slot was written"
+    assert not np.isnan(got_t[present]).any(), "a present tuple was left unwritten"
+    pad = padding_mask(out, ext, blk).reshape(present.size, per)
+    assert np.all(got_t[present][pad[present]] == 0.0), "padding of present tuples must be +0"
+    # masked elements t > s inside the diagonal tuples are written as 0
+    tmask = O.to_relation(np.triu(np.ones((ext["s"], ext["t"]), dtype=np.uint8), 1)[None].repeat(
+        int(np.prod([ext[c] for c in out[:-2]])), 0).reshape([ext[c] for c in out]), out, ext, blk)
+    tmask = tmask.reshape(present.size, per).astype(bool)
+    assert np.all(got_t[present][tmask[present]] == 0.0), "elements with t > s must be +0"
+    err = normwise_err(got_t[present], want_t[present])
+    tol = F32_TOL if odt == "f32" else 8e-3
+    assert err < tol, f"normwise error {err:.3e}"
+
+
+def test_causal_output_densifies_with_zeros_above_the_diagonal(ctx):
+    """With the binding's zeroed allocation, a densified causal score relation
+    equals the oracle's dense result everywhere (t > s gives +0)."""
+    spec, ext, blk = "qsd,qtd->qst", dict(q=2, s=200, t=200, d=64), dict(q=1, s=4, t=4, d=1)
+    xs = [I.draw(gen, [2, 200, 64], "normal", "bf16") for gen in I.streams(43, 2)]
+    rels = [jagg.from_dense(ctx, x.to("cuda"), lt, blk) for x, lt in zip(xs, ("qsd", "qtd"))]
+    call = jagg.EinsumCall(ctx, spec, rels, blk, causal=("s", "t"))
+    call.run()
+    got = to_np(jagg.to_dense(ctx, call.out))
+    want = O.round_to(O.dense(spec, [to_np(x) for x in xs], ext, causal=("s", "t")), "f32")
+    assert np.all(got[:, np.triu_indices(200, 1)[0], np.triu_indices(200, 1)[1]] == 0.0)
+    assert normwise_err(got, want) < F32_TOL

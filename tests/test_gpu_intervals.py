@@ -224,6 +224,19 @@ def test_interval_einsum_rejects(ctx, spec, g, agg, blk_a, blk_b):
         jagg.EinsumCall(ctx, spec, rels, blk_a, g=g, agg=agg).run()
 
 
+def test_interval_rms_scale_needs_positive_eps(ctx):
+    """A padded row of an interval letter computes 0 * rsqrt(0 * beta + eps):
+    +0 for eps > 0 (checked with padding by test_interval_einsum_parity),
+    NaN for eps = 0, so eps <= 0 is refused before any launch."""
+    ext = dict(s=8, h=8)
+    blk = dict(s=[0, 3, 8], h=2)
+    rels = [make(ctx, lt, ext, blk) for lt in ("sh", "s", "h")]
+    for eps in (0.0, -1e-6):
+        with pytest.raises(jagg.JaggError, match="eps"):
+            jagg.EinsumCall(ctx, "sh,s,h->sh", rels, blk, g="rms_scale", agg="none", beta=0.125, eps=eps).run()
+    jagg.EinsumCall(ctx, "sh,s,h->sh", rels, blk, g="rms_scale", agg="none", beta=0.125, eps=1e-6).run()
+
+
 def test_interval_relation_rejects_bad_bounds(ctx):
     for bnd in ([1, 4, 8], [0, 4, 7], [0, 4, 4, 8], [0, 5, 3, 8]):
         with pytest.raises(jagg.JaggError):

@@ -17,7 +17,7 @@ from oracle import oracle as O
 from tensor_relational_einsum_amd import inputs as I
 from tensor_relational_einsum_amd import jagg
 from tensor_relational_einsum_amd.runner import ChainRunner
-from parity_util import bits, normwise_err, oracle_bits, padding_mask, rel_dense, to_np
+from parity_util import bits, normwise_err, oracle_bits, oracle_chain, padding_mask, rel_dense, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -437,36 +437,6 @@ def test_bf16_rounding_bit_exact(trace_ctx):
 
 
 # ----------------------------------------------------------------- chains
-
-def oracle_chain(w, dense, stop=None):
-    """Evaluates a workload chain on the oracle, rounding each result to its
-    stored dtype exactly where the HIP path stores it."""
-    vals = {k: to_np(v) for k, v in dense.items()}
-    for st in w.chain:
-        if isinstance(st, I.Step):
-            ins = st.spec.split("->")[0].split(",")
-            xs = []
-            for name, lt in zip(st.ins, ins):
-                xs.append(vals[name])
-            if st.g == "attention":
-                y = O.attention_dense(st.spec, xs, w.extents, alpha=st.alpha, causal=st.causal)
-            else:
-                y = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
-                            causal=st.causal)
-            vals[st.out] = O.round_to(y, st.out_dtype)
-        else:
-            src_letters = None
-            for t in w.tensors:
-                if t[0] == st.src:
-                    src_letters = t[1]
-            if src_letters is None:
-                src_letters = next(s for s in w.chain if getattr(s, "out", None) == st.src).spec.split("->")[1]
-            perm = [src_letters.index(c) for c in st.letters]
-            vals[st.out] = np.ascontiguousarray(vals[st.src].transpose(perm))
-        if stop is not None and st.out == stop:
-            break
-    return vals
-
 
 def test_attention_chain_small(ctx):
     w = I.attention_chain(b=1, h=2, s=256, d=64, nb=4)

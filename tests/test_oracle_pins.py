@@ -429,3 +429,29 @@ def test_example_5_4_reblocking():
     per = f["per_producer_block"][0]
     for p in range(kp):
         assert np.array_equal(pblocks[p], np.concatenate(list(blocks[p * per:(p + 1) * per])))
+
+
+@pytest.mark.parametrize("spec,ext", [
+    ("ij,jk->ik", dict(i=7, j=13, k=5)),
+    ("bsh,hqd->bsqd", dict(b=2, s=5, h=12, q=3, d=4)),
+    ("bsqd,qdh->bsh", dict(b=2, s=5, h=12, q=3, d=4)),
+    ("bsf,fh->bsh", dict(b=1, s=6, f=9, h=7)),
+    ("abcd,cde->abe", dict(a=3, b=4, c=5, d=2, e=6)),
+])
+def test_blas_contraction_equals_dense_loops(spec, ext):
+    """O.contract (numpy's float64 BLAS path) against O.dense's plain loops."""
+    ins, _ = spec.split("->")
+    gens = np.random.default_rng(7)
+    xs = [gens.standard_normal([ext[c] for c in lt]) for lt in ins.split(",")]
+    want = O.dense(spec, xs, ext)
+    got = O.contract(spec, xs[0], xs[1], ext)
+    assert got.shape == want.shape
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_blas_contraction_closed_form():
+    """Rank-one operands: A[i,j] = u_i v_j and B[j,k] = v_j w_k give
+    C[i,k] = u_i w_k sum_j v_j^2 exactly (small integers, no rounding)."""
+    u, v, w = np.arange(1, 5.0), np.array([1.0, -2.0, 3.0]), np.array([2.0, 0.0, -1.0, 5.0, 1.0])
+    C = O.contract("ij,jk->ik", np.outer(u, v), np.outer(v, w), dict(i=4, j=3, k=5))
+    assert np.array_equal(C, np.outer(u, w) * 14.0)
