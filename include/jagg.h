@@ -230,6 +230,24 @@ jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const ja
 jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
                         const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes);
 
+/* jagg_einsum without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It runs the same kernels as jagg_einsum
+ * on the same arguments, with the workspace taken from a static device array
+ * of JAGG_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends (its address is fetched once per device,
+ * in jagg_ctx_create).  It allocates nothing.
+ * A call whose workspace (jagg_einsum_workspace) exceeds the scratch is
+ * refused with JAGG_E_WORKSPACE before any launch.  Nothing in the scratch
+ * needs clearing between calls: the join kernel writes every list slot and
+ * key count, and a re-blocking copy writes every byte it later reads.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (several streams or contexts in flight at once) race and must be
+ * serialised by the caller; calls queued on one stream are ordered. */
+#define JAGG_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+jagg_status jagg_einsum_noalloc(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                                const int32_t *blockings, jagg_relation *out);
+
 /* Number of output keys and reduced-letter combinations per key of the join
  * of this spec under `blockings`; host only. */
 jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter,

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -29,6 +30,7 @@ struct jagg_ctx {
   bool trace;
   bool debug_sync;
   bool capturing;  // between jagg_capture_begin and jagg_capture_end
+  void *scratch;   // this device's copy of `scratch` (jagg_einsum_noalloc)
 };
 
 struct jagg_graph {
@@ -53,7 +55,30 @@ struct jagg_relation {
   int64_t bnd[kMaxLetters][kMaxIv + 1];
 };
 
+// Workspace of jagg_einsum_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never names it directly (the
+// name is a host-side stand-in there); it uses the device address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+static __device__ __align__(256) char scratch[JAGG_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch (device must be current); once per device.
+hipError_t scratch_of_device(int device, void **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 jagg_status fail(jagg_ctx *ctx, jagg_status s, const char *fmt, ...) {
   if (ctx) {
@@ -1422,6 +1447,161 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
   return JAGG_OK;
 }
 
+// jagg_einsum's body; `noalloc` marks the static scratch as the workspace
+// (a size error then names the scratch limit).
+jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                        const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes,
+                        bool noalloc) {
+  if (!ctx || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  Bound b;
+  jagg_status st = bind(ctx, spec, in, n_in, blockings, b);
+  if (st != JAGG_OK) return st;
+  // output relation must be the spec's output under `blockings`
+  if (out->r != int(b.p.out.size()))
+    return fail(ctx, JAGG_E_SHAPE, "out relation has %d dimensions, output '%s' names %d", out->r, b.p.out.c_str(),
+                int(b.p.out.size()));
+  jagg_relation out_view = *out;  // interval letters as uniform ones, like the inputs
+  for (int q = 0; q < out->r; ++q) {
+    const int c = b.p.out[q] - 'a';
+    if (out->iv[q] != int32_t(b.iv_letter[c]))
+      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' must be %s-blocked like the inputs", 'a' + c,
+                  b.iv_letter[c] ? "interval" : "uniformly");
+    if (out->iv[q]) {
+      if (out->k[q] != b.L.k[c] ||
+          memcmp(out->bnd[q], b.iv_bnd[c], sizeof(int64_t) * size_t(out->k[q] + 1)) != 0)
+        return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has other bounds than the inputs", 'a' + c);
+      out_view.n[q] = int64_t(out->k[q]) * out->e[q];
+      out_view.iv[q] = 0;
+    }
+    if (out_view.n[q] != b.L.n[c])
+      return fail(ctx, JAGG_E_SHAPE, "out letter '%c' has extent %lld, expected %lld", 'a' + c, (long long)out->n[q],
+                  (long long)b.L.n[c]);
+    if (out->k[q] != b.L.k[c])
+      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has %d blocks, the spec asks %d", 'a' + c, out->k[q], b.L.k[c]);
+  }
+  out = &out_view;
+  if (out->dt != spec->out_dtype) return fail(ctx, JAGG_E_SHAPE, "out relation dtype differs from spec->out_dtype");
+  {
+    const char *ob = static_cast<const char *>(out->buf);
+    const size_t on = size_t(out->n_tuples * out->be) * esz_of(out->dt);
+    for (int j = 0; j < n_in; ++j) {
+      const char *ib = static_cast<const char *>(in[j]->buf);
+      const size_t inn = size_t(in[j]->n_tuples * in[j]->be) * esz_of(in[j]->dt);
+      if (ib < ob + on && ob < ib + inn) return fail(ctx, JAGG_E_INVALID, "out relation overlaps input %d", j);
+    }
+  }
+  if (noalloc && b.total > ws_bytes)
+    return fail(ctx, JAGG_E_WORKSPACE, "the call needs %zu bytes of workspace; the static scratch holds %zu",
+                b.total, ws_bytes);
+  if (!workspace || ws_bytes < b.total)
+    return fail(ctx, JAGG_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, b.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(ctx, JAGG_E_WORKSPACE, "workspace not 256-byte aligned");
+
+  // classify before launching anything: a contraction is a MUL/SUM over two
+  // inputs where every reduced letter is in both inputs and each input
+  // contributes output letters of its own; any other aggregating spec is a
+  // streaming reduce, and a spec without aggregation is a map.
+  enum { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
+  if (spec->agg == JAGG_AGG_SOFTMAX) {
+    kind = ATTENTION;
+  } else if (spec->agg != JAGG_AGG_NONE) {
+    kind = REDUCE;
+    if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
+      bool both = true, m_any = false, n_any = false;
+      for (char c : b.p.reduced)
+        both = both && b.p.in[0].find(c) != std::string::npos && b.p.in[1].find(c) != std::string::npos;
+      for (char c : b.p.out) {
+        const bool i0 = b.p.in[0].find(c) != std::string::npos, i1 = b.p.in[1].find(c) != std::string::npos;
+        m_any = m_any || (i0 && !i1);
+        n_any = n_any || (i1 && !i0);
+      }
+      if (both && m_any && n_any) kind = CONTRACT;
+    }
+  }
+
+  char *ws = static_cast<char *>(workspace);
+  int32_t *list = reinterpret_cast<int32_t *>(ws);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + b.list_bytes);
+  size_t off = b.list_bytes + b.counts_bytes;
+  // (0) inputs blocked differently: re-block into the workspace
+  jagg_relation tmp[kMaxIn];
+  const jagg_relation *use[kMaxIn];
+  for (int j = 0; j < n_in; ++j) {
+    use[j] = b.in[j];
+    if (!b.needs_reblock[j]) continue;
+    jagg_relation &T = tmp[j];
+    T = *b.in[j];
+    for (int q = 0; q < T.r; ++q) T.k[q] = b.L.k[b.p.in[j][q] - 'a'];
+    if ((st = geometry(ctx, T.r, T.n, T.k, nullptr, T.e, &T.n_tuples, &T.be)) != JAGG_OK) return st;
+    T.buf = ws + off;
+    T.bytes = b.reblock_bytes[j];
+    off += b.reblock_bytes[j];
+    use[j] = &T;
+  }
+  // plan the block kernel (host only) before any launch
+  EwArgs ew;
+  ContractArgs ca;
+  int dtype = 0, va = 1, vb = 1;
+  bool akc = true, bkc = true;
+  if (kind == CONTRACT) {
+    if ((st = plan_contract(ctx, spec, b, use, out, list, counts, ca, dtype, akc, bkc, va, vb)) != JAGG_OK) return st;
+  }
+  AttnArgs at;
+  int att_d = 0;
+  if (kind == ATTENTION && (st = plan_attention(ctx, spec, b, use, out, list, counts, at, att_d)) != JAGG_OK)
+    return st;
+  if ((kind == MAP || kind == REDUCE) && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK)
+    return st;
+  std::vector<RelayoutArgs> reblocks;
+  std::vector<int> reblock_vec;
+  for (int j = 0; j < n_in; ++j) {
+    if (!b.needs_reblock[j]) continue;
+    RelayoutArgs ra;
+    int vbytes = 0;
+    if ((st = plan_relayout(ctx, *b.in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
+    reblocks.push_back(ra);
+    reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
+    if (ctx->trace) fprintf(stderr, "[jagg] %s: reblock input %d into the workspace\n", spec->einsum, j);
+  }
+  // launches
+  for (size_t i = 0; i < reblocks.size(); ++i)
+    if ((st = after_launch(ctx, launch_relayout(reblocks[i], reblock_vec[i] / 16, reblock_vec[i] % 16, ctx->stream),
+                           "reblock input")) != JAGG_OK)
+      return st;
+  b.join.list = list;
+  b.join.counts = counts;
+  if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
+  if (kind == ATTENTION) {
+    const hipError_t e = launch_attention(at, att_d, spec->causal_s != 0, spec->out_dtype == JAGG_BF16, ctx->stream);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: attention d%d, %d keys x %d batch x %d s-tiles\n", spec->einsum, att_d, at.n_keys,
+              at.nbatch, at.s_tiles);
+    return after_launch(ctx, e, "attention");
+  }
+  if (kind == CONTRACT) {
+    // 256x256 tiles where the block is large enough and the grid still fills the chip
+    const int F = dtype ? 8 : 4;
+    const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + 255) / 256);
+    const bool big = va == F && vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
+    // per-XCD renumbering pays where several tiles of one output block share panels
+    const int bm = big ? 256 : 128;
+    ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
+    ca.group_m = (ca.remap && ca.km > 0 && ca.batch == 1) ? kGroupM : 0;
+    const int ob = spec->out_dtype == JAGG_BF16;
+    const char *which = "";
+    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which)
+                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", spec->einsum, which, (long long)ca.n_keys,
+              ca.batch);
+    return after_launch(ctx, e, "contract");
+  }
+  const char *which = "";
+  const hipError_t e = launch_ew(ctx, ew, spec->agg, &which);
+  if (ctx->trace) fprintf(stderr, "[jagg] %s: %s, %lld keys\n", spec->einsum, which, (long long)ew.n_keys);
+  return after_launch(ctx, e, which);
+}
+
 const char *env_or(const char *k) {
   const char *v = getenv(k);
   return v ? v : "";
@@ -1436,10 +1616,13 @@ jagg_status jagg_ctx_create(int device, void *hip_stream, jagg_ctx **out) {
   if (!out) return JAGG_E_INVALID;
   *out = nullptr;
   int n = 0;
-  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return JAGG_E_DEVICE;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n || device >= kMaxDevices) return JAGG_E_DEVICE;
   if (hipSetDevice(device) != hipSuccess) return JAGG_E_DEVICE;
+  void *scr = nullptr;
+  if (scratch_of_device(device, &scr) != hipSuccess || !scr) return JAGG_E_DEVICE;
   jagg_ctx *c = new jagg_ctx;
   c->device = device;
+  c->scratch = scr;
   c->stream = reinterpret_cast<hipStream_t>(hip_stream);
   c->trace = env_or("JAGG_TRACE")[0] == '1';
   c->debug_sync = env_or("JAGG_DEBUG_SYNC")[0] == '1';
@@ -1598,151 +1781,13 @@ jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const ja
 
 jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
                         const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes) {
-  if (!ctx || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
-  Bound b;
-  jagg_status st = bind(ctx, spec, in, n_in, blockings, b);
-  if (st != JAGG_OK) return st;
-  // output relation must be the spec's output under `blockings`
-  if (out->r != int(b.p.out.size()))
-    return fail(ctx, JAGG_E_SHAPE, "out relation has %d dimensions, output '%s' names %d", out->r, b.p.out.c_str(),
-                int(b.p.out.size()));
-  jagg_relation out_view = *out;  // interval letters as uniform ones, like the inputs
-  for (int q = 0; q < out->r; ++q) {
-    const int c = b.p.out[q] - 'a';
-    if (out->iv[q] != int32_t(b.iv_letter[c]))
-      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' must be %s-blocked like the inputs", 'a' + c,
-                  b.iv_letter[c] ? "interval" : "uniformly");
-    if (out->iv[q]) {
-      if (out->k[q] != b.L.k[c] ||
-          memcmp(out->bnd[q], b.iv_bnd[c], sizeof(int64_t) * size_t(out->k[q] + 1)) != 0)
-        return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has other bounds than the inputs", 'a' + c);
-      out_view.n[q] = int64_t(out->k[q]) * out->e[q];
-      out_view.iv[q] = 0;
-    }
-    if (out_view.n[q] != b.L.n[c])
-      return fail(ctx, JAGG_E_SHAPE, "out letter '%c' has extent %lld, expected %lld", 'a' + c, (long long)out->n[q],
-                  (long long)b.L.n[c]);
-    if (out->k[q] != b.L.k[c])
-      return fail(ctx, JAGG_E_BLOCKING, "out letter '%c' has %d blocks, the spec asks %d", 'a' + c, out->k[q], b.L.k[c]);
-  }
-  out = &out_view;
-  if (out->dt != spec->out_dtype) return fail(ctx, JAGG_E_SHAPE, "out relation dtype differs from spec->out_dtype");
-  {
-    const char *ob = static_cast<const char *>(out->buf);
-    const size_t on = size_t(out->n_tuples * out->be) * esz_of(out->dt);
-    for (int j = 0; j < n_in; ++j) {
-      const char *ib = static_cast<const char *>(in[j]->buf);
-      const size_t inn = size_t(in[j]->n_tuples * in[j]->be) * esz_of(in[j]->dt);
-      if (ib < ob + on && ob < ib + inn) return fail(ctx, JAGG_E_INVALID, "out relation overlaps input %d", j);
-    }
-  }
-  if (!workspace || ws_bytes < b.total)
-    return fail(ctx, JAGG_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, b.total);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(ctx, JAGG_E_WORKSPACE, "workspace not 256-byte aligned");
+  return einsum_impl(ctx, spec, in, n_in, blockings, out, workspace, ws_bytes, false);
+}
 
-  // classify before launching anything: a contraction is a MUL/SUM over two
-  // inputs where every reduced letter is in both inputs and each input
-  // contributes output letters of its own; any other aggregating spec is a
-  // streaming reduce, and a spec without aggregation is a map.
-  enum { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
-  if (spec->agg == JAGG_AGG_SOFTMAX) {
-    kind = ATTENTION;
-  } else if (spec->agg != JAGG_AGG_NONE) {
-    kind = REDUCE;
-    if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
-      bool both = true, m_any = false, n_any = false;
-      for (char c : b.p.reduced)
-        both = both && b.p.in[0].find(c) != std::string::npos && b.p.in[1].find(c) != std::string::npos;
-      for (char c : b.p.out) {
-        const bool i0 = b.p.in[0].find(c) != std::string::npos, i1 = b.p.in[1].find(c) != std::string::npos;
-        m_any = m_any || (i0 && !i1);
-        n_any = n_any || (i1 && !i0);
-      }
-      if (both && m_any && n_any) kind = CONTRACT;
-    }
-  }
-
-  char *ws = static_cast<char *>(workspace);
-  int32_t *list = reinterpret_cast<int32_t *>(ws);
-  int32_t *counts = reinterpret_cast<int32_t *>(ws + b.list_bytes);
-  size_t off = b.list_bytes + b.counts_bytes;
-  // (0) inputs blocked differently: re-block into the workspace
-  jagg_relation tmp[kMaxIn];
-  const jagg_relation *use[kMaxIn];
-  for (int j = 0; j < n_in; ++j) {
-    use[j] = b.in[j];
-    if (!b.needs_reblock[j]) continue;
-    jagg_relation &T = tmp[j];
-    T = *b.in[j];
-    for (int q = 0; q < T.r; ++q) T.k[q] = b.L.k[b.p.in[j][q] - 'a'];
-    if ((st = geometry(ctx, T.r, T.n, T.k, nullptr, T.e, &T.n_tuples, &T.be)) != JAGG_OK) return st;
-    T.buf = ws + off;
-    T.bytes = b.reblock_bytes[j];
-    off += b.reblock_bytes[j];
-    use[j] = &T;
-  }
-  // plan the block kernel (host only) before any launch
-  EwArgs ew;
-  ContractArgs ca;
-  int dtype = 0, va = 1, vb = 1;
-  bool akc = true, bkc = true;
-  if (kind == CONTRACT) {
-    if ((st = plan_contract(ctx, spec, b, use, out, list, counts, ca, dtype, akc, bkc, va, vb)) != JAGG_OK) return st;
-  }
-  AttnArgs at;
-  int att_d = 0;
-  if (kind == ATTENTION && (st = plan_attention(ctx, spec, b, use, out, list, counts, at, att_d)) != JAGG_OK)
-    return st;
-  if ((kind == MAP || kind == REDUCE) && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK)
-    return st;
-  std::vector<RelayoutArgs> reblocks;
-  std::vector<int> reblock_vec;
-  for (int j = 0; j < n_in; ++j) {
-    if (!b.needs_reblock[j]) continue;
-    RelayoutArgs ra;
-    int vbytes = 0;
-    if ((st = plan_relayout(ctx, *b.in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
-    reblocks.push_back(ra);
-    reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
-    if (ctx->trace) fprintf(stderr, "[jagg] %s: reblock input %d into the workspace\n", spec->einsum, j);
-  }
-  // launches
-  for (size_t i = 0; i < reblocks.size(); ++i)
-    if ((st = after_launch(ctx, launch_relayout(reblocks[i], reblock_vec[i] / 16, reblock_vec[i] % 16, ctx->stream),
-                           "reblock input")) != JAGG_OK)
-      return st;
-  b.join.list = list;
-  b.join.counts = counts;
-  if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
-  if (kind == ATTENTION) {
-    const hipError_t e = launch_attention(at, att_d, spec->causal_s != 0, spec->out_dtype == JAGG_BF16, ctx->stream);
-    if (ctx->trace)
-      fprintf(stderr, "[jagg] %s: attention d%d, %d keys x %d batch x %d s-tiles\n", spec->einsum, att_d, at.n_keys,
-              at.nbatch, at.s_tiles);
-    return after_launch(ctx, e, "attention");
-  }
-  if (kind == CONTRACT) {
-    // 256x256 tiles where the block is large enough and the grid still fills the chip
-    const int F = dtype ? 8 : 4;
-    const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + 255) / 256);
-    const bool big = va == F && vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
-    // per-XCD renumbering pays where several tiles of one output block share panels
-    const int bm = big ? 256 : 128;
-    ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
-    ca.group_m = (ca.remap && ca.km > 0 && ca.batch == 1) ? kGroupM : 0;
-    const int ob = spec->out_dtype == JAGG_BF16;
-    const char *which = "";
-    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which)
-                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which);
-    if (ctx->trace)
-      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", spec->einsum, which, (long long)ca.n_keys,
-              ca.batch);
-    return after_launch(ctx, e, "contract");
-  }
-  const char *which = "";
-  const hipError_t e = launch_ew(ctx, ew, spec->agg, &which);
-  if (ctx->trace) fprintf(stderr, "[jagg] %s: %s, %lld keys\n", spec->einsum, which, (long long)ew.n_keys);
-  return after_launch(ctx, e, which);
+jagg_status jagg_einsum_noalloc(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                                const int32_t *blockings, jagg_relation *out) {
+  if (!ctx) return JAGG_E_INVALID;
+  return einsum_impl(ctx, spec, in, n_in, blockings, out, ctx->scratch, JAGG_NOALLOC_SCRATCH_BYTES, true);
 }
 
 jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter, const int32_t *blockings,

@@ -22,8 +22,11 @@ ESZ = {"f32": 4, "bf16": 2}
 STATUS = {0: "ok", -1: "invalid argument", -2: "shape mismatch", -3: "bad blocking", -4: "unsupported spec",
           -5: "workspace too small", -6: "device error"}
 
+NOALLOC_SCRATCH_BYTES = 32 << 20  # JAGG_NOALLOC_SCRATCH_BYTES in jagg.h
+
 EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
-           "jagg_relation_bytes_iv", "jagg_relation_create_iv", "jagg_relation_destroy", "jagg_repartition", "jagg_einsum_workspace", "jagg_einsum", "jagg_join_shape",
+           "jagg_relation_bytes_iv", "jagg_relation_create_iv", "jagg_relation_destroy", "jagg_repartition",
+           "jagg_einsum_workspace", "jagg_einsum", "jagg_einsum_noalloc", "jagg_join_shape",
            "jagg_join_list", "jagg_capture_begin", "jagg_capture_end", "jagg_graph_launch", "jagg_graph_destroy",
            "jagg_status_str", "jagg_last_error"]
 
@@ -72,6 +75,7 @@ def lib():
                                             ctypes.POINTER(ctypes.c_size_t)]
         L.jagg_einsum.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp, vp,
                                   ctypes.c_size_t]
+        L.jagg_einsum_noalloc.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp]
         L.jagg_join_shape.argtypes = [ctypes.POINTER(jagg_spec), i64p, i32p, i64p, i64p]
         L.jagg_join_list.argtypes = [vp, ctypes.POINTER(jagg_spec), i64p, i32p, vp, vp]
         L.jagg_capture_begin.argtypes = [vp]
@@ -317,6 +321,14 @@ class EinsumCall:
                                           self.blk, self.out.handle, ctypes.c_void_p(self.workspace.data_ptr()),
                                           self.workspace.numel()))
         return self.out
+
+    def run_noalloc(self, out: Relation | None = None) -> Relation:
+        """The same spec through jagg_einsum_noalloc (the library's static
+        device scratch instead of this call's workspace)."""
+        out = out if out is not None else self.out
+        self.ctx._check(lib().jagg_einsum_noalloc(self.ctx.handle, ctypes.byref(self.spec), self.in_arr,
+                                                  len(self.inputs), self.blk, out.handle))
+        return out
 
 
 def einsum(ctx: Context, einsum: str, inputs, blockings: dict, out: Relation | None = None, **kw) -> Relation:

@@ -158,3 +158,10 @@ def test_product_and_oracle_do_not_import_each_other():
         if f.endswith((".py", ".c")):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "tensor_relational_einsum_amd" not in text and "jagg.h" not in text, f
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define JAGG_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "JAGG_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == jagg.NOALLOC_SCRATCH_BYTES
