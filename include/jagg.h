@@ -154,7 +154,9 @@ jagg_status jagg_relation_bytes(const char *letters, const int64_t *extents, con
  * `buf_bytes` bytes (at least jagg_relation_bytes(), 16-byte aligned).
  * letters[i] names dimension i, extents[i] >= 1 its extent, nblocks[i] its
  * block count.  Host metadata only; nothing is launched, the buffer is not
- * touched.  Limits: at most 8 letters, at most 2^31 elements. */
+ * touched.  Limits: at most 8 letters, fewer than 2^36 elements and 2^31
+ * tuples (a block kernel may ask less of its blocks: JAGG_E_UNSUPPORTED from
+ * the call that would run it). */
 jagg_status jagg_relation_create(jagg_ctx *ctx, const char *letters, const int64_t *extents,
                                  const int32_t *nblocks, jagg_dtype dtype, void *dev_buf, size_t buf_bytes,
                                  jagg_relation **out);

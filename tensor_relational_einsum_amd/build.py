@@ -22,6 +22,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 
 
+CALIB_LIB = os.path.join(HERE, "libjagg_calib.so")
+
+
+def build_calib() -> str:
+    """libjagg_calib.so: the matrix-core probe the benchmark measures the
+    machine's MFMA rate with (include/jagg_calib.h)."""
+    tmp = CALIB_LIB + ".tmp"
+    subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "calib.hip"), "-o", tmp], check=True)
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     procs = []
@@ -48,6 +60,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
     os.replace(tmp, LIB)
+    build_calib()
     return LIB
 
 

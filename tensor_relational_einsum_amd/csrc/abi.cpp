@@ -419,6 +419,7 @@ static bool plan_relayout_lds(const std::vector<Dim> &dims, int esz, int v, Rela
     a.tile[i] = {outer[i].ext, outer[i].src, outer[i].dst, -1, 0, make_fastdiv(uint32_t(outer[i].ext))};
   for (int i = int(outer.size()); i < kMaxLdsOuter; ++i) a.tile[i] = {1, 0, 0, -1, 0, make_fastdiv(1)};
   a.n_lane = 0;
+  if (n_tiles >= (int64_t(1) << 31)) return false;
   a.n_tiles = n_tiles;
   a.lanes = 256;
   return true;
@@ -593,6 +594,10 @@ jagg_status plan_relayout(jagg_ctx *ctx, const jagg_relation &S, const jagg_rela
   a.n_lane = int(lane.size());
   for (size_t i = 0; i < lane.size(); ++i)
     a.lane[i] = {lane[i].ext, lane[i].src, lane[i].dst, lane[i].chk, lane[i].xs, make_fastdiv(uint32_t(lane[i].ext))};
+  // the kernels count tiles in 32 bits
+  if (n_tiles >= (int64_t(1) << 31))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "relayout of %lld tiles of %lld vectors exceeds 2^31 tiles",
+                (long long)n_tiles, (long long)lanes);
   a.n_tiles = n_tiles;
   a.lanes = int32_t(lanes);
   a.src = S.buf;
@@ -847,6 +852,9 @@ jagg_status plan_relayout_iv(jagg_ctx *ctx, const jagg_relation &S, const jagg_r
     if (ok) break;
   }
   a.v = v;
+  // the interval kernels index both relations with 32-bit element offsets
+  if (S.n_tuples * S.be >= (int64_t(1) << 31) || D.n_tuples * D.be >= (int64_t(1) << 31))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "an interval relayout takes relations under 2^31 elements");
   a.n_vec = uint32_t(D.n_tuples * D.be / v);
   a.be_v = make_fastdiv(uint32_t(D.be / v));
   vec_bytes = v * esz;
@@ -1732,8 +1740,13 @@ jagg_status jagg_relation_create_iv(jagg_ctx *ctx, const char *letters, const in
       R.iv[i] = 1;
       for (int j = 0; j <= R.k[i]; ++j) R.bnd[i][j] = bounds[i][j];
     }
+  // offsets across a relation are 64-bit in every kernel and tuple ids
+  // 32-bit; each block kernel's planner checks the block sizes it takes
   const int64_t elems = R.n_tuples * R.be;
-  if (elems >= (int64_t(1) << 31)) return fail(ctx, JAGG_E_UNSUPPORTED, "relation of %lld elements exceeds 2^31", (long long)elems);
+  if (elems >= kMaxRelationElems)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "relation of %lld elements reaches 2^36", (long long)elems);
+  if (R.n_tuples >= (int64_t(1) << 31))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "relation of %lld tuples reaches 2^31", (long long)R.n_tuples);
   const size_t need = size_t(elems) * size_t(esz_of(dtype));
   if (!dev_buf) return fail(ctx, JAGG_E_INVALID, "NULL device buffer");
   if (reinterpret_cast<uintptr_t>(dev_buf) % 16) return fail(ctx, JAGG_E_INVALID, "device buffer not 16-byte aligned");

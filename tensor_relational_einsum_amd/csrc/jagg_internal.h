@@ -8,6 +8,7 @@
 namespace jagg {
 
 constexpr int kMaxLetters = 8;   // per relation
+constexpr int64_t kMaxRelationElems = int64_t(1) << 36;  // elements of one relation
 constexpr int kMaxIn = 3;        // inputs per spec
 constexpr int kMaxDims = 24;     // relayout dims after splitting (<= 3 per letter)
 constexpr int kMaxChk = 8;       // relayout letters whose range must be checked

@@ -9,7 +9,12 @@ Random numbers: ``numpy.random.Generator(PCG64)`` seeded from
 ``SeedSequence(1000 + config)``, one spawned child stream per tensor, in the
 order the tensors are listed in each recipe.  uniform[-1, 1) and N(0, sigma^2)
 are drawn in float64, cast to float32, and rounded to bfloat16 (torch's CPU
-cast, round-to-nearest-even) where the tensor is bfloat16.
+cast, round-to-nearest-even) where the tensor is bfloat16.  The matrix chains
+(up to 3.8e9 elements per chain) use ``normal32`` instead: the tensor's
+stream spawns 64 children, child c draws the c-th of 64 equal flat chunks
+as float32 N(0, 1), which is scaled by sigma in float32 and rounded to
+bfloat16; the chunks are drawn on 16 threads, and the values do not depend
+on the thread count.
 """
 from __future__ import annotations
 
@@ -25,9 +30,43 @@ def streams(seed: int, n: int):
     return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(n)]
 
 
+N_CHUNKS = 64
+
+
+def _normal32(gen, shape, sigma: float) -> np.ndarray:
+    """float32 N(0, sigma^2) in N_CHUNKS flat chunks, chunk c from the c-th
+    child of the stream's seed sequence (drawn on a thread pool)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    kids = gen.bit_generator.seed_seq.spawn(N_CHUNKS)
+    bounds = [n * c // N_CHUNKS for c in range(N_CHUNKS + 1)]
+
+    def fill(c):
+        seg = out[bounds[c]:bounds[c + 1]]
+        np.random.Generator(np.random.PCG64(kids[c])).standard_normal(seg.size, dtype=np.float32, out=seg)
+        if sigma != 1.0:
+            np.multiply(seg, np.float32(sigma), out=seg)
+
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(fill, range(N_CHUNKS)))
+    return out.reshape(shape)
+
+
 def draw(gen, shape, dist: str, dtype: str, sigma: float = 1.0, mean: float = 0.0) -> torch.Tensor:
-    """One tensor from one stream. dist: 'uniform' (on [-1,1)), 'normal'."""
+    """One tensor from one stream. dist: 'uniform' (on [-1,1)), 'normal',
+    'normal32' (float32 draws in chunks; mean 0 only)."""
     shape = tuple(int(s) for s in shape)
+    if dist == "normal32":
+        if mean != 0.0:
+            raise ValueError("normal32 draws have mean 0")
+        t = torch.from_numpy(_normal32(gen, shape, sigma))
+        if dtype == "bf16":
+            return t.to(torch.bfloat16)
+        if dtype != "f32":
+            raise ValueError(dtype)
+        return t
     if dist == "uniform":
         x = gen.uniform(-1.0, 1.0, size=shape)
     elif dist == "normal":
@@ -255,6 +294,65 @@ def multi_index(a=96, b=300, c=64, d=48, e=1000, blk=(5, 7, 4, 3, 6)) -> Workloa
         name=f"contract_abcd_cde_{a}x{b}x{c}x{d}x{e}_fp32_blk" + "".join(map(str, blk)), extents=ext,
         tensors=[("A", "abcd", "uniform", "f32", 1.0, 0.0, bl), ("B", "cde", "uniform", "f32", 1.0, 0.0, bl)],
         chain=[Step("C", "abcd,cde->abe", ["A", "B"], "mul", "sum", "f32", bl)], seed=1005)
+
+
+# Matrix chains A-E ("Every Kernel Is a Join", Sec. 6, the second workload
+# family): dimensions d_0 .. d_n (matrix M_i is d_(i-1) x d_i) and the printed
+# parenthesization, as nested tuples of 1-based matrix numbers.
+CHAINS = {
+    # nine matrices, interior dimensions alternating 16384 and 6144, ends 10240
+    "A": ([10240] + [16384, 6144] * 4 + [10240], (((1, 2), ((3, 4), ((5, 6), (7, 8)))), 9)),
+    # five matrices, interior alternating 20480 and 5120, ends 9216
+    "B": ([9216, 20480, 5120, 20480, 5120, 9216], ((1, 2), ((3, 4), 5))),
+    # three matrices 10240 x 12288 x 32768 x 2048, right-associated
+    "C": ([10240, 12288, 32768, 2048], (1, (2, 3))),
+    # nine matrices: ends 24576, necks 1536, interior 20480
+    "D": ([24576, 1536] + [20480] * 6 + [1536, 24576], ((1, (2, (3, (4, (5, (6, (7, 8))))))), 9)),
+    # thirteen matrices: ends 49152, necks 1024, interior 20480
+    "E": ([49152, 1024] + [20480] * 10 + [1024, 49152],
+          ((1, (2, (3, (4, (5, (6, (7, (8, (9, (10, (11, 12))))))))))), 13)),
+}
+CHAIN_LETTERS = "abcdefghijklmnopqrstuvwxyz"
+
+
+def chain_blocks(n: int) -> int:
+    """Blocks per chain index: 4 where that leaves blocks that are multiples
+    of 256, else 2 (the 1536-wide necks: 768-wide blocks)."""
+    return 4 if n % 1024 == 0 else (2 if n % 512 == 0 else 1)
+
+
+def matrix_chain(label: str) -> Workload:
+    """Matrix chain `label` (A-E): M_1 ... M_n in bf16, every product a
+    contraction 'xy,yz->xz' (bf16 output, fp32 accumulation) in the printed
+    parenthesization.  Index i (between M_i and M_(i+1)) is letter i of the
+    alphabet, blocked by chain_blocks.  M_1 ~ N(0, 1) and M_i ~ N(0, 1/d_(i-1))
+    for i >= 2, so every partial product has entries of order one whatever
+    the association."""
+    dims, tree = CHAINS[label]
+    n = len(dims) - 1
+    L = CHAIN_LETTERS
+    ext = {L[i]: dims[i] for i in range(n + 1)}
+    blk = {L[i]: chain_blocks(dims[i]) for i in range(n + 1)}
+    tens = []
+    for i in range(1, n + 1):
+        sigma = 1.0 if i == 1 else 1.0 / math.sqrt(dims[i - 1])
+        tens.append((f"M{i}", L[i - 1] + L[i], "normal32", "bf16", sigma, 0.0, blk))
+    chain = []
+
+    def walk(t):
+        """Appends the products of subtree t; returns (name, first, last)."""
+        if isinstance(t, int):
+            return f"M{t}", t, t
+        (la, a0, a1), (rb, b0, b1) = walk(t[0]), walk(t[1])
+        assert b0 == a1 + 1
+        name = f"P{a0}_{b1}"
+        spec = f"{L[a0 - 1]}{L[a1]},{L[a1]}{L[b1]}->{L[a0 - 1]}{L[b1]}"
+        chain.append(Step(name, spec, [la, rb], "mul", "sum", "bf16", blk))
+        return name, a0, b1
+
+    walk(tree)
+    return Workload(name=f"matrix_chain_{label}_{n}x_bf16", extents=ext, tensors=tens, chain=chain,
+                    seed=1010 + "ABCDE".index(label) + 1)
 
 
 def generate(w: Workload) -> dict:

@@ -77,19 +77,24 @@ def test_interval_limits_in_a_contraction(ctx):
 
 
 def test_relation_element_limit(ctx):
-    """A relation of 2^31 elements is refused before anything is touched;
-    one just under the limit is accepted (metadata only)."""
+    """A relation of 2^36 elements, or of 2^31 tuples, is refused before
+    anything is touched; one just under the limits is accepted (metadata
+    only: nothing reads the buffer)."""
     buf = torch.empty(16, dtype=torch.uint8, device="cuda")
     h = jagg.ctypes.c_void_p()
     L = jagg.lib()
-    big = jagg._i64([1 << 16, 1 << 15])
-    with pytest.raises(jagg.JaggError):
-        ctx._check(L.jagg_relation_create(ctx.handle, b"ij", big, jagg._i32([1, 1]), jagg.DT["bf16"],
+
+    def create(ext, blk):
+        ctx._check(L.jagg_relation_create(ctx.handle, b"ij", jagg._i64(ext), jagg._i32(blk), jagg.DT["bf16"],
                                           jagg.ctypes.c_void_p(buf.data_ptr()), 1 << 40, jagg.ctypes.byref(h)))
-    ok = jagg._i64([(1 << 16) - 1, 1 << 15])
-    ctx._check(L.jagg_relation_create(ctx.handle, b"ij", ok, jagg._i32([1, 1]), jagg.DT["bf16"],
-                                      jagg.ctypes.c_void_p(buf.data_ptr()), 1 << 40, jagg.ctypes.byref(h)))
-    L.jagg_relation_destroy(h)
+        L.jagg_relation_destroy(h)
+
+    with pytest.raises(jagg.JaggError, match="2\\^36"):
+        create([1 << 18, 1 << 18], [1, 1])
+    with pytest.raises(jagg.JaggError, match="2\\^31"):
+        create([1 << 16, 1 << 16], [1 << 16, 1 << 15])
+    create([(1 << 18) - 1, 1 << 18], [1, 1])
+    create([1 << 16, (1 << 15) - 1], [1 << 16, (1 << 15) - 1])  # 2^31 - 2^16 one-element tuples
 
 
 def test_large_repartition_in_full(ctx):

@@ -8,6 +8,7 @@ S(S+1)/2 pairs t <= s; a segment pair keeps the pairs inside each segment.
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -92,3 +93,29 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py")], capture_output=True, text=True,
                        timeout=300, env=env)
     assert r.returncode == 2 and "exactly one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("label", list("ABCDE"))
+def test_matrix_chain_recipe_matches_the_pages(label):
+    """Every Kernel Is a Join, Sec. 6: each multiply of a chain averages about
+    8192^3 scalar multiplies; chain C is right-associated; D and E end in one
+    large product across a thin neck."""
+    w = I.matrix_chain(label)
+    macs = []
+    for st in w.chain:
+        (la, lb) = st.spec.split("->")[0].split(",")
+        macs.append(w.extents[la[0]] * w.extents[la[1]] * w.extents[lb[1]])
+    assert len(macs) == len(w.tensors) - 1
+    assert abs(np.mean(macs) / 8192 ** 3 - 1.0) < 0.05
+    # every matrix is used once, in order, and the last product covers M1..Mn
+    assert w.chain[-1].out == f"P1_{len(w.tensors)}"
+    used = [n for st in w.chain for n in st.ins if n.startswith("M")]
+    assert sorted(used, key=lambda s: int(s[1:])) == [f"M{i}" for i in range(1, len(w.tensors) + 1)]
+    if label == "C":
+        assert [st.out for st in w.chain] == ["P2_3", "P1_3"]
+    if label in "DE":
+        last = w.chain[-1].spec.split("->")[0].split(",")
+        assert w.extents[last[0][1]] <= 1536 and w.extents[last[0][0]] >= 24576
+    for st in w.chain:  # every block a multiple of the 256-wide tile
+        for c in st.spec.replace(",", "").replace("->", ""):
+            assert (w.extents[c] // st.blockings[c]) % 256 == 0
