@@ -41,6 +41,12 @@
 #ifndef JAGG_DMA_STAGES
 #define JAGG_DMA_STAGES 4
 #endif
+#ifndef JAGG_DMA_WHOLE_STEP
+#define JAGG_DMA_WHOLE_STEP 0
+#endif
+#ifndef JAGG_DMA_ODD
+#define JAGG_DMA_ODD 0
+#endif
 
 #include "contract_impl.h"
 
@@ -154,21 +160,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // the walk over (joined tuple, K-tile): position and tuple ids of the next
   // step to load; past the last step the loads use an empty resource (every
-  // lane reads zeros) so that every step issues the same number of loads
+  // lane reads zeros) so that every step issues the same number of loads.
+  // The byte address of the step's origin in each operand and the bytes from
+  // there to the end of its block are formed once per joined tuple and then
+  // stepped by a constant: the per-step work stays a few scalar adds, which
+  // issue in the shadow of one MFMA instead of idling the matrix core.
   int ld = 0, le = 0, lkt = 0;
   int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
   i32x4_rsrc rs_a, rs_b;  // resources of the step being loaded
-  int k_left = 0;
+  int k_left = 0, k_next = p.K;
   char *ld_buf = smem;
+  const int64_t a_step = int64_t(BK) * p.sAk * 2, b_step = int64_t(BK) * p.sBk * 2;
+  uint64_t pa, pb;  // byte addresses of the next step's origins
+  int64_t na, nb;   // bytes from there to the end of the block
+  auto tuple_origin = [&]() {
+    pa = reinterpret_cast<uint64_t>(p.A) + uint64_t(la * p.beA + a_org) * 2;
+    pb = reinterpret_cast<uint64_t>(p.B) + uint64_t(lb * p.beB + b_org) * 2;
+    na = (p.beA - a_org) * 2;
+    nb = (p.beB - b_org) * 2;
+  };
+  tuple_origin();
   auto prep = [&](char *buf) {
-    const int k0 = lkt * BK;
-    const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
-    const uint16_t *pa = reinterpret_cast<const uint16_t *>(p.A) + la * p.beA + ao;
-    const uint16_t *pb = reinterpret_cast<const uint16_t *>(p.B) + lb * p.beB + bo;
     const bool live = ld < steps;
-    rs_a = dma_rsrc(pa, live ? (p.beA - ao) * 2 : 0);
-    rs_b = dma_rsrc(pb, live ? (p.beB - bo) * 2 : 0);
-    k_left = p.K - k0;
+    rs_a = dma_rsrc(reinterpret_cast<const void *>(pa), live ? na : 0);
+    rs_b = dma_rsrc(reinterpret_cast<const void *>(pb), live ? nb : 0);
+    k_left = k_next;
     ld_buf = buf;
   };
   auto dma_a = [&](int i) { da.issue(i, rs_a, k_left, ld_buf, wave_s); };
@@ -177,10 +193,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ++ld;
     if (++lkt == KT) {
       lkt = 0;
+      k_next = p.K;
       if (++le < cnt) {
         la = ents[le * 3 + p.a_slot];
         lb = ents[le * 3 + p.b_slot];
       }
+      tuple_origin();
+    } else {
+      k_next -= BK;
+      pa += a_step;
+      pb += b_step;
+      na -= a_step;
+      nb -= b_step;
     }
   };
   constexpr int NA = DmaOperand<A_KC, NT>::NI, NB = DmaOperand<B_KC, NT>::NI;
@@ -268,6 +292,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Past the last step the reads see zero fill or stale data that no MFMA
   // consumes.
   static_assert(TM * TN == 16 && TM + TN <= 8 && NA <= 4 && NB <= 4, "interleave pattern");
+#if JAGG_DMA_WHOLE_STEP
+  // phase B issues all NA + NB loads of the step it prepared, one after
+  // every other MFMA, so both operands' loads get two steps to land
+  auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
+      if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
+      if ((k & 1) == JAGG_DMA_ODD && k / 2 < NA + NB) dma(k / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  constexpr int PRO = NS - 1;  // steps loaded whole before the loop
+  constexpr int PRO_WAIT = (NS - 2) * (NA + NB);
+#else
   auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -277,10 +316,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  constexpr int PRO = NS - 2;  // steps loaded whole before the loop (plus half of one)
+  constexpr int PRO_WAIT = (NS - 3) * (NA + NB) + NA;
+#endif
 
   Frags f0, f1;
-  // prologue: steps 0..NS-3 whole, the first half of step NS-2
-  for (int s = 0; s < NS - 2; ++s) {
+  // prologue: the first PRO steps whole (and, with split steps, the first
+  // half of step NS-2)
+  for (int s = 0; s < PRO; ++s) {
     prep(stage(s));
 #pragma unroll
     for (int i = 0; i < NA; ++i) dma_a(i);
@@ -288,24 +331,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < NB; ++i) dma_b(i);
     advance();
   }
+#if !JAGG_DMA_WHOLE_STEP
   prep(stage(NS - 2));
 #pragma unroll
   for (int i = 0; i < NA; ++i) dma_a(i);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 3) * (NA + NB) + NA) : "memory");
+#endif
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(PRO_WAIT) : "memory");
 #pragma unroll
   for (int x = 0; x < TM + TN; ++x) read_frag(stage(0), 0, f0, x);
   for (int s = 0; s < steps; ++s) {
     __builtin_amdgcn_sched_barrier(0);
+#if JAGG_DMA_WHOLE_STEP
+    phase(f0, stage(s), 1, f1, [&](int) {});
+#else
     phase(f0, stage(s), 1, f1, [&](int i) {
       if (i < NB) dma_b(i);
     });
     advance();
+#endif
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 3) * (NA + NB)) : "memory");
     prep(stage(s + NS - 1));
+#if JAGG_DMA_WHOLE_STEP
+    phase(f1, stage(s + 1), 0, f0, [&](int i) {
+      if (i < NA) dma_a(i);
+      else dma_b(i - NA);
+    });
+    advance();
+#else
     phase(f1, stage(s + 1), 0, f0, [&](int i) {
       if (i < NA) dma_a(i);
     });
+#endif
   }
 
   // the zero-fill loads past the last step may still be in flight: let them
