@@ -232,6 +232,33 @@ jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const ja
 jagg_status jagg_einsum(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
                         const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes);
 
+/* Prepared specs.  A chain that runs the same spec over the same relations
+ * again and again (every step of a model block) repeats the host planning
+ * and the join enumeration of jagg_einsum each time, although both depend
+ * only on the spec, the relations' geometry and `blockings` ("Every Kernel
+ * Is a Join", Def. 3.7: the join is a function of the tuples' keys, not of
+ * their blocks' values).  jagg_plan_create does what jagg_einsum does up to
+ * the join: it checks and plans the call (same arguments and errors as
+ * jagg_einsum) and launches the join-enumeration kernel, on the ctx stream,
+ * into `workspace` (at least jagg_einsum_workspace() bytes, 256-byte
+ * aligned).  jagg_plan_run then launches the rest of jagg_einsum -- any
+ * re-blocking of inputs into the workspace and the block kernel -- without
+ * joining again, and computes exactly what jagg_einsum computes on the
+ * relations' current contents.
+ * The plan keeps the device addresses it was given: the caller keeps the
+ * input and output buffers and the workspace alive and unmoved while the
+ * plan lives, and must not use the workspace for anything else (it holds
+ * the plan's join list); the relation handles themselves may be destroyed.
+ * A plan is run on a context of the device it was made on (JAGG_E_INVALID
+ * otherwise); runs may be recorded by jagg_capture_begin / _end.
+ * jagg_plan_destroy frees the host metadata only. */
+typedef struct jagg_plan jagg_plan;
+jagg_status jagg_plan_create(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                             const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes,
+                             jagg_plan **plan);
+jagg_status jagg_plan_run(jagg_ctx *ctx, const jagg_plan *plan);
+jagg_status jagg_plan_destroy(jagg_plan *plan);
+
 /* jagg_einsum without a workspace argument, for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It runs the same kernels as jagg_einsum

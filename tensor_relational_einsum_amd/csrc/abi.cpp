@@ -38,6 +38,8 @@ struct jagg_graph {
   hipGraphExec_t exec;
 };
 
+struct jagg_plan;  // holds a PlannedCall (defined with the planner below)
+
 struct jagg_relation {
   jagg_ctx *ctx;
   int r;
@@ -1455,11 +1457,31 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
   return JAGG_OK;
 }
 
-// jagg_einsum's body; `noalloc` marks the static scratch as the workspace
-// (a size error then names the scratch limit).
-jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
-                        const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes,
-                        bool noalloc) {
+// Everything jagg_einsum decides on the host for one call: the kernel
+// arguments (which embed the relation, join-list and workspace addresses)
+// and the launch choices.  Built once per call, or once per jagg_plan.
+struct PlannedCall {
+  enum Kind { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
+  std::string einsum;
+  int agg = 0;
+  bool out_bf16 = false, causal = false;
+  std::vector<RelayoutArgs> reblocks;
+  std::vector<int> reblock_vec;  // vector bytes * 16 + element bytes
+  JoinArgs join;
+  EwArgs ew;
+  ContractArgs ca;
+  int dtype = 0, va = 1, vb = 1;
+  bool akc = true, bkc = true, big = false;
+  AttnArgs at;
+  int att_d = 0;
+  size_t ws_total = 0;
+};
+
+// Binds and checks the call and plans every launch, host only.  `noalloc`
+// marks the static scratch as the workspace (a size error then names it).
+jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                       const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes, bool noalloc,
+                       PlannedCall &P) {
   if (!ctx || !out) return fail(ctx, JAGG_E_INVALID, "NULL argument");
   Bound b;
   jagg_status st = bind(ctx, spec, in, n_in, blockings, b);
@@ -1504,16 +1526,21 @@ jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   if (!workspace || ws_bytes < b.total)
     return fail(ctx, JAGG_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, b.total);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(ctx, JAGG_E_WORKSPACE, "workspace not 256-byte aligned");
+  P.ws_total = b.total;
+  P.einsum = spec->einsum;
+  P.agg = spec->agg;
+  P.out_bf16 = spec->out_dtype == JAGG_BF16;
+  P.causal = spec->causal_s != 0;
 
   // classify before launching anything: a contraction is a MUL/SUM over two
   // inputs where every reduced letter is in both inputs and each input
   // contributes output letters of its own; any other aggregating spec is a
   // streaming reduce, and a spec without aggregation is a map.
-  enum { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
+  P.kind = PlannedCall::MAP;
   if (spec->agg == JAGG_AGG_SOFTMAX) {
-    kind = ATTENTION;
+    P.kind = PlannedCall::ATTENTION;
   } else if (spec->agg != JAGG_AGG_NONE) {
-    kind = REDUCE;
+    P.kind = PlannedCall::REDUCE;
     if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
       bool both = true, m_any = false, n_any = false;
       for (char c : b.p.reduced)
@@ -1523,7 +1550,7 @@ jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
         m_any = m_any || (i0 && !i1);
         n_any = n_any || (i1 && !i0);
       }
-      if (both && m_any && n_any) kind = CONTRACT;
+      if (both && m_any && n_any) P.kind = PlannedCall::CONTRACT;
     }
   }
 
@@ -1547,67 +1574,95 @@ jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
     use[j] = &T;
   }
   // plan the block kernel (host only) before any launch
-  EwArgs ew;
-  ContractArgs ca;
-  int dtype = 0, va = 1, vb = 1;
-  bool akc = true, bkc = true;
-  if (kind == CONTRACT) {
-    if ((st = plan_contract(ctx, spec, b, use, out, list, counts, ca, dtype, akc, bkc, va, vb)) != JAGG_OK) return st;
-  }
-  AttnArgs at;
-  int att_d = 0;
-  if (kind == ATTENTION && (st = plan_attention(ctx, spec, b, use, out, list, counts, at, att_d)) != JAGG_OK)
+  if (P.kind == PlannedCall::CONTRACT &&
+      (st = plan_contract(ctx, spec, b, use, out, list, counts, P.ca, P.dtype, P.akc, P.bkc, P.va, P.vb)) != JAGG_OK)
     return st;
-  if ((kind == MAP || kind == REDUCE) && (st = plan_ew(ctx, spec, b, use, out, list, counts, ew)) != JAGG_OK)
+  if (P.kind == PlannedCall::ATTENTION &&
+      (st = plan_attention(ctx, spec, b, use, out, list, counts, P.at, P.att_d)) != JAGG_OK)
     return st;
-  std::vector<RelayoutArgs> reblocks;
-  std::vector<int> reblock_vec;
+  if ((P.kind == PlannedCall::MAP || P.kind == PlannedCall::REDUCE) &&
+      (st = plan_ew(ctx, spec, b, use, out, list, counts, P.ew)) != JAGG_OK)
+    return st;
   for (int j = 0; j < n_in; ++j) {
     if (!b.needs_reblock[j]) continue;
     RelayoutArgs ra;
     int vbytes = 0;
     if ((st = plan_relayout(ctx, *b.in[j], *use[j], ra, vbytes)) != JAGG_OK) return st;
-    reblocks.push_back(ra);
-    reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
+    P.reblocks.push_back(ra);
+    P.reblock_vec.push_back(vbytes * 16 + esz_of(in[j]->dt));
     if (ctx->trace) fprintf(stderr, "[jagg] %s: reblock input %d into the workspace\n", spec->einsum, j);
   }
-  // launches
-  for (size_t i = 0; i < reblocks.size(); ++i)
-    if ((st = after_launch(ctx, launch_relayout(reblocks[i], reblock_vec[i] / 16, reblock_vec[i] % 16, ctx->stream),
-                           "reblock input")) != JAGG_OK)
-      return st;
-  b.join.list = list;
-  b.join.counts = counts;
-  if ((st = after_launch(ctx, launch_join(b.join, ctx->stream), "join")) != JAGG_OK) return st;
-  if (kind == ATTENTION) {
-    const hipError_t e = launch_attention(at, att_d, spec->causal_s != 0, spec->out_dtype == JAGG_BF16, ctx->stream);
-    if (ctx->trace)
-      fprintf(stderr, "[jagg] %s: attention d%d, %d keys x %d batch x %d s-tiles\n", spec->einsum, att_d, at.n_keys,
-              at.nbatch, at.s_tiles);
-    return after_launch(ctx, e, "attention");
-  }
-  if (kind == CONTRACT) {
+  if (P.kind == PlannedCall::CONTRACT) {
+    ContractArgs &ca = P.ca;
     // 256x256 tiles where the block is large enough and the grid still fills the chip
-    const int F = dtype ? 8 : 4;
+    const int F = P.dtype ? 8 : 4;
     const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + 255) / 256);
-    const bool big = va == F && vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
+    P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
     // per-XCD renumbering pays where several tiles of one output block share panels
-    const int bm = big ? 256 : 128;
+    const int bm = P.big ? 256 : 128;
     ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
     ca.group_m = (ca.remap && ca.km > 0 && ca.batch == 1) ? kGroupM : 0;
-    const int ob = spec->out_dtype == JAGG_BF16;
-    const char *which = "";
-    const hipError_t e = dtype ? launch_contract_bf16(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which)
-                               : launch_contract_f32(ca, ob, akc, bkc, va, vb, big, ctx->stream, &which);
+  }
+  P.join = b.join;
+  P.join.list = list;
+  P.join.counts = counts;
+  return JAGG_OK;
+}
+
+}  // namespace
+
+struct jagg_plan {
+  int device;
+  PlannedCall call;
+};
+
+namespace {
+
+jagg_status launch_join_of(jagg_ctx *ctx, const PlannedCall &P) {
+  return after_launch(ctx, launch_join(P.join, ctx->stream), "join");
+}
+
+// Launches a planned call: re-blocking copies, the join (unless a plan has
+// already listed it), then the block kernel.
+jagg_status launch_call(jagg_ctx *ctx, const PlannedCall &P, bool with_join) {
+  jagg_status st;
+  for (size_t i = 0; i < P.reblocks.size(); ++i)
+    if ((st = after_launch(ctx, launch_relayout(P.reblocks[i], P.reblock_vec[i] / 16, P.reblock_vec[i] % 16,
+                                                ctx->stream),
+                           "reblock input")) != JAGG_OK)
+      return st;
+  if (with_join && (st = launch_join_of(ctx, P)) != JAGG_OK) return st;
+  const char *e_name = P.einsum.c_str();
+  if (P.kind == PlannedCall::ATTENTION) {
+    const hipError_t e = launch_attention(P.at, P.att_d, P.causal, P.out_bf16, ctx->stream);
     if (ctx->trace)
-      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", spec->einsum, which, (long long)ca.n_keys,
-              ca.batch);
+      fprintf(stderr, "[jagg] %s: attention d%d, %d keys x %d batch x %d s-tiles\n", e_name, P.att_d, P.at.n_keys,
+              P.at.nbatch, P.at.s_tiles);
+    return after_launch(ctx, e, "attention");
+  }
+  if (P.kind == PlannedCall::CONTRACT) {
+    const int ob = P.out_bf16;
+    const char *which = "";
+    const hipError_t e = P.dtype ? launch_contract_bf16(P.ca, ob, P.akc, P.bkc, P.va, P.vb, P.big, ctx->stream, &which)
+                                 : launch_contract_f32(P.ca, ob, P.akc, P.bkc, P.va, P.vb, P.big, ctx->stream, &which);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", e_name, which, (long long)P.ca.n_keys,
+              P.ca.batch);
     return after_launch(ctx, e, "contract");
   }
   const char *which = "";
-  const hipError_t e = launch_ew(ctx, ew, spec->agg, &which);
-  if (ctx->trace) fprintf(stderr, "[jagg] %s: %s, %lld keys\n", spec->einsum, which, (long long)ew.n_keys);
+  const hipError_t e = launch_ew(ctx, P.ew, P.agg, &which);
+  if (ctx->trace) fprintf(stderr, "[jagg] %s: %s, %lld keys\n", e_name, which, (long long)P.ew.n_keys);
   return after_launch(ctx, e, which);
+}
+
+jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                        const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes,
+                        bool noalloc) {
+  PlannedCall P;
+  jagg_status st = build_call(ctx, spec, in, n_in, blockings, out, workspace, ws_bytes, noalloc, P);
+  if (st != JAGG_OK) return st;
+  return launch_call(ctx, P, true);
 }
 
 const char *env_or(const char *k) {
@@ -1801,6 +1856,36 @@ jagg_status jagg_einsum_noalloc(jagg_ctx *ctx, const jagg_spec *spec, const jagg
                                 const int32_t *blockings, jagg_relation *out) {
   if (!ctx) return JAGG_E_INVALID;
   return einsum_impl(ctx, spec, in, n_in, blockings, out, ctx->scratch, JAGG_NOALLOC_SCRATCH_BYTES, true);
+}
+
+jagg_status jagg_plan_create(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in, int n_in,
+                             const int32_t *blockings, jagg_relation *out, void *workspace, size_t ws_bytes,
+                             jagg_plan **plan) {
+  if (!ctx || !plan) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  *plan = nullptr;
+  jagg_plan *P = new jagg_plan;
+  P->device = ctx->device;
+  jagg_status st = build_call(ctx, spec, in, n_in, blockings, out, workspace, ws_bytes, false, P->call);
+  if (st == JAGG_OK) st = launch_join_of(ctx, P->call);
+  if (st != JAGG_OK) {
+    delete P;
+    return st;
+  }
+  *plan = P;
+  return JAGG_OK;
+}
+
+jagg_status jagg_plan_run(jagg_ctx *ctx, const jagg_plan *plan) {
+  if (!ctx || !plan) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  if (plan->device != ctx->device)
+    return fail(ctx, JAGG_E_INVALID, "plan made for device %d, context on device %d", plan->device, ctx->device);
+  return launch_call(ctx, plan->call, false);
+}
+
+jagg_status jagg_plan_destroy(jagg_plan *plan) {
+  if (!plan) return JAGG_E_INVALID;
+  delete plan;
+  return JAGG_OK;
 }
 
 jagg_status jagg_join_shape(const jagg_spec *spec, const int64_t *extents_by_letter, const int32_t *blockings,

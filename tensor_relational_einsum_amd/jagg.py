@@ -26,7 +26,8 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # JAGG_NOALLOC_SCRATCH_BYTES in jagg.h
 
 EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
            "jagg_relation_bytes_iv", "jagg_relation_create_iv", "jagg_relation_destroy", "jagg_repartition",
-           "jagg_einsum_workspace", "jagg_einsum", "jagg_einsum_noalloc", "jagg_join_shape",
+           "jagg_einsum_workspace", "jagg_einsum", "jagg_einsum_noalloc", "jagg_plan_create", "jagg_plan_run",
+           "jagg_plan_destroy", "jagg_join_shape",
            "jagg_join_list", "jagg_capture_begin", "jagg_capture_end", "jagg_graph_launch", "jagg_graph_destroy",
            "jagg_status_str", "jagg_last_error"]
 
@@ -76,6 +77,10 @@ def lib():
         L.jagg_einsum.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp, vp,
                                   ctypes.c_size_t]
         L.jagg_einsum_noalloc.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp]
+        L.jagg_plan_create.argtypes = [vp, ctypes.POINTER(jagg_spec), ctypes.POINTER(vp), ctypes.c_int, i32p, vp, vp,
+                                       ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.jagg_plan_run.argtypes = [vp, vp]
+        L.jagg_plan_destroy.argtypes = [vp]
         L.jagg_join_shape.argtypes = [ctypes.POINTER(jagg_spec), i64p, i32p, i64p, i64p]
         L.jagg_join_list.argtypes = [vp, ctypes.POINTER(jagg_spec), i64p, i32p, vp, vp]
         L.jagg_capture_begin.argtypes = [vp]
@@ -321,6 +326,32 @@ class EinsumCall:
                                           self.blk, self.out.handle, ctypes.c_void_p(self.workspace.data_ptr()),
                                           self.workspace.numel()))
         return self.out
+
+    def prepare(self) -> "EinsumCall":
+        """Plans the call once (jagg_plan_create: the host planning and the
+        join, into a workspace of the plan's own); run_plan() then launches
+        the block kernel only."""
+        if getattr(self, "plan", None) is None:
+            self.plan_ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=f"cuda:{self.ctx.device}")
+            h = ctypes.c_void_p()
+            self.ctx._check(lib().jagg_plan_create(self.ctx.handle, ctypes.byref(self.spec), self.in_arr,
+                                                   len(self.inputs), self.blk, self.out.handle,
+                                                   ctypes.c_void_p(self.plan_ws.data_ptr()), self.plan_ws.numel(),
+                                                   ctypes.byref(h)))
+            self.plan = h
+        return self
+
+    def run_plan(self) -> Relation:
+        self.ctx._check(lib().jagg_plan_run(self.ctx.handle, self.plan))
+        return self.out
+
+    def __del__(self):
+        try:
+            if getattr(self, "plan", None):
+                lib().jagg_plan_destroy(self.plan)
+                self.plan = None
+        except Exception:
+            pass
 
     def run_noalloc(self, out: Relation | None = None) -> Relation:
         """The same spec through jagg_einsum_noalloc (the library's static

@@ -1,7 +1,10 @@
 """Runs a workload chain (see ``inputs``) through the C ABI.
 
 Builds every relation and workspace once, then ``run()`` issues one library
-call per step on the context's stream; nothing is computed in Python.
+call per step on the context's stream; nothing is computed in Python.  By
+default every einsum step is a prepared plan (jagg_plan_create at set-up:
+host planning and join once; jagg_plan_run per step); ``planned=False``
+calls jagg_einsum every time instead.
 """
 from __future__ import annotations
 
@@ -12,8 +15,8 @@ from .inputs import Relayout, Step, Workload
 
 
 class ChainRunner:
-    def __init__(self, ctx: jagg.Context, w: Workload, dense: dict):
-        self.ctx, self.w = ctx, w
+    def __init__(self, ctx: jagg.Context, w: Workload, dense: dict, planned: bool = True):
+        self.ctx, self.w, self.planned = ctx, w, planned
         dev = f"cuda:{ctx.device}"
         self.rel: dict[str, jagg.Relation] = {}
         self.dense_dev = {}
@@ -46,13 +49,14 @@ class ChainRunner:
             if kind == "einsum" and obj.workspace.numel() < ws.numel():
                 obj.workspace = ws
         self.workspace = ws
+        if planned:
+            for kind, obj, _ in self.calls:
+                if kind == "einsum":
+                    obj.prepare()
 
     def run(self):
-        for kind, obj, _ in self.calls:
-            if kind == "einsum":
-                obj.run()
-            else:
-                jagg.repartition(self.ctx, obj[0], obj[1])
+        for i in range(len(self.calls)):
+            self.run_step(i)
 
     def capture(self) -> jagg.Graph:
         """The whole chain recorded into one graph (every buffer it uses is
@@ -62,7 +66,10 @@ class ChainRunner:
     def run_step(self, i: int):
         kind, obj, _ = self.calls[i]
         if kind == "einsum":
-            obj.run()
+            if self.planned:
+                obj.run_plan()
+            else:
+                obj.run()
         else:
             jagg.repartition(self.ctx, obj[0], obj[1])
 
