@@ -111,6 +111,17 @@ def spec_bytes(run: ChainRunner, st, ext: dict) -> float:
     return b
 
 
+def unit_info(run: ChainRunner, w: I.Workload, u: int):
+    """(name, op, flops, bytes, steps) of one unit of a chain pass."""
+    _, _, idx = run.units[u]
+    sts = [w.chain[i] for i in idx]
+    name = "+".join(st.out for st in sts)
+    op = " | ".join(st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}" for st in sts)
+    f = sum(spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0 for st in sts)
+    by = sum(spec_bytes(run, st, w.extents) for st in sts)
+    return name, op, f, by, sts
+
+
 def counter_traffic() -> float | None:
     """HBM bytes per launch of the bf16 contraction kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernel source is still
@@ -197,8 +208,10 @@ def timed_graph(run: ChainRunner, steps: int, warmup: int) -> float:
 
 
 def timed_chain(run: ChainRunner, steps: int, warmup: int, flush_buf=None):
+    """`steps` passes of the chain, events around every unit (a step, or a
+    group of independent steps run as one plan group)."""
     stream = run.ctx.stream
-    n = len(run.calls)
+    n = len(run.units)
     for _ in range(warmup):
         run.run()
     torch.cuda.synchronize()
@@ -209,7 +222,7 @@ def timed_chain(run: ChainRunner, steps: int, warmup: int, flush_buf=None):
             flush_caches(flush_buf)
         ev[k][0].record(stream)
         for i in range(n):
-            run.run_step(i)
+            run.run_unit(i)
             ev[k][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -287,10 +300,9 @@ def other_config(ctx, w: I.Workload, flush_buf, warmup: int = 2, peaks: dict | N
     in_dtype = run.rel[big.ins[0]].dtype
     peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS
     specs = []
-    for i, st in enumerate(w.chain):
-        by = spec_bytes(run, st, w.extents)
-        f = spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0
-        e = {"name": st.out, "op": st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}",
+    for i in range(len(run.units)):
+        name, op, f, by, _ = unit_info(run, w, i)
+        e = {"name": name, "op": op,
              "ms": round(float(call_ms[i]), 4), "GB/s": round(by / (call_ms[i] * 1e-3) / 1e9, 1),
              "frac_hbm": round(by / (call_ms[i] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3)}
         if f:
@@ -482,22 +494,21 @@ def main():
     call_ms = per_call.mean(axis=0)
     breakdown = []
     dom_flops = dom_ms = dom_bytes = 0.0
-    dom_launches = 0
-    for i, st in enumerate(steps):
-        f = spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0
-        by = spec_bytes(run, st, w.extents)
-        ent = {"name": st.out, "op": st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}",
-               "ms": round(float(call_ms[i]), 4)}
+    dom_launches = dom_specs = 0
+    for i in range(len(run.units)):
+        name, op, f, by, sts = unit_info(run, w, i)
+        ent = {"name": name, "op": op, "ms": round(float(call_ms[i]), 4)}
         if f:
             ent["TFLOP/s"] = round(f / (call_ms[i] * 1e-3) / 1e12, 2)
         ent["GB/s"] = round(by / (call_ms[i] * 1e-3) / 1e9, 1)
         breakdown.append(ent)
-        if (isinstance(st, I.Step) and f and not st.causal and st.g == "mul"
-                and run.rel[st.ins[0]].dtype == "bf16"):
+        if all(isinstance(st, I.Step) and st.g == "mul" and st.agg == "sum" and not st.causal
+               and len(st.ins) == 2 and run.rel[st.ins[0]].dtype == "bf16" for st in sts) and f:
             dom_flops += f
             dom_ms += float(call_ms[i])
             dom_bytes += by
             dom_launches += 1
+            dom_specs += len(sts)
     # the arithmetic type of the dominant kernel: the inputs of the largest contraction
     big = max((st for st in steps if isinstance(st, I.Step)), key=lambda st: spec_flops(st, w.extents))
     in_dtype = run.rel[big.ins[0]].dtype
@@ -508,8 +519,9 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": tr,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": round(dom_bytes / dom_launches),
-                "kernel": "contract_dma_kernel<bf16> (projection / FFN specs, 256x256 tiles)",
-                "launches_per_step": dom_launches,
+                "kernel": "contract_dma_kernel / contract_dma_group_kernel <bf16> (projection / FFN specs, "
+                          "256x256 tiles; independent projections of one form share a launch)",
+                "launches_per_step": dom_launches, "specs_per_step": dom_specs,
                 "avg_launch_ms": round(dom_ms / dom_launches, 4)}
     else:
         peak = PEAK_F32_TFLOPS if in_dtype == "f32" else PEAK_BF16_TFLOPS

@@ -259,6 +259,21 @@ jagg_status jagg_plan_create(jagg_ctx *ctx, const jagg_spec *spec, const jagg_re
 jagg_status jagg_plan_run(jagg_ctx *ctx, const jagg_plan *plan);
 jagg_status jagg_plan_destroy(jagg_plan *plan);
 
+/* A group of independent plans run as one unit: jagg_plan_run on the group
+ * computes exactly what running its members in order computes.  Members
+ * that are contractions of one form -- the bf16 kernel with 256 x 256 tiles,
+ * and the same geometry (extents, blockings, layouts, dtypes, alpha), only
+ * their relations differ -- share one launch, up to 4 per launch (e.g. the
+ * Q, K and V projections of a block, or the gate and up projections): the
+ * grid of each is one range of a common grid, so the last partial wave of
+ * tiles and the launch edges are shared.  Other members launch one after
+ * the other.  Members must be independent: no member may write memory
+ * (output or workspace) that another reads or writes (JAGG_E_INVALID).  The
+ * group copies what it needs from `plans` (which may be destroyed after);
+ * the addresses they were made with must stay valid as for each plan.
+ * Groups may be members of groups (their members are taken). */
+jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans, jagg_plan **group);
+
 /* jagg_einsum without a workspace argument, for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It runs the same kernels as jagg_einsum

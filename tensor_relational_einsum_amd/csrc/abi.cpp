@@ -1475,6 +1475,8 @@ struct PlannedCall {
   AttnArgs at;
   int att_d = 0;
   size_t ws_total = 0;
+  // device byte ranges the call reads (inputs) and writes (output, workspace)
+  std::vector<std::pair<const char *, size_t>> reads, writes;
 };
 
 // Binds and checks the call and plans every launch, host only.  `noalloc`
@@ -1527,6 +1529,10 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
     return fail(ctx, JAGG_E_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, b.total);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(ctx, JAGG_E_WORKSPACE, "workspace not 256-byte aligned");
   P.ws_total = b.total;
+  for (int j = 0; j < n_in; ++j)
+    P.reads.push_back({static_cast<const char *>(in[j]->buf), size_t(in[j]->n_tuples * in[j]->be) * esz_of(in[j]->dt)});
+  P.writes.push_back({static_cast<const char *>(out->buf), size_t(out->n_tuples * out->be) * esz_of(out->dt)});
+  P.writes.push_back({static_cast<const char *>(workspace), b.total});
   P.einsum = spec->einsum;
   P.agg = spec->agg;
   P.out_bf16 = spec->out_dtype == JAGG_BF16;
@@ -1614,6 +1620,9 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
 struct jagg_plan {
   int device;
   PlannedCall call;
+  // a group (jagg_plan_group): its members, and the members each launch runs
+  std::vector<PlannedCall> members;
+  std::vector<std::vector<int>> launches;
 };
 
 namespace {
@@ -1622,16 +1631,47 @@ jagg_status launch_join_of(jagg_ctx *ctx, const PlannedCall &P) {
   return after_launch(ctx, launch_join(P.join, ctx->stream), "join");
 }
 
-// Launches a planned call: re-blocking copies, the join (unless a plan has
-// already listed it), then the block kernel.
-jagg_status launch_call(jagg_ctx *ctx, const PlannedCall &P, bool with_join) {
+jagg_status launch_reblocks(jagg_ctx *ctx, const PlannedCall &P) {
   jagg_status st;
   for (size_t i = 0; i < P.reblocks.size(); ++i)
     if ((st = after_launch(ctx, launch_relayout(P.reblocks[i], P.reblock_vec[i] / 16, P.reblock_vec[i] % 16,
                                                 ctx->stream),
                            "reblock input")) != JAGG_OK)
       return st;
+  return JAGG_OK;
+}
+
+jagg_status launch_kernel(jagg_ctx *ctx, const PlannedCall &P);
+
+// Launches a planned call: re-blocking copies, the join (unless a plan has
+// already listed it), then the block kernel.
+jagg_status launch_call(jagg_ctx *ctx, const PlannedCall &P, bool with_join) {
+  jagg_status st;
+  if ((st = launch_reblocks(ctx, P)) != JAGG_OK) return st;
   if (with_join && (st = launch_join_of(ctx, P)) != JAGG_OK) return st;
+  return launch_kernel(ctx, P);
+}
+
+// True when two planned contractions differ only in their addresses (same
+// kernel, same geometry): one grouped launch can run both.
+bool same_contraction_form(const PlannedCall &x, const PlannedCall &y) {
+  if (x.kind != PlannedCall::CONTRACT || y.kind != PlannedCall::CONTRACT) return false;
+  if (x.dtype != y.dtype || x.va != y.va || x.vb != y.vb || x.akc != y.akc || x.bkc != y.bkc || x.big != y.big ||
+      x.out_bf16 != y.out_bf16)
+    return false;
+  ContractArgs u, v;  // byte copies (plan_contract zeroes the padding)
+  memcpy(&u, &x.ca, sizeof(u));
+  memcpy(&v, &y.ca, sizeof(v));
+  u.A = v.A = nullptr;
+  u.B = v.B = nullptr;
+  u.C = v.C = nullptr;
+  u.list = v.list = nullptr;
+  u.counts = v.counts = nullptr;
+  return memcmp(&u, &v, sizeof(u)) == 0;
+}
+
+// Block kernel of a planned call.
+jagg_status launch_kernel(jagg_ctx *ctx, const PlannedCall &P) {
   const char *e_name = P.einsum.c_str();
   if (P.kind == PlannedCall::ATTENTION) {
     const hipError_t e = launch_attention(P.at, P.att_d, P.causal, P.out_bf16, ctx->stream);
@@ -1879,7 +1919,87 @@ jagg_status jagg_plan_run(jagg_ctx *ctx, const jagg_plan *plan) {
   if (!ctx || !plan) return fail(ctx, JAGG_E_INVALID, "NULL argument");
   if (plan->device != ctx->device)
     return fail(ctx, JAGG_E_INVALID, "plan made for device %d, context on device %d", plan->device, ctx->device);
-  return launch_call(ctx, plan->call, false);
+  if (plan->members.empty()) return launch_call(ctx, plan->call, false);
+  jagg_status st;
+  for (const PlannedCall &m : plan->members)
+    if ((st = launch_reblocks(ctx, m)) != JAGG_OK) return st;
+  for (const std::vector<int> &L : plan->launches) {
+    if (L.size() == 1) {
+      if ((st = launch_kernel(ctx, plan->members[L[0]])) != JAGG_OK) return st;
+      continue;
+    }
+    const PlannedCall &m0 = plan->members[L[0]];
+    DmaGroupArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    ga.common = m0.ca;
+    ga.n = int32_t(L.size());
+    for (size_t i = 0; i < L.size(); ++i) {
+      const ContractArgs &c = plan->members[L[i]].ca;
+      ga.A[i] = c.A;
+      ga.B[i] = c.B;
+      ga.C[i] = c.C;
+      ga.list[i] = c.list;
+      ga.counts[i] = c.counts;
+    }
+    hipError_t e = hipSuccess;
+    if (!launch_contract_bf16_group(ga, m0.out_bf16, m0.akc, m0.bkc, m0.va, m0.vb, m0.big, ctx->stream, &e))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "grouped launch refused its form");  // jagg_plan_group checked it
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] group of %d: contract bf16 256x256 lds pipeline, one launch (%s, ...)\n", ga.n,
+              m0.einsum.c_str());
+    if ((st = after_launch(ctx, e, "grouped contract")) != JAGG_OK) return st;
+  }
+  return JAGG_OK;
+}
+
+jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans, jagg_plan **group) {
+  if (!ctx || !plans || !group || n < 1) return fail(ctx, JAGG_E_INVALID, "NULL argument or empty group");
+  *group = nullptr;
+  std::vector<const PlannedCall *> calls;
+  for (int i = 0; i < n; ++i) {
+    const jagg_plan *q = plans[i];
+    if (!q) return fail(ctx, JAGG_E_INVALID, "plan %d is NULL", i);
+    if (q->device != ctx->device) return fail(ctx, JAGG_E_INVALID, "plan %d is for another device", i);
+    if (q->members.empty()) {
+      calls.push_back(&q->call);
+    } else {
+      for (const PlannedCall &m : q->members) calls.push_back(&m);
+    }
+  }
+  // independence: nothing one member writes may be read or written by another
+  auto overlap = [](const std::pair<const char *, size_t> &x, const std::pair<const char *, size_t> &y) {
+    return x.first < y.first + y.second && y.first < x.first + x.second;
+  };
+  for (size_t i = 0; i < calls.size(); ++i)
+    for (size_t j = 0; j < calls.size(); ++j) {
+      if (i == j) continue;
+      for (const auto &w : calls[i]->writes) {
+        for (const auto &r : calls[j]->reads)
+          if (overlap(w, r)) return fail(ctx, JAGG_E_INVALID, "group member %zu writes what member %zu reads", i, j);
+        for (const auto &w2 : calls[j]->writes)
+          if (overlap(w, w2)) return fail(ctx, JAGG_E_INVALID, "group members %zu and %zu write the same memory", i, j);
+      }
+    }
+  jagg_plan *G = new jagg_plan;
+  G->device = ctx->device;
+  for (const PlannedCall *c : calls) G->members.push_back(*c);
+  // launches: members of one contraction form share a launch (up to kMaxGroup)
+  std::vector<bool> done(calls.size(), false);
+  for (size_t i = 0; i < calls.size(); ++i) {
+    if (done[i]) continue;
+    std::vector<int> L{int(i)};
+    done[i] = true;
+    const bool groupable = calls[i]->kind == PlannedCall::CONTRACT && calls[i]->dtype == 1 && calls[i]->big &&
+                           calls[i]->va == 8 && calls[i]->vb == 8 && !calls[i]->ca.causal_red;
+    for (size_t j = i + 1; groupable && j < calls.size() && int(L.size()) < kMaxGroup; ++j)
+      if (!done[j] && same_contraction_form(*calls[i], *calls[j])) {
+        L.push_back(int(j));
+        done[j] = true;
+      }
+    G->launches.push_back(L);
+  }
+  *group = G;
+  return JAGG_OK;
 }
 
 jagg_status jagg_plan_destroy(jagg_plan *plan) {

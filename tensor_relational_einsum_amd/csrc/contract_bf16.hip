@@ -27,4 +27,20 @@ hipError_t launch_contract_bf16(const ContractArgs &a, int out_bf16, bool a_kc, 
                 : "bf16 128x128";
   return launch_typed<uint16_t>(a, out_bf16, a_kc, b_kc, va, vb, big, st);
 }
+bool launch_contract_bf16_group(const DmaGroupArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
+                                hipStream_t st, hipError_t *err) {
+  if (!(big && va == 8 && vb == 8 && !a.common.causal_red)) return false;
+#define JAGG_DMA_G(OB)                                                         \
+  if (a_kc && b_kc) *err = launch_dma_group<OB, true, true>(a, st);           \
+  else if (a_kc && !b_kc) *err = launch_dma_group<OB, true, false>(a, st);    \
+  else if (!a_kc && b_kc) *err = launch_dma_group<OB, false, true>(a, st);    \
+  else *err = launch_dma_group<OB, false, false>(a, st);
+  if (out_bf16) {
+    JAGG_DMA_G(1)
+  } else {
+    JAGG_DMA_G(0)
+  }
+#undef JAGG_DMA_G
+  return true;
+}
 }  // namespace jagg

@@ -120,9 +120,9 @@ struct DmaOperand {
   }
 };
 
+// One 256 x 256 output tile: logical tile w of the contraction p.
 template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_kernel(
-    const ContractArgs p) {
+__device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // 4 wavefronts, one per SIMD, each owning a 128 x 128 quarter of the tile
   constexpr int NT = 256, WAVES_N = 2;
   constexpr int WTM = 128, WTN = 128, TM = WTM / 32, TN = WTN / 32;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   int tn, tm, bt;
   int64_t key;
-  decode_tile(p, tm, tn, bt, key);
+  decode_tile(p, w, tm, tn, bt, key);
   const int32_t cnt = p.counts[key];
   if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier
   // the join list is read-only for the kernel's lifetime: reading it through
@@ -371,6 +371,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
 }
 
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_kernel(
+    const ContractArgs p) {
+  dma_tile<OUT_BF16, A_KC, B_KC, NS>(p, logical_tile(p.remap));
+}
+
+// Several independent contractions of one geometry (every field of `common`
+// but the operand, output and join-list addresses) in one launch of n T
+// logical tiles, T per problem.  One launch instead of several shares the
+// last partial wave of tiles and the launch edges.
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_group_kernel(
+    const DmaGroupArgs ga) {
+  const int64_t w = logical_tile(ga.common.remap);
+  int g;
+  int64_t local;
+  const ContractArgs &c = ga.common;
+  if (c.group_m) {
+    // the grouped tile order of one problem walks M-panel groups, each over
+    // every N panel; the problems take turns per M-panel group, so all XCDs
+    // sweep one problem's B operand at a time (as one problem alone does)
+    // and share the A panels of a group between the problems
+    const int64_t Mp = int64_t(c.km) * c.tiles_m, Np = int64_t(c.kn) * c.tiles_n;
+    const int64_t n_groups = (Mp + c.group_m - 1) / c.group_m;
+    const int64_t per_group = int64_t(c.group_m) * Np;
+    const int64_t full = (n_groups - 1) * ga.n * per_group;
+    int64_t gi, r;
+    if (w < full) {
+      const int64_t vg = w / per_group;
+      r = w - vg * per_group;
+      gi = vg / ga.n;
+      g = int(vg - gi * ga.n);
+    } else {
+      const int64_t last = (Mp - (n_groups - 1) * c.group_m) * Np;
+      const int64_t rem = w - full;
+      g = int(rem / last);
+      r = rem - int64_t(g) * last;
+      gi = n_groups - 1;
+    }
+    local = gi * per_group + r;
+  } else {
+    g = int(w / ga.tiles);
+    local = w - int64_t(g) * ga.tiles;
+  }
+  ContractArgs p = ga.common;
+  p.A = ga.A[g];
+  p.B = ga.B[g];
+  p.C = ga.C[g];
+  p.list = ga.list[g];
+  p.counts = ga.counts[g];
+  dma_tile<OUT_BF16, A_KC, B_KC, NS>(p, local);
+}
+
 template <int OB, bool AK, bool BKC>
 static hipError_t launch_dma(const ContractArgs &a, hipStream_t st) {
   ContractArgs b = a;
@@ -378,6 +431,18 @@ static hipError_t launch_dma(const ContractArgs &a, hipStream_t st) {
   b.tiles_n = (a.N + 255) / 256;
   const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
   hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES>), dim3(unsigned(grid)), dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+template <int OB, bool AK, bool BKC>
+static hipError_t launch_dma_group(const DmaGroupArgs &a, hipStream_t st) {
+  DmaGroupArgs b = a;
+  b.common.tiles_m = (a.common.M + 255) / 256;
+  b.common.tiles_n = (a.common.N + 255) / 256;
+  b.tiles = b.common.n_keys * b.common.batch * int64_t(b.common.tiles_m) * b.common.tiles_n;
+  const int64_t grid = b.tiles * b.n;
+  hipLaunchKernelGGL((contract_dma_group_kernel<OB, AK, BKC, JAGG_DMA_STAGES>), dim3(unsigned(grid)), dim3(256), 0,
+                     st, b);
   return hipGetLastError();
 }
 

@@ -253,12 +253,18 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[TM][TN], const uint4 *a,
 // workgroup -> (tile row, tile column, batch index, output key).  Where
 // neighbouring tiles share operand panels, the numbering gives each XCD a
 // contiguous run of tiles (dispatch round-robins workgroups over the 8 XCDs).
-__device__ __forceinline__ void decode_tile(const ContractArgs &p, int &tm, int &tn, int &bt, int64_t &key) {
+// Logical tile of this workgroup: with `remap`, the dispatch order (which
+// deals workgroups round-robin to the 8 XCDs) is renumbered so that each
+// XCD works through one contiguous range of logical tiles.
+__device__ __forceinline__ int64_t logical_tile(bool remap) {
   int64_t w = blockIdx.x;
-  {
-    const int64_t G = gridDim.x;
-    if (p.remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
-  }
+  const int64_t G = gridDim.x;
+  if (remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+  return w;
+}
+
+__device__ __forceinline__ void decode_tile(const ContractArgs &p, int64_t w, int &tm, int &tn, int &bt,
+                                            int64_t &key) {
   if (p.group_m) {
     // Tiles of all output keys form one grid of M panels x N panels, walked
     // column-major in groups of group_m M panels: the tiles that run
@@ -410,7 +416,7 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
 
   int tn, tm, bt;
   int64_t key;
-  decode_tile(p, tm, tn, bt, key);
+  decode_tile(p, logical_tile(p.remap), tm, tn, bt, key);
 
   const int32_t cnt = p.counts[key];
   if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier

@@ -197,6 +197,25 @@ struct ContractArgs {
   // km, kn = key blocks along M and N; group_m = M panels per group (0: off)
   int32_t km, kn, group_m;
 };
+// Independent contractions of one geometry run as one launch of the bf16
+// 256 x 256 LDS-pipelined kernel: `common` holds the shared geometry, the
+// arrays each problem's addresses.
+constexpr int kMaxGroup = 4;
+struct DmaGroupArgs {
+  ContractArgs common;
+  const void *A[kMaxGroup];
+  const void *B[kMaxGroup];
+  void *C[kMaxGroup];
+  const int32_t *list[kMaxGroup];
+  const int32_t *counts[kMaxGroup];
+  int32_t n;
+  int64_t tiles;  // tiles of one problem (set by the launcher)
+};
+// Launches the group when the common form takes the 256 x 256 LDS-pipelined
+// kernel (bf16, 16-byte vectors, no causal mask on the reduced letter);
+// returns false, launching nothing, otherwise.
+bool launch_contract_bf16_group(const DmaGroupArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
+                                hipStream_t st, hipError_t *err);
 // out_bf16: 0 f32 / 1 bf16 output; a_kc / b_kc: operand contiguous along K;
 // va / vb: vector width (elements) of global loads (16 bytes or one element);
 // big: 256x256 tiles (8 wavefronts) instead of 128x128 (4 wavefronts);

@@ -3,8 +3,11 @@
 Builds every relation and workspace once, then ``run()`` issues one library
 call per step on the context's stream; nothing is computed in Python.  By
 default every einsum step is a prepared plan (jagg_plan_create at set-up:
-host planning and join once; jagg_plan_run per step); ``planned=False``
-calls jagg_einsum every time instead.
+host planning and join once; jagg_plan_run per step), and consecutive
+einsum steps that do not read each other's outputs run as one plan group
+(jagg_plan_group: contractions of one form share a launch); ``units`` lists
+what one pass launches.  ``planned=False`` calls jagg_einsum for every step
+instead.
 """
 from __future__ import annotations
 
@@ -53,10 +56,37 @@ class ChainRunner:
             for kind, obj, _ in self.calls:
                 if kind == "einsum":
                     obj.prepare()
+        # units of one pass: (kind, object, step indices)
+        self.units = []
+        i = 0
+        while i < len(self.calls):
+            kind, obj, name = self.calls[i]
+            j = i + 1
+            if planned and kind == "einsum":
+                written = {name}
+                while j < len(self.calls) and self.calls[j][0] == "einsum":
+                    ins = {n for n in w.chain[j].ins}
+                    if ins & written or self.calls[j][2] in written:
+                        break
+                    written.add(self.calls[j][2])
+                    j += 1
+            if j - i > 1:
+                self.units.append(("group", jagg.PlanGroup(ctx, [self.calls[k][1] for k in range(i, j)]),
+                                   list(range(i, j))))
+            else:
+                self.units.append((kind, obj, [i]))
+            i = j
 
     def run(self):
-        for i in range(len(self.calls)):
-            self.run_step(i)
+        for u in range(len(self.units)):
+            self.run_unit(u)
+
+    def run_unit(self, u: int):
+        kind, obj, steps = self.units[u]
+        if kind == "group":
+            obj.run()
+        else:
+            self.run_step(steps[0])
 
     def capture(self) -> jagg.Graph:
         """The whole chain recorded into one graph (every buffer it uses is
