@@ -229,6 +229,87 @@ int oracle_dense(const char *spec, int g, int agg, double alpha, double beta, do
 }
 
 /* ------------------------------------------------------------------------ */
+/* Contractions whose recompose step applies a map to the aggregated value   */
+/* (as attention's recompose writes a / l).  Def. 3.7: join, SUM the block   */
+/* products of equal output key, then recompose; here the recompose also     */
+/* takes an addend or a second sum of the same join:                         */
+/*   RC_MUL_PLUS  out[o] = alpha * sum_r in0 in1 + in2[o]   (in2 holds only  */
+/*                output letters: one addend per output element)             */
+/*   RC_SWIGLU    a = sum_r in0 in1, b = sum_r in0 in2 (in1, in2 over the    */
+/*                same letters), out[o] = alpha * a / (1 + e^-a) * b         */
+/* Dense form, unrounded double; `idx` as for oracle_dense.                  */
+/* ------------------------------------------------------------------------ */
+enum { RC_MUL_PLUS = 0, RC_SWIGLU = 1 };
+
+int oracle_dense_recompose(const char *spec, int kind, double alpha, const int64_t *ext26,
+                           const double *const *ins, const int64_t *idx, int64_t n_out, double *out) {
+  ospec p;
+  int rc = parse_spec(spec, &p);
+  if (rc) return rc;
+  if (p.n_in != 3 || p.n_reduced == 0) return OR_UNSUPPORTED;
+  if (kind == RC_MUL_PLUS) {
+    for (int a = 0; a < p.in_len[2]; ++a)
+      if (!strchr(p.out, p.in[2][a])) return OR_UNSUPPORTED; /* the addend holds output letters only */
+  } else if (kind == RC_SWIGLU) {
+    if (strcmp(p.in[1], p.in[2]) != 0) return OR_UNSUPPORTED; /* both sums over the same join */
+  } else {
+    return OR_UNSUPPORTED;
+  }
+  for (int a = 0; a < p.n_letters; ++a)
+    if (ext26[p.order[a] - 'a'] < 1) return OR_BAD_SHAPE;
+  int64_t in_stride[OR_MAX_IN][26];
+  memset(in_stride, 0, sizeof(in_stride));
+  for (int j = 0; j < p.n_in; ++j) {
+    int64_t s = 1;
+    for (int a = p.in_len[j] - 1; a >= 0; --a) {
+      in_stride[j][p.in[j][a] - 'a'] = s;
+      s *= ext26[p.in[j][a] - 'a'];
+    }
+  }
+  int64_t out_total = 1;
+  for (int a = 0; a < p.out_len; ++a) out_total *= ext26[p.out[a] - 'a'];
+  int64_t red_total = 1;
+  for (int a = 0; a < p.n_reduced; ++a) red_total *= ext26[p.reduced[a] - 'a'];
+  if (!idx) n_out = out_total;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t q = 0; q < n_out; ++q) {
+    int64_t coord[26];
+    memset(coord, 0, sizeof(coord));
+    int64_t rem = idx ? idx[q] : q;
+    for (int a = p.out_len - 1; a >= 0; --a) {
+      int64_t e = ext26[p.out[a] - 'a'];
+      coord[p.out[a] - 'a'] = rem % e;
+      rem /= e;
+    }
+    double s1 = 0.0, s2 = 0.0;
+    for (int64_t r = 0; r < red_total; ++r) {
+      int64_t rr = r;
+      for (int a = p.n_reduced - 1; a >= 0; --a) {
+        int64_t e = ext26[p.reduced[a] - 'a'];
+        coord[p.reduced[a] - 'a'] = rr % e;
+        rr /= e;
+      }
+      double x[OR_MAX_IN];
+      for (int j = 0; j < p.n_in; ++j) {
+        int64_t off = 0;
+        for (int a = 0; a < p.in_len[j]; ++a) off += coord[p.in[j][a] - 'a'] * in_stride[j][p.in[j][a] - 'a'];
+        x[j] = ins[j][off];
+      }
+      s1 += x[0] * x[1];
+      if (kind == RC_SWIGLU) s2 += x[0] * x[2];
+    }
+    if (kind == RC_MUL_PLUS) {
+      int64_t off = 0;
+      for (int a = 0; a < p.in_len[2]; ++a) off += coord[p.in[2][a] - 'a'] * in_stride[2][p.in[2][a] - 'a'];
+      out[q] = alpha * s1 + ins[2][off];
+    } else {
+      out[q] = alpha * (s1 / (1.0 + exp(-s1))) * s2;
+    }
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Relation geometry (Def. 3.1 intervals, padded blocks).                    */
 /* ------------------------------------------------------------------------ */
 

@@ -88,6 +88,8 @@ def _load():
                                                    ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_softmax_merge.argtypes = [ctypes.c_double] * 6 + [ctypes.c_void_p]
         lib.oracle_softmax_merge.restype = None
+        lib.oracle_dense_recompose.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.c_double, i64p, dpp, i64p,
+                                               ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         lib.oracle_round.restype = None
         _lib = lib
@@ -387,3 +389,61 @@ def contract(spec, a, b, extents):
             raise OracleError(f"input {lt} has shape {x.shape}, expected {want}")
         xs.append(x)
     return np.einsum(spec, xs[0], xs[1], optimize=True)
+
+
+RECOMPOSE_CODES = {"mul_plus": 0, "swiglu": 1}
+
+
+def dense_recompose(spec, kind, inputs, extents, alpha=1.0, sample=None):
+    """A contraction whose recompose step maps the aggregated value, dense
+    form, unrounded float64 (see oracle.c, oracle_dense_recompose):
+    'mul_plus': alpha * sum_r in0 in1 + in2 (in2 over output letters only);
+    'swiglu': alpha * silu(sum_r in0 in1) * sum_r in0 in2.
+    ``sample``: flat output indices, as for ``dense``."""
+    lib = _load()
+    ins, out_letters = _parse(spec)
+    arrs = []
+    for lt, x in zip(ins, inputs):
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        want = tuple(int(extents.get(c, -1)) for c in lt)
+        if x.shape != want:
+            raise OracleError(f"input {lt} has shape {x.shape}, expected {want}")
+        arrs.append(x)
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    ext = _ext26(extents)
+    if sample is None:
+        out = np.zeros(tuple(int(extents[c]) for c in out_letters), dtype=np.float64)
+        rc = lib.oracle_dense_recompose(spec.encode(), RECOMPOSE_CODES[kind], alpha, _i64p(ext), ptrs, None, 0,
+                                        out.ctypes.data)
+    else:
+        idx = np.ascontiguousarray(np.asarray(sample, dtype=np.int64))
+        out = np.zeros(idx.shape[0], dtype=np.float64)
+        rc = lib.oracle_dense_recompose(spec.encode(), RECOMPOSE_CODES[kind], alpha, _i64p(ext), ptrs, _i64p(idx),
+                                        idx.shape[0], out.ctypes.data)
+    _check(rc, "oracle_dense_recompose")
+    return out
+
+
+def relational_recompose(spec, kind, rel_inputs, extents, blockings, alpha=1.0):
+    """The relational form (Def. 3.7) of ``dense_recompose``: the join and
+    SUM of the contraction(s) by ``relational``, then the recompose map on
+    the aggregated output blocks -- plus the addend relation's block of the
+    same key ('mul_plus'), or silu(a) * b of the two sums ('swiglu').  The
+    addend must be blocked like the output.  Returns (out relation float64
+    unrounded, present per output tuple)."""
+    ins, out_letters = _parse(spec)
+    if len(ins) != 3:
+        raise OracleError("a recompose spec takes three inputs")
+    sub = f"{ins[0]},{ins[1]}->{out_letters}"
+    a, present = relational(sub, rel_inputs[:2], extents, blockings, alpha=1.0)
+    if kind == "mul_plus":
+        if sorted(ins[2]) != sorted(out_letters):
+            raise OracleError("the addend must hold exactly the output letters")
+        addend = repartition(np.asarray(rel_inputs[2], dtype=np.float64), ins[2], blockings, out_letters, blockings,
+                             extents)
+        return alpha * a + addend, present
+    if kind == "swiglu":
+        b, _ = relational(f"{ins[0]},{ins[2]}->{out_letters}", [rel_inputs[0], rel_inputs[2]], extents, blockings,
+                          alpha=1.0)
+        return alpha * (a / (1.0 + np.exp(-a))) * b, present
+    raise OracleError(kind)

@@ -455,3 +455,73 @@ def test_blas_contraction_closed_form():
     u, v, w = np.arange(1, 5.0), np.array([1.0, -2.0, 3.0]), np.array([2.0, 0.0, -1.0, 5.0, 1.0])
     C = O.contract("ij,jk->ik", np.outer(u, v), np.outer(v, w), dict(i=4, j=3, k=5))
     assert np.array_equal(C, np.outer(u, w) * 14.0)
+
+
+# Contractions with a recompose map (oracle_dense_recompose): the residual
+# form 'mul_plus' and the gated form 'swiglu'.
+RECOMPOSE_CASES = [
+    ("bsqd,qdh,bsh->bsh", dict(b=2, s=5, q=3, d=4, h=6)),
+    ("ij,jk,ik->ik", dict(i=7, j=9, k=5)),
+]
+
+
+@pytest.mark.parametrize("spec,ext", RECOMPOSE_CASES)
+def test_mul_plus_matches_numpy(spec, ext):
+    ins, _ = spec.split("->")
+    rng = np.random.default_rng(11)
+    xs = [rng.standard_normal([ext[c] for c in lt]) for lt in ins.split(",")]
+    got = O.dense_recompose(spec, "mul_plus", xs, ext, alpha=0.5)
+    lt = ins.split(",")
+    want = 0.5 * np.einsum(f"{lt[0]},{lt[1]}->{spec.split('->')[1]}", xs[0], xs[1]) + xs[2]
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    # special cases: a zero addend is the plain contraction, a zero factor the addend
+    zero = O.dense_recompose(spec, "mul_plus", [xs[0], xs[1], np.zeros_like(xs[2])], ext, alpha=0.5)
+    assert np.array_equal(zero, O.dense(f"{lt[0]},{lt[1]}->{spec.split('->')[1]}", xs[:2], ext, alpha=0.5))
+    only = O.dense_recompose(spec, "mul_plus", [xs[0], np.zeros_like(xs[1]), xs[2]], ext)
+    assert np.array_equal(only, xs[2])
+
+
+def test_swiglu_matches_torch():
+    import torch
+    spec, ext = "bsh,hf,hf->bsf", dict(b=2, s=6, h=8, f=5)
+    rng = np.random.default_rng(12)
+    x, wg, wu = (rng.standard_normal([ext[c] for c in lt]) for lt in ("bsh", "hf", "hf"))
+    got = O.dense_recompose(spec, "swiglu", [x, wg, wu], ext)
+    tx = torch.from_numpy(x)
+    want = (torch.nn.functional.silu(tx @ torch.from_numpy(wg)) * (tx @ torch.from_numpy(wu))).numpy()
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    # silu(0) = 0: a zero gate weight gives zero
+    assert np.array_equal(O.dense_recompose(spec, "swiglu", [x, np.zeros_like(wg), wu], ext), np.zeros((2, 6, 5)))
+    # sampled outputs equal the full evaluation
+    idx = np.array([0, 7, 33, 59])
+    assert np.array_equal(O.dense_recompose(spec, "swiglu", [x, wg, wu], ext, sample=idx), got.reshape(-1)[idx])
+
+
+def test_recompose_rejects_malformed():
+    ext = dict(i=3, j=4, k=5)
+    x = [np.ones((3, 4)), np.ones((4, 5)), np.ones((4, 5))]
+    with pytest.raises(O.OracleError):  # the addend holds a reduced letter
+        O.dense_recompose("ij,jk,jk->ik", "mul_plus", x, ext)
+    with pytest.raises(O.OracleError):  # the two sums over different letters
+        O.dense_recompose("ij,jk,ik->ik", "swiglu", [x[0], x[1], np.ones((3, 5))], ext)
+
+
+@pytest.mark.parametrize("kind,spec,ext,blk", [
+    ("mul_plus", "bsqd,qdh,bsh->bsh", dict(b=2, s=7, q=3, d=4, h=10), dict(b=1, s=3, q=2, d=1, h=4)),
+    ("swiglu", "bsh,hf,hf->bsf", dict(b=1, s=9, h=10, f=7), dict(b=1, s=2, h=3, f=3)),
+])
+def test_relational_recompose_equals_dense(kind, spec, ext, blk):
+    """Def. 3.7 with the recompose map (join, SUM, then the map on the
+    aggregated blocks) against the dense definition, ragged blocks included."""
+    ins, out = spec.split("->")
+    ins = ins.split(",")
+    rng = np.random.default_rng(13)
+    xs = [rng.standard_normal([ext[c] for c in lt]) for lt in ins]
+    rels = [O.to_relation(x, lt, ext, blk) for x, lt in zip(xs, ins)]
+    got_rel, present = O.relational_recompose(spec, kind, rels, ext, blk, alpha=0.75)
+    assert present.all()
+    got = O.from_relation(got_rel, out, ext, blk)
+    want = O.dense_recompose(spec, kind, xs, ext, alpha=0.75)
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+    pad = O.to_relation(np.ones([ext[c] for c in out], dtype=np.uint8), out, ext, blk) == 0
+    assert np.all(got_rel[pad] == 0.0)
