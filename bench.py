@@ -2,10 +2,14 @@
 
 One step = one pass of the whole hot path over the LLaMA-7B-shaped block
 (4 x 2048 tokens, hidden 4096, 32 heads x 128, SwiGLU 11008, bf16 weights):
-every operator is a join-agg spec (join enumeration, MFMA block contraction,
-streaming map / SUM-MAX reduce) and the head-major relayouts around the
-causal attention are repartitions.  Inputs are seeded synthetic tensors
-already resident in HBM when the timed region starts.
+every operator is a join-agg spec -- prepared once (planning and join
+enumeration), then per step the MFMA block contractions (the residual adds
+and the SwiGLU gate as the recompose maps of the contractions feeding them),
+attention as one spec whose aggregation merges online-softmax triples, and
+the streaming RMS-norm reduce and map.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.  The same block with
+separate residual / gate specs, and with the five-spec attention chain
+between head-major repartitions, are timed beside it.
 
 Prints one JSON line: value = algorithmic TFLOP/s of the step (contraction
 FLOPs, causal attention counted element-wise) with the chain recorded once
@@ -64,6 +68,10 @@ def spec_flops(st: I.Step, ext: dict) -> float:
         groups = [set(q) | set(k), set(v) | set(st.spec.split("->")[1])]
     elif st.g == "mul" and st.agg == "sum" and len(st.ins) == 2:
         groups = [set("".join(ins))]
+    elif st.g == "mul_plus":  # the contraction; the addend is not a product
+        groups = [set(ins[0]) | set(ins[1])]
+    elif st.g == "swiglu":  # two contractions over one join
+        groups = [set(ins[0]) | set(ins[1]), set(ins[0]) | set(ins[2])]
     else:
         return 0.0
     total = 0.0
@@ -416,7 +424,10 @@ def cpu_baseline(w: I.Workload, dense: dict, target_s: float = 12.0) -> dict:
         k = max(1000, int(budget / (per_flop * per_out)))
         idx = rng.integers(0, math.prod(out_shape), k)
         t0 = time.perf_counter()
-        O.dense(st.spec, [vals[n] for n in st.ins], w.extents, sample=idx)
+        if st.g in ("mul_plus", "swiglu"):
+            O.dense_recompose(st.spec, st.g, [vals[n] for n in st.ins], w.extents, sample=idx)
+        else:
+            O.dense(st.spec, [vals[n] for n in st.ins], w.extents, sample=idx)
         t_total += time.perf_counter() - t0
         flops += k * per_out
         samples += k
@@ -435,6 +446,7 @@ OTHER_CONFIGS = [
     ("attention_gqa_causal", I.attention_gqa),
     ("attention_packed_causal", I.attention_packed),
     ("multi_index_fp32", I.multi_index),
+    ("llama_block_unfused_epilogues", lambda: I.llama_block(fused_attention=True)),
     ("llama_block_attention_chain", I.llama_block),
 ] + [(f"matrix_chain_{c}", (lambda c=c: I.matrix_chain(c))) for c in "ABCDE"]
 
@@ -445,7 +457,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama",
-                    choices=["llama", "llama_chain", "attention", "attention_chain", "attention_gqa",
+                    choices=["llama", "llama_unfused_epilogues", "llama_chain", "attention", "attention_chain",
+                             "attention_gqa",
                              "attention_packed", "multi_index", "matmul"] + [f"chain_{c}" for c in "ABCDE"],
                     help="llama / attention: fused attention; *_chain: the five-spec attention chain; "
                          "chain_A .. chain_E: the matrix chains")
@@ -467,7 +480,9 @@ def main():
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
     ctx = jagg.Context(0, stream)
-    makers = {"llama": lambda: I.llama_block(fused_attention=True), "llama_chain": I.llama_block,
+    makers = {"llama": lambda: I.llama_block(fused_attention=True, fused_epilogues=True),
+              "llama_unfused_epilogues": lambda: I.llama_block(fused_attention=True),
+              "llama_chain": I.llama_block,
               "attention": lambda: I.attention_chain(fused=True), "attention_chain": I.attention_chain,
               "attention_gqa": I.attention_gqa, "attention_packed": I.attention_packed,
               "multi_index": I.multi_index, "matmul": I.matmul_256}
@@ -502,8 +517,8 @@ def main():
             ent["TFLOP/s"] = round(f / (call_ms[i] * 1e-3) / 1e12, 2)
         ent["GB/s"] = round(by / (call_ms[i] * 1e-3) / 1e9, 1)
         breakdown.append(ent)
-        if all(isinstance(st, I.Step) and st.g == "mul" and st.agg == "sum" and not st.causal
-               and len(st.ins) == 2 and run.rel[st.ins[0]].dtype == "bf16" for st in sts) and f:
+        if all(isinstance(st, I.Step) and st.g in ("mul", "mul_plus", "swiglu") and st.agg == "sum"
+               and not st.causal and run.rel[st.ins[0]].dtype == "bf16" for st in sts) and f:
             dom_flops += f
             dom_ms += float(call_ms[i])
             dom_bytes += by
@@ -565,7 +580,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
     cpu = None
-    if not args.no_cpu_baseline and args.workload in ("llama", "llama_chain"):
+    if not args.no_cpu_baseline and args.workload in ("llama", "llama_unfused_epilogues", "llama_chain"):
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, dense)
     out = {

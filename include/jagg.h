@@ -78,8 +78,28 @@ typedef enum {
   JAGG_G_RMS_SCALE = 5,   /* x0 / sqrt(x1 * beta + eps) * x2         */
   JAGG_G_SILU_MUL = 6,    /* x0 / (1 + exp(-x0)) * x1                */
   JAGG_G_ADD = 7,         /* x0 + x1 (+ x2)                          */
-  JAGG_G_ATTENTION = 8    /* with JAGG_AGG_SOFTMAX; see below        */
+  JAGG_G_ATTENTION = 8,   /* with JAGG_AGG_SOFTMAX; see below        */
+  JAGG_G_MUL_PLUS = 9,    /* contraction + addend; see below         */
+  JAGG_G_SWIGLU = 10      /* gated pair of contractions; see below   */
 } jagg_g;
+
+/* Contractions whose recompose step maps the aggregated value (Def. 3.7:
+ * join, SUM the block products of equal output key, recompose; as the
+ * attention aggregation's recompose writes a / l).  Both take three inputs
+ * and agg = JAGG_AGG_SUM, no causal or segment pair:
+ *  - JAGG_G_MUL_PLUS: out = alpha * sum_r x0 x1 + x2, where x2 holds exactly
+ *    the output letters in the output's order and blocking (one addend per
+ *    output element: a residual add fused into the product that feeds it).
+ *  - JAGG_G_SWIGLU: a = sum_r x0 x1 and b = sum_r x0 x2 over one join (x2
+ *    laid out as x1: the same letters, dtype and blocking), out = alpha *
+ *    silu(a) * b with silu(a) = a / (1 + e^-a): the gate and up projections of
+ *    a SwiGLU feed-forward layer and their product, without writing either
+ *    projection.  Runs on the bf16 256 x 128-tile pipeline only: bf16
+ *    operands in 16-byte vectors, x0 contiguous along the reduced letters,
+ *    x1 / x2 contributing the output's innermost letters, at least 256 such
+ *    tiles (JAGG_E_UNSUPPORTED otherwise).
+ * The inputs are read as stored (bf16 or f32 addend); sums accumulate in
+ * fp32 and the map is applied before the single rounding to out_dtype. */
 
 /* Attention as one join-agg (g = JAGG_G_ATTENTION, agg = JAGG_AGG_SOFTMAX).
  * The spec is "Q,K,V->O" with the letter roles "X s D, X t D, X t E -> X s E":

@@ -208,13 +208,18 @@ bool g_arity_ok(int g, int n) {
     case JAGG_G_SILU_MUL: return n == 2;
     case JAGG_G_EXP_SUB_DIV:
     case JAGG_G_RMS_SCALE:
-    case JAGG_G_ATTENTION: return n == 3;
+    case JAGG_G_ATTENTION:
+    case JAGG_G_MUL_PLUS:
+    case JAGG_G_SWIGLU: return n == 3;
   }
   return false;
 }
 
 jagg_status check_spec(jagg_ctx *ctx, const jagg_spec *sp, const Spec &p) {
-  if (sp->g < JAGG_G_MUL || sp->g > JAGG_G_ATTENTION) return fail(ctx, JAGG_E_INVALID, "unknown g %d", int(sp->g));
+  if (sp->g < JAGG_G_MUL || sp->g > JAGG_G_SWIGLU) return fail(ctx, JAGG_E_INVALID, "unknown g %d", int(sp->g));
+  if ((sp->g == JAGG_G_MUL_PLUS || sp->g == JAGG_G_SWIGLU) && (sp->agg != JAGG_AGG_SUM || sp->causal_s))
+    return fail(ctx, JAGG_E_UNSUPPORTED, "g %d is a contraction with a recompose map: SUM, no causal pair",
+                int(sp->g));
   if (sp->agg < JAGG_AGG_NONE || sp->agg > JAGG_AGG_SOFTMAX) return fail(ctx, JAGG_E_INVALID, "unknown aggregation");
   if ((sp->agg == JAGG_AGG_SOFTMAX) != (sp->g == JAGG_G_ATTENTION))
     return fail(ctx, JAGG_E_UNSUPPORTED, "the softmax-triple aggregation pairs only with g = ATTENTION");
@@ -1450,6 +1455,25 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
         return fail(ctx, JAGG_E_UNSUPPORTED, "causal contraction over a reduced letter needs 16-byte aligned operands");
     }
   }
+  a.ent_w = 1 + p.n_in;
+  if (sp->g == JAGG_G_MUL_PLUS) {
+    // the addend is laid out as the output: same letters in the same order,
+    // same blocking, so its element offset is the output's
+    const jagg_relation &X = *ins[2];
+    if (p.in[2] != p.out || X.n_tuples != out->n_tuples || X.be != out->be)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "MUL_PLUS: input 2 must hold the output letters in the output's order");
+    a.epi = 1;
+    a.X = X.buf;
+    a.x_bf16 = X.dt == JAGG_BF16;
+  } else if (sp->g == JAGG_G_SWIGLU) {
+    const jagg_relation &R2 = *ins[2];
+    if (ib != 1 || p.in[2] != p.in[1] || R2.dt != RB.dt || R2.n_tuples != RB.n_tuples || R2.be != RB.be)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "SWIGLU: input 2 must be laid out as input 1, on the N side");
+    if (R2.be * esz_of(R2.dt) >= (int64_t(1) << 31))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "contraction block of 2 GiB or more");
+    a.epi = 2;
+    a.B2 = R2.buf;
+  }
   if (ctx->trace)
     fprintf(stderr, "[jagg] contract %s: %s batch %d M %d N %d K %d A%s/v%d B%s/v%d keys %lld per_key %d\n",
             sp->einsum, dtype ? "bf16" : "f32", a.batch, a.M, a.N, a.K, a_kc ? "k" : "m", va, b_kc ? "k" : "n", vb,
@@ -1547,7 +1571,8 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
     P.kind = PlannedCall::ATTENTION;
   } else if (spec->agg != JAGG_AGG_NONE) {
     P.kind = PlannedCall::REDUCE;
-    if (spec->agg == JAGG_AGG_SUM && spec->g == JAGG_G_MUL && n_in == 2 && !b.p.reduced.empty()) {
+    const bool recompose = spec->g == JAGG_G_MUL_PLUS || spec->g == JAGG_G_SWIGLU;
+    if (spec->agg == JAGG_AGG_SUM && ((spec->g == JAGG_G_MUL && n_in == 2) || recompose) && !b.p.reduced.empty()) {
       bool both = true, m_any = false, n_any = false;
       for (char c : b.p.reduced)
         both = both && b.p.in[0].find(c) != std::string::npos && b.p.in[1].find(c) != std::string::npos;
@@ -1558,6 +1583,8 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
       }
       if (both && m_any && n_any) P.kind = PlannedCall::CONTRACT;
     }
+    if (recompose && P.kind != PlannedCall::CONTRACT)
+      return fail(ctx, JAGG_E_UNSUPPORTED, "g %d needs a contraction of inputs 0 and 1", int(spec->g));
   }
 
   char *ws = static_cast<char *>(workspace);
@@ -1602,8 +1629,12 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
     ContractArgs &ca = P.ca;
     // 256x256 tiles where the block is large enough and the grid still fills the chip
     const int F = P.dtype ? 8 : 4;
-    const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + 255) / 256);
-    P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= 256 && big_tiles >= 256 && !ca.causal_red;
+    const int BNt = ca.epi == 2 ? 128 : 256;
+    const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + BNt - 1) / BNt);
+    P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= BNt && big_tiles >= 256 && !ca.causal_red;
+    if (ca.epi == 2 && !(P.big && P.dtype && P.akc))
+      return fail(ctx, JAGG_E_UNSUPPORTED, "SWIGLU runs on the 256 x 128 bf16 pipeline: bf16 operands in 16-byte "
+                  "vectors, input 0 contiguous along the reduced letters, at least 256 tiles of 256 x 128");
     // per-XCD renumbering pays where several tiles of one output block share panels
     const int bm = P.big ? 256 : 128;
     ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;
@@ -1667,6 +1698,8 @@ bool same_contraction_form(const PlannedCall &x, const PlannedCall &y) {
   u.C = v.C = nullptr;
   u.list = v.list = nullptr;
   u.counts = v.counts = nullptr;
+  u.X = v.X = nullptr;
+  u.B2 = v.B2 = nullptr;
   return memcmp(&u, &v, sizeof(u)) == 0;
 }
 
@@ -1940,6 +1973,8 @@ jagg_status jagg_plan_run(jagg_ctx *ctx, const jagg_plan *plan) {
       ga.C[i] = c.C;
       ga.list[i] = c.list;
       ga.counts[i] = c.counts;
+      ga.X[i] = c.X;
+      ga.B2[i] = c.B2;
     }
     hipError_t e = hipSuccess;
     if (!launch_contract_bf16_group(ga, m0.out_bf16, m0.akc, m0.bkc, m0.va, m0.vb, m0.big, ctx->stream, &e))
@@ -1990,7 +2025,8 @@ jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans,
     std::vector<int> L{int(i)};
     done[i] = true;
     const bool groupable = calls[i]->kind == PlannedCall::CONTRACT && calls[i]->dtype == 1 && calls[i]->big &&
-                           calls[i]->va == 8 && calls[i]->vb == 8 && !calls[i]->ca.causal_red;
+                           calls[i]->va == 8 && calls[i]->vb == 8 && !calls[i]->ca.causal_red &&
+                           (calls[i]->ca.epi == 0 || calls[i]->akc);
     for (size_t j = i + 1; groupable && j < calls.size() && int(L.size()) < kMaxGroup; ++j)
       if (!done[j] && same_contraction_form(*calls[i], *calls[j])) {
         L.push_back(int(j));

@@ -85,12 +85,18 @@ constexpr int kDmaRowBytes = kDmaBK * 2;   // bytes of one K-contiguous row
 constexpr int kDmaTileBytes = 256 * kDmaRowBytes;  // one operand tile (16 KB)
 
 // One operand's DMA loads: 256 rows (M or N) by 32 K values; R*4 slots over
-// NT threads, NI instructions each.
-template <bool KC, int NT>
+// NT threads, NI instructions each.  SPLIT: the 256 rows are two operands of
+// 128 rows each (the gate and up weights of SwiGLU): instructions i < NI/2
+// fill rows 0..127 from the first, the others rows 128..255 from the second,
+// each row index taken modulo 128 in its own operand.  An M/N-contiguous
+// split tile is stored as two [32 K rows][16 slots] halves (slot c of K row
+// k at c ^ 4 (k & 3)) so that one instruction's 1 KB stays in one half.
+template <bool KC, int NT, bool SPLIT = false>
 struct DmaOperand {
   static constexpr int SLOTS = 256 * 4;
   static constexpr int NI = SLOTS / NT;
   static_assert(SLOTS % NT == 0 && NT % 64 == 0, "tile does not split over the wavefronts");
+  static_assert(!SPLIT || (NI % 2 == 0 && NT == 256), "split halves must fall on instruction boundaries");
   uint32_t off[NI];   // byte offset from the step's origin, or kOob for rows past the edge
   int32_t kidx[NI];   // K index of the lane's vector inside the step
 
@@ -102,8 +108,12 @@ struct DmaOperand {
       int row, k;
       if (KC) {
         const int r = P >> 2, q = (P & 3) ^ ((r >> 2) & 3);
-        row = r;
+        row = SPLIT ? (r & 127) : r;
         k = q * 8;
+      } else if (SPLIT) {
+        const int Q = P & 511, kr = Q >> 4, c = (Q & 15) ^ ((kr & 3) << 2);
+        row = c * 8;
+        k = kr;
       } else {
         const int kr = P >> 5, c = (P & 31) ^ ((kr & 3) << 2);
         row = c * 8;
@@ -120,14 +130,22 @@ struct DmaOperand {
   }
 };
 
-// One 256 x 256 output tile: logical tile w of the contraction p.
-template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+// One 256 x 256 output tile: logical tile w of the contraction p.  SW
+// (SwiGLU): the tile is 256 rows x 128 output columns, its B tile the same
+// 128 columns of B and of B2; each wavefront owns 128 rows x 64 columns of
+// both products (fragments j = 0, 1 of B, j = 2, 3 of B2, the same columns)
+// and recomposes silu(AB) * (AB2) in registers.
+// EPI: the recompose map, fixed per instantiation so that the epilogue
+// unrolls with the accumulators in registers: 0 none, 1 / 2 add an f32 /
+// bf16 addend laid out as C (MUL_PLUS), 3 SwiGLU.
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
 __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
+  constexpr bool SW = EPI == 3;
   // 4 wavefronts, one per SIMD, each owning a 128 x 128 quarter of the tile
   constexpr int NT = 256, WAVES_N = 2;
-  constexpr int WTM = 128, WTN = 128, TM = WTM / 32, TN = WTN / 32;
-  constexpr int BM = 256, BN = 256, BK = kDmaBK;
-  constexpr int L = DmaOperand<A_KC, NT>::NI + DmaOperand<B_KC, NT>::NI;  // loads per step per thread
+  constexpr int WTM = 128, WTN = SW ? 64 : 128, TM = WTM / 32, TN = 4;
+  constexpr int BM = 256, BN = SW ? 128 : 256, BK = kDmaBK;
+  constexpr int L = DmaOperand<A_KC, NT>::NI + DmaOperand<B_KC, NT, SW>::NI;  // loads per step per thread
   static_assert(NS >= 3 && NS <= 5, "stage count");
   __shared__ __attribute__((aligned(1024))) char smem[NS * 2 * kDmaTileBytes];
   auto stage = [&](int s) { return smem + (s % NS) * (2 * kDmaTileBytes); };
@@ -140,7 +158,7 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // the join list is read-only for the kernel's lifetime: reading it through
   // the constant address space keeps the tuple-id reads on the scalar unit
   typedef const __attribute__((address_space(4))) int32_t *const_i32p;
-  const const_i32p ents = (const_i32p)(p.list + key * int64_t(p.per_key) * 3);
+  const const_i32p ents = (const_i32p)(p.list + key * int64_t(p.per_key) * p.ent_w);
 
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = (p.K + BK - 1) / BK;
@@ -154,7 +172,7 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   const int wave = threadIdx.x >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   DmaOperand<A_KC, NT> da;
-  DmaOperand<B_KC, NT> db;
+  DmaOperand<B_KC, NT, SW> db;
   da.init(wave, lane, p.M - m0, p.sAm, p.sAk);
   db.init(wave, lane, p.N - n0, p.sBn, p.sBk);
 
@@ -167,7 +185,7 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // issue in the shadow of one MFMA instead of idling the matrix core.
   int ld = 0, le = 0, lkt = 0;
   int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
-  i32x4_rsrc rs_a, rs_b;  // resources of the step being loaded
+  i32x4_rsrc rs_a, rs_b, rs_b2;  // resources of the step being loaded (rs_b2: SwiGLU's B2)
   int k_left = 0, k_next = p.K;
   char *ld_buf = smem;
   const int64_t a_step = int64_t(BK) * p.sAk * 2, b_step = int64_t(BK) * p.sBk * 2;
@@ -184,19 +202,28 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
     const bool live = ld < steps;
     rs_a = dma_rsrc(reinterpret_cast<const void *>(pa), live ? na : 0);
     rs_b = dma_rsrc(reinterpret_cast<const void *>(pb), live ? nb : 0);
+    // B2 has B's geometry: the same offsets from its own base
+    if constexpr (SW)
+      rs_b2 = dma_rsrc(reinterpret_cast<const void *>(pb - reinterpret_cast<uint64_t>(p.B) +
+                                                      reinterpret_cast<uint64_t>(p.B2)),
+                       live ? nb : 0);
     k_left = k_next;
     ld_buf = buf;
   };
   auto dma_a = [&](int i) { da.issue(i, rs_a, k_left, ld_buf, wave_s); };
-  auto dma_b = [&](int i) { db.issue(i, rs_b, k_left, ld_buf + kDmaTileBytes, wave_s); };
+  auto dma_b = [&](int i) {
+    constexpr int NBH = DmaOperand<B_KC, NT, SW>::NI / 2;
+    if constexpr (SW) db.issue(i, i < NBH ? rs_b : rs_b2, k_left, ld_buf + kDmaTileBytes, wave_s);
+    else db.issue(i, rs_b, k_left, ld_buf + kDmaTileBytes, wave_s);
+  };
   auto advance = [&]() {
     ++ld;
     if (++lkt == KT) {
       lkt = 0;
       k_next = p.K;
       if (++le < cnt) {
-        la = ents[le * 3 + p.a_slot];
-        lb = ents[le * 3 + p.b_slot];
+        la = ents[le * p.ent_w + p.a_slot];
+        lb = ents[le * p.ent_w + p.b_slot];
       }
       tuple_origin();
     } else {
@@ -207,7 +234,7 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
       nb -= b_step;
     }
   };
-  constexpr int NA = DmaOperand<A_KC, NT>::NI, NB = DmaOperand<B_KC, NT>::NI;
+  constexpr int NA = DmaOperand<A_KC, NT>::NI, NB = DmaOperand<B_KC, NT, SW>::NI;
 
   const int wm = (wave / WAVES_N) * WTM, wn = (wave % WAVES_N) * WTN;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -224,7 +251,15 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
     const int slot = (col0 >> 3) + 2 * (g16 & 1) + ((s16 & 3) >> 1);
     return kr * 512 + ((slot ^ ((kr & 3) << 2)) << 4) + 8 * (s16 & 1);
   };
-  int a_addr[A_KC ? 2 : TM], b_addr[B_KC ? 2 : TN];
+  // SwiGLU split halves, M/N-contiguous: [32 K rows][16 slots] per half
+  auto rc_addr_h = [&](int col0) {
+    const int kr = 8 * (g16 >> 1) + (s16 >> 2);
+    const int slot = ((col0 & 127) >> 3) + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+    return (col0 >> 7) * 8192 + kr * 256 + ((slot ^ ((kr & 3) << 2)) << 4) + 8 * (s16 & 1);
+  };
+  // B row (N) of fragment j of this wavefront: j < 2 from B, j >= 2 from B2
+  auto b_row = [&](int j) { return SW ? (j >> 1) * 128 + wn + 32 * (j & 1) : wn + 32 * j; };
+  int a_addr[A_KC ? 2 : TM], b_addr[B_KC ? (SW ? 2 * TN : 2) : TN];
   if constexpr (A_KC) {
     a_addr[0] = kc_addr(wm, 0);
     a_addr[1] = kc_addr(wm, 1);
@@ -232,9 +267,18 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) a_addr[i] = rc_addr(wm + 32 * i);
   }
-  if constexpr (B_KC) {
+  if constexpr (B_KC && SW) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      b_addr[2 * j] = kc_addr(b_row(j), 0) + kDmaTileBytes;
+      b_addr[2 * j + 1] = kc_addr(b_row(j), 1) + kDmaTileBytes;
+    }
+  } else if constexpr (B_KC) {
     b_addr[0] = kc_addr(wn, 0) + kDmaTileBytes;
     b_addr[1] = kc_addr(wn, 1) + kDmaTileBytes;
+  } else if constexpr (SW) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_addr[j] = rc_addr_h(b_row(j)) + kDmaTileBytes;
   } else {
 #pragma unroll
     for (int j = 0; j < TN; ++j) b_addr[j] = rc_addr(wn + 32 * j) + kDmaTileBytes;
@@ -244,10 +288,11 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   auto frag_kc = [&](const char *base, int addr, int i) {
     return *reinterpret_cast<const uint4 *>(base + addr + i * 32 * kDmaRowBytes);
   };
-  auto frag_rc = [&](const char *base, int addr, int kc) {
-    char *p0 = const_cast<char *>(base) + addr + kc * 16 * 512;
+  // pitch: bytes per K row (512, or 256 in a SwiGLU half)
+  auto frag_rc = [&](const char *base, int addr, int kc, int pitch = 512) {
+    char *p0 = const_cast<char *>(base) + addr + kc * 16 * pitch;
     i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0));
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0 + 4 * 512));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p0 + 4 * pitch));
     uint4 r;
     __builtin_memcpy(&r.x, &lo, 8);
     __builtin_memcpy(&r.z, &hi, 8);
@@ -263,7 +308,9 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
       if constexpr (A_KC) f.a[x] = frag_kc(S, a_addr[kc], x);
       else f.a[x] = frag_rc(S, a_addr[x], kc);
     } else {
-      if constexpr (B_KC) f.b[x - TM] = frag_kc(S, b_addr[kc], x - TM);
+      if constexpr (B_KC && SW) f.b[x - TM] = *reinterpret_cast<const uint4 *>(S + b_addr[2 * (x - TM) + kc]);
+      else if constexpr (B_KC) f.b[x - TM] = frag_kc(S, b_addr[kc], x - TM);
+      else if constexpr (SW) f.b[x - TM] = frag_rc(S, b_addr[x - TM], kc, 256);
       else f.b[x - TM] = frag_rc(S, b_addr[x - TM], kc);
     }
   };
@@ -368,20 +415,46 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // the zero-fill loads past the last step may still be in flight: let them
   // land before the workgroup's LDS can be handed to another workgroup
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  store_tile<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+  if constexpr (SW) {
+    // recompose: silu(A B) * (A B2), fragments j and j + 2 hold one column
+    const int lrow2 = lane & 31, lhalf2 = lane >> 5;
+    char *Cb = reinterpret_cast<char *>(p.C);
+    const int64_t cbase = int64_t(ents[0]) * p.beC + int64_t(bt) * p.sCb;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm + i * 32 + (v >> 2) * 8 + lhalf2 * 4 + (v & 3);
+          const int n = n0 + wn + j * 32 + lrow2;
+          if (m < p.M && n < p.N) {
+            const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
+            const float x = p.alpha * gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            const int64_t off = cbase + int64_t(m) * p.sCm + n;
+            if (OUT_BF16)
+              reinterpret_cast<uint16_t *>(Cb)[off] = f32_to_bf16(x);
+            else
+              reinterpret_cast<float *>(Cb)[off] = x;
+          }
+        }
+  } else {
+    if constexpr (EPI == 0) store_tile_plain<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+    else store_tile_plus<OUT_BF16, TM, TN, EPI - 1, true>(p, acc, ents[0], bt, m0 + wm, n0 + wn, lane);
+  }
 }
 
-template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_kernel(
     const ContractArgs p) {
-  dma_tile<OUT_BF16, A_KC, B_KC, NS>(p, logical_tile(p.remap));
+  dma_tile<OUT_BF16, A_KC, B_KC, NS, EPI>(p, logical_tile(p.remap));
 }
 
 // Several independent contractions of one geometry (every field of `common`
 // but the operand, output and join-list addresses) in one launch of n T
 // logical tiles, T per problem.  One launch instead of several shares the
 // last partial wave of tiles and the launch edges.
-template <int OUT_BF16, bool A_KC, bool B_KC, int NS>
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_group_kernel(
     const DmaGroupArgs ga) {
   const int64_t w = logical_tile(ga.common.remap);
@@ -421,28 +494,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   p.C = ga.C[g];
   p.list = ga.list[g];
   p.counts = ga.counts[g];
-  dma_tile<OUT_BF16, A_KC, B_KC, NS>(p, local);
+  p.X = ga.X[g];
+  p.B2 = ga.B2[g];
+  dma_tile<OUT_BF16, A_KC, B_KC, NS, EPI>(p, local);
 }
 
-template <int OB, bool AK, bool BKC>
+template <int OB, bool AK, bool BKC, int EPI = 0>
 static hipError_t launch_dma(const ContractArgs &a, hipStream_t st) {
   ContractArgs b = a;
   b.tiles_m = (a.M + 255) / 256;
-  b.tiles_n = (a.N + 255) / 256;
+  b.tiles_n = EPI == 3 ? (a.N + 127) / 128 : (a.N + 255) / 256;
   const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
-  hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES>), dim3(unsigned(grid)), dim3(256), 0, st, b);
+  hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES, EPI>), dim3(unsigned(grid)), dim3(256), 0,
+                     st, b);
   return hipGetLastError();
 }
 
-template <int OB, bool AK, bool BKC>
+template <int OB, bool AK, bool BKC, int EPI = 0>
 static hipError_t launch_dma_group(const DmaGroupArgs &a, hipStream_t st) {
   DmaGroupArgs b = a;
   b.common.tiles_m = (a.common.M + 255) / 256;
-  b.common.tiles_n = (a.common.N + 255) / 256;
+  b.common.tiles_n = EPI == 3 ? (a.common.N + 127) / 128 : (a.common.N + 255) / 256;
   b.tiles = b.common.n_keys * b.common.batch * int64_t(b.common.tiles_m) * b.common.tiles_n;
   const int64_t grid = b.tiles * b.n;
-  hipLaunchKernelGGL((contract_dma_group_kernel<OB, AK, BKC, JAGG_DMA_STAGES>), dim3(unsigned(grid)), dim3(256), 0,
-                     st, b);
+  hipLaunchKernelGGL((contract_dma_group_kernel<OB, AK, BKC, JAGG_DMA_STAGES, EPI>), dim3(unsigned(grid)), dim3(256),
+                     0, st, b);
   return hipGetLastError();
 }
 

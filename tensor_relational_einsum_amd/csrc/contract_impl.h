@@ -293,8 +293,8 @@ __device__ __forceinline__ void decode_tile(const ContractArgs &p, int64_t w, in
 // wavefront (fragment element v of lane l: row 8*(v/4) + 4*(l/32) + v%4,
 // column l%32).  m0 / n0: tile origin plus the wavefront's offset.
 template <int OUT_BF16, int TM, int TN>
-__device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
-                                           int bt, int64_t key, int64_t ks, int m0, int n0, int lane) {
+__device__ __forceinline__ void store_tile_plain(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                             int bt, int64_t key, int64_t ks, int m0, int n0, int lane) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   char *Cb = reinterpret_cast<char *>(p.C);
   const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
@@ -322,6 +322,77 @@ __device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (
             reinterpret_cast<float *>(Cb)[off] = x;
         }
       }
+}
+
+// MUL_PLUS epilogue (XDT 0: f32 addend, 1: bf16): out = alpha * acc + X,
+// X laid out as C.  Loads and stores are buffer operations on the output
+// block: element (m, n) of the wavefront's fragments sits at a per-lane
+// base plus a row term that is a compile-time row times the row stride, and
+// elements outside the block get an offset past its end, which the hardware
+// reads as 0 and drops on store -- no branches, 32-bit offsets.  The
+// addends of fragment f + 1 are loaded before fragment f is stored: a load
+// waits for the stores issued before it (vector memory operations complete
+// in issue order), so a load between every two stores would make each
+// addend a full round trip.  Without PREFETCH (kernels with no registers to
+// spare) each fragment's addends are loaded just before its stores.
+template <int OUT_BF16, int TM, int TN, int XDT, bool PREFETCH>
+__device__ __forceinline__ void store_tile_plus(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                                int bt, int m0, int n0, int lane) {
+  constexpr int XSZ = XDT ? 2 : 4, OSZ = OUT_BF16 ? 2 : 4;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
+  const int64_t left = p.beC - int64_t(bt) * p.sCb;  // elements from cbase to the block's end
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(static_cast<const char *>(p.X) + cbase * XSZ, left * XSZ);
+  const __amdgpu_buffer_rsrc_t rc = tile_rsrc(static_cast<char *>(p.C) + cbase * OSZ, left * OSZ);
+  const int rows_left = p.M - (m0 + lhalf * 4);                    // valid rows from this lane's first
+  const uint32_t lane_base = uint32_t((m0 + lhalf * 4) * p.sCm + n0 + lrow);
+  bool col_ok[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) col_ok[j] = n0 + j * 32 + lrow < p.N;
+  auto elem = [&](int i, int j, int v) {  // element offset inside the block, or past its end
+    const int r = i * 32 + (v >> 2) * 8 + (v & 3);
+    return (r < rows_left && col_ok[j]) ? lane_base + uint32_t(r * p.sCm + j * 32) : (kOob / 4);
+  };
+  float xs[2][16];
+  auto load_frag = [&](int f, float (&dst)[16]) {
+    const int i = f / TN, j = f % TN;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const uint32_t e = elem(i, j, v);
+      if constexpr (XDT) dst[v] = bf16_to_f32(buf_load<2>(rx, e * 2));
+      else dst[v] = __uint_as_float(buf_load<4>(rx, e * 4));
+    }
+  };
+  if constexpr (PREFETCH) load_frag(0, xs[0]);
+#pragma unroll
+  for (int f = 0; f < TM * TN; ++f) {
+    if constexpr (PREFETCH) {
+      if (f + 1 < TM * TN) load_frag(f + 1, xs[(f + 1) & 1]);
+    } else {
+      load_frag(f, xs[f & 1]);
+    }
+    const int i = f / TN, j = f % TN;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float x = p.alpha * acc[i][j][v] + xs[f & 1][v];
+      const uint32_t e = elem(i, j, v);
+      if constexpr (OUT_BF16) __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), rc, int(e * 2), 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rc, int(e * 4), 0, 0);
+    }
+  }
+}
+
+// The epilogue, with the MUL_PLUS addend's dtype fixed per instantiation so
+// that each version unrolls completely (accumulators stay in registers).
+template <int OUT_BF16, int TM, int TN>
+__device__ __forceinline__ void store_tile(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                           int bt, int64_t key, int64_t ks, int m0, int n0, int lane) {
+  if (p.epi == 1) {
+    if (p.x_bf16) store_tile_plus<OUT_BF16, TM, TN, 1, false>(p, acc, out_id, bt, m0, n0, lane);
+    else store_tile_plus<OUT_BF16, TM, TN, 0, false>(p, acc, out_id, bt, m0, n0, lane);
+  } else {
+    store_tile_plain<OUT_BF16, TM, TN>(p, acc, out_id, bt, key, ks, m0, n0, lane);
+  }
 }
 
 // Epilogue through LDS: the wavefronts write their scaled (and causally
@@ -420,7 +491,7 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
 
   const int32_t cnt = p.counts[key];
   if (cnt == 0) return;  // output tuple absent (causal); uniform, before any barrier
-  const int32_t *ents = p.list + key * int64_t(p.per_key) * 3;
+  const int32_t *ents = p.list + key * int64_t(p.per_key) * p.ent_w;
 
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = (p.K + BK - 1) / BK;
@@ -454,8 +525,8 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
     if (++lkt == KT) {
       lkt = 0;
       if (++le < cnt) {
-        la = ents[le * 3 + p.a_slot];
-        lb = ents[le * 3 + p.b_slot];
+        la = ents[le * p.ent_w + p.a_slot];
+        lb = ents[le * p.ent_w + p.b_slot];
       }
     }
   };
@@ -463,7 +534,7 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
   // applied just before the LDS store so the loads stay in flight meanwhile
   auto mask_step = [&](TA &xa) {
     if (MASK && p.causal_red) {
-      const int64_t aid = ents[pe * 3 + p.a_slot];
+      const int64_t aid = ents[pe * p.ent_w + p.a_slot];
       const int64_t kt_blk = (aid / p.ct_w) % p.ct_k;
       if (kt_blk == ks) xa.mask_causal(ks * p.e_s, kt_blk * p.e_t, p.div_s, p.div_t, m0, pk0);
     }
@@ -558,7 +629,7 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
     // pays only where output rows start 16-byte aligned (row stores); else
     // the fragments go out directly (the test is uniform over the workgroup)
     constexpr int VE = OUT_BF16 ? 8 : 4;
-    if ((ents[0] * p.beC + int64_t(bt) * p.sCb) % VE == 0 && p.sCm % VE == 0) {
+    if ((ents[0] * p.beC + int64_t(bt) * p.sCb) % VE == 0 && p.sCm % VE == 0 && p.epi == 0) {
       store_tile_lds<OUT_BF16, TM, TN, BM, BN, NT>(p, acc, ents[0], bt, key, ks, m0, n0, wm, wn, lane, smem);
       return;
     }

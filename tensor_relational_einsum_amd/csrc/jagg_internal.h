@@ -196,6 +196,13 @@ struct ContractArgs {
   // (M-letter blocks) x (N-letter blocks) in that order and batch == 1:
   // km, kn = key blocks along M and N; group_m = M panels per group (0: off)
   int32_t km, kn, group_m;
+  int32_t ent_w;                // join-list entry width (1 + inputs)
+  // recompose map: 0 none; 1 add the addend X (laid out as C) to each
+  // element; 2 SwiGLU: C = silu(A B) * (A B2), B2 laid out as B
+  int32_t epi;
+  const void *X;
+  int32_t x_bf16;
+  const void *B2;
 };
 // Independent contractions of one geometry run as one launch of the bf16
 // 256 x 256 LDS-pipelined kernel: `common` holds the shared geometry, the
@@ -208,6 +215,8 @@ struct DmaGroupArgs {
   void *C[kMaxGroup];
   const int32_t *list[kMaxGroup];
   const int32_t *counts[kMaxGroup];
+  const void *X[kMaxGroup];
+  const void *B2[kMaxGroup];
   int32_t n;
   int64_t tiles;  // tiles of one problem (set by the launcher)
 };

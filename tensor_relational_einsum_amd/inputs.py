@@ -219,7 +219,7 @@ def attention_packed(b=2, kv=8, group=4, ends=PACKED_ENDS, d=128) -> Workload:
 
 
 def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_blk=4, q_blk=4, f_blk=8,
-                fused_attention=False) -> Workload:
+                fused_attention=False, fused_epilogues=False) -> Workload:
     """LLaMA-7B-shaped decoder block, every op a join-agg spec.
 
     x (fp32) -> RMSNorm*g1 -> Q,K,V -> causal attention (scale 1/sqrt(d)) ->
@@ -227,7 +227,10 @@ def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_b
     No RoPE, no biases.  Attention is either the five-spec chain between
     relayouts to head-major order and back, or one spec whose aggregation
     merges online-softmax triples, read and written in the projections'
-    own layout (no relayout).
+    own layout (no relayout).  With ``fused_epilogues`` the residual adds
+    and the SiLU gate are the recompose maps of the contractions that feed
+    them (g = mul_plus: x2 = x + O Wo, y = x2 + H Wd; g = swiglu: H =
+    silu(r2 Wg) * (r2 Wu)), so A, G, U and D are never stored.
     """
     ext = {"b": b, "s": s, "t": s, "h": hid, "q": heads, "d": d, "e": d, "f": ffn}
     proj = {"b": 1, "s": s_blk, "t": s_blk, "h": h_blk, "q": q_blk, "d": 1}
@@ -271,18 +274,30 @@ def llama_block(b=4, s=2048, hid=4096, heads=32, d=128, ffn=11008, s_blk=16, h_b
             Step("Oh", "bqst,bqtd->bqsd", ["P", "V"], "mul", "sum", "bf16", att, causal=c),
             Relayout("O", "Oh", "bsqd", proj),
         ]
-    chain += [
-        Step("A", "bsqd,qdh->bsh", ["O", "Wo"], "mul", "sum", "f32", proj),
-        Step("x2", "bsh,bsh->bsh", ["x", "A"], "add", "none", "f32", proj),
-        Step("ss2", "bsh->bs", ["x2"], "square", "sum", "f32", ffb),
-        Step("r2", "bsh,bs,h->bsh", ["x2", "ss2", "g2"], "rms_scale", "none", "bf16", ffb, beta=inv_h, eps=1e-6),
-        Step("G", "bsh,hf->bsf", ["r2", "Wg"], "mul", "sum", "f32", ffb),
-        Step("U", "bsh,hf->bsf", ["r2", "Wu"], "mul", "sum", "f32", ffb),
-        Step("H", "bsf,bsf->bsf", ["G", "U"], "silu_mul", "none", "bf16", ffb),
-        Step("D", "bsf,fh->bsh", ["H", "Wd"], "mul", "sum", "f32", ffb),
-        Step("y", "bsh,bsh->bsh", ["x2", "D"], "add", "none", "f32", ffb),
-    ]
+    if fused_epilogues:
+        chain += [
+            Step("x2", "bsqd,qdh,bsh->bsh", ["O", "Wo", "x"], "mul_plus", "sum", "f32", proj),
+            Step("ss2", "bsh->bs", ["x2"], "square", "sum", "f32", ffb),
+            Step("r2", "bsh,bs,h->bsh", ["x2", "ss2", "g2"], "rms_scale", "none", "bf16", ffb, beta=inv_h, eps=1e-6),
+            Step("H", "bsh,hf,hf->bsf", ["r2", "Wg", "Wu"], "swiglu", "sum", "bf16", ffb),
+            Step("y", "bsf,fh,bsh->bsh", ["H", "Wd", "x2"], "mul_plus", "sum", "f32", ffb),
+        ]
+    else:
+        chain += [
+            Step("A", "bsqd,qdh->bsh", ["O", "Wo"], "mul", "sum", "f32", proj),
+            Step("x2", "bsh,bsh->bsh", ["x", "A"], "add", "none", "f32", proj),
+            Step("ss2", "bsh->bs", ["x2"], "square", "sum", "f32", ffb),
+            Step("r2", "bsh,bs,h->bsh", ["x2", "ss2", "g2"], "rms_scale", "none", "bf16", ffb, beta=inv_h,
+                 eps=1e-6),
+            Step("G", "bsh,hf->bsf", ["r2", "Wg"], "mul", "sum", "f32", ffb),
+            Step("U", "bsh,hf->bsf", ["r2", "Wu"], "mul", "sum", "f32", ffb),
+            Step("H", "bsf,bsf->bsf", ["G", "U"], "silu_mul", "none", "bf16", ffb),
+            Step("D", "bsf,fh->bsh", ["H", "Wd"], "mul", "sum", "f32", ffb),
+            Step("y", "bsh,bsh->bsh", ["x2", "D"], "add", "none", "f32", ffb),
+        ]
     name = f"llama7b_block_b{b}_s{s}_bf16_" + ("fused_attention" if fused_attention else "attention_chain")
+    if fused_epilogues:
+        name += "_fused_epilogues"
     return Workload(name=name, extents=ext, tensors=tens, chain=chain, seed=1004)
 
 

@@ -14,7 +14,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjagg.so")
 
 G = {"mul": 0, "ident": 1, "square": 2, "exp_sub": 3, "exp_sub_div": 4, "rms_scale": 5, "silu_mul": 6, "add": 7,
-     "attention": 8}
+     "attention": 8, "mul_plus": 9, "swiglu": 10}
 AGG = {"none": 0, "sum": 1, "max": 2, "softmax": 3}
 DT = {"f32": 0, "bf16": 1}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}

@@ -70,6 +70,8 @@ def oracle_chain(w, dense, stop=None):
                 if st.segment is not None:
                     seg = (st.segment[0], st.segment[1], st.blockings[st.segment[0]])
                 y = O.attention_dense(st.spec, xs, w.extents, alpha=st.alpha, causal=st.causal, segments=seg)
+            elif st.g in ("mul_plus", "swiglu"):
+                y = O.dense_recompose(st.spec, st.g, xs, w.extents, alpha=st.alpha)
             else:
                 y = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
                             causal=st.causal)
@@ -146,13 +148,21 @@ def llama_block_rows(w, dense, b, rows):
             oh = rnd(O.dense("bqst,bqtd->bqsd", [Pp, vh], e1), steps["Oh"].out_dtype)
             Orows.append(np.ascontiguousarray(oh.transpose(0, 2, 1, 3)))
     Oa = np.concatenate(Orows, axis=1)
-    A = rnd(O.contract("bsqd,qdh->bsh", Oa, Wo, er), steps["A"].out_dtype)
-    x2 = rnd(O.dense("bsh,bsh->bsh", [xr, A], er, g="add", agg="none"), steps["x2"].out_dtype)
-    r2 = rms(x2, g2, ("ss2", "r2"), R)
-    G = rnd(O.contract("bsh,hf->bsf", r2, Wg, er), steps["G"].out_dtype)
-    U = rnd(O.contract("bsh,hf->bsf", r2, Wu, er), steps["U"].out_dtype)
-    Hh = rnd(O.dense("bsf,bsf->bsf", [G, U], er, g="silu_mul", agg="none"), steps["H"].out_dtype)
-    Dd = rnd(O.contract("bsf,fh->bsh", Hh, Wd, er), steps["D"].out_dtype)
-    y = rnd(O.dense("bsh,bsh->bsh", [x2, Dd], er, g="add", agg="none"), steps["y"].out_dtype)
+    if steps["x2"].g == "mul_plus":
+        # the residual adds and the SiLU gate as recompose maps of the
+        # contractions feeding them: sums in float64, one rounding each
+        x2 = rnd(O.dense_recompose("bsqd,qdh,bsh->bsh", "mul_plus", [Oa, Wo, xr], er), steps["x2"].out_dtype)
+        r2 = rms(x2, g2, ("ss2", "r2"), R)
+        Hh = rnd(O.dense_recompose("bsh,hf,hf->bsf", "swiglu", [r2, Wg, Wu], er), steps["H"].out_dtype)
+        y = rnd(O.dense_recompose("bsf,fh,bsh->bsh", "mul_plus", [Hh, Wd, x2], er), steps["y"].out_dtype)
+    else:
+        A = rnd(O.contract("bsqd,qdh->bsh", Oa, Wo, er), steps["A"].out_dtype)
+        x2 = rnd(O.dense("bsh,bsh->bsh", [xr, A], er, g="add", agg="none"), steps["x2"].out_dtype)
+        r2 = rms(x2, g2, ("ss2", "r2"), R)
+        G = rnd(O.contract("bsh,hf->bsf", r2, Wg, er), steps["G"].out_dtype)
+        U = rnd(O.contract("bsh,hf->bsf", r2, Wu, er), steps["U"].out_dtype)
+        Hh = rnd(O.dense("bsf,bsf->bsf", [G, U], er, g="silu_mul", agg="none"), steps["H"].out_dtype)
+        Dd = rnd(O.contract("bsf,fh->bsh", Hh, Wd, er), steps["D"].out_dtype)
+        y = rnd(O.dense("bsh,bsh->bsh", [x2, Dd], er, g="add", agg="none"), steps["y"].out_dtype)
     assert Oa.shape == (1, R, Q_, D_) and y.shape == (1, R, Hd)
     return {"O": Oa[0], "x2": x2[0], "y": y[0]}

@@ -44,9 +44,10 @@ def sctx():
         c.close()
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused_attention", "attention_chain"])
-def test_llama_block_graph_rows_from_original_inputs(sctx, fused):
-    w = I.llama_block(fused_attention=fused)
+@pytest.mark.parametrize("fused,epi", [(True, True), (True, False), (False, False)],
+                         ids=["fused_attention_fused_epilogues", "fused_attention", "attention_chain"])
+def test_llama_block_graph_rows_from_original_inputs(sctx, fused, epi):
+    w = I.llama_block(fused_attention=fused, fused_epilogues=epi)
     dense = I.generate(w)
     want = {b: llama_block_rows(w, dense, b, rows) for b, rows in LLAMA_ROWS}
     with torch.cuda.stream(sctx.stream):

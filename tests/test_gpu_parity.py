@@ -558,6 +558,8 @@ def sampled_spec_check(ctx, run, w, n_samples=400, seed=2):
         xs = [to_np(dense_of(n)) for n in st.ins]
         if st.g == "attention":
             want = O.attention_dense(st.spec, xs, w.extents, alpha=st.alpha, causal=st.causal, sample=idx)
+        elif st.g in ("mul_plus", "swiglu"):
+            want = O.dense_recompose(st.spec, st.g, xs, w.extents, alpha=st.alpha, sample=idx)
         else:
             want = O.dense(st.spec, xs, w.extents, g=st.g, agg=st.agg, alpha=st.alpha, beta=st.beta, eps=st.eps,
                            causal=st.causal, sample=idx)
@@ -613,10 +615,12 @@ def test_llama_block_small_fused_attention(ctx):
     sampled_spec_check(ctx, run, w, n_samples=200)
 
 
-def test_llama_block_config_sampled_fused_attention(ctx):
-    """The full LLaMA-7B-shaped block with fused attention, as bench.py
-    times it: every spec checked on sampled outputs."""
-    w = I.llama_block(fused_attention=True)
+@pytest.mark.parametrize("epi", [True, False])
+def test_llama_block_config_sampled_fused_attention(ctx, epi):
+    """The full LLaMA-7B-shaped block with fused attention (and, as bench.py
+    times it, fused residual / SwiGLU recompose maps): every spec checked on
+    sampled outputs."""
+    w = I.llama_block(fused_attention=True, fused_epilogues=epi)
     dense = I.generate(w)
     run = ChainRunner(ctx, w, dense)
     run.run()

@@ -11,10 +11,10 @@ from tensor_relational_einsum_amd import inputs as I
 from parity_util import llama_block_rows, oracle_chain
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_block_rows_equal_full_chain(fused):
+@pytest.mark.parametrize("fused,epi", [(True, False), (False, False), (True, True)])
+def test_block_rows_equal_full_chain(fused, epi):
     w = I.llama_block(b=2, s=48, hid=256, heads=2, d=128, ffn=320, s_blk=3, h_blk=2, q_blk=2, f_blk=2,
-                      fused_attention=fused)
+                      fused_attention=fused, fused_epilogues=epi)
     dense = I.generate(w)
     full = oracle_chain(w, dense)
     for b, rows in ((0, [0, 1, 15, 16, 47]), (1, [7, 30])):
