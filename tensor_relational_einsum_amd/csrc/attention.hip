@@ -16,7 +16,8 @@
 //  - Scores are computed transposed, S^T = K Q^T (M = t, N = s, K = D), so
 //    that lane l owns one query row s = l % 32 of its wavefront and 32 of
 //    the tile's 64 keys; lane l ^ 32 holds the other 32.  A row maximum is
-//    32 in-lane maxima and one cross-half exchange.
+//    32 in-lane maxima and one exchange of the wavefront's halves
+//    (v_permlane32_swap, no LDS round trip).
 //  - The output is accumulated transposed too, O^T = V^T P^T (M = E, N = s,
 //    K = t): lane l again owns row s, so rescaling by exp(m_old - m_new) is
 //    one scalar per lane, and P^T is the B operand straight from the score
@@ -24,14 +25,35 @@
 //    half) in a lane's first 8 values; the V^T fragment is read with the
 //    same key permutation through two ds_read_b64_tr_b16 (the sum over the
 //    16 keys of an MFMA step does not depend on their order).
-//  - Q fragments stay in registers for the whole walk; K and V tiles of 64
-//    keys are staged in LDS (rows padded by 16 / 64 bytes against bank
-//    conflicts) with two stages: the global loads of tile i+1 are in flight
-//    while tile i is computed, one barrier per tile.
+//  - Row sums l come from v_dot2c_f32_bf16 on the packed probabilities (one
+//    instruction per two keys), so l adds exactly the bf16 values that the
+//    PV product multiplies.
+//  - Q fragments stay in registers for the whole walk.  K and V tiles of 64
+//    keys are written to LDS by buffer loads with the LDS destination (no
+//    registers hold data in flight), unpadded, with an XOR swizzle of
+//    16-byte slots that keeps the fragment reads conflict-free:
+//      K: slot c of key row r at c ^ ((r / RP) % SPR)
+//      V: slot c of key row r at c ^ ((4 (r / RP)) % SPR)
+//    (SPR = D / 8 slots per row, RP = 16 / SPR rows per 256 bytes).  Two K
+//    and two V buffers: the loads of K for tile i + 2 and of V for tile
+//    i + 1 are issued at the top of iteration i, after the barrier that ends
+//    every read of the buffers they overwrite.
+//  - Software pipeline, per wavefront: iteration i issues the S MFMAs of
+//    tile i + 1 with the exponentials of the upper key half of tile i
+//    between them (phase A), then the PV MFMAs of tile i with the maximum,
+//    reference update and lower-half exponentials of tile i + 1 between
+//    them (phase B).  The VALU work of one tile thus runs in the shadow of
+//    the MFMAs of its neighbours instead of between them.
+//  - Every wavefront walks every tile of its workgroup's walk; under a
+//    causal pair the masked scores of keys past a wavefront's rows give
+//    probabilities 0 (a uniform pipeline costs the few diagonal tiles a
+//    wavefront would otherwise skip).
 //  - Softmax works in base 2: the maximum is taken on the raw scores and
 //    exp2(score * alpha log2 e - m) is one FMA and one exp (alpha > 0).
 //  - The 128 x E output tile goes through LDS so that rows leave as 16-byte
 //    stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "jagg_internal.h"
 
@@ -41,6 +63,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -76,26 +99,55 @@ __device__ __forceinline__ uint4 tr_pair(const char *p0, const char *p1) {
   return r;
 }
 
+// maximum of x over lanes l and l ^ 32 (the two halves of a query row)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Keeps x in place: an empty volatile asm that reads and writes x.  Volatile
+// asm keeps its order against the scheduling barriers, so pinning a VALU
+// slice's inputs and outputs holds the slice between the two MFMAs it was
+// written between (pure arithmetic would otherwise be moved next to its
+// first use, away from the MFMA shadow it is meant to fill).
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
+
+// acc + the two bf16 halves of w
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 }  // namespace
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
-  constexpr int KP = D * 2 + 16;  // K tile row pitch (bytes)
-  constexpr int VP = D * 2 + 64;  // V tile row pitch
-  constexpr int KBYTES = kKeys * KP;
-  constexpr int STAGE = KBYTES + kKeys * VP;
+  constexpr int SPR = D / 8;             // 16-byte slots per K / V row
+  constexpr int RB = D * 2;              // bytes per K / V row
+  constexpr int RP = 16 / SPR;           // rows per 256 bytes
+  constexpr int TB = kKeys * RB;         // bytes of one K or V tile
+  constexpr int NL = kKeys * SPR / 256;  // LDS loads per thread per tile and operand
   constexpr int OESZ = OUT_BF16 ? 2 : 4;
   constexpr int OP = D * OESZ + 16;  // output staging row pitch
-  constexpr int LDS = 2 * STAGE > kRows * OP ? 2 * STAGE : kRows * OP;
-  constexpr int CPR = D / 8;       // 16-byte chunks per K / V row
-  constexpr int RPP = 256 / CPR;   // rows per pass of the workgroup
-  constexpr int NP = kKeys / RPP;  // passes per tile
+  constexpr int LDS = 4 * TB > kRows * OP ? 4 * TB : kRows * OP;
   constexpr int KS = D / 16;       // MFMA steps over D
   constexpr int ET = D / 32;       // 32-wide E tiles
-  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  constexpr int NQA = 2 * KS;      // S MFMAs per tile and wavefront
+  constexpr int NQB = 4 * ET;      // PV MFMAs per tile and wavefront
+  static_assert(NL >= 1 && NL <= 4 && RP * SPR == 16, "tile geometry");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  char *const kbuf = smem;           // K tiles at kbuf + b * TB, b = 0, 1
+  char *const vbuf = smem + 2 * TB;  // V tiles
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   // workgroup -> (batch index inside the block, output key, s tile).  With
   // xcd_group, the workgroups of one batch index (which share its K and V)
@@ -122,9 +174,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   }
   const int32_t cnt = a.counts[key];
   // the join list is read-only for the kernel's lifetime: reading it through
-  // the constant address space keeps the tuple-id reads on the scalar unit.
-  // A vector load there would make the walk wait (vmcnt counts in issue
-  // order) for the next tile's K / V loads issued just before it.
+  // the constant address space keeps the tuple-id reads on the scalar unit
   typedef const __attribute__((address_space(4))) int32_t *const_i32p;
   const const_i32p ents = (const_i32p)(a.list + int64_t(key) * a.per_key * 4);
 
@@ -187,19 +237,39 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     }
   }
 
-  // K / V tile loads: each lane's byte offset inside a tile is fixed; the
-  // tile's origin goes into the (scalar) buffer base, and the buffer ends at
-  // the tuple's last valid row, so rows past it read zeros
-  uint32_t koff[NP], voff[NP];
+  // LDS loads: lane l of load n of this wavefront fills physical slot
+  // P = (4 n + wave) * 64 + l of a tile; the offsets below pick the global
+  // 16 bytes that belong there under each operand's swizzle.  A tile's
+  // origin goes into the (scalar) buffer base, and the buffer ends at the
+  // tuple's last row, so rows past it read zeros.
+  uint32_t kdo[NL], vdo[NL];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int row = p * RPP + tid / CPR, ch = tid % CPR;
-    koff[p] = uint32_t((int64_t(row) * a.tK + ch * 8) * 2);
-    voff[p] = uint32_t((int64_t(row) * a.tV + ch * 8) * 2);
+  for (int n = 0; n < NL; ++n) {
+    const int P = (4 * n + wave) * 64 + lane, r = P / SPR, ph = P % SPR;
+    const int ck = ph ^ ((r / RP) % SPR), cv = ph ^ ((4 * (r / RP)) % SPR);
+    kdo[n] = uint32_t((int64_t(r) * a.tK + 8 * ck) * 2);
+    vdo[n] = uint32_t((int64_t(r) * a.tV + 8 * cv) * 2);
   }
-  // tuple ids and key range of one tile of the walk; the loop reads them one
-  // iteration ahead, so the scalar loads overlap the LDS stores and the
-  // barrier instead of stalling the top of an iteration
+  // Fragment read addresses inside a tile.  K (ds_read_b128): row l32 (+32
+  // for the second key half), logical slot 2 k + hi; the swizzle makes the
+  // address (row base with slot hi ^ f) ^ 32 k.  V (two ds_read_b64_tr_b16):
+  // key row 16 (q % 4) + rl (+8), logical slot 4 (q / 4) + cl, half s16 % 2;
+  // the swizzle flips only the 4 (q / 4) part.
+  const int g = lane >> 4, s16 = lane & 15;
+  uint32_t kaddr[KS], vaddr[ET];
+  {
+    const int fk = (l32 / RP) % SPR;
+    const uint32_t kb0 = uint32_t(l32 * RB + 16 * (hi ^ fk));
+#pragma unroll
+    for (int k = 0; k < KS; ++k) kaddr[k] = kb0 ^ uint32_t(32 * k);
+    const int rl = 4 * (g >> 1) + (s16 >> 2), cl = 2 * (g & 1) + ((s16 & 3) >> 1);
+    const int fv4 = (((4 * (rl / RP)) % SPR) >> 2);
+    const uint32_t vb0 = uint32_t(rl * RB + 16 * cl + 8 * (s16 & 1));
+#pragma unroll
+    for (int e = 0; e < ET; ++e) vaddr[e] = vb0 + uint32_t(64 * (e ^ fv4));
+  }
+
+  // tuple ids and key range of one tile of the walk
   struct TileIds {
     int64_t kt, vt;           // K and V tuple ids
     int32_t tt, T0, t_valid;  // tile inside the tuple, its first key, keys [0, t_valid) that exist
@@ -217,159 +287,237 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
     r.t_valid = tv > kKeys ? kKeys : tv;
     return r;
   };
-  uint4 kr[NP], vr[NP];
-  auto load_tile = [&](const TileIds &ti) {
-    const int64_t kt = ti.kt, vt = ti.vt;
-    const int64_t r0 = int64_t(ti.tt) * kKeys;  // first row of the tile
-    const int64_t kbase = kt * a.beK + oK + r0 * a.tK, vbase = vt * a.beV + oV + r0 * a.tV;
-    const int64_t kend = oK + int64_t(a.e_t - 1) * a.tK + D, vend = oV + int64_t(a.e_t - 1) * a.tV + D;
-    const __amdgpu_buffer_rsrc_t rk =
-        rsrc(static_cast<const char *>(a.K) + kbase * 2, (kt * a.beK + kend - kbase) * 2);
-    const __amdgpu_buffer_rsrc_t rv =
-        rsrc(static_cast<const char *>(a.V) + vbase * 2, (vt * a.beV + vend - vbase) * 2);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      kr[p] = bload(rk, koff[p]);
-      vr[p] = bload(rv, voff[p]);
-    }
+  // LDS address of this wavefront's first 1 KB of the K buffer 0; buffer b
+  // of K, V and load n add compile-time constants
+  const uint32_t lds_w = uint32_t(reinterpret_cast<uintptr_t>((lds_dma_ptr)(smem))) + uint32_t(wave_s) * 1024u;
+  auto load_k = [&](auto par, const TileIds &ti) {
+    constexpr int B = decltype(par)::value;
+    const int64_t kbase = ti.kt * a.beK + oK + int64_t(ti.tt) * kKeys * a.tK;
+    const int64_t kend = ti.kt * a.beK + oK + int64_t(a.e_t - 1) * a.tK + D;
+    const i32x4_rsrc rk = dma_rsrc(static_cast<const char *>(a.K) + kbase * 2, (kend - kbase) * 2);
+    dma16_at<B * TB>(rk, kdo[0], lds_w);
+    if constexpr (NL > 1) dma16_at<B * TB + 4096>(rk, kdo[1], lds_w);
+    if constexpr (NL > 2) dma16_at<B * TB + 8192>(rk, kdo[2], lds_w);
+    if constexpr (NL > 3) dma16_at<B * TB + 12288>(rk, kdo[3], lds_w);
   };
-  auto store_tile = [&](int stage) {
-    char *ks = smem + stage * STAGE;
-    char *vs = ks + KBYTES;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int row = p * RPP + tid / CPR, ch = tid % CPR;
-      *reinterpret_cast<uint4 *>(ks + row * KP + ch * 16) = kr[p];
-      *reinterpret_cast<uint4 *>(vs + row * VP + ch * 16) = vr[p];
-    }
+  auto load_v = [&](auto par, const TileIds &ti) {
+    constexpr int B = decltype(par)::value;
+    const int64_t vbase = ti.vt * a.beV + oV + int64_t(ti.tt) * kKeys * a.tV;
+    const int64_t vend = ti.vt * a.beV + oV + int64_t(a.e_t - 1) * a.tV + D;
+    const i32x4_rsrc rv = dma_rsrc(static_cast<const char *>(a.V) + vbase * 2, (vend - vbase) * 2);
+    dma16_at<(2 + B) * TB>(rv, vdo[0], lds_w);
+    if constexpr (NL > 1) dma16_at<(2 + B) * TB + 4096>(rv, vdo[1], lds_w);
+    if constexpr (NL > 2) dma16_at<(2 + B) * TB + 8192>(rv, vdo[2], lds_w);
+    if constexpr (NL > 3) dma16_at<(2 + B) * TB + 12288>(rv, vdo[3], lds_w);
   };
-
   f32x16 acc[ET];
 #pragma unroll
   for (int et = 0; et < ET; ++et)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[et][v] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  TileIds cur{}, nxt{};  // the tile being computed, the one being loaded
-  if (n_it > 0) {
-    cur = tile_ids(0);
-    load_tile(cur);
-    store_tile(0);
-  }
-  if (n_it > 1) nxt = tile_ids(1);
-  // Every global load so far (Q fragments, first tile) has landed: said
-  // explicitly (vmcnt(0)), the compiler's wait counting enters the loop with
-  // nothing pending and does not make the S^T MFMAs of each tile wait for
-  // the next tile's loads, which it would otherwise treat as possibly
-  // carrying Q
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  const int g = lane >> 4, s16 = lane & 15;
+  float m_run = -INFINITY, l_run = 0.0f, base = 0.0f, corr = 1.0f;
+  bool moved = false;
   const float scale = a.scale_log2;  // > 0
-  for (int it = 0; it < n_it; ++it) {
-    const bool more = it + 1 < n_it;
-    if (more) load_tile(nxt);
-    const int32_t T0 = cur.T0, t_valid = cur.t_valid;
-    if (!(CAUSAL && T0 > wave_s_last)) {
-      const char *ks = smem + (it & 1) * STAGE;
-      const char *vs = ks + KBYTES;
-      // S^T = K Q^T for the 64 keys x 32 rows of this wavefront
-      f32x16 sacc[2];
+
+  // S^T of the tile in K buffer b: MFMA q (key half q % 2, D step q / 2),
+  // with K fragments read two MFMAs ahead; between MFMA q and q + 1 runs
+  // slice q of the VALU work `valu` (a callable taking the slice index)
+  auto scores = [&](f32x16 (&sc)[2], int b, auto &&valu) {
+    const char *ks = kbuf + b * TB;
+    auto kread = [&](int q) { return *reinterpret_cast<const uint4 *>(ks + kaddr[q >> 1] + (q & 1) * 32 * RB); };
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[mt][v] = 0.0f;
+    uint4 kring[3];
+    kring[0] = kread(0);
+    kring[1] = kread(1);
+#pragma unroll
+    for (int q = 0; q < NQA; ++q) {
+      if (q + 2 < NQA) kring[(q + 2) % 3] = kread(q + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      sc[q & 1] = mma(kring[q % 3], qf[q >> 1], sc[q & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      valu(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // O^T += V^T P^T for the tile in V buffer b, with slice q of `valu`
+  // after MFMA q
+  auto pv = [&](const uint32_t (&pw)[16], int b, auto &&valu) {
+    const char *vs = vbuf + b * TB;
+    auto vread = [&](int q) {
+      const char *p = vs + vaddr[q >> 2] + (q & 3) * 16 * RB;
+      return tr_pair(p, p + 8 * RB);
+    };
+    uint4 vring[3];
+    vring[0] = vread(0);
+    vring[1] = vread(1);
+#pragma unroll
+    for (int q = 0; q < NQB; ++q) {
+      if (q + 2 < NQB) vring[(q + 2) % 3] = vread(q + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int k = q & 3;
+      acc[q >> 2] = mma(vring[q % 3], uint4{pw[4 * k], pw[4 * k + 1], pw[4 * k + 2], pw[4 * k + 3]}, acc[q >> 2]);
+      __builtin_amdgcn_sched_barrier(0);
+      valu(q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // drop missing keys and, under the causal pair, t > s
+  auto mask = [&](f32x16 (&sc)[2], const TileIds &ti) {
+    const bool full = ti.t_valid == kKeys && !(CAUSAL && ti.T0 + kKeys - 1 > wave_s_first);
+    if (!full) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.0f;
-      // K fragments two MFMAs ahead of their use, as the V fragments below
-      auto kread = [&](int q) {
-        return *reinterpret_cast<const uint4 *>(ks + (32 * (q & 1) + l32) * KP + 32 * (q >> 1) + 16 * hi);
-      };
-      {
-        uint4 kring[3];
-        kring[0] = kread(0);
-        kring[1] = kread(1);
-#pragma unroll
-        for (int q = 0; q < 2 * KS; ++q) {
-          if (q + 2 < 2 * KS) kring[(q + 2) % 3] = kread(q + 2);
-          __builtin_amdgcn_sched_barrier(0);
-          sacc[q & 1] = mma(kring[q % 3], qf[q >> 1], sacc[q & 1]);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int v = 0; v < 16; ++v) {
+          const int tl = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
+          if (tl >= ti.t_valid || (CAUSAL && ti.T0 + tl > s_glob)) sc[mt][v] = -INFINITY;
         }
-      }
-      // drop missing keys and, under the causal pair, t > s
-      const bool full = t_valid == kKeys && !(CAUSAL && T0 + kKeys - 1 > wave_s_first);
-      if (!full) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int tl = 32 * mt + 8 * (v >> 2) + 4 * hi + (v & 3);
-            if (tl >= t_valid || (CAUSAL && T0 + tl > s_glob)) sacc[mt][v] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[mt][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale;  // base-2 maximum of the tile (scale > 0)
+    }
+  };
+  // Softmax work of one tile, as numbered items spread over MFMA slices.
+  // Lower half (keys of sc[0], run in phase B): items 0..15 fold the 32
+  // scores into the maximum, item 16 moves the reference, items 17..24
+  // produce the probability pairs 0..7.  Upper half (sc[1], phase A): items
+  // 0..7 produce pairs 8..15.  A pair is two exponentials, one bf16 pack and
+  // one row-sum step.
+  constexpr int kLoItems = 25, kHiItems = 8;
+  float mx = -INFINITY;
+  auto pair = [&](const f32x16 (&sc)[2], uint32_t (&pw)[16], int j) {
+    const int mt = j >> 3, v = 2 * (j & 7);
+    float s0 = sc[mt][v], s1 = sc[mt][v + 1];
+    pin(s0);
+    pin(s1);
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, scale, -base));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, scale, -base));
+    pw[j] = pack_bf16x2(p0, p1);
+    l_run = add_pair(pw[j], l_run);
+    pin(pw[j]);
+    pin(l_run);
+  };
+  auto lo_item = [&](const f32x16 (&sc)[2], uint32_t (&pw)[16], int it) {
+    if (it < 16) {
+      const int mt = it >> 3, v = 2 * (it & 7);
+      mx = fmaxf(fmaxf(mx, sc[mt][v]), sc[mt][v + 1]);
+      pin(mx);
+    } else if (it == 16) {
       // The reference m of the running triple moves only when the tile's
       // maximum exceeds it by more than 8 (then p <= 2^8 always): the merge
       // is exact for any common reference, and most tiles skip the rescale.
-      const float m_new = mx > m_run + 8.0f ? mx : m_run;
-      const float base = m_new == -INFINITY ? 0.0f : m_new;
-      const float corr = __builtin_amdgcn_exp2f(m_run - base);
-      float sum = 0.0f;
-      uint4 pf[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][8 * h + j], scale, -base));
-            sum += p[j];
-          }
-          pf[2 * mt + h] = uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                 pack_bf16x2(p[6], p[7])};
-        }
-      if (!__all(m_new == m_run)) {  // some row moved its reference
-        l_run *= corr;
-#pragma unroll
-        for (int et = 0; et < ET; ++et)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[et][v] *= corr;
-      }
-      l_run += sum;
+      const float t = halves_max(mx) * scale;  // base-2 maximum of the tile (scale > 0)
+      mx = -INFINITY;
+      const float m_new = t > m_run + 8.0f ? t : m_run;
+      base = m_new == -INFINITY ? 0.0f : m_new;
+      corr = __builtin_amdgcn_exp2f(m_run - base);
+      moved = !__all(m_new == m_run);
+      l_run *= corr;
       m_run = m_new;
-      // O^T += V^T P^T, with V^T read in the keys' score order; the V
-      // fragments are read two MFMAs ahead of their use (a ring of three),
-      // so the LDS latency hides behind the MFMAs in between
-      auto vread = [&](int q) {
-        const int n = 32 * (q >> 2) + 16 * (g & 1) + 4 * (s16 & 3);
-        const int kb = 16 * (q & 3) + 4 * (g >> 1) + (s16 >> 2);
-        return tr_pair(vs + kb * VP + n * 2, vs + (kb + 8) * VP + n * 2);
-      };
-      uint4 vring[3];
-      vring[0] = vread(0);
-      vring[1] = vread(1);
-#pragma unroll
-      for (int q = 0; q < 4 * ET; ++q) {
-        if (q + 2 < 4 * ET) vring[(q + 2) % 3] = vread(q + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        acc[q >> 2] = mma(vring[q % 3], pf[q & 3], acc[q >> 2]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      pin(base);
+      pin(l_run);
+    } else {
+      pair(sc, pw, it - 17);
     }
-    cur = nxt;
-    if (it + 2 < n_it) nxt = tile_ids(it + 2);
-    if (more) store_tile((it + 1) & 1);
+  };
+  // Phase B slices by cost: the 16 maximum items (one v_max3 each) fill the
+  // first NQB / 8 slices, the reference update the next, and the 8 pairs
+  // (two exponentials each, the expensive items) spread over the rest.
+  constexpr int kMaxSl = NQB / 8 > 0 ? NQB / 8 : 1;
+  auto lo_slice = [](int it) {
+    if (it < 16) return it * kMaxSl / 16;
+    if (it == 16) return kMaxSl;
+    return kMaxSl + 1 + (it - 17) * (NQB - kMaxSl - 1) / 8;
+  };
+  // slice q of n slices takes items [q * items / n, (q + 1) * items / n)
+  auto slice = [](int q, int n, int items, auto &&item) {
+#pragma unroll
+    for (int it = q * items / n; it < (q + 1) * items / n; ++it) item(it);
+  };
+  auto none = [](int) {};
+
+  // two score sets and two probability sets, alternating between tiles
+  f32x16 sA[2], sB[2];
+  uint32_t pA[16], pB[16];
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  TileIds t1{}, t2{};  // tiles i + 1 and i + 2 of the walk
+  if (n_it > 0) {
+    const TileIds t0 = tile_ids(0);
+    load_k(P0{}, t0);
+    load_v(P0{}, t0);
+    if (n_it > 1) {
+      t1 = tile_ids(1);
+      load_k(P1{}, t1);
+    }
+    if (n_it > 2) t2 = tile_ids(2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and the first loads
     __syncthreads();
+    scores(sA, 0, none);
+    mask(sA, t0);
+#pragma unroll
+    for (int it = 0; it < kLoItems; ++it) lo_item(sA, pA, it);
+  }
+
+  // one iteration of the walk (parity par = i % 2), for a tile i with a
+  // successor: tile i's scores in sc, the lower half of its probabilities in
+  // pc; the next tile's scores go to sn, its lower half to pn
+  auto top = [&](auto par, int i) {
+    constexpr int B = decltype(par)::value;
+    // every wavefront is done with iteration i - 1: the S reads of K buffer
+    // i % 2 and the PV reads of V buffer (i + 1) % 2; the loads issued at
+    // the top of i - 1 (K of tile i + 1, V of tile i) have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (i + 2 < n_it) load_k(std::integral_constant<int, B>{}, t2);
+    if (i + 1 < n_it) load_v(std::integral_constant<int, 1 - B>{}, t1);
+  };
+  auto step = [&](auto par, int i, f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&pc)[16], uint32_t (&pn)[16]) {
+    constexpr int B = decltype(par)::value;
+    top(par, i);
+    // phase A: S of tile i + 1 || upper-half probabilities of tile i
+    scores(sn, 1 - B, [&](int q) { slice(q, NQA, kHiItems, [&](int j) { pair(sc, pc, 8 + j); }); });
+    mask(sn, t1);
+    // phase B: PV of tile i || maximum and lower-half probabilities of tile i + 1
+    pv(pc, B, [&](int q) {
+#pragma unroll
+      for (int it = 0; it < kLoItems; ++it)
+        if (lo_slice(it) == q) lo_item(sn, pn, it);
+    });
+    // tile i + 1 moved the reference of some row: rescale what tiles <= i
+    // accumulated (after their PV, before tile i + 1's)
+    if (moved) {
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[et][v] *= corr;
+    }
+    t1 = t2;
+    if (i + 3 < n_it) t2 = tile_ids(i + 3);
+  };
+  // the walk's last tile
+  auto last = [&](auto par, int i, const f32x16 (&sc)[2], uint32_t (&pc)[16]) {
+    constexpr int B = decltype(par)::value;
+    top(par, i);
+#pragma unroll
+    for (int j = 0; j < kHiItems; ++j) pair(sc, pc, 8 + j);
+    pv(pc, B, none);
+  };
+  int i = 0;
+  for (; i + 2 < n_it; i += 2) {
+    step(P0{}, i, sA, sB, pA, pB);
+    step(P1{}, i + 1, sB, sA, pB, pA);
+  }
+  if (n_it - i == 2) {
+    step(P0{}, i, sA, sB, pA, pB);
+    last(P1{}, i + 1, sB, pB);
+  } else if (n_it - i == 1) {
+    last(P0{}, i, sA, pA);
   }
 
   // recompose: a / l for rows that exist and are inside the relation, 0 elsewhere
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  __syncthreads();  // every wavefront is done reading the last tiles
+  const float l_tot = halves_sum(l_run);
   const float inv = (row_ok && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
   {
     char *orow = smem + (32 * wave + l32) * OP;

@@ -24,6 +24,10 @@
 //    below hit all 64 banks:
 //      K-contiguous [256 rows][4 slots]: slot q of row r at q ^ ((r >> 2) & 3)
 //      M/N-contiguous [32 K rows][32 slots]: slot c of row k at c ^ (4 * (k & 3))
+//  - For bf16 outputs the MFMAs take the B fragment first, which computes
+//    each 32 x 32 accumulator transposed: a lane then holds four consecutive
+//    output columns per group of four values, and the epilogue writes a
+//    group with one 8-byte store instead of four element stores.
 //  - Out-of-range lanes (rows past the block edge, the K tail) pass an offset
 //    past the buffer's end and write zeros, as the plain buffer load does.
 //  - Each step is two phases of 16 MFMAs around one barrier; the fragment
@@ -51,34 +55,6 @@
 #include "contract_impl.h"
 
 namespace jagg {
-
-typedef __attribute__((address_space(3))) void *lds_dma_ptr;
-typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
-
-// Buffer resource as four scalar words: base, stride 0, byte count, and the
-// gfx950 word-3 flags (raw buffer, 32-bit data format); lanes whose offset
-// lies at or past `bytes` read zeros.
-__device__ __forceinline__ i32x4_rsrc dma_rsrc(const void *base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_rsrc r;
-  r.x = int(uint32_t(a));
-  r.y = int(uint32_t(a >> 32) & 0xffffu);
-  r.z = int(bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-// One 16-byte buffer load per lane into LDS: the wavefront's 64 vectors land
-// contiguously at `lds` (lane l at lds + 16 l).  Written as inline assembly
-// so that the compiler's wait-count pass does not track it: its per-object
-// tracking of LDS-writing loads loses precision across the loop back edge
-// and would wait for every stage on the first step of each unrolled pass.
-// The kernel waits for these loads itself (vmcnt, in issue order).
-__device__ __forceinline__ void dma16(i32x4_rsrc rs, uint32_t voff, const char *lds) {
-  const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_dma_ptr)(lds)));
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
-               : "memory", "m0");
-}
 
 constexpr int kDmaBK = 32;                 // K elements per step
 constexpr int kDmaRowBytes = kDmaBK * 2;   // bytes of one K-contiguous row
@@ -141,6 +117,10 @@ struct DmaOperand {
 template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
 __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   constexpr bool SW = EPI == 3;
+  // bf16 outputs: accumulators transposed (B fragment first), stored in
+  // 8-byte column groups; f32 outputs keep the plain layout, whose element
+  // stores write whole 128-byte row runs per half wavefront
+  constexpr bool TR = OUT_BF16;
   // 4 wavefronts, one per SIMD, each owning a 128 x 128 quarter of the tile
   constexpr int NT = 256, WAVES_N = 2;
   constexpr int WTM = 128, WTN = SW ? 64 : 128, TM = WTM / 32, TN = 4;
@@ -345,7 +325,8 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
+      if constexpr (TR) Mma<uint16_t>::run(acc[k / TN][k % TN], fm.b[k % TN], fm.a[k / TN]);
+      else Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
       if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
       if ((k & 1) == JAGG_DMA_ODD && k / 2 < NA + NB) dma(k / 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -357,7 +338,8 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
+      if constexpr (TR) Mma<uint16_t>::run(acc[k / TN][k % TN], fm.b[k % TN], fm.a[k / TN]);
+      else Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
       if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
       if (k >= 8 && (k & 1) == 0 && (k - 8) / 2 < 4) dma((k - 8) / 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -415,7 +397,53 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // the zero-fill loads past the last step may still be in flight: let them
   // land before the workgroup's LDS can be handed to another workgroup
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (SW) {
+  if constexpr (SW && TR) {
+    // recompose: silu(A B) * (A B2), fragments j and j + 2 hold one column
+    // range; transposed accumulators (B fragment first in the MFMA): group g
+    // of lane l is row 32 i + l % 32, columns 32 j + 8 g + 4 (l / 32) + 0..3
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int OSZ = OUT_BF16 ? 2 : 4;
+    const int lrow2 = lane & 31, lhalf2 = lane >> 5;
+    const int64_t cbase = int64_t(ents[0]) * p.beC + int64_t(bt) * p.sCb;
+    const bool wide = ((p.sCm | int64_t(p.N) | cbase) & 3) == 0;
+    const __amdgpu_buffer_rsrc_t rc =
+        tile_rsrc(static_cast<char *>(p.C) + cbase * OSZ, (p.beC - int64_t(bt) * p.sCb) * OSZ);
+    auto gate = [&](float gv, float uv) { return p.alpha * gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv; };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = m0 + wm + i * 32 + lrow2, n = n0 + wn + j * 32 + 8 * g + 4 * lhalf2;
+          float x[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) x[c] = gate(acc[i][j][4 * g + c], acc[i][j + 2][4 * g + c]);
+          if (wide) {
+            const bool ok = m < p.M && n < p.N;
+            const uint32_t e = uint32_t(int64_t(m) * p.sCm + n);
+            if constexpr (OUT_BF16) {
+              const u32x2 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+              __builtin_amdgcn_raw_buffer_store_b64(v, rc, int(ok ? e * 2 : kOob), 0, 0);
+            } else {
+              const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                               __float_as_uint(x[3])};
+              __builtin_amdgcn_raw_buffer_store_b128(v, rc, int(ok ? e * 4 : kOob), 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (m < p.M && n + c < p.N) {
+                const int64_t off = cbase + int64_t(m) * p.sCm + n + c;
+                if (OUT_BF16)
+                  reinterpret_cast<uint16_t *>(p.C)[off] = f32_to_bf16(x[c]);
+                else
+                  reinterpret_cast<float *>(p.C)[off] = x[c];
+              }
+          }
+        }
+  } else if constexpr (SW) {
     // recompose: silu(A B) * (A B2), fragments j and j + 2 hold one column
     const int lrow2 = lane & 31, lhalf2 = lane >> 5;
     char *Cb = reinterpret_cast<char *>(p.C);
@@ -438,6 +466,8 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
               reinterpret_cast<float *>(Cb)[off] = x;
           }
         }
+  } else if constexpr (TR) {
+    store_tile_t<OUT_BF16, TM, TN, EPI>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
   } else {
     if constexpr (EPI == 0) store_tile_plain<OUT_BF16, TM, TN>(p, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
     else store_tile_plus<OUT_BF16, TM, TN, EPI - 1, true>(p, acc, ents[0], bt, m0 + wm, n0 + wn, lane);

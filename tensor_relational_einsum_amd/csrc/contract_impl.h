@@ -382,6 +382,124 @@ __device__ __forceinline__ void store_tile_plus(const ContractArgs &p, const f32
   }
 }
 
+// Epilogue of the LDS-DMA kernels, whose MFMAs take the B fragment as the
+// first operand: the accumulator of fragment (i, j) then holds the tile
+// transposed, element v of lane l at row 32 i + l % 32 and column
+// 32 j + 8 (v / 4) + 4 (l / 32) + v % 4, so each group of four values is
+// four consecutive columns of one row.  With rows and N a multiple of 4
+// elements a group leaves as one 8-byte (bf16) or 16-byte (f32) buffer
+// store, and a MUL_PLUS addend group arrives as one load of the same width:
+// a quarter of the memory instructions of element stores.  Rows past M and
+// groups past N take an offset past the block's end (nothing written, zeros
+// read).  Other layouts store element by element.
+// EPI: 0 scale (and the causal output mask), 1 / 2 add an f32 / bf16 addend
+// laid out as C (MUL_PLUS); the addends of fragment f + 1 are loaded before
+// fragment f is stored (vector memory operations complete in issue order,
+// so a load issued after a store waits for it).
+template <int OUT_BF16, int TM, int TN, int EPI>
+__device__ __forceinline__ void store_tile_t(const ContractArgs &p, const f32x16 (&acc)[TM][TN], int64_t out_id,
+                                             int bt, int64_t key, int64_t ks, int m0, int n0, int lane) {
+  constexpr int OSZ = OUT_BF16 ? 2 : 4, XSZ = EPI == 2 ? 2 : 4;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int64_t cbase = out_id * p.beC + int64_t(bt) * p.sCb;
+  const int64_t left = p.beC - int64_t(bt) * p.sCb;  // elements from cbase to the block's end
+  int64_t kt_out = 0;
+  if (EPI == 0 && p.causal_out) kt_out = (key / p.ct_w) % p.ct_k;
+  auto masked = [&](float x, int m, int n) {
+    if (EPI == 0 && p.causal_out) {
+      const int64_t sg = ks * p.e_s + (uint32_t(m) - fd_div(uint32_t(m), p.div_s) * p.div_s.d);
+      const int64_t tg = kt_out * p.e_t + (uint32_t(n) - fd_div(uint32_t(n), p.div_t) * p.div_t.d);
+      if (tg > sg) return 0.0f;
+    }
+    return x;
+  };
+  if (((p.sCm | int64_t(p.N) | cbase) & 3) == 0) {
+    const __amdgpu_buffer_rsrc_t rc = tile_rsrc(static_cast<char *>(p.C) + cbase * OSZ, left * OSZ);
+    __amdgpu_buffer_rsrc_t rx = rc;
+    if constexpr (EPI != 0) rx = tile_rsrc(static_cast<const char *>(p.X) + cbase * XSZ, left * XSZ);
+    // element offset of group g of fragment (i, j) inside the block, and
+    // whether it exists
+    auto goff = [&](int i, int j, int g, bool &ok) {
+      const int m = m0 + 32 * i + lrow, n = n0 + 32 * j + 8 * g + 4 * lhalf;
+      ok = m < p.M && n < p.N;
+      return uint32_t(int64_t(m) * p.sCm + n);
+    };
+    float xs[2][16];
+    auto load_frag = [&](int f, float (&dst)[16]) {
+      const int i = f / TN, j = f % TN;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bool ok;
+        const uint32_t e = goff(i, j, g, ok);
+        if constexpr (EPI == 1) {
+          const uint4 v = buf_load<16>(rx, ok ? e * 4 : kOob);
+          dst[4 * g] = __uint_as_float(v.x);
+          dst[4 * g + 1] = __uint_as_float(v.y);
+          dst[4 * g + 2] = __uint_as_float(v.z);
+          dst[4 * g + 3] = __uint_as_float(v.w);
+        } else {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, int(ok ? e * 2 : kOob), 0, 0);
+          dst[4 * g] = __uint_as_float(v.x << 16);
+          dst[4 * g + 1] = __uint_as_float(v.x & 0xffff0000u);
+          dst[4 * g + 2] = __uint_as_float(v.y << 16);
+          dst[4 * g + 3] = __uint_as_float(v.y & 0xffff0000u);
+        }
+      }
+    };
+    if constexpr (EPI != 0) load_frag(0, xs[0]);
+#pragma unroll
+    for (int f = 0; f < TM * TN; ++f) {
+      const int i = f / TN, j = f % TN;
+      if constexpr (EPI != 0) {
+        if (f + 1 < TM * TN) load_frag(f + 1, xs[(f + 1) & 1]);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bool ok;
+        const uint32_t e = goff(i, j, g, ok);
+        float x[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          x[c] = p.alpha * acc[i][j][4 * g + c];
+          if constexpr (EPI != 0) x[c] += xs[f & 1][4 * g + c];
+          else x[c] = masked(x[c], m0 + 32 * i + lrow, n0 + 32 * j + 8 * g + 4 * lhalf + c);
+        }
+        if constexpr (OUT_BF16) {
+          const u32x2 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, rc, int(ok ? e * 2 : kOob), 0, 0);
+        } else {
+          const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                           __float_as_uint(x[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rc, int(ok ? e * 4 : kOob), 0, 0);
+        }
+      }
+    }
+  } else {
+    char *Cb = reinterpret_cast<char *>(p.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + 32 * i + lrow, n = n0 + 32 * j + 8 * (v >> 2) + 4 * lhalf + (v & 3);
+          if (m < p.M && n < p.N) {
+            const int64_t off = cbase + int64_t(m) * p.sCm + n;
+            float x = p.alpha * acc[i][j][v];
+            if constexpr (EPI == 1) x += reinterpret_cast<const float *>(p.X)[off];
+            else if constexpr (EPI == 2) x += bf16_to_f32(reinterpret_cast<const uint16_t *>(p.X)[off]);
+            else x = masked(x, m, n);
+            if (OUT_BF16)
+              reinterpret_cast<uint16_t *>(Cb)[off] = f32_to_bf16(x);
+            else
+              reinterpret_cast<float *>(Cb)[off] = x;
+          }
+        }
+  }
+}
+
 // The epilogue, with the MUL_PLUS addend's dtype fixed per instantiation so
 // that each version unrolls completely (accumulators stay in registers).
 template <int OUT_BF16, int TM, int TN>

@@ -21,6 +21,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, jagg_bf16x2));
 }
 
+typedef __attribute__((address_space(3))) void *lds_dma_ptr;
+typedef int i32x4_rsrc __attribute__((ext_vector_type(4)));
+
+// Buffer resource as four scalar words: base, stride 0, byte count, and the
+// gfx950 word-3 flags (raw buffer, 32-bit data format); lanes whose offset
+// lies at or past `bytes` read zeros.
+__device__ __forceinline__ i32x4_rsrc dma_rsrc(const void *base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_rsrc r;
+  r.x = int(uint32_t(a));
+  r.y = int(uint32_t(a >> 32) & 0xffffu);
+  r.z = int(bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// One 16-byte buffer load per lane into LDS: the wavefront's 64 vectors land
+// contiguously at `lds` (lane l at lds + 16 l).  Written as inline assembly
+// so that the compiler's wait-count pass does not track it: its per-object
+// tracking of LDS-writing loads loses precision across the loop back edge
+// and would wait for every stage on the first step of each unrolled pass.
+// The kernel waits for these loads itself (vmcnt, in issue order).
+__device__ __forceinline__ void dma16(i32x4_rsrc rs, uint32_t voff, const char *lds) {
+  const uint32_t m0 = uint32_t(reinterpret_cast<uintptr_t>((lds_dma_ptr)(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0)
+               : "memory", "m0");
+}
+
+// dma16 with the LDS destination given as an SGPR base plus a constant: the
+// add happens in the asm block, so the compiler keeps one base register live
+// instead of one register per destination.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_at(i32x4_rsrc rs, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_base),
+               "i"(OFF)
+               : "memory", "m0");
+}
+
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T *p);
 template <>
