@@ -1241,6 +1241,9 @@ jagg_status plan_attention(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, c
   a.list = list;
   a.counts = counts;
   a.per_key = int32_t(b.join.per_key);
+  if (a.per_key > kMaxAttnTuples)
+    return fail(ctx, JAGG_E_UNSUPPORTED, "attention joins at most %d K/V tuples per output tuple (t blocked %d ways)",
+                kMaxAttnTuples, a.per_key);
   a.n_keys = int32_t(b.join.n_keys);
   a.beQ = Q.be;
   a.beK = K.be;

@@ -142,6 +142,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   constexpr int NQB = 4 * ET;      // PV MFMAs per tile and wavefront
   static_assert(NL >= 1 && NL <= 4 && RP * SPR == 16, "tile geometry");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  // per joined tuple of the key: K tuple, V tuple, first key, end of its keys
+  __shared__ int4 etab[kMaxAttnTuples];
   char *const kbuf = smem;           // K tiles at kbuf + b * TB, b = 0, 1
   char *const vbuf = smem + 2 * TB;  // V tiles
 
@@ -270,31 +272,51 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   }
 
   // tuple ids and key range of one tile of the walk
+  // The joined tuples' ids and key ranges, one lane per tuple, into LDS:
+  // the walk then reads a tuple's record with one LDS read instead of a
+  // chain of scalar loads and divisions per tile.  (Scalar loads would also
+  // share their wait counter with the fragment reads, and return out of
+  // order, so every pending one would turn the fragment waits into full
+  // waits.)
+  for (int e = tid; e < cnt; e += 256) {
+    const int32_t kt = a.list[int64_t(key) * a.per_key * 4 + e * 4 + 2];
+    const int32_t vt = a.list[int64_t(key) * a.per_key * 4 + e * 4 + 3];
+    const uint32_t kap = fd_mod(fd_div(uint32_t(kt), a.div_Wt), a.div_kt);
+    etab[e] = int4{kt, vt, t_lo(kap), t_end(kap)};
+  }
   struct TileIds {
-    int64_t kt, vt;           // K and V tuple ids
+    int32_t kt, vt;           // K and V tuple ids
     int32_t tt, T0, t_valid;  // tile inside the tuple, its first key, keys [0, t_valid) that exist
   };
-  auto tile_ids = [&](int it) {
-    const int e = it / tpe;
+  // tile tt of joined tuple e (the table is written and a barrier passed)
+  auto tile_ids = [&](int e, int tt) {
+    const int4 rec = etab[e];
     TileIds r;
-    r.tt = it - e * tpe;
-    r.kt = ents[e * 4 + 2];
-    r.vt = ents[e * 4 + 3];
-    const uint32_t kap = fd_mod(fd_div(uint32_t(r.kt), a.div_Wt), a.div_kt);
-    r.T0 = t_lo(kap) + r.tt * kKeys;
-    int32_t tv = a.e_t - r.tt * kKeys;
-    if (t_end(kap) - r.T0 < tv) tv = t_end(kap) - r.T0;
+    r.kt = __builtin_amdgcn_readfirstlane(rec.x);
+    r.vt = __builtin_amdgcn_readfirstlane(rec.y);
+    r.tt = tt;
+    r.T0 = __builtin_amdgcn_readfirstlane(rec.z) + tt * kKeys;
+    int32_t tv = a.e_t - tt * kKeys;
+    const int32_t te = __builtin_amdgcn_readfirstlane(rec.w) - r.T0;
+    if (te < tv) tv = te;
     r.t_valid = tv > kKeys ? kKeys : tv;
     return r;
   };
   // LDS address of this wavefront's first 1 KB of the K buffer 0; buffer b
   // of K, V and load n add compile-time constants
   const uint32_t lds_w = uint32_t(reinterpret_cast<uintptr_t>((lds_dma_ptr)(smem))) + uint32_t(wave_s) * 1024u;
+  // byte geometry of a tile load: origin of the batch index's rows in tuple
+  // 0, bytes per tuple, bytes per tile of keys, bytes from a tuple's row 0 to
+  // the end of its last row
+  const char *const k0 = static_cast<const char *>(a.K) + oK * 2;
+  const char *const v0 = static_cast<const char *>(a.V) + oV * 2;
+  const int64_t kblk = a.beK * 2, vblk = a.beV * 2;
+  const int32_t ktile = int32_t(kKeys * a.tK * 2), vtile = int32_t(kKeys * a.tV * 2);
+  const int32_t kspan = int32_t((int64_t(a.e_t - 1) * a.tK + D) * 2), vspan = int32_t((int64_t(a.e_t - 1) * a.tV + D) * 2);
   auto load_k = [&](auto par, const TileIds &ti) {
     constexpr int B = decltype(par)::value;
-    const int64_t kbase = ti.kt * a.beK + oK + int64_t(ti.tt) * kKeys * a.tK;
-    const int64_t kend = ti.kt * a.beK + oK + int64_t(a.e_t - 1) * a.tK + D;
-    const i32x4_rsrc rk = dma_rsrc(static_cast<const char *>(a.K) + kbase * 2, (kend - kbase) * 2);
+    const int32_t skip = ti.tt * ktile;
+    const i32x4_rsrc rk = dma_rsrc(k0 + int64_t(ti.kt) * kblk + skip, kspan - skip);
     dma16_at<B * TB>(rk, kdo[0], lds_w);
     if constexpr (NL > 1) dma16_at<B * TB + 4096>(rk, kdo[1], lds_w);
     if constexpr (NL > 2) dma16_at<B * TB + 8192>(rk, kdo[2], lds_w);
@@ -302,9 +324,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   };
   auto load_v = [&](auto par, const TileIds &ti) {
     constexpr int B = decltype(par)::value;
-    const int64_t vbase = ti.vt * a.beV + oV + int64_t(ti.tt) * kKeys * a.tV;
-    const int64_t vend = ti.vt * a.beV + oV + int64_t(a.e_t - 1) * a.tV + D;
-    const i32x4_rsrc rv = dma_rsrc(static_cast<const char *>(a.V) + vbase * 2, (vend - vbase) * 2);
+    const int32_t skip = ti.tt * vtile;
+    const i32x4_rsrc rv = dma_rsrc(v0 + int64_t(ti.vt) * vblk + skip, vspan - skip);
     dma16_at<(2 + B) * TB>(rv, vdo[0], lds_w);
     if constexpr (NL > 1) dma16_at<(2 + B) * TB + 4096>(rv, vdo[1], lds_w);
     if constexpr (NL > 2) dma16_at<(2 + B) * TB + 8192>(rv, vdo[2], lds_w);
@@ -442,15 +463,25 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   TileIds t1{}, t2{};  // tiles i + 1 and i + 2 of the walk
+  int ne = 0, ntt = 0;  // joined tuple and tile of the next tile whose ids are read
+  auto next_ids = [&]() {
+    const TileIds r = tile_ids(ne, ntt);
+    if (++ntt == tpe) {
+      ntt = 0;
+      ++ne;
+    }
+    return r;
+  };
+  __syncthreads();  // the tuple table is written
   if (n_it > 0) {
-    const TileIds t0 = tile_ids(0);
+    const TileIds t0 = next_ids();
     load_k(P0{}, t0);
     load_v(P0{}, t0);
     if (n_it > 1) {
-      t1 = tile_ids(1);
+      t1 = next_ids();
       load_k(P1{}, t1);
     }
-    if (n_it > 2) t2 = tile_ids(2);
+    if (n_it > 2) t2 = next_ids();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and the first loads
     __syncthreads();
     scores(sA, 0, none);
@@ -475,6 +506,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   auto step = [&](auto par, int i, f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&pc)[16], uint32_t (&pn)[16]) {
     constexpr int B = decltype(par)::value;
     top(par, i);
+    // the ids of tile i + 3
+    TileIds t3{};
+    if (i + 3 < n_it) t3 = next_ids();
     // phase A: S of tile i + 1 || upper-half probabilities of tile i
     scores(sn, 1 - B, [&](int q) { slice(q, NQA, kHiItems, [&](int j) { pair(sc, pc, 8 + j); }); });
     mask(sn, t1);
@@ -493,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc[et][v] *= corr;
     }
     t1 = t2;
-    if (i + 3 < n_it) t2 = tile_ids(i + 3);
+    t2 = t3;
   };
   // the walk's last tile
   auto last = [&](auto par, int i, const f32x16 (&sc)[2], uint32_t (&pc)[16]) {

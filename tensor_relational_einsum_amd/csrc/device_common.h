@@ -51,12 +51,14 @@ __device__ __forceinline__ void dma16(i32x4_rsrc rs, uint32_t voff, const char *
 
 // dma16 with the LDS destination given as an SGPR base plus a constant: the
 // add happens in the asm block, so the compiler keeps one base register live
-// instead of one register per destination.
+// instead of one register per destination.  The add writes SCC, which the
+// clobber list declares (the compiler may otherwise hold a carry or a branch
+// condition in SCC across the block).
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16_at(i32x4_rsrc rs, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_base),
                "i"(OFF)
-               : "memory", "m0");
+               : "memory", "m0", "scc");
 }
 
 template <typename T>

@@ -361,6 +361,9 @@ struct AttnArgs {
   int32_t iv;
   int32_t bnd[kMaxIv + 1];
 };
+// joined K/V tuples per output tuple of the fused attention kernel (its
+// per-tuple table lives in LDS)
+constexpr int kMaxAttnTuples = 512;
 // d: 64 or 128 (the padded D = E extent)
 hipError_t launch_attention(const AttnArgs &a, int d, bool causal, bool out_bf16, hipStream_t st);
 
