@@ -36,8 +36,8 @@
 //      V: slot c of key row r at c ^ ((4 (r / RP)) % SPR)
 //    (SPR = D / 8 slots per row, RP = 16 / SPR rows per 256 bytes).  Two K
 //    and two V buffers: the loads of K for tile i + 2 and of V for tile
-//    i + 1 are issued at the top of iteration i, after the barrier that ends
-//    every read of the buffers they overwrite.
+//    i + 1 are issued during iteration i, after the barrier that ends every
+//    read of the buffers they overwrite, one between every other S MFMA.
 //  - Software pipeline, per wavefront: iteration i issues the S MFMAs of
 //    tile i + 1 with the exponentials of the upper key half of tile i
 //    between them (phase A), then the PV MFMAs of tile i with the maximum,
@@ -313,23 +313,36 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   const int64_t kblk = a.beK * 2, vblk = a.beV * 2;
   const int32_t ktile = int32_t(kKeys * a.tK * 2), vtile = int32_t(kKeys * a.tV * 2);
   const int32_t kspan = int32_t((int64_t(a.e_t - 1) * a.tK + D) * 2), vspan = int32_t((int64_t(a.e_t - 1) * a.tV + D) * 2);
-  auto load_k = [&](auto par, const TileIds &ti) {
-    constexpr int B = decltype(par)::value;
+  // buffer resources of a tile's K and V rows; a tile past the walk gets an
+  // empty buffer (its loads write zeros and read no memory)
+  auto rsrc_k = [&](const TileIds &ti, bool live) {
     const int32_t skip = ti.tt * ktile;
-    const i32x4_rsrc rk = dma_rsrc(k0 + int64_t(ti.kt) * kblk + skip, kspan - skip);
-    dma16_at<B * TB>(rk, kdo[0], lds_w);
-    if constexpr (NL > 1) dma16_at<B * TB + 4096>(rk, kdo[1], lds_w);
-    if constexpr (NL > 2) dma16_at<B * TB + 8192>(rk, kdo[2], lds_w);
-    if constexpr (NL > 3) dma16_at<B * TB + 12288>(rk, kdo[3], lds_w);
+    return dma_rsrc(k0 + int64_t(ti.kt) * kblk + skip, live ? kspan - skip : 0);
+  };
+  auto rsrc_v = [&](const TileIds &ti, bool live) {
+    const int32_t skip = ti.tt * vtile;
+    return dma_rsrc(v0 + int64_t(ti.vt) * vblk + skip, live ? vspan - skip : 0);
+  };
+  // load n of a tile into the LDS buffer at byte offset BASE (n is a
+  // constant once the callers are unrolled)
+  auto dma_n = [&](auto base, int n, const i32x4_rsrc &r, const uint32_t (&off)[NL]) {
+    constexpr uint32_t BASE = decltype(base)::value;
+    if (n == 0) dma16_at<BASE>(r, off[0], lds_w);
+    else if (n == 1) dma16_at<BASE + 4096>(r, off[NL > 1 ? 1 : 0], lds_w);
+    else if (n == 2) dma16_at<BASE + 8192>(r, off[NL > 2 ? 2 : 0], lds_w);
+    else if (n == 3) dma16_at<BASE + 12288>(r, off[NL > 3 ? 3 : 0], lds_w);
+  };
+  auto load_k = [&](auto par, const TileIds &ti) {
+    constexpr uint32_t B = decltype(par)::value;
+    const i32x4_rsrc rk = rsrc_k(ti, true);
+#pragma unroll
+    for (int n = 0; n < NL; ++n) dma_n(std::integral_constant<uint32_t, B * TB>{}, n, rk, kdo);
   };
   auto load_v = [&](auto par, const TileIds &ti) {
-    constexpr int B = decltype(par)::value;
-    const int32_t skip = ti.tt * vtile;
-    const i32x4_rsrc rv = dma_rsrc(v0 + int64_t(ti.vt) * vblk + skip, vspan - skip);
-    dma16_at<(2 + B) * TB>(rv, vdo[0], lds_w);
-    if constexpr (NL > 1) dma16_at<(2 + B) * TB + 4096>(rv, vdo[1], lds_w);
-    if constexpr (NL > 2) dma16_at<(2 + B) * TB + 8192>(rv, vdo[2], lds_w);
-    if constexpr (NL > 3) dma16_at<(2 + B) * TB + 12288>(rv, vdo[3], lds_w);
+    constexpr uint32_t B = decltype(par)::value;
+    const i32x4_rsrc rv = rsrc_v(ti, true);
+#pragma unroll
+    for (int n = 0; n < NL; ++n) dma_n(std::integral_constant<uint32_t, (2 + B) * TB>{}, n, rv, vdo);
   };
   f32x16 acc[ET];
 #pragma unroll
@@ -371,15 +384,18 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
       const char *p = vs + vaddr[q >> 2] + (q & 3) * 16 * RB;
       return tr_pair(p, p + 8 * RB);
     };
+    // MFMA q: E tile q % ET, keys 16 (q / ET) .. + 15, so that consecutive
+    // MFMAs accumulate into different registers
+    auto vq = [&](int q) { return vread(4 * (q % ET) + q / ET); };
     uint4 vring[3];
-    vring[0] = vread(0);
-    vring[1] = vread(1);
+    vring[0] = vq(0);
+    vring[1] = vq(1);
 #pragma unroll
     for (int q = 0; q < NQB; ++q) {
-      if (q + 2 < NQB) vring[(q + 2) % 3] = vread(q + 2);
+      if (q + 2 < NQB) vring[(q + 2) % 3] = vq(q + 2);
       __builtin_amdgcn_sched_barrier(0);
-      const int k = q & 3;
-      acc[q >> 2] = mma(vring[q % 3], uint4{pw[4 * k], pw[4 * k + 1], pw[4 * k + 2], pw[4 * k + 3]}, acc[q >> 2]);
+      const int k = q / ET;
+      acc[q % ET] = mma(vring[q % 3], uint4{pw[4 * k], pw[4 * k + 1], pw[4 * k + 2], pw[4 * k + 3]}, acc[q % ET]);
       __builtin_amdgcn_sched_barrier(0);
       valu(q);
       __builtin_amdgcn_sched_barrier(0);
@@ -398,25 +414,30 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
         }
     }
   };
-  // Softmax work of one tile, as numbered items spread over MFMA slices.
-  // Lower half (keys of sc[0], run in phase B): items 0..15 fold the 32
-  // scores into the maximum, item 16 moves the reference, items 17..24
-  // produce the probability pairs 0..7.  Upper half (sc[1], phase A): items
-  // 0..7 produce pairs 8..15.  A pair is two exponentials, one bf16 pack and
-  // one row-sum step.
-  constexpr int kLoItems = 25, kHiItems = 8;
-  float mx = -INFINITY;
-  auto pair = [&](const f32x16 (&sc)[2], uint32_t (&pw)[16], int j) {
-    const int mt = j >> 3, v = 2 * (j & 7);
-    float s0 = sc[mt][v], s1 = sc[mt][v + 1];
-    pin(s0);
-    pin(s1);
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, scale, -base));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, scale, -base));
-    pw[j] = pack_bf16x2(p0, p1);
-    l_run = add_pair(pw[j], l_run);
-    pin(pw[j]);
-    pin(l_run);
+  // Softmax work of one tile as numbered items, spread over MFMA slices by
+  // their VALU cost.  Phase B (under the PV MFMAs of the previous tile)
+  // runs items 0..15, which fold the 32 scores into the maximum, item 16,
+  // which moves the reference, and the first kLoB probability items; phase
+  // A (under the S MFMAs of the next tile) runs the other 32 - kLoB.
+  // Probability item u (key value u of the lane: half u / 16, value u % 16)
+  // is one FMA and one exponential; an odd u also packs the pair into a bf16
+  // word of P and adds it to the row sum.  kLoB balances the two phases.
+  constexpr int kLoB = D == 128 ? 12 : 14;
+  constexpr int kLoItems = 17 + kLoB;
+  float mx = -INFINITY, ph = 0.0f;
+  auto prob = [&](const f32x16 (&sc)[2], uint32_t (&pw)[16], int u) {
+    float sv = sc[u >> 4][u & 15];
+    pin(sv);
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, scale, -base));
+    if ((u & 1) == 0) {
+      ph = p;
+      pin(ph);
+    } else {
+      pw[u >> 1] = pack_bf16x2(ph, p);
+      l_run = add_pair(pw[u >> 1], l_run);
+      pin(pw[u >> 1]);
+      pin(l_run);
+    }
   };
   auto lo_item = [&](const f32x16 (&sc)[2], uint32_t (&pw)[16], int it) {
     if (it < 16) {
@@ -438,22 +459,30 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
       pin(base);
       pin(l_run);
     } else {
-      pair(sc, pw, it - 17);
+      prob(sc, pw, it - 17);
     }
   };
-  // Phase B slices by cost: the 16 maximum items (one v_max3 each) fill the
-  // first NQB / 8 slices, the reference update the next, and the 8 pairs
-  // (two exponentials each, the expensive items) spread over the rest.
-  constexpr int kMaxSl = NQB / 8 > 0 ? NQB / 8 : 1;
-  auto lo_slice = [](int it) {
-    if (it < 16) return it * kMaxSl / 16;
-    if (it == 16) return kMaxSl;
-    return kMaxSl + 1 + (it - 17) * (NQB - kMaxSl - 1) / 8;
-  };
-  // slice q of n slices takes items [q * items / n, (q + 1) * items / n)
-  auto slice = [](int q, int n, int items, auto &&item) {
+  // relative VALU cost of an item and the slice it runs in: slices take
+  // equal shares of their phase's total cost, items in order
+  auto cost_lo = [](int it) { return it < 16 ? 1 : it == 16 ? 3 : ((it - 17) & 1) ? 7 : 5; };
+  auto cost_u = [](int u) { return (u & 1) ? 7 : 5; };
+  auto lo_slice = [&](int it) {
+    int before = 0, total = 0;
 #pragma unroll
-    for (int it = q * items / n; it < (q + 1) * items / n; ++it) item(it);
+    for (int x = 0; x < kLoItems; ++x) {
+      if (x < it) before += cost_lo(x);
+      total += cost_lo(x);
+    }
+    return before * NQB / total;
+  };
+  auto hi_slice = [&](int u) {  // u = kLoB .. 31
+    int before = 0, total = 0;
+#pragma unroll
+    for (int x = kLoB; x < 32; ++x) {
+      if (x < u) before += cost_u(x);
+      total += cost_u(x);
+    }
+    return before * NQA / total;
   };
   auto none = [](int) {};
 
@@ -493,24 +522,35 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   // one iteration of the walk (parity par = i % 2), for a tile i with a
   // successor: tile i's scores in sc, the lower half of its probabilities in
   // pc; the next tile's scores go to sn, its lower half to pn
-  auto top = [&](auto par, int i) {
-    constexpr int B = decltype(par)::value;
+  auto top = [&]() {
     // every wavefront is done with iteration i - 1: the S reads of K buffer
-    // i % 2 and the PV reads of V buffer (i + 1) % 2; the loads issued at
-    // the top of i - 1 (K of tile i + 1, V of tile i) have landed
+    // i % 2 and the PV reads of V buffer (i + 1) % 2; the loads issued in
+    // iteration i - 1 (K of tile i + 1, V of tile i) have landed
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (i + 2 < n_it) load_k(std::integral_constant<int, B>{}, t2);
-    if (i + 1 < n_it) load_v(std::integral_constant<int, 1 - B>{}, t1);
   };
   auto step = [&](auto par, int i, f32x16 (&sc)[2], f32x16 (&sn)[2], uint32_t (&pc)[16], uint32_t (&pn)[16]) {
-    constexpr int B = decltype(par)::value;
-    top(par, i);
+    constexpr uint32_t B = decltype(par)::value;
+    top();
+    // this iteration loads K of tile i + 2 into K buffer i % 2 and V of tile
+    // i + 1 into V buffer (i + 1) % 2, one load after every other S MFMA of
+    // phase A: a burst of loads right after the barrier would back up the
+    // vector memory path and hold up the in-order wavefront
+    const i32x4_rsrc rk = rsrc_k(t2, i + 2 < n_it), rv = rsrc_v(t1, true);
     // the ids of tile i + 3
     TileIds t3{};
     if (i + 3 < n_it) t3 = next_ids();
-    // phase A: S of tile i + 1 || upper-half probabilities of tile i
-    scores(sn, 1 - B, [&](int q) { slice(q, NQA, kHiItems, [&](int j) { pair(sc, pc, 8 + j); }); });
+    // phase A: S of tile i + 1 || upper-half probabilities of tile i, loads
+    scores(sn, 1 - B, [&](int q) {
+#pragma unroll
+      for (int u = kLoB; u < 32; ++u)
+        if (hi_slice(u) == q) prob(sc, pc, u);
+      if (q & 1) {
+        const int d = q >> 1;
+        if (d < NL) dma_n(std::integral_constant<uint32_t, B * TB>{}, d, rk, kdo);
+        else if (d < 2 * NL) dma_n(std::integral_constant<uint32_t, (3 - B) * TB>{}, d - NL, rv, vdo);
+      }
+    });
     mask(sn, t1);
     // phase B: PV of tile i || maximum and lower-half probabilities of tile i + 1
     pv(pc, B, [&](int q) {
@@ -532,9 +572,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   // the walk's last tile
   auto last = [&](auto par, int i, const f32x16 (&sc)[2], uint32_t (&pc)[16]) {
     constexpr int B = decltype(par)::value;
-    top(par, i);
+    top();
 #pragma unroll
-    for (int j = 0; j < kHiItems; ++j) pair(sc, pc, 8 + j);
+    for (int u = kLoB; u < 32; ++u) prob(sc, pc, u);
     pv(pc, B, none);
   };
   int i = 0;
