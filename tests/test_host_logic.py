@@ -111,6 +111,26 @@ def test_matrix_chain_recipe_matches_the_pages(label):
     assert w.chain[-1].out == f"P1_{len(w.tensors)}"
     used = [n for st in w.chain for n in st.ins if n.startswith("M")]
     assert sorted(used, key=lambda s: int(s[1:])) == [f"M{i}" for i in range(1, len(w.tensors) + 1)]
+    # the printed dimensions: ends, necks and interior (Sec. 6)
+    dims = [w.extents[t[1][0]] for t in w.tensors] + [w.extents[w.tensors[-1][1][1]]]
+    printed = {
+        "A": [10240] + [16384, 6144] * 4 + [10240],
+        "B": [9216] + [20480, 5120] * 2 + [9216],
+        "C": [10240, 12288, 32768, 2048],
+        "D": [24576, 1536] + [20480] * 6 + [1536, 24576],
+        "E": [49152, 1024] + [20480] * 10 + [1024, 49152],
+    }
+    assert dims == printed[label]
+    # the printed parenthesizations, as the order of the products
+    order = {
+        "A": ["P1_2", "P3_4", "P5_6", "P7_8", "P5_8", "P3_8", "P1_8", "P1_9"],
+        "B": ["P1_2", "P3_4", "P3_5", "P1_5"],
+        "C": ["P2_3", "P1_3"],
+        "D": ["P7_8", "P6_8", "P5_8", "P4_8", "P3_8", "P2_8", "P1_8", "P1_9"],
+        "E": ["P11_12", "P10_12", "P9_12", "P8_12", "P7_12", "P6_12", "P5_12", "P4_12", "P3_12", "P2_12",
+              "P1_12", "P1_13"],
+    }
+    assert [st.out for st in w.chain] == order[label]
     if label == "C":
         assert [st.out for st in w.chain] == ["P2_3", "P1_3"]
     if label in "DE":
