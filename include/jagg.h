@@ -96,8 +96,8 @@ typedef enum {
  *    a SwiGLU feed-forward layer and their product, without writing either
  *    projection.  Runs on the bf16 256 x 128-tile pipeline only: bf16
  *    operands in 16-byte vectors, x0 contiguous along the reduced letters,
- *    x1 / x2 contributing the output's innermost letters, at least 256 such
- *    tiles (JAGG_E_UNSUPPORTED otherwise).
+ *    x1 / x2 contributing the output's innermost letters
+ *    (JAGG_E_UNSUPPORTED otherwise); any extents.
  * The inputs are read as stored (bf16 or f32 addend); sums accumulate in
  * fp32 and the map is applied before the single rounding to out_dtype. */
 

@@ -1635,9 +1635,13 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
     const int BNt = ca.epi == 2 ? 128 : 256;
     const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + BNt - 1) / BNt);
     P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= BNt && big_tiles >= 256 && !ca.causal_red;
+    // SWIGLU has only the 256 x 128 pipeline, which bounds-checks ragged M
+    // and N, so it takes it at any size (the size rule above only picks the
+    // faster kernel)
+    if (ca.epi == 2) P.big = P.va == F && P.vb == F && !ca.causal_red;
     if (ca.epi == 2 && !(P.big && P.dtype && P.akc))
       return fail(ctx, JAGG_E_UNSUPPORTED, "SWIGLU runs on the 256 x 128 bf16 pipeline: bf16 operands in 16-byte "
-                  "vectors, input 0 contiguous along the reduced letters, at least 256 tiles of 256 x 128");
+                  "vectors, input 0 contiguous along the reduced letters");
     // per-XCD renumbering pays where several tiles of one output block share panels
     const int bm = P.big ? 256 : 128;
     ca.remap = !ca.causal_out && !ca.causal_red && int64_t((ca.M + bm - 1) / bm) * ((ca.N + bm - 1) / bm) >= 4;

@@ -109,10 +109,26 @@ def test_swiglu_lds_pipeline(ctx, capfd, wl, nf, odt):
     assert normwise_err(got, want) < (1e-5 if odt == "f32" else 8e-3)
 
 
+# SwiGLU below one 256 x 128 tile and over ragged blocks: the pipeline
+# bounds-checks rows and columns, so it takes any extents
+SMALL_SWIGLU_CASES = [
+    (dict(b=1, s=100, h=64, f=72), dict(b=1, s=1, h=1, f=1)),
+    (dict(b=2, s=300, h=128, f=208), dict(b=1, s=2, h=2, f=2)),
+]
+
+
+@pytest.mark.parametrize("ext,blk", SMALL_SWIGLU_CASES)
+def test_swiglu_small_and_ragged(ctx, capfd, ext, blk):
+    got, want, trace = run_recompose(ctx, capfd, "bsh,hf,hf->bsf", "swiglu", ext, blk, ["bf16", "bf16", "bf16"],
+                                     "bf16", alpha=0.75)
+    assert "256x128 lds pipeline, swiglu" in trace
+    assert normwise_err(got, want) < 8e-3
+
+
 def test_recompose_rejects(ctx):
     blk = dict(i=1, j=1, k=1)
-    rels = [jagg.Relation(ctx, lt, [64, 64], [1, 1], "bf16", zeroed=True) for lt in ("ij", "jk", "jk")]
-    with pytest.raises(jagg.JaggError, match="SWIGLU"):  # too small for the 256 x 128 pipeline
+    rels = [jagg.Relation(ctx, lt, [64, 64], [1, 1], "f32", zeroed=True) for lt in ("ij", "jk", "jk")]
+    with pytest.raises(jagg.JaggError, match="SWIGLU"):  # fp32 operands: no 256 x 128 bf16 pipeline
         jagg.EinsumCall(ctx, "ij,jk,jk->ik", rels, blk, g="swiglu", agg="sum").run()
     with pytest.raises(jagg.JaggError):  # the addend holds a reduced letter
         jagg.EinsumCall(ctx, "ij,jk,jk->ik", rels, blk, g="mul_plus", agg="sum").run()
