@@ -112,7 +112,8 @@ typedef enum {
  * triples in join-list order.  Requirements (else JAGG_E_UNSUPPORTED):
  * alpha > 0; Q, K and V in bfloat16; D and E one block each, of equal padded extent 64 or
  * 128, innermost in their operands; row strides and block sizes multiples of
- * 8 elements; blocks under 2 GiB. */
+ * 8 elements; blocks under 2 GiB; at most 512 joined K/V tuples per output
+ * tuple (t blocked at most 512 ways). */
 
 /* One join-agg spec.  out[o] = alpha * AGG over the reduced letters of
  * g(x0, ...).  `einsum` is "in0,in1,...->out" (1 to 3 inputs); operand
