@@ -184,3 +184,22 @@ def test_causal_output_densifies_with_zeros_above_the_diagonal(ctx):
     want = O.round_to(O.dense(spec, [to_np(x) for x in xs], ext, causal=("s", "t")), "f32")
     assert np.all(got[:, np.triu_indices(200, 1)[0], np.triu_indices(200, 1)[1]] == 0.0)
     assert normwise_err(got, want) < F32_TOL
+
+
+def test_attention_joined_tuple_limit(ctx):
+    """The fused attention kernel keeps a key's joined K/V tuples in an LDS
+    table of 512 entries: t blocked 520 ways is refused before any launch,
+    512 ways runs."""
+    def call(nt):
+        ext = dict(s=64, t=8 * nt, d=64, e=64)
+        blk = dict(s=1, t=nt, d=1, e=1)
+        rels = [jagg.Relation(ctx, lt, [ext[c] for c in lt], [blk[c] for c in lt], "bf16", zeroed=True)
+                for lt in ("sd", "td", "te")]
+        return jagg.EinsumCall(ctx, "sd,td,te->se", rels, blk, g="attention", agg="softmax", alpha=0.125)
+    with pytest.raises(jagg.JaggError, match="512"):
+        call(520).run()
+    c = call(512)
+    c.run()
+    torch.cuda.synchronize()
+    # all-zero inputs: uniform probabilities over zero values
+    assert torch.count_nonzero(c.out.data).item() == 0
