@@ -323,6 +323,8 @@ def other_config(ctx, w: I.Workload, flush_buf, warmup: int = 2, peaks: dict | N
            "eager": eager, "graph": graph, "specs": specs}
     if peaks and in_dtype == "bf16" and peaks.get("mfma_bf16_TFLOP/s"):
         out["frac_measured_mfma"] = round(tf / peaks["mfma_bf16_TFLOP/s"], 4)
+    if peaks and in_dtype == "f32" and peaks.get("mfma_f32_TFLOP/s"):
+        out["frac_measured_mfma"] = round(tf / peaks["mfma_f32_TFLOP/s"], 4)
     del run
     torch.cuda.synchronize()
     return out
@@ -372,6 +374,27 @@ def machine_peaks(stream, flush_buf) -> dict:
     out["mfma"] = dict(st, flop=flop, kernel="v_mfma_f32_32x32x16_bf16 loop, 16 accumulators per wavefront, "
                                              "1024 workgroups x 4 wavefronts")
     out["mfma_bf16_TFLOP/s"] = round(flop / (st["ms_median"] * 1e-3) / 1e12, 1)
+
+    # the fp32 probe: the same loop shape on v_mfma_f32_32x32x2f32, on
+    # uniform[-1, 1) operands like the fp32 workloads
+    lib.jagg_calib_mfma_f32.argtypes = lib.jagg_calib_mfma_bf16.argtypes
+    ops32 = I.draw(I.streams(78, 1)[0], [512], "uniform", "f32").to("cuda")
+    iters32 = 1024
+    flop32 = blocks * 4 * iters32 * 16 * 4096.0
+
+    def launch32():
+        rc = lib.jagg_calib_mfma_f32(ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(ops32.data_ptr()),
+                                     ctypes.c_void_p(sink.data_ptr()), blocks, iters32)
+        if rc != 0:
+            raise RuntimeError(f"fp32 MFMA probe launch failed ({rc})")
+
+    for _ in range(3):
+        launch32()
+    rounds = [timed_reps(stream, launch32) for _ in range(ROUNDS)]
+    st = rounds_stats(rounds)
+    out["mfma_f32"] = dict(st, flop=flop32, kernel="v_mfma_f32_32x32x2f32 loop, 16 accumulators per wavefront, "
+                                                   "1024 workgroups x 4 wavefronts")
+    out["mfma_f32_TFLOP/s"] = round(flop32 / (st["ms_median"] * 1e-3) / 1e12, 1)
     return out
 
 

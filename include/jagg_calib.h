@@ -5,8 +5,8 @@
  * "Stax (5): Caching and Measurement", Section 13.1 ("Machine parameters"):
  * a roofline is read against the rates the machine actually reaches, so the
  * benchmark measures them beside the nominal datasheet peaks.  The HBM rate
- * is a plain device copy (timed by the caller); the matrix-core rate is this
- * probe: a loop of bf16 MFMAs on operands held in registers.
+ * is a plain device copy (timed by the caller); the matrix-core rates are
+ * these probes: loops of bf16 or fp32 MFMAs on operands held in registers.
  */
 #ifndef JAGG_CALIB_H
 #define JAGG_CALIB_H
@@ -28,6 +28,14 @@ extern "C" {
  * kept.  FLOPs of one launch: n_blocks * 4 * iters * 16 * 32768.
  * Returns 0, or -6 when the launch fails. */
 int jagg_calib_mfma_bf16(void *hip_stream, const void *operands, float *sink, int n_blocks, int iters);
+
+/* The fp32 form of the same probe: each wavefront loads eight fp32 operand
+ * registers from `operands` (device, at least 512 floats) and runs `iters`
+ * rounds of the 4 x 4 products into 16 fp32 32x32 accumulators with
+ * v_mfma_f32_32x32x2f32 (4096 FLOP each).  FLOPs of one launch:
+ * n_blocks * 4 * iters * 16 * 4096.  Returns 0, or -6 when the launch
+ * fails. */
+int jagg_calib_mfma_f32(void *hip_stream, const float *operands, float *sink, int n_blocks, int iters);
 
 #ifdef __cplusplus
 }

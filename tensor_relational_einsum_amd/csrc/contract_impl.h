@@ -252,14 +252,17 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[TM][TN], const uint4 *a,
 
 // workgroup -> (tile row, tile column, batch index, output key).  Where
 // neighbouring tiles share operand panels, the numbering gives each XCD a
-// contiguous run of tiles (dispatch round-robins workgroups over the 8 XCDs).
-// Logical tile of this workgroup: with `remap`, the dispatch order (which
-// deals workgroups round-robin to the 8 XCDs) is renumbered so that each
-// XCD works through one contiguous range of logical tiles.
+// contiguous run of tiles.  Dispatch deals workgroups round-robin to the 8
+// XCDs, so XCD x runs workgroups x, x + 8, ...: q + (x < r) of them for a
+// grid of G = 8 q + r.  With `remap` the i-th of them takes logical tile
+// x q + min(x, r) + i, which numbers each XCD's workgroups as one contiguous
+// range and covers 0 .. G-1 once for any G.
 __device__ __forceinline__ int64_t logical_tile(bool remap) {
   int64_t w = blockIdx.x;
-  const int64_t G = gridDim.x;
-  if (remap && (G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+  if (remap) {
+    const int64_t G = gridDim.x, q = G >> 3, r = G & 7, x = w & 7;
+    w = x * q + (x < r ? x : r) + (w >> 3);
+  }
   return w;
 }
 
