@@ -31,6 +31,17 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(jagg.EXPORTS)
 
 
+def test_calibration_library_exports_every_declared_function():
+    # libjagg_calib.so: the machine-peak probes the benchmark times
+    from tensor_relational_einsum_amd import build as B
+    text = open(os.path.join(ROOT, "include", "jagg_calib.h")).read()
+    names = sorted(set(re.findall(r"\b(jagg_\w+)\s*\(", text)))
+    assert names == ["jagg_calib_mfma_bf16", "jagg_calib_mfma_f32"]
+    L = ctypes.CDLL(B.CALIB_LIB)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in jagg_calib.h but not exported"
+
+
 @pytest.mark.parametrize("letters,ext,blk,dtype", [
     ("ij", (256, 256), (4, 4), "f32"),
     ("abcd", (96, 300, 64, 48), (5, 7, 4, 3), "f32"),
