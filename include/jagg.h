@@ -295,6 +295,27 @@ jagg_status jagg_plan_destroy(jagg_plan *plan);
  * Groups may be members of groups (their members are taken). */
 jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans, jagg_plan **group);
 
+/* A dependent pair run as one pass ("Stax (5): Caching and Measurement",
+ * Section 7: a reduction and the pointwise map that reads its result at the
+ * same row index fuse vertically; Section 13.2, Proposition 13.3: the gain
+ * is the ratio of bytes moved).  `first` must be the plan of a SUM of
+ * JAGG_G_SQUARE over the innermost letter r of its one input x, to an f32
+ * output ss ("X r -> X"); `second` the plan of a JAGG_G_RMS_SCALE map
+ * ("X r, X, r -> X r") whose inputs are that x, that ss and a scale over r,
+ * into an output laid out like x.  jagg_plan_run on the fused plan writes
+ * both ss and the map's output, each as running `first` then `second`
+ * writes it, except that the row sums of squares are added in another
+ * order (last-bit differences in ss, and in the output through it).
+ * Limits: uniform blockings, no re-blocked input, a block extent of r that
+ * is a multiple of 256, rows of at most 4096 elements (r-blocks x block
+ * extent), x, the scale and the output 16-byte aligned; anything else
+ * returns JAGG_E_UNSUPPORTED and the caller runs the two plans one after the
+ * other.  The map's output must not overlap x (JAGG_E_INVALID).  The fused
+ * plan reads the first plan's join list: both plans' buffers and
+ * workspaces must stay valid and unmoved while it lives, as for a group;
+ * `first` and `second` may be destroyed. */
+jagg_status jagg_plan_fuse(jagg_ctx *ctx, const jagg_plan *first, const jagg_plan *second, jagg_plan **fused);
+
 /* jagg_einsum without a workspace argument, for callers that cannot
  * allocate device memory (code under stream capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It runs the same kernels as jagg_einsum

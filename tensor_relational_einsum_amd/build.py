@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libjagg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["abi.cpp", "relayout.hip", "join.hip", "elementwise.hip", "stream.hip", "flat.hip", "attention.hip", "contract_bf16.hip", "contract_f32.hip"]
+SOURCES = ["abi.cpp", "relayout.hip", "join.hip", "elementwise.hip", "stream.hip", "flat.hip", "attention.hip", "contract_bf16.hip", "contract_f32.hip", "norm.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # keep the compiler from forming packed fp32 ops
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1488,10 +1488,12 @@ jagg_status plan_contract(jagg_ctx *ctx, const jagg_spec *sp, const Bound &b, co
 // arguments (which embed the relation, join-list and workspace addresses)
 // and the launch choices.  Built once per call, or once per jagg_plan.
 struct PlannedCall {
-  enum Kind { MAP, REDUCE, CONTRACT, ATTENTION } kind = MAP;
+  enum Kind { MAP, REDUCE, CONTRACT, ATTENTION, NORM } kind = MAP;
   std::string einsum;
   int agg = 0;
   bool out_bf16 = false, causal = false;
+  bool has_iv = false;  // some letter is interval-blocked
+  NormArgs norm;        // NORM: a fused reduce / RMS-scale pair (jagg_plan_fuse)
   std::vector<RelayoutArgs> reblocks;
   std::vector<int> reblock_vec;  // vector bytes * 16 + element bytes
   JoinArgs join;
@@ -1564,6 +1566,7 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
   P.agg = spec->agg;
   P.out_bf16 = spec->out_dtype == JAGG_BF16;
   P.causal = spec->causal_s != 0;
+  for (int c = 0; c < 26; ++c) P.has_iv = P.has_iv || b.iv_letter[c];
 
   // classify before launching anything: a contraction is a MUL/SUM over two
   // inputs where every reduced letter is in both inputs and each input
@@ -1713,6 +1716,13 @@ bool same_contraction_form(const PlannedCall &x, const PlannedCall &y) {
 // Block kernel of a planned call.
 jagg_status launch_kernel(jagg_ctx *ctx, const PlannedCall &P) {
   const char *e_name = P.einsum.c_str();
+  if (P.kind == PlannedCall::NORM) {
+    const hipError_t e = launch_norm(P.norm, ctx->stream);
+    if (ctx->trace)
+      fprintf(stderr, "[jagg] %s: rms norm pair in one pass, %d keys x %d rows\n", e_name, P.norm.n_keys,
+              P.norm.rows);
+    return after_launch(ctx, e, "rms norm pair");
+  }
   if (P.kind == PlannedCall::ATTENTION) {
     const hipError_t e = launch_attention(P.at, P.att_d, P.causal, P.out_bf16, ctx->stream);
     if (ctx->trace)
@@ -1743,6 +1753,76 @@ jagg_status einsum_impl(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relatio
   jagg_status st = build_call(ctx, spec, in, n_in, blockings, out, workspace, ws_bytes, noalloc, P);
   if (st != JAGG_OK) return st;
   return launch_call(ctx, P, true);
+}
+
+// The checks of jagg_plan_fuse: `R` a sum-of-squares reduce of x over its
+// innermost letter r, `M` the RMS-scale map of (x, R's output, a scale over
+// r) into a relation laid out like x; every mismatch is JAGG_E_UNSUPPORTED
+// (the caller runs the two plans apart).
+jagg_status plan_norm_pair(jagg_ctx *ctx, const PlannedCall &R, const PlannedCall &M, NormArgs &n) {
+  memset(&n, 0, sizeof(n));
+  auto no = [&](const char *why) { return fail(ctx, JAGG_E_UNSUPPORTED, "no fused RMS-norm pair: %s", why); };
+  if (R.kind != PlannedCall::REDUCE || M.kind != PlannedCall::MAP) return no("the first plan must be a reduce, the second a map");
+  if (!R.reblocks.empty() || !M.reblocks.empty()) return no("a plan re-blocks an input");
+  if (R.has_iv || M.has_iv) return no("interval-blocked letters");
+  const EwArgs &r = R.ew, &m = M.ew;
+  if (r.g != JAGG_G_SQUARE || r.agg != JAGG_AGG_SUM || r.n_in != 1 || r.n_red != 1 || r.causal || r.inner_red != 0 ||
+      r.out_dt != 0)
+    return no("the reduce must be an f32 SUM of squares over the innermost letter of its one input");
+  if (m.g != JAGG_G_RMS_SCALE || m.agg != JAGG_AGG_NONE || m.n_in != 3 || m.causal)
+    return no("the map must be RMS_SCALE of three inputs");
+  if (m.in[0] != r.in[0] || m.in_dt[0] != r.in_dt[0] || m.be_in[0] != r.be_in[0])
+    return no("the map's input 0 must be the reduce's input");
+  if (m.in[1] != r.out) return no("the map's input 1 must be the reduce's output");
+  Spec pr, pm;
+  jagg_status st;
+  if ((st = parse(ctx, R.einsum.c_str(), pr)) != JAGG_OK || (st = parse(ctx, M.einsum.c_str(), pm)) != JAGG_OK)
+    return st;
+  const std::string &X = pr.in[0], &Xm = pm.in[0];
+  if (X.size() != Xm.size() || pr.out != X.substr(0, X.size() - 1) ||
+      pm.in[1] != Xm.substr(0, Xm.size() - 1) || pm.in[2] != Xm.substr(Xm.size() - 1) || pm.out != Xm)
+    return no("the letters must read 'X r -> X' and 'X r, X, r -> X r'");
+  const int64_t e_r = r.e_red[0], rows = r.be_out;
+  const int last = m.r_out - 1;
+  if (r.be_in[0] != rows * e_r || m.be_out != r.be_in[0] || m.rows_per_block != rows || m.be_in[1] != rows ||
+      m.be_in[2] != e_r || m.e_out[last] != e_r || m.n_out[last] != r.n_red_ext[0] || m.k_out[last] != r.k_red[0])
+    return no("the relations' blocks do not line up");
+  if (e_r % 256 != 0 || int64_t(r.per_key) * (e_r / 256) > kNormMaxVec)
+    return no("rows must be a multiple of 256 elements per block and at most 4096 elements long");
+  const int64_t chunks = (rows + 3) / 4;
+  if (r.n_keys * chunks >= (int64_t(1) << 31)) return no("too many rows");
+  auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (!al(r.in[0]) || !al(m.in[2]) || !al(m.out)) return no("x, the scale and the output must be 16-byte aligned");
+  for (const auto &w : M.writes)
+    for (const auto &q : R.reads)
+      if (w.first < q.first + q.second && q.first < w.first + w.second)
+        return fail(ctx, JAGG_E_INVALID, "the map's output overlaps the reduce's input");
+  n.x = r.in[0];
+  n.x_dt = r.in_dt[0];
+  n.be_x = r.be_in[0];
+  n.ss = static_cast<float *>(r.out);
+  n.gam = m.in[2];
+  n.g_dt = m.in_dt[2];
+  n.be_g = m.be_in[2];
+  n.y = m.out;
+  n.y_dt = m.out_dt;
+  n.list = r.list;
+  n.counts = r.counts;
+  n.per_key = r.per_key;
+  n.n_keys = int32_t(r.n_keys);
+  n.rows = int32_t(rows);
+  n.chunks = int32_t(chunks);
+  n.div_chunks = make_fastdiv(uint32_t(chunks));
+  n.e_r = int32_t(e_r);
+  n.n_r = int32_t(r.n_red_ext[0]);
+  n.nvb = int32_t(e_r / 256);
+  n.div_wr = make_fastdiv(uint32_t(r.w_red0[0]));
+  n.div_kr = make_fastdiv(uint32_t(r.k_red[0]));
+  n.alpha_r = r.alpha;
+  n.alpha_m = m.alpha;
+  n.beta = m.beta;
+  n.eps = m.eps;
+  return JAGG_OK;
 }
 
 const char *env_or(const char *k) {
@@ -2042,6 +2122,32 @@ jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans,
     G->launches.push_back(L);
   }
   *group = G;
+  return JAGG_OK;
+}
+
+jagg_status jagg_plan_fuse(jagg_ctx *ctx, const jagg_plan *first, const jagg_plan *second, jagg_plan **fused) {
+  if (!ctx || !first || !second || !fused) return fail(ctx, JAGG_E_INVALID, "NULL argument");
+  *fused = nullptr;
+  if (first->device != ctx->device || second->device != ctx->device)
+    return fail(ctx, JAGG_E_INVALID, "a plan is for another device");
+  if (!first->members.empty() || !second->members.empty())
+    return fail(ctx, JAGG_E_UNSUPPORTED, "no fused RMS-norm pair: groups do not fuse");
+  const PlannedCall &R = first->call, &M = second->call;
+  NormArgs n;
+  const jagg_status st = plan_norm_pair(ctx, R, M, n);
+  if (st != JAGG_OK) return st;
+  jagg_plan *F = new jagg_plan;
+  F->device = ctx->device;
+  PlannedCall &P = F->call;
+  P.kind = PlannedCall::NORM;
+  P.einsum = R.einsum + " + " + M.einsum;
+  P.norm = n;
+  P.reads = R.reads;
+  for (const auto &q : M.reads)
+    if (q.first != static_cast<const char *>(R.ew.out)) P.reads.push_back(q);
+  P.writes = R.writes;
+  P.writes.insert(P.writes.end(), M.writes.begin(), M.writes.end());
+  *fused = F;
   return JAGG_OK;
 }
 

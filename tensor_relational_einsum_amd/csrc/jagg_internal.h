@@ -328,6 +328,39 @@ struct FlatArgs {
 hipError_t launch_flat_map(const FlatArgs &a, int g, hipStream_t st);  // 8 elements per vector
 hipError_t launch_flat_reduce(const FlatArgs &a, int vec, int lpr, int g, int agg, hipStream_t st);
 
+// ---------------------------------------------------------- RMS-norm pair
+// A sum-of-squares reduce over the innermost letter r of x and the RMS-scale
+// map that reads its result, run as one pass ("Stax (5): Caching and
+// Measurement", Section 7: vertical fusion of a reduction and the pointwise
+// map that reads it at the same row index): one wavefront per row loads the
+// row's pieces (one per r-block, listed by the reduce's join) once, writes
+// the row statistic and then the scaled row.  y is numbered and laid out
+// like x; the scale relation has the one letter r.
+constexpr int kNormMaxVec = 16;  // 4-element vectors per lane: rows of at most 4096 elements
+struct NormArgs {
+  const void *x;           // f32 or bf16 blocks of be_x elements
+  int32_t x_dt;
+  int64_t be_x;
+  float *ss;               // f32 blocks of `rows` elements, tuple id = reduce key
+  const void *gam;         // r-block kr at tuple id kr, blocks of be_g elements
+  int32_t g_dt;
+  int64_t be_g;
+  void *y;                 // tuple id = x's
+  int32_t y_dt;
+  const int32_t *list;     // the reduce's join list: (ss tuple, x tuple) per entry
+  const int32_t *counts;
+  int32_t per_key;
+  int32_t n_keys;
+  int32_t rows;            // rows per block
+  int32_t chunks;          // workgroups per key (4 rows each)
+  FastDiv div_chunks;
+  int32_t e_r, n_r;        // block extent and extent of r
+  int32_t nvb;             // vectors per lane per r-block: e_r / 256
+  FastDiv div_wr, div_kr;  // r-block of an x tuple id: (id / w_r) % k_r
+  float alpha_r, alpha_m, beta, eps;
+};
+hipError_t launch_norm(const NormArgs &a, hipStream_t st);
+
 // ---------------------------------------------------------------- attention
 // One workgroup: 128 rows of s (32 per wavefront) of one output key and one
 // batch index inside the block; it walks the key's joined (K, V) tuples in

@@ -27,7 +27,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # JAGG_NOALLOC_SCRATCH_BYTES in jagg.h
 EXPORTS = ["jagg_ctx_create", "jagg_ctx_destroy", "jagg_relation_bytes", "jagg_relation_create",
            "jagg_relation_bytes_iv", "jagg_relation_create_iv", "jagg_relation_destroy", "jagg_repartition",
            "jagg_einsum_workspace", "jagg_einsum", "jagg_einsum_noalloc", "jagg_plan_create", "jagg_plan_run",
-           "jagg_plan_destroy", "jagg_plan_group", "jagg_join_shape",
+           "jagg_plan_destroy", "jagg_plan_group", "jagg_plan_fuse", "jagg_join_shape",
            "jagg_join_list", "jagg_capture_begin", "jagg_capture_end", "jagg_graph_launch", "jagg_graph_destroy",
            "jagg_status_str", "jagg_last_error"]
 
@@ -82,6 +82,7 @@ def lib():
         L.jagg_plan_run.argtypes = [vp, vp]
         L.jagg_plan_destroy.argtypes = [vp]
         L.jagg_plan_group.argtypes = [vp, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.jagg_plan_fuse.argtypes = [vp, vp, vp, ctypes.POINTER(vp)]
         L.jagg_join_shape.argtypes = [ctypes.POINTER(jagg_spec), i64p, i32p, i64p, i64p]
         L.jagg_join_list.argtypes = [vp, ctypes.POINTER(jagg_spec), i64p, i32p, vp, vp]
         L.jagg_capture_begin.argtypes = [vp]
@@ -373,6 +374,30 @@ class PlanGroup:
         arr = (ctypes.c_void_p * len(self.calls))(*[c.plan.value for c in self.calls])
         h = ctypes.c_void_p()
         ctx._check(lib().jagg_plan_group(ctx.handle, len(self.calls), arr, ctypes.byref(h)))
+        self.handle = h
+
+    def run(self):
+        self.ctx._check(lib().jagg_plan_run(self.ctx.handle, self.handle))
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib().jagg_plan_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass
+
+
+class PlanFused:
+    """A sum-of-squares reduce and the RMS-scale map that reads it, run as
+    one pass (jagg_plan_fuse).  Raises JaggError (status -4, unsupported)
+    when the pair does not have that form.  The calls (and their relations
+    and workspaces) must stay alive."""
+
+    def __init__(self, ctx: Context, first: "EinsumCall", second: "EinsumCall"):
+        self.ctx, self.calls = ctx, [first.prepare(), second.prepare()]
+        h = ctypes.c_void_p()
+        ctx._check(lib().jagg_plan_fuse(ctx.handle, first.plan, second.plan, ctypes.byref(h)))
         self.handle = h
 
     def run(self):

@@ -5,9 +5,11 @@ call per step on the context's stream; nothing is computed in Python.  By
 default every einsum step is a prepared plan (jagg_plan_create at set-up:
 host planning and join once; jagg_plan_run per step), and consecutive
 einsum steps that do not read each other's outputs run as one plan group
-(jagg_plan_group: contractions of one form share a launch); ``units`` lists
-what one pass launches.  ``planned=False`` calls jagg_einsum for every step
-instead.
+(jagg_plan_group: contractions of one form share a launch), and a
+sum-of-squares reduce followed by the RMS-scale map that reads it runs as
+one fused plan (jagg_plan_fuse) where the pair has the form that allows it
+(``fuse_norms``); ``units`` lists what one pass launches.  ``planned=False``
+calls jagg_einsum for every step instead.
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ from .inputs import Relayout, Step, Workload
 
 
 class ChainRunner:
-    def __init__(self, ctx: jagg.Context, w: Workload, dense: dict, planned: bool = True):
+    def __init__(self, ctx: jagg.Context, w: Workload, dense: dict, planned: bool = True, fuse_norms: bool = True):
         self.ctx, self.w, self.planned = ctx, w, planned
         dev = f"cuda:{ctx.device}"
         self.rel: dict[str, jagg.Relation] = {}
@@ -61,6 +63,17 @@ class ChainRunner:
         i = 0
         while i < len(self.calls):
             kind, obj, name = self.calls[i]
+            if planned and fuse_norms and self._norm_pair(i):
+                try:
+                    fused = jagg.PlanFused(ctx, obj, self.calls[i + 1][1])
+                except jagg.JaggError as e:
+                    if e.status != -4:  # anything but "unsupported form" is an error
+                        raise
+                    fused = None
+                if fused is not None:
+                    self.units.append(("fused", fused, [i, i + 1]))
+                    i += 2
+                    continue
             j = i + 1
             if planned and kind == "einsum":
                 written = {name}
@@ -77,13 +90,22 @@ class ChainRunner:
                 self.units.append((kind, obj, [i]))
             i = j
 
+    def _norm_pair(self, i: int) -> bool:
+        """Steps i and i+1 are a sum of squares and the RMS-scale map that
+        reads it together with the same input."""
+        if i + 1 >= len(self.calls) or self.calls[i][0] != "einsum" or self.calls[i + 1][0] != "einsum":
+            return False
+        a, b = self.w.chain[i], self.w.chain[i + 1]
+        return ((a.g, a.agg, b.g, b.agg) == ("square", "sum", "rms_scale", "none")
+                and list(b.ins[:2]) == [a.ins[0], a.out])
+
     def run(self):
         for u in range(len(self.units)):
             self.run_unit(u)
 
     def run_unit(self, u: int):
         kind, obj, steps = self.units[u]
-        if kind == "group":
+        if kind in ("group", "fused"):
             obj.run()
         else:
             self.run_step(steps[0])

@@ -35,7 +35,9 @@ def test_planned_chain_equals_unplanned(ctx, fused):
                       fused_attention=fused)
     dense = I.generate(w)
     eager = ChainRunner(ctx, w, dense, planned=False)
-    planned = ChainRunner(ctx, w, dense, planned=True)
+    # the fused RMS-norm pair adds its row sums in another order; planning
+    # alone must change nothing
+    planned = ChainRunner(ctx, w, dense, planned=True, fuse_norms=False)
     for r in (eager, planned):
         for _ in range(2):
             r.run()
