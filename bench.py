@@ -126,7 +126,13 @@ def unit_info(run: ChainRunner, w: I.Workload, u: int):
     name = "+".join(st.out for st in sts)
     op = " | ".join(st.spec if isinstance(st, I.Step) else f"relayout->{st.letters}" for st in sts)
     f = sum(spec_flops(st, w.extents) if isinstance(st, I.Step) else 0.0 for st in sts)
-    by = sum(spec_bytes(run, st, w.extents) for st in sts)
+    if run.units[u][0] == "fused":
+        # one pass: each relation the pair touches moves once (x and the
+        # scale read, the row statistic and the output written)
+        names = {n for st in sts for n in list(st.ins) + [st.out]}
+        by = sum(math.prod(run.rel[n].extents) * jagg.ESZ[run.rel[n].dtype] for n in names)
+    else:
+        by = sum(spec_bytes(run, st, w.extents) for st in sts)
     return name, op, f, by, sts
 
 
