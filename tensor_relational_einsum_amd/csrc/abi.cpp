@@ -904,6 +904,8 @@ struct Bound {
   jagg_relation shadow[kMaxIn];
   bool needs_reblock[kMaxIn];
   size_t list_bytes, counts_bytes, reblock_bytes[kMaxIn], total;
+  int split = 1;            // parts of a split contraction walk (1: none)
+  size_t split_bytes = 0;   // workspace for their fp32 partial sums
   JoinArgs join;
 };
 
@@ -1008,6 +1010,69 @@ jagg_status bind_intervals(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relati
   return JAGG_OK;
 }
 
+// Parts of a contraction's walk over (joined tuple, K-step of 32) run by
+// separate workgroups when its 256 x 256 tiles fill the chip's 256 CUs in
+// few or ragged waves (a chain product with a thin output and a deep
+// reduction): each part writes fp32 partial sums and a sum kernel adds them
+// in order.  The count minimises a cost in units of one K-step of a tile:
+// waves(tiles x S) x (steps / S + 8 for a workgroup's start and end), plus,
+// for S > 1, the partials written and read again (8 S bytes per output
+// element, about 3 MB per unit at the copy rate).  At least 16 steps a part.
+int split_parts(int64_t tiles, int64_t steps, int64_t out_elems) {
+  constexpr int64_t kCUs = 256;
+  if (tiles <= 0 || steps <= 0) return 1;
+  double best = 0.0;
+  int best_s = 1;
+  for (int S = 1; S <= 16; S *= 2) {
+    if (S > 1 && steps / S < 16) break;
+    double t = double((tiles * S + kCUs - 1) / kCUs) * (double(steps) / S + 8.0);
+    if (S > 1) t += 8.0 * S * double(out_elems) / 3.0e6;
+    if (S == 1 || t < best) {
+      best = t;
+      best_s = S;
+    }
+  }
+  return best_s;
+}
+
+// The split of a bf16 MUL / SUM contraction without a causal or segment pair
+// or interval letters, counted as the 256 x 256 kernel tiles it (the kernel
+// may still decline, e.g. for operands without 16-byte vectors; the space
+// then goes unused).
+void plan_split(const jagg_spec *sp, const jagg_relation *const *in, int n_in, Bound &b) {
+  b.split = 1;
+  b.split_bytes = 0;
+  if (n_in != 2 || sp->g != JAGG_G_MUL || sp->agg != JAGG_AGG_SUM || sp->causal_s || sp->seg_s) return;
+  if (in[0]->dt != JAGG_BF16 || in[1]->dt != JAGG_BF16) return;
+  for (int c = 0; c < 26; ++c)
+    if (b.iv_letter[c]) return;
+  const Spec &p = b.p;
+  if (p.reduced.empty()) return;
+  auto e = [&](char c) { return (b.L.n[c - 'a'] + b.L.k[c - 'a'] - 1) / b.L.k[c - 'a']; };
+  int64_t M = 1, N = 1, Bt = 1, K = 1, be_out = 1;
+  bool m_any = false, n_any = false;
+  for (char c : p.reduced) {
+    if (p.in[0].find(c) == std::string::npos || p.in[1].find(c) == std::string::npos) return;
+    K *= e(c);
+  }
+  for (char c : p.out) {
+    const bool i0 = p.in[0].find(c) != std::string::npos, i1 = p.in[1].find(c) != std::string::npos;
+    if (i0 && i1) Bt *= e(c);
+    else if (i0) M *= e(c), m_any = true;
+    else N *= e(c), n_any = true;
+    be_out *= e(c);
+  }
+  if (!m_any || !n_any || M < 256 || N < 256) return;
+  const int64_t tiles = b.join.n_keys * Bt * ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t steps = int64_t(b.join.per_key) * ((K + 31) / 32);
+  const int64_t out_elems = b.join.n_keys * be_out;
+  if (out_elems >= (int64_t(1) << 29)) return;  // each part addressed with 32-bit byte offsets
+  const int S = split_parts(tiles, steps, out_elems);
+  if (S <= 1) return;
+  b.split = S;
+  b.split_bytes = align256(size_t(S) * size_t((out_elems + 63) / 64 * 64) * 4);
+}
+
 jagg_status bind(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const *in, int n_in,
                  const int32_t *blockings, Bound &b) {
   if (!sp || !in || !blockings) return fail(ctx, JAGG_E_INVALID, "NULL argument");
@@ -1068,6 +1133,8 @@ jagg_status bind(jagg_ctx *ctx, const jagg_spec *sp, const jagg_relation *const 
       b.total += b.reblock_bytes[j];
     }
   }
+  plan_split(sp, in, n_in, b);
+  b.total += b.split_bytes;
   return JAGG_OK;
 }
 
@@ -1551,6 +1618,13 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
       if (ib < ob + on && ob < ib + inn) return fail(ctx, JAGG_E_INVALID, "out relation overlaps input %d", j);
     }
   }
+  if (noalloc) {
+    // the static scratch is sized for join lists and re-blocked inputs:
+    // split walks take no part of it
+    b.total -= b.split_bytes;
+    b.split = 1;
+    b.split_bytes = 0;
+  }
   if (noalloc && b.total > ws_bytes)
     return fail(ctx, JAGG_E_WORKSPACE, "the call needs %zu bytes of workspace; the static scratch holds %zu",
                 b.total, ws_bytes);
@@ -1637,7 +1711,17 @@ jagg_status build_call(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation
     const int F = P.dtype ? 8 : 4;
     const int BNt = ca.epi == 2 ? 128 : 256;
     const int64_t big_tiles = ca.n_keys * ca.batch * int64_t((ca.M + 255) / 256) * ((ca.N + BNt - 1) / BNt);
-    P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= BNt && big_tiles >= 256 && !ca.causal_red;
+    // a split walk: the partial sums go after the join list and any
+    // re-blocked inputs in the workspace (bind sized it)
+    if (b.split > 1 && P.dtype && P.va == 8 && P.vb == 8 && ca.epi == 0 && !ca.causal_red && !ca.causal_out &&
+        ca.M >= 256 && ca.N >= 256 && (reinterpret_cast<uintptr_t>(out->buf) & 15) == 0) {
+      ca.split = b.split;
+      ca.part = reinterpret_cast<float *>(ws + off);
+      ca.part_stride = (int64_t(out->n_tuples) * out->be + 63) / 64 * 64;
+    }
+    // (a split walk fills the chip with its parts)
+    P.big = P.va == F && P.vb == F && ca.M >= 256 && ca.N >= BNt && (big_tiles >= 256 || ca.split > 1) &&
+            !ca.causal_red;
     // SWIGLU has only the 256 x 128 pipeline, which bounds-checks ragged M
     // and N, so it takes it at any size (the size rule above only picks the
     // faster kernel)
@@ -1710,6 +1794,7 @@ bool same_contraction_form(const PlannedCall &x, const PlannedCall &y) {
   u.counts = v.counts = nullptr;
   u.X = v.X = nullptr;
   u.B2 = v.B2 = nullptr;
+  u.part = v.part = nullptr;
   return memcmp(&u, &v, sizeof(u)) == 0;
 }
 
@@ -1736,9 +1821,12 @@ jagg_status launch_kernel(jagg_ctx *ctx, const PlannedCall &P) {
     const hipError_t e = P.dtype ? launch_contract_bf16(P.ca, ob, P.akc, P.bkc, P.va, P.vb, P.big, ctx->stream, &which)
                                  : launch_contract_f32(P.ca, ob, P.akc, P.bkc, P.va, P.vb, P.big, ctx->stream, &which);
     if (ctx->trace)
-      fprintf(stderr, "[jagg] %s: contract %s, %lld keys x %d batch\n", e_name, which, (long long)P.ca.n_keys,
-              P.ca.batch);
-    return after_launch(ctx, e, "contract");
+      fprintf(stderr, "[jagg] %s: contract %s%s, %lld keys x %d batch\n", e_name, which,
+              P.ca.split > 1 ? ", split walk" : "", (long long)P.ca.n_keys, P.ca.batch);
+    if (P.ca.split > 1 && ctx->trace) fprintf(stderr, "[jagg] %s: walk in %d parts, then their sum\n", e_name, P.ca.split);
+    jagg_status st = after_launch(ctx, e, "contract");
+    if (st != JAGG_OK || P.ca.split <= 1) return st;
+    return after_launch(ctx, launch_split_sum(P.ca, ob, P.ca.n_keys * P.ca.beC, ctx->stream), "split sum");
   }
   const char *which = "";
   const hipError_t e = launch_ew(ctx, P.ew, P.agg, &which);
@@ -2113,7 +2201,7 @@ jagg_status jagg_plan_group(jagg_ctx *ctx, int n, const jagg_plan *const *plans,
     done[i] = true;
     const bool groupable = calls[i]->kind == PlannedCall::CONTRACT && calls[i]->dtype == 1 && calls[i]->big &&
                            calls[i]->va == 8 && calls[i]->vb == 8 && !calls[i]->ca.causal_red &&
-                           (calls[i]->ca.epi == 0 || calls[i]->akc);
+                           (calls[i]->ca.epi == 0 || calls[i]->akc) && calls[i]->ca.split <= 1;
     for (size_t j = i + 1; groupable && j < calls.size() && int(L.size()) < kMaxGroup; ++j)
       if (!done[j] && same_contraction_form(*calls[i], *calls[j])) {
         L.push_back(int(j));

@@ -3,6 +3,47 @@
 #include "contract_dma.h"
 
 namespace jagg {
+namespace {
+typedef float sum_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int sum_u32x2 __attribute__((ext_vector_type(2)));
+
+// The parts of a split walk added in part order, scaled by alpha and
+// written as C: four consecutive elements per thread (every element of the
+// output relation, padding included, is one of some tile's).
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict__ part, int S, int64_t stride,
+                                                        void *__restrict__ out, int out_bf16, float alpha,
+                                                        int64_t n) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 4 <= n) {
+    sum_f32x4 s = *reinterpret_cast<const sum_f32x4 *>(part + i);
+    for (int q = 1; q < S; ++q) s += *reinterpret_cast<const sum_f32x4 *>(part + q * stride + i);
+    s *= alpha;
+    if (out_bf16)
+      *reinterpret_cast<sum_u32x2 *>(static_cast<uint16_t *>(out) + i) =
+          sum_u32x2{pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
+    else
+      *reinterpret_cast<sum_f32x4 *>(static_cast<float *>(out) + i) = s;
+    return;
+  }
+  for (int64_t j = i; j < n; ++j) {
+    float s = part[j];
+    for (int q = 1; q < S; ++q) s += part[q * stride + j];
+    s *= alpha;
+    if (out_bf16) static_cast<uint16_t *>(out)[j] = f32_to_bf16(s);
+    else static_cast<float *>(out)[j] = s;
+  }
+}
+}  // namespace
+
+hipError_t launch_split_sum(const ContractArgs &a, int out_bf16, int64_t n_out, hipStream_t st) {
+  if (a.split <= 1 || !a.part || n_out > a.part_stride) return hipErrorInvalidValue;
+  const int64_t blocks = (n_out + 1023) / 1024;
+  hipLaunchKernelGGL(split_sum_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, a.part, int(a.split), a.part_stride,
+                     a.C, out_bf16, a.alpha, n_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_contract_bf16(const ContractArgs &a, int out_bf16, bool a_kc, bool b_kc, int va, int vb, bool big,
                                 hipStream_t st, const char **which) {
   // 256x256 tiles over 16-byte vectors without a causal mask on the reduced

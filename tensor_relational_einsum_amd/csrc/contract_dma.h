@@ -114,8 +114,10 @@ struct DmaOperand {
 // EPI: the recompose map, fixed per instantiation so that the epilogue
 // unrolls with the accumulators in registers: 0 none, 1 / 2 add an f32 /
 // bf16 addend laid out as C (MUL_PLUS), 3 SwiGLU.
-template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
+// SPLIT: one part of a split walk (EPI 0 only; see ContractArgs::split).
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0, bool SPLIT = false>
 __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
+  static_assert(!SPLIT || EPI == 0, "a split walk has no recompose map");
   constexpr bool SW = EPI == 3;
   // bf16 outputs: accumulators transposed (B fragment first), stored in
   // 8-byte column groups; f32 outputs keep the plain layout, whose element
@@ -130,6 +132,12 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   __shared__ __attribute__((aligned(1024))) char smem[NS * 2 * kDmaTileBytes];
   auto stage = [&](int s) { return smem + (s % NS) * (2 * kDmaTileBytes); };
 
+  // split walk: part q of the tile (the parts' tiles numbered part-major)
+  int part = 0;
+  if constexpr (SPLIT) {
+    part = __builtin_amdgcn_readfirstlane(int(w / p.n_tiles));
+    w -= int64_t(part) * p.n_tiles;
+  }
   int tn, tm, bt;
   int64_t key;
   decode_tile(p, w, tm, tn, bt, key);
@@ -142,7 +150,13 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
 
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = (p.K + BK - 1) / BK;
-  const int steps = cnt * KT;
+  int steps = cnt * KT, s_begin = 0;
+  if constexpr (SPLIT) {
+    // uniform values the compiler cannot prove uniform through the
+    // divisions: the buffer resources built from them must be scalar
+    s_begin = __builtin_amdgcn_readfirstlane(int(int64_t(steps) * part / p.split));
+    steps = __builtin_amdgcn_readfirstlane(int(int64_t(steps) * (part + 1) / p.split)) - s_begin;
+  }
   const int64_t a_org = int64_t(bt) * p.sAb + int64_t(m0) * p.sAm;
   const int64_t b_org = int64_t(bt) * p.sBb + int64_t(n0) * p.sBn;
   int64_t ks = 0;
@@ -164,9 +178,13 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // stepped by a constant: the per-step work stays a few scalar adds, which
   // issue in the shadow of one MFMA instead of idling the matrix core.
   int ld = 0, le = 0, lkt = 0;
-  int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
+  if constexpr (SPLIT) {
+    le = __builtin_amdgcn_readfirstlane(s_begin / KT);
+    lkt = s_begin - le * KT;
+  }
+  int64_t la = ents[le * p.ent_w + p.a_slot], lb = ents[le * p.ent_w + p.b_slot];
   i32x4_rsrc rs_a, rs_b, rs_b2;  // resources of the step being loaded (rs_b2: SwiGLU's B2)
-  int k_left = 0, k_next = p.K;
+  int k_left = 0, k_next = p.K - lkt * BK;
   char *ld_buf = smem;
   const int64_t a_step = int64_t(BK) * p.sAk * 2, b_step = int64_t(BK) * p.sBk * 2;
   uint64_t pa, pb;  // byte addresses of the next step's origins
@@ -178,6 +196,12 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
     nb = (p.beB - b_org) * 2;
   };
   tuple_origin();
+  if constexpr (SPLIT) {  // a part starting inside a joined tuple's K walk
+    pa += uint64_t(int64_t(lkt) * a_step);
+    pb += uint64_t(int64_t(lkt) * b_step);
+    na -= int64_t(lkt) * a_step;
+    nb -= int64_t(lkt) * b_step;
+  }
   auto prep = [&](char *buf) {
     const bool live = ld < steps;
     rs_a = dma_rsrc(reinterpret_cast<const void *>(pa), live ? na : 0);
@@ -397,7 +421,15 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   // the zero-fill loads past the last step may still be in flight: let them
   // land before the workgroup's LDS can be handed to another workgroup
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (SW && TR) {
+  if constexpr (SPLIT) {
+    // one part of a split walk: its fp32 sums, laid out as C, into the
+    // part's slice of the workspace (the sum kernel applies alpha)
+    ContractArgs q = p;
+    q.C = p.part + int64_t(part) * p.part_stride;
+    q.alpha = 1.0f;
+    if constexpr (TR) store_tile_t<0, TM, TN, 0>(q, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+    else store_tile_plain<0, TM, TN>(q, acc, ents[0], bt, key, ks, m0 + wm, n0 + wn, lane);
+  } else if constexpr (SW && TR) {
     // recompose: silu(A B) * (A B2), fragments j and j + 2 hold one column
     // range; transposed accumulators (B fragment first in the MFMA): group g
     // of lane l is row 32 i + l % 32, columns 32 j + 8 g + 4 (l / 32) + 0..3
@@ -474,10 +506,10 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
   }
 }
 
-template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0>
+template <int OUT_BF16, bool A_KC, bool B_KC, int NS, int EPI = 0, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void contract_dma_kernel(
     const ContractArgs p) {
-  dma_tile<OUT_BF16, A_KC, B_KC, NS, EPI>(p, logical_tile(p.remap));
+  dma_tile<OUT_BF16, A_KC, B_KC, NS, EPI, SPLIT>(p, logical_tile(p.remap));
 }
 
 // Several independent contractions of one geometry (every field of `common`
@@ -534,8 +566,15 @@ static hipError_t launch_dma(const ContractArgs &a, hipStream_t st) {
   ContractArgs b = a;
   b.tiles_m = (a.M + 255) / 256;
   b.tiles_n = EPI == 3 ? (a.N + 127) / 128 : (a.N + 255) / 256;
-  const int64_t grid = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
-  hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES, EPI>), dim3(unsigned(grid)), dim3(256), 0,
+  b.n_tiles = b.n_keys * b.batch * int64_t(b.tiles_m) * b.tiles_n;
+  if constexpr (EPI == 0) {
+    if (a.split > 1) {
+      hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES, 0, true>),
+                         dim3(unsigned(b.n_tiles * a.split)), dim3(256), 0, st, b);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((contract_dma_kernel<OB, AK, BKC, JAGG_DMA_STAGES, EPI>), dim3(unsigned(b.n_tiles)), dim3(256), 0,
                      st, b);
   return hipGetLastError();
 }

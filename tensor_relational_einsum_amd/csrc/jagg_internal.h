@@ -203,7 +203,17 @@ struct ContractArgs {
   const void *X;
   int32_t x_bf16;
   const void *B2;
+  // split walk (split > 1, bf16 256 x 256 tiles, no recompose map): part q
+  // of a tile walks steps [q steps / split, (q + 1) steps / split) of its
+  // (joined tuple, K-step) walk and writes fp32 sums, laid out as C, at
+  // part + q * part_stride; launch_split_sum then adds the parts in order,
+  // scales by alpha and writes C.  n_tiles: tiles of one part.
+  int32_t split;
+  int64_t n_tiles;
+  float *part;
+  int64_t part_stride;
 };
+hipError_t launch_split_sum(const ContractArgs &a, int out_bf16, int64_t n_out, hipStream_t st);
 // Independent contractions of one geometry run as one launch of the bf16
 // 256 x 256 LDS-pipelined kernel: `common` holds the shared geometry, the
 // arrays each problem's addresses.
