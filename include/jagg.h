@@ -230,9 +230,12 @@ jagg_status jagg_relation_destroy(jagg_relation *rel);
 jagg_status jagg_repartition(jagg_ctx *ctx, const jagg_relation *src, jagg_relation *dst);
 
 /* Bytes of device workspace jagg_einsum needs for this call (join list,
- * key counts, and room for re-blocking any input whose blocking differs
- * from `blockings`). `blockings` gives the block count of every letter of
- * the spec, in order of first appearance in the einsum string. */
+ * key counts, room for re-blocking any input whose blocking differs from
+ * `blockings`, and, for a bf16 MUL / SUM contraction whose output tiles
+ * fill the GPU in few or ragged waves, the fp32 partial sums of its split
+ * walk: see step (2) of jagg_einsum). `blockings` gives the block count of
+ * every letter of the spec, in order of first appearance in the einsum
+ * string. */
 jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const jagg_relation *const *in,
                                   int n_in, const int32_t *blockings, size_t *bytes);
 
@@ -242,7 +245,13 @@ jagg_status jagg_einsum_workspace(jagg_ctx *ctx, const jagg_spec *spec, const ja
  *   (1) join: the join-enumeration kernel lists, for every output key, the
  *       input tuples that agree on every shared letter;
  *   (2) each joined tuple goes through g and is aggregated into its output
- *       key, accumulation in fp32 (MFMA for contractions);
+ *       key, accumulation in fp32 (MFMA for contractions).  A bf16 MUL /
+ *       SUM contraction (no causal or segment pair, no recompose map) whose
+ *       256 x 256 output tiles would fill the GPU in few or ragged waves
+ *       splits each tile's walk over its joined tuples and K into parts
+ *       run side by side; their fp32 partial sums go to the workspace and
+ *       a second kernel adds them in part order (Def. 3.7: the SUM is
+ *       associative and commutative, so only the rounding order changes);
  *   (3) recompose: the output relation `out` (letters of the spec's output,
  *       blocked by `blockings`, dtype spec->out_dtype) is written in place,
  *       padding +0.
@@ -323,8 +332,10 @@ jagg_status jagg_plan_fuse(jagg_ctx *ctx, const jagg_plan *first, const jagg_pla
  * of JAGG_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
  * runs on until the process ends (its address is fetched once per device,
  * in jagg_ctx_create).  It allocates nothing.
- * A call whose workspace (jagg_einsum_workspace) exceeds the scratch is
- * refused with JAGG_E_WORKSPACE before any launch.  Nothing in the scratch
+ * It never splits a contraction's walk (step (2) of jagg_einsum), so its
+ * workspace is jagg_einsum_workspace less the room for split partial sums; a
+ * call whose workspace exceeds the scratch is refused with JAGG_E_WORKSPACE
+ * before any launch.  Nothing in the scratch
  * needs clearing between calls: the join kernel writes every list slot and
  * key count, and a re-blocking copy writes every byte it later reads.
  * Every call on one GPU shares that GPU's scratch: calls that may overlap on
