@@ -152,27 +152,44 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const AttnArgs a) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   // workgroup -> (batch index inside the block, output key, s tile).  With
-  // xcd_group, the workgroups of one batch index (which share its K and V)
-  // are numbered so that they all land on one XCD: dispatch deals
-  // workgroups to the 8 XCDs round-robin, each XCD with its own L2.
+  // xcd_group (non-causal launches), the workgroups of one batch index
+  // (which share its K and V) are numbered so that they all land on one
+  // XCD: dispatch deals workgroups to the 8 XCDs round-robin, each XCD with
+  // its own L2.  Causal launches are ordered by work instead (below).
   uint32_t w = blockIdx.x;
-  if (a.xcd_group) {
+  if (a.xcd_group && !a.reverse) {
     const uint32_t xcd = w & 7u, local = w >> 3;
     const uint32_t grp = fd_div(local, a.div_group);
     w = (grp * 8u + xcd) * a.div_group.d + (local - grp * a.div_group.d);
   }
-  uint32_t st = fd_mod(w, a.div_st);
-  if (a.reverse) st = a.div_st.d - 1 - st;  // causal: later row tiles walk more keys, so they go first
-  w = fd_div(w, a.div_st);
-  const uint32_t kq = w % uint32_t(a.n_keys);
-  const uint32_t bi = w / uint32_t(a.n_keys);
-  uint32_t key = kq;
+  uint32_t st, bi, key;
   if (a.reverse) {
-    // causal: a key's work grows with its s-block, so launch the keys by
-    // s-block, heaviest first (key = (hi * ks + kappa_s) * Ws + lo)
-    const uint32_t sb = fd_div(kq, a.div_per_s), rest = kq - sb * a.div_per_s.d;
+    // causal: a workgroup walks more keys the later its rows, so every
+    // workgroup of one work class is dispatched before any lighter one,
+    // across all batch indices and keys (the longest first, which keeps the
+    // launch's tail short).  Class: s-block, then s-tile; packed sequences:
+    // s-tile, then s-block, each sequence starting its causal walk at its
+    // own first row
+    const uint32_t minor_n = uint32_t(a.nbatch) * a.div_per_s.d;
+    const uint32_t cls = w / minor_n, minor = w - cls * minor_n;
+    const uint32_t ks = a.div_ks.d, nst = a.div_st.d;
+    uint32_t sb;
+    if (a.iv) {
+      st = nst - 1 - cls / ks;
+      sb = cls % ks;
+    } else {
+      sb = ks - 1 - cls / nst;
+      st = nst - 1 - cls % nst;
+    }
+    bi = minor / a.div_per_s.d;
+    const uint32_t rest = minor - bi * a.div_per_s.d;
     const uint32_t hi = fd_div(rest, a.div_Ws), lo = rest - hi * a.div_Ws.d;
-    key = (hi * a.div_ks.d + (a.div_ks.d - 1 - sb)) * a.div_Ws.d + lo;
+    key = (hi * ks + sb) * a.div_Ws.d + lo;
+  } else {
+    st = fd_mod(w, a.div_st);
+    w = fd_div(w, a.div_st);
+    key = w % uint32_t(a.n_keys);
+    bi = w / uint32_t(a.n_keys);
   }
   const int32_t cnt = a.counts[key];
   // the join list is read-only for the kernel's lifetime: reading it through
