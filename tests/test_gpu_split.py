@@ -130,3 +130,47 @@ def test_split_walk_plan_and_graph_replays(sctx, capfd):
         torch.cuda.synchronize()
         assert torch.equal(call.out.data, eager)
     g.close()
+
+
+def test_split_walk_with_a_reblocked_input(ctx, capfd):
+    # A arrives blocked (i 2, j 2) while the spec asks (i 1, j 3): the
+    # re-blocked copy and the partial sums share the workspace
+    ext, blk = dict(i=512, j=7704, k=512), dict(i=1, j=3, k=1)
+    gens = I.streams(17, 2)
+    a = I.draw(gens[0], [512, 7704], "normal", "bf16")
+    b = I.draw(gens[1], [7704, 512], "normal", "bf16", 1.0 / np.sqrt(7704))
+    A = jagg.from_dense(ctx, a.to("cuda"), "ij", dict(i=2, j=2))
+    B = jagg.from_dense(ctx, b.to("cuda"), "jk", blk)
+    call = jagg.EinsumCall(ctx, "ij,jk->ik", [A, B], blk, g="mul", agg="sum", out_dtype="f32")
+    call.workspace.fill_(0x5A)
+    capfd.readouterr()
+    call.run()
+    torch.cuda.synchronize()
+    trace = capfd.readouterr().err
+    assert "reblock input 0" in trace and "walk in 8 parts" in trace, trace
+    want = O.dense("ij,jk->ik", [to_np(a), to_np(b)], ext, g="mul", agg="sum")
+    got = O.from_relation(to_np(call.out.data), "ik", ext, blk)
+    assert normwise_err(got, want) < 1e-5
+
+
+def test_noalloc_runs_the_walk_whole(ctx, capfd):
+    # the no-allocation entry point never splits; its result agrees with the
+    # split call up to the order of the fp32 additions
+    ext, blk = dict(i=512, j=7704, k=512), dict(i=1, j=3, k=1)
+    gens = I.streams(19, 2)
+    a = I.draw(gens[0], [512, 7704], "normal", "bf16")
+    b = I.draw(gens[1], [7704, 512], "normal", "bf16", 1.0 / np.sqrt(7704))
+    A = jagg.from_dense(ctx, a.to("cuda"), "ij", blk)
+    B = jagg.from_dense(ctx, b.to("cuda"), "jk", blk)
+    call = jagg.EinsumCall(ctx, "ij,jk->ik", [A, B], blk, g="mul", agg="sum", out_dtype="f32")
+    capfd.readouterr()
+    call.run()
+    torch.cuda.synchronize()
+    assert "walk in 8 parts" in capfd.readouterr().err
+    split = to_np(call.out.data)
+    whole = jagg.relation_like(ctx, "ik", ext, blk, "f32")
+    capfd.readouterr()
+    call.run_noalloc(whole)
+    torch.cuda.synchronize()
+    assert "split walk" not in capfd.readouterr().err
+    assert normwise_err(to_np(whole.data), split) < 1e-5
