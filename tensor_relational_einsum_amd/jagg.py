@@ -370,8 +370,10 @@ class PlanGroup:
     and workspaces) must stay alive."""
 
     def __init__(self, ctx: Context, calls):
-        self.ctx, self.calls = ctx, [c.prepare() for c in calls]
-        arr = (ctypes.c_void_p * len(self.calls))(*[c.plan.value for c in self.calls])
+        # prepared calls, or fused pairs (PlanFused), which are plans already
+        self.ctx, self.calls = ctx, [c if isinstance(c, PlanFused) else c.prepare() for c in calls]
+        arr = (ctypes.c_void_p * len(self.calls))(
+            *[c.handle.value if isinstance(c, PlanFused) else c.plan.value for c in self.calls])
         h = ctypes.c_void_p()
         ctx._check(lib().jagg_plan_group(ctx.handle, len(self.calls), arr, ctypes.byref(h)))
         self.handle = h

@@ -161,3 +161,41 @@ def test_block_runs_both_norms_fused(ctx):
     for st in w.chain:
         a, b = to_np(fused.rel[st.out].data), to_np(apart.rel[st.out].data)
         assert normwise_err(a, b) < 2e-2, st.out
+
+
+def test_fused_pair_in_a_group_and_refusal_of_a_reblocked_input(ctx):
+    # a fused pair may be a member of a plan group beside an independent plan
+    ext, blk = dict(b=1, s=64, h=1024), dict(b=1, s=2, h=4)
+    x, gam, red, mp = make_pair(ctx, "bsh", ext, blk, "f32", "bf16", "bf16", seed=23)
+    fused = jagg.PlanFused(ctx, red, mp)
+    gens = I.streams(29, 2)
+    a = I.draw(gens[0], [256, 512], "normal", "f32")
+    b = I.draw(gens[1], [512, 192], "normal", "f32")
+    cblk = dict(i=2, j=2, k=2)
+    A = jagg.from_dense(ctx, a.to("cuda"), "ij", cblk)
+    B = jagg.from_dense(ctx, b.to("cuda"), "jk", cblk)
+    mm = jagg.EinsumCall(ctx, "ij,jk->ik", [A, B], cblk)
+    group = jagg.PlanGroup(ctx, [fused, mm])
+    red.out.data.fill_(3)
+    mp.out.data.fill_(3)
+    mm.out.data.fill_(3)
+    group.run()
+    torch.cuda.synchronize()
+    xd, gd = to_np(x), to_np(gam)
+    ss_want = O.round_to(O.dense("bsh->bs", [xd], ext, g="square", agg="sum"), "f32")
+    y_want = O.round_to(O.dense("bsh,bs,h->bsh", [xd, ss_want, gd], ext, g="rms_scale", agg="none",
+                                beta=1.0 / ext["h"], eps=1e-6), "bf16")
+    assert normwise_err(O.from_relation(to_np(red.out.data), "bs", ext, blk), ss_want) < F32_TOL
+    assert normwise_err(O.from_relation(to_np(mp.out.data), "bsh", ext, blk), y_want) < BF16_OUT_TOL
+    mm_want = O.round_to(O.dense("ij,jk->ik", [to_np(a), to_np(b)], dict(i=256, j=512, k=192)), "f32")
+    assert normwise_err(O.from_relation(to_np(mm.out.data), "ik", dict(i=256, j=512, k=192), cblk), mm_want) < F32_TOL
+    # an input blocked otherwise than the spec asks is re-blocked by the plan:
+    # the pair is refused as unsupported (the two plans still run apart)
+    X = jagg.from_dense(ctx, x.to("cuda"), "bsh", dict(b=1, s=4, h=4))
+    G = jagg.from_dense(ctx, gam.to("cuda"), "h", blk)
+    red2 = jagg.EinsumCall(ctx, "bsh->bs", [X], blk, g="square", agg="sum", out_dtype="f32")
+    mp2 = jagg.EinsumCall(ctx, "bsh,bs,h->bsh", [X, red2.out, G], blk, g="rms_scale", agg="none",
+                          out_dtype="bf16", beta=1.0 / ext["h"], eps=1e-6)
+    with pytest.raises(jagg.JaggError) as e:
+        jagg.PlanFused(ctx, red2, mp2)
+    assert e.value.status == -4
