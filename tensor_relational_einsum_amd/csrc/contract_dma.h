@@ -45,12 +45,6 @@
 #ifndef JAGG_DMA_STAGES
 #define JAGG_DMA_STAGES 4
 #endif
-#ifndef JAGG_DMA_WHOLE_STEP
-#define JAGG_DMA_WHOLE_STEP 0
-#endif
-#ifndef JAGG_DMA_ODD
-#define JAGG_DMA_ODD 0
-#endif
 
 #include "contract_impl.h"
 
@@ -183,46 +177,56 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
     lkt = s_begin - le * KT;
   }
   int64_t la = ents[le * p.ent_w + p.a_slot], lb = ents[le * p.ent_w + p.b_slot];
-  i32x4_rsrc rs_a, rs_b, rs_b2;  // resources of the step being loaded (rs_b2: SwiGLU's B2)
-  int k_left = 0, k_next = p.K - lkt * BK;
-  char *ld_buf = smem;
+  int k_next = p.K - lkt * BK;
   const int64_t a_step = int64_t(BK) * p.sAk * 2, b_step = int64_t(BK) * p.sBk * 2;
   uint64_t pa, pb;  // byte addresses of the next step's origins
-  int64_t na, nb;   // bytes from there to the end of the block
+  uint64_t ea, eb;  // byte addresses of the ends of their blocks
   auto tuple_origin = [&]() {
     pa = reinterpret_cast<uint64_t>(p.A) + uint64_t(la * p.beA + a_org) * 2;
     pb = reinterpret_cast<uint64_t>(p.B) + uint64_t(lb * p.beB + b_org) * 2;
-    na = (p.beA - a_org) * 2;
-    nb = (p.beB - b_org) * 2;
+    ea = reinterpret_cast<uint64_t>(p.A) + uint64_t((la + 1) * p.beA) * 2;
+    eb = reinterpret_cast<uint64_t>(p.B) + uint64_t((lb + 1) * p.beB) * 2;
   };
   tuple_origin();
   if constexpr (SPLIT) {  // a part starting inside a joined tuple's K walk
     pa += uint64_t(int64_t(lkt) * a_step);
     pb += uint64_t(int64_t(lkt) * b_step);
-    na -= int64_t(lkt) * a_step;
-    nb -= int64_t(lkt) * b_step;
   }
-  auto prep = [&](char *buf) {
-    const bool live = ld < steps;
-    rs_a = dma_rsrc(reinterpret_cast<const void *>(pa), live ? na : 0);
-    rs_b = dma_rsrc(reinterpret_cast<const void *>(pb), live ? nb : 0);
+  // Each operand has its own load state (resource, valid K, LDS target), so
+  // that the next step's state is built in an MFMA slot of its own while the
+  // other operand's loads of the current step are still being issued.
+  i32x4_rsrc rs_a, rs_b, rs_b2;  // rs_b2: SwiGLU's B2
+  int kl_a = 0, kl_b = 0;
+  char *buf_a = smem, *buf_b = smem;
+  auto prep_a = [&](char *buf) {
+    rs_a = dma_rsrc(reinterpret_cast<const void *>(pa), ld < steps ? int64_t(ea - pa) : 0);
+    kl_a = k_next;
+    buf_a = buf;
+  };
+  auto prep_b = [&](char *buf) {
+    const int64_t nb = ld < steps ? int64_t(eb - pb) : 0;
+    rs_b = dma_rsrc(reinterpret_cast<const void *>(pb), nb);
     // B2 has B's geometry: the same offsets from its own base
     if constexpr (SW)
       rs_b2 = dma_rsrc(reinterpret_cast<const void *>(pb - reinterpret_cast<uint64_t>(p.B) +
                                                       reinterpret_cast<uint64_t>(p.B2)),
-                       live ? nb : 0);
-    k_left = k_next;
-    ld_buf = buf;
+                       nb);
+    kl_b = k_next;
+    buf_b = buf;
   };
-  auto dma_a = [&](int i) { da.issue(i, rs_a, k_left, ld_buf, wave_s); };
+  auto dma_a = [&](int i) { da.issue(i, rs_a, kl_a, buf_a, wave_s); };
   auto dma_b = [&](int i) {
     constexpr int NBH = DmaOperand<B_KC, NT, SW>::NI / 2;
-    if constexpr (SW) db.issue(i, i < NBH ? rs_b : rs_b2, k_left, ld_buf + kDmaTileBytes, wave_s);
-    else db.issue(i, rs_b, k_left, ld_buf + kDmaTileBytes, wave_s);
+    if constexpr (SW) db.issue(i, i < NBH ? rs_b : rs_b2, kl_b, buf_b + kDmaTileBytes, wave_s);
+    else db.issue(i, rs_b, kl_b, buf_b + kDmaTileBytes, wave_s);
   };
+  // straight-line steps; a branch only where a joined tuple's K walk ends
   auto advance = [&]() {
     ++ld;
-    if (++lkt == KT) {
+    k_next -= BK;
+    pa += a_step;
+    pb += b_step;
+    if (__builtin_expect(++lkt == KT, 0)) {
       lkt = 0;
       k_next = p.K;
       if (++le < cnt) {
@@ -230,12 +234,6 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
         lb = ents[le * p.ent_w + p.b_slot];
       }
       tuple_origin();
-    } else {
-      k_next -= BK;
-      pa += a_step;
-      pb += b_step;
-      na -= a_step;
-      nb -= b_step;
     }
   };
   constexpr int NA = DmaOperand<A_KC, NT>::NI, NB = DmaOperand<B_KC, NT, SW>::NI;
@@ -328,94 +326,80 @@ __device__ __forceinline__ void dma_tile(const ContractArgs &p, int64_t w) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // Step s (stage s mod NS), with chunk 0 of its stage already in f0:
-  //   phase A: MFMAs of chunk 0, with the reads of chunk 1 and the second
-  //     half of step s+NS-2's loads (into stage s-2) between them;
+  //   phase A: MFMAs of chunk 0, with the reads of chunk 1 and B's loads of
+  //     step s+NS-2 (into stage s-2) between them; the walk moves to step
+  //     s+NS-1 and A's load state for it is built, each in a free slot;
   //   wait for this wavefront's loads of stage s+1 and for its LDS reads,
   //     barrier (stage s+1 now visible to all; every read of stage s-1,
   //     last read in step s-1, complete);
   //   phase B: MFMAs of chunk 1, with the reads of chunk 0 of stage s+1 and
-  //     the first half of step s+NS-1's loads (into stage s-1) between them.
-  // One wavefront per SIMD issues in order, so memory instructions placed
-  // between MFMAs issue in the MFMA shadow instead of stalling it; spreading
-  // the loads over the step also keeps the vector memory path from being
-  // flooded right after the barrier.  Scheduling barriers pin the order.
+  //     A's loads of step s+NS-1 (into stage s-1) between them; B's load
+  //     state for that step is built in a free slot after them.
+  // One wavefront per SIMD issues in order, about one instruction per four
+  // cycles, so everything placed between two MFMAs issues in the shadow of
+  // the first as long as it fits in its 32 cycles: the reads, the loads and
+  // the walk's scalar bookkeeping each get slots of their own instead of
+  // meeting in one run between the phases.  Spreading the loads over the
+  // step also keeps the vector memory path from being flooded right after
+  // the barrier.  Scheduling barriers pin the order.
   // Stage s-2 is free since step s-1's barrier and stage s-1 since step s's.
   // Past the last step the reads see zero fill or stale data that no MFMA
   // consumes.
   static_assert(TM * TN == 16 && TM + TN <= 8 && NA <= 4 && NB <= 4, "interleave pattern");
-#if JAGG_DMA_WHOLE_STEP
-  // phase B issues all NA + NB loads of the step it prepared, one after
-  // every other MFMA, so both operands' loads get two steps to land
-  auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if constexpr (TR) Mma<uint16_t>::run(acc[k / TN][k % TN], fm.b[k % TN], fm.a[k / TN]);
-      else Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
-      if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
-      if ((k & 1) == JAGG_DMA_ODD && k / 2 < NA + NB) dma(k / 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  constexpr int PRO = NS - 1;  // steps loaded whole before the loop
-  constexpr int PRO_WAIT = (NS - 2) * (NA + NB);
-#else
-  auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma) {
+  auto phase = [&](const Frags &fm, const char *rd_stage, int rd_kc, Frags &fr, auto &&dma, auto &&book) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if constexpr (TR) Mma<uint16_t>::run(acc[k / TN][k % TN], fm.b[k % TN], fm.a[k / TN]);
       else Mma<uint16_t>::run(acc[k / TN][k % TN], fm.a[k / TN], fm.b[k % TN]);
       if (k < TM + TN) read_frag(rd_stage, rd_kc, fr, k);
       if (k >= 8 && (k & 1) == 0 && (k - 8) / 2 < 4) dma((k - 8) / 2);
+      book(k);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  constexpr int PRO = NS - 2;  // steps loaded whole before the loop (plus half of one)
+  constexpr int PRO = NS - 2;  // steps loaded whole before the loop (plus A's half of one)
   constexpr int PRO_WAIT = (NS - 3) * (NA + NB) + NA;
-#endif
 
   Frags f0, f1;
-  // prologue: the first PRO steps whole (and, with split steps, the first
-  // half of step NS-2)
+  // prologue: the first PRO steps whole, then step NS-2's A loads (its B
+  // loads go out in the first phase of the loop)
   for (int s = 0; s < PRO; ++s) {
-    prep(stage(s));
+    prep_a(stage(s));
+    prep_b(stage(s));
 #pragma unroll
     for (int i = 0; i < NA; ++i) dma_a(i);
 #pragma unroll
     for (int i = 0; i < NB; ++i) dma_b(i);
     advance();
   }
-#if !JAGG_DMA_WHOLE_STEP
-  prep(stage(NS - 2));
+  prep_a(stage(NS - 2));
+  prep_b(stage(NS - 2));
 #pragma unroll
   for (int i = 0; i < NA; ++i) dma_a(i);
-#endif
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(PRO_WAIT) : "memory");
 #pragma unroll
   for (int x = 0; x < TM + TN; ++x) read_frag(stage(0), 0, f0, x);
   for (int s = 0; s < steps; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-#if JAGG_DMA_WHOLE_STEP
-    phase(f0, stage(s), 1, f1, [&](int) {});
-#else
-    phase(f0, stage(s), 1, f1, [&](int i) {
-      if (i < NB) dma_b(i);
-    });
-    advance();
-#endif
+    phase(
+        f0, stage(s), 1, f1,
+        [&](int i) {
+          if (i < NB) dma_b(i);
+        },
+        [&](int k) {
+          if (k == 9) advance();
+          if (k == 11) prep_a(stage(s + NS - 1));
+        });
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 3) * (NA + NB)) : "memory");
-    prep(stage(s + NS - 1));
-#if JAGG_DMA_WHOLE_STEP
-    phase(f1, stage(s + 1), 0, f0, [&](int i) {
-      if (i < NA) dma_a(i);
-      else dma_b(i - NA);
-    });
-    advance();
-#else
-    phase(f1, stage(s + 1), 0, f0, [&](int i) {
-      if (i < NA) dma_a(i);
-    });
-#endif
+    phase(
+        f1, stage(s + 1), 0, f0,
+        [&](int i) {
+          if (i < NA) dma_a(i);
+        },
+        [&](int k) {
+          if (k == 13) prep_b(stage(s + NS - 1));
+        });
   }
 
   // the zero-fill loads past the last step may still be in flight: let them
