@@ -223,6 +223,10 @@ LDS_PIPELINE_CASES = [
     ("ji,kj->ik", dict(i=2112, j=208, k=2112), dict(i=8, j=2, k=8), "f32", None),
     # one long K walk per key (K = 528: 16 full steps and a tail of 16)
     ("ij,jk->ik", dict(i=2112, j=528, k=2112), dict(i=8, j=1, k=8), "bf16", None),
+    # every step of the walk is a joined tuple of its own (32-wide K blocks),
+    # and a K tail inside every step (24-wide K blocks)
+    ("ij,jk->ik", dict(i=2112, j=256, k=2112), dict(i=8, j=8, k=8), "bf16", None),
+    ("ji,kj->ik", dict(i=2112, j=192, k=2112), dict(i=8, j=8, k=8), "f32", None),
     # causal pair in the output (mask applied in the epilogue)
     ("bhsd,bhtd->bhst", dict(b=2, h=4, s=1056, t=1056, d=128), dict(b=1, h=1, s=4, t=4, d=1), "f32", ("s", "t")),
 ]

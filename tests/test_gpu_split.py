@@ -4,8 +4,9 @@ fp32 partial sums, and a sum kernel adds the parts in order (JAGG_TRACE
 names the split).  Against the oracle's dense definition on the same bf16
 inputs: 1e-5 normwise for an f32 result, 8e-3 for one bf16 rounding;
 output padding +0.  Cases: parts that start inside a joined tuple and cross
-tuple boundaries, a ragged last K-tile, ragged M and N, a batch letter,
-alpha != 1, and a contraction with enough tiles that takes no split.
+tuple boundaries, parts over one-step tuples, a ragged last K-tile, ragged M
+and N, a batch letter, alpha != 1, and a contraction with enough tiles that
+takes no split.
 """
 import os
 
@@ -45,6 +46,8 @@ CASES = [
     # 3 tuples of 81 K-tiles (2568 = 80 x 32 + 8): 8 parts of about 30 steps
     # that start inside tuples and cross tuple boundaries
     ("ij,jk->ik", dict(i=512, j=7704, k=512), dict(i=1, j=3, k=1), "bf16", 1.0, 8),
+    # 256 joined tuples of one K-step each: every part starts on a tuple
+    ("ij,jk->ik", dict(i=512, j=8192, k=512), dict(i=1, j=256, k=1), "bf16", 1.0, 16),
     # ragged M and N, an f32 result
     ("ij,jk->ik", dict(i=300, j=4096, k=704), dict(i=1, j=1, k=1), "f32", 1.0, 8),
     # a batch letter
