@@ -633,23 +633,32 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
   // used and no step waits on a scalar load
   int le = 0, lkt = 0;  // position of the next load
   int64_t la = ents[p.a_slot], lb = ents[p.b_slot];
+  // ids of the tuple after the current one (the last one's, at the end)
+  int64_t la_n = ents[(cnt > 1 ? 1 : 0) * p.ent_w + p.a_slot], lb_n = ents[(cnt > 1 ? 1 : 0) * p.ent_w + p.b_slot];
   int pe = 0, pk0 = 0;  // position of the load in flight (for the causal mask)
-  auto load_next = [&](TA &xa, TB &xb) {
+  // live = false: a step past the walk's end, loaded from an empty buffer
+  // (every lane reads zeros, no memory is touched)
+  auto load_next = [&](TA &xa, TB &xb, bool live = true) {
     const int k0 = lkt * BK;
     pe = le;
     pk0 = k0;
     const int64_t ao = a_org + int64_t(k0) * p.sAk, bo = b_org + int64_t(k0) * p.sBk;
     const T *pa = reinterpret_cast<const T *>(p.A) + la * p.beA + ao;
     const T *pb = reinterpret_cast<const T *>(p.B) + lb * p.beB + bo;
-    xa.load(tile_rsrc(pa, (p.beA - ao) * ESZ), p.M - m0, p.K - k0);
-    xb.load(tile_rsrc(pb, (p.beB - bo) * ESZ), p.N - n0, p.K - k0);
-    if (++lkt == KT) {
-      lkt = 0;
-      if (++le < cnt) {
-        la = ents[le * p.ent_w + p.a_slot];
-        lb = ents[le * p.ent_w + p.b_slot];
-      }
-    }
+    xa.load(tile_rsrc(pa, live ? (p.beA - ao) * ESZ : 0), p.M - m0, p.K - k0);
+    xb.load(tile_rsrc(pb, live ? (p.beB - bo) * ESZ : 0), p.N - n0, p.K - k0);
+    // Branch-free step of the walk: the next tuple's ids are read one call
+    // ahead and taken where the current tuple's K walk ends, by arithmetic on
+    // the 0/1 wrap flag.  A branch here splits the loop body, and the
+    // accumulators are then copied out of and back into AGPRs on every step.
+    const int wrap = int(lkt + 1 == KT);
+    lkt = (lkt + 1) * (1 - wrap);
+    le += wrap;
+    la += int64_t(wrap) * (la_n - la);
+    lb += int64_t(wrap) * (lb_n - lb);
+    const int e_n = min(le + 1, cnt - 1);
+    la_n = ents[e_n * p.ent_w + p.a_slot];
+    lb_n = ents[e_n * p.ent_w + p.b_slot];
   };
   // causal pair with t reduced: zero A where t > s, on the diagonal block only;
   // applied just before the LDS store so the loads stay in flight meanwhile
@@ -724,6 +733,12 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
     xb.store(lds + A_BYTES);
   };
 
+  // fp32 operands with two stages and no causal mask on the reduced letter
+  // keep two register sets: step s+2's loads are issued before step s
+  // computes, so a load has two steps of MFMA work to land instead of one
+  // (fp32 operands are twice the bytes per FLOP of bf16, and a large A
+  // streams from HBM rather than from the Infinity Cache)
+  constexpr bool PF2 = NSTG == 2 && !MASK && ESZ == 4;
   if constexpr (NSTG == 1) {
     for (int s = 0; s < steps; ++s) {
       load_next(ta[0], tb[0]);
@@ -731,6 +746,36 @@ __attribute__((amdgpu_waves_per_eu(NSTG == 1 ? 4 : 1))) void contract_kernel(con
       __syncthreads();
       compute(smem);
       __syncthreads();
+    }
+  } else if constexpr (PF2) {
+    // step j is loaded into set j % 2; every iteration issues the same loads
+    // (past the walk's end from an empty buffer) and stores one set, so the
+    // waits the compiler places before a store cover only the older set
+    TA ta1;
+    TB tb1;
+    ta1.init(p.sAm, p.sAk);
+    tb1.init(p.sBn, p.sBk);
+    load_next(ta[0], tb[0]);
+    load_next(ta1, tb1, steps > 1);
+    store_step(ta[0], tb[0], smem);
+    __syncthreads();
+    // iteration s (parity P): the set of parity P is free (step s is in
+    // stage P); it takes step s+2's loads while stage P computes, then the
+    // other set (step s+1) goes to stage P ^ 1, last read in iteration s-1
+    auto iter = [&](auto par, int s) {
+      constexpr int P = decltype(par)::value;
+      TA &fa = P ? ta1 : ta[0];
+      TB &fb = P ? tb1 : tb[0];
+      TA &na = P ? ta[0] : ta1;
+      TB &nb = P ? tb[0] : tb1;
+      load_next(fa, fb, s + 2 < steps);
+      compute(smem + P * STAGE);
+      store_step(na, nb, smem + (P ^ 1) * STAGE);
+      __syncthreads();
+    };
+    for (int s = 0; s < steps; s += 2) {
+      iter(std::integral_constant<int, 0>{}, s);
+      if (s + 1 < steps) iter(std::integral_constant<int, 1>{}, s + 1);
     }
   } else {
     load_next(ta[0], tb[0]);
